@@ -1,0 +1,159 @@
+"""Lookahead gather with two ping-pong slots -- oracle (test infrastructure only).
+
+Weight-sharding page (zdszero.github.io):
+* section "lookahead and ping-pong slot": while layer l computes, the gather
+  of layer l+1 is issued on a side stream; layer l+1 waits for that gather's
+  completion event before it computes; full weights live in only two slots
+  that alternate by layer, so the gather of l+1 overwrites the slot layer l-1
+  used and must first wait for l-1's compute to finish (the gate event);
+* section "implementation in SGLang": the model loop is reset(),
+  pre_dispatch(start), then per layer maybe_dispatch(i+1), the layer's
+  forward, update_done_event(i);
+* section "CUDA graph and the draft model": after one launch the current
+  stream waits at most once (wait_ready_once), and the sequence is fixed.
+
+Readings where the page is silent: the first dispatched layer uses slot 0,
+i.e. layer l uses slot (l - start) mod 2; a gather with no previous layer in
+this forward is gated by a forward-start event that reset() records on the
+compute stream (it covers the previous forward's readers).
+
+An op is a tuple (name, stream, layer, slot) with names
+  record_start  wait_start  wait_done  copy  record_ready  wait_ready  record_done
+and layer/slot -1 where they do not apply.  ``check_trace`` is an independent
+happens-before checker: it does not reuse ``expected_trace``.
+"""
+from __future__ import annotations
+
+COMPUTE, SIDE = "compute", "side"
+
+
+def slot_of(layer: int, start: int) -> int:
+    return (layer - start) % 2
+
+
+def expected_trace(start: int, end: int) -> list[tuple]:
+    """Launch/wait sequence of one forward over layers [start, end)."""
+    ops: list[tuple] = [("record_start", COMPUTE, -1, -1)]
+    if end <= start:
+        return ops
+
+    def dispatch(layer: int) -> None:
+        prev = layer - 2  # the last reader of the slot this gather overwrites
+        if prev >= start:
+            ops.append(("wait_done", SIDE, prev, -1))
+        else:
+            ops.append(("wait_start", SIDE, -1, -1))
+        ops.append(("copy", SIDE, layer, slot_of(layer, start)))
+        ops.append(("record_ready", SIDE, layer, -1))
+
+    dispatch(start)  # pre_dispatch(start)
+    for layer in range(start, end):
+        if layer + 1 < end:
+            dispatch(layer + 1)  # maybe_dispatch(layer + 1)
+        ops.append(("wait_ready", COMPUTE, layer, slot_of(layer, start)))
+        ops.append(("record_done", COMPUTE, layer, -1))
+    return ops
+
+
+def _event(op: tuple):
+    name, _, layer, _ = op
+    if name in ("record_start", "wait_start"):
+        return ("start",)
+    if name in ("record_ready", "wait_ready"):
+        return ("ready", layer)
+    if name in ("record_done", "wait_done"):
+        return ("done", layer)
+    return None
+
+
+def check_trace(forwards: list[list[tuple]]) -> list[str]:
+    """Check the data-race and data-flow properties of one or more forwards
+    enqueued back to back.  Returns a list of violations (empty if clean).
+
+    Model: each stream runs its ops in order; ``wait_*`` on a stream orders
+    everything after it behind the latest ``record_*`` of the same event
+    enqueued before the wait (a wait with no earlier record orders nothing).
+    Layer l's compute reads its slot between its ``wait_ready`` and its
+    ``record_done`` on the compute stream.  Violations reported:
+      * a copy and a compute on the same slot that are not ordered;
+      * a compute whose latest ordered copy into its slot is not its layer's;
+      * a layer whose compute stream waited for ready more than once or never.
+    """
+    nodes: list[tuple] = []  # (kind, stream, layer, slot, forward)
+    edges: dict[int, set[int]] = {}
+    last_on_stream: dict[str, int] = {}
+    last_record: dict[tuple, int] = {}
+    problems: list[str] = []
+
+    def add(kind, stream, layer, slot, fwd):
+        idx = len(nodes)
+        nodes.append((kind, stream, layer, slot, fwd))
+        edges[idx] = set()
+        if stream in last_on_stream:
+            edges[last_on_stream[stream]].add(idx)
+        last_on_stream[stream] = idx
+        return idx
+
+    for f, ops in enumerate(forwards):
+        waits: dict[int, int] = {}
+        reading: dict[int, int] = {}
+        for op in ops:
+            name, stream, layer, slot = op
+            ev = _event(op)
+            if name == "record_done":
+                # the layer's compute runs on the compute stream right before its done record
+                if layer in reading:
+                    add("compute", stream, layer, reading[layer], f)
+                else:
+                    problems.append(f"forward {f}: layer {layer} computed without waiting for ready")
+            if name.startswith("record"):
+                last_record[ev] = add(name, stream, layer, slot, f)
+            elif name.startswith("wait"):
+                idx = add(name, stream, layer, slot, f)
+                if ev in last_record:
+                    edges[last_record[ev]].add(idx)
+                if name == "wait_ready":
+                    waits[layer] = waits.get(layer, 0) + 1
+                    reading[layer] = slot
+            elif name == "copy":
+                add("copy", stream, layer, slot, f)
+            else:
+                problems.append(f"unknown op {op}")
+        for layer, n in waits.items():
+            if n != 1:
+                problems.append(f"forward {f}: layer {layer} waited for ready {n} times")
+
+    # transitive closure by DFS from each node (traces are small)
+    reach: list[set[int]] = []
+    for s in range(len(nodes)):
+        seen, stack = set(), [s]
+        while stack:
+            u = stack.pop()
+            for v in edges[u]:
+                if v not in seen:
+                    seen.add(v)
+                    stack.append(v)
+        reach.append(seen)
+
+    def before(a: int, b: int) -> bool:
+        return b in reach[a]
+
+    copies = [i for i, n in enumerate(nodes) if n[0] == "copy"]
+    computes = [i for i, n in enumerate(nodes) if n[0] == "compute"]
+    for c in computes:
+        _, _, layer, slot, f = nodes[c]
+        ordered_writes = []
+        for w in copies:
+            if nodes[w][3] != slot:
+                continue
+            if before(w, c):
+                ordered_writes.append(w)
+            elif not before(c, w):
+                wl, wf = nodes[w][2], nodes[w][4]
+                problems.append(
+                    f"race: copy of layer {wl} (forward {wf}) into slot {slot} is unordered with "
+                    f"the compute of layer {layer} (forward {f})")
+        latest = [w for w in ordered_writes if not any(before(w, o) for o in ordered_writes if o != w)]
+        if len(latest) != 1 or nodes[latest[0]][2] != layer or nodes[latest[0]][4] != f:
+            problems.append(f"forward {f}: layer {layer} does not read its own weights from slot {slot}")
+    return problems

@@ -1,0 +1,68 @@
+"""Pins for the lookahead / ping-pong launch sequence (weight-sharding page,
+sections on lookahead and ping-pong slots, on the SGLang implementation and
+on CUDA graphs).  The happens-before checker is independent of the sequence
+generator; mistakes planted in the sequence must be caught by it."""
+import pytest
+
+from oracle import scheduler as sch
+
+
+@pytest.mark.parametrize("start,end", [(0, 1), (0, 2), (1, 5), (1, 93), (3, 11)])
+def test_expected_trace_is_race_free(start, end):
+    t = sch.expected_trace(start, end)
+    assert sch.check_trace([t]) == []
+    assert sch.check_trace([t, t, t]) == []  # back-to-back forwards
+
+
+def test_slots_alternate_and_two_suffice():
+    t = sch.expected_trace(1, 9)
+    copies = [(op[2], op[3]) for op in t if op[0] == "copy"]
+    assert copies == [(layer, (layer - 1) % 2) for layer in range(1, 9)]
+    assert {s for _, s in copies} == {0, 1}
+    waits = [op for op in t if op[0] == "wait_ready"]
+    assert [w[2] for w in waits] == list(range(1, 9))
+
+
+def test_gate_waits_for_layer_two_back():
+    t = sch.expected_trace(0, 6)
+    for i, op in enumerate(t):
+        if op[0] == "copy" and op[2] >= 2:
+            assert t[i - 1] == ("wait_done", "side", op[2] - 2, -1)
+
+
+def test_missing_gate_is_a_race():
+    t = [op for op in sch.expected_trace(0, 4) if op[0] != "wait_done"]
+    problems = sch.check_trace([t])
+    assert any("race" in p for p in problems)
+
+
+def test_missing_ready_wait_is_caught():
+    t = sch.expected_trace(0, 4)
+    bad = [op for op in t if not (op[0] == "wait_ready" and op[2] == 2)]
+    assert sch.check_trace([bad])
+
+
+def test_double_ready_wait_is_caught():
+    t = sch.expected_trace(0, 3)
+    i = t.index(("wait_ready", "compute", 1, 1))
+    bad = t[:i + 1] + [t[i]] + t[i + 1:]
+    assert any("2 times" in p for p in sch.check_trace([bad]))
+
+
+def test_next_forward_needs_start_event():
+    # Without the start record, the next forward's first gathers race with the
+    # previous forward's last computes on the same slots.
+    t = sch.expected_trace(0, 4)
+    no_start = [op for op in t if op[0] != "record_start"]
+    assert sch.check_trace([t, no_start])
+
+
+def test_wrong_slot_is_caught():
+    t = sch.expected_trace(0, 4)
+    bad = [(n, s, layer, 1 - slot) if (n == "wait_ready" and layer == 3) else (n, s, layer, slot)
+           for n, s, layer, slot in t]
+    assert sch.check_trace([bad])
+
+
+def test_empty_range():
+    assert sch.expected_trace(5, 5) == [("record_start", "compute", -1, -1)]
