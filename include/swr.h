@@ -1,0 +1,299 @@
+/*
+ * swr.h -- sharded weight reassembly on one MI355X (gfx950): C ABI.
+ *
+ * The method (weight_sharding, zdszero.github.io): every layer keeps its
+ * replicated weights as N byte chunks of one flat buffer T; just before the
+ * layer runs, the chunks are gathered back into a full-weight workspace slot
+ * and the layer's GEMMs read the weights through zero-copy views of that slot.
+ * Here the N chunks all live in one GPU's HBM and the gather is an on-device
+ * copy kernel on a side stream.
+ *
+ * Conventions shared by every entry point
+ *   - Weights are out_features x in_features, row-major, K (= in) contiguous
+ *     (weight_sharding, section "core abstraction").
+ *   - dtype SWR_BF16: 2-byte bfloat16 elements.  SWR_FP8_E4M3FN: 1-byte OCP
+ *     E4M3FN codes whose value is decode(code) * row_scale[row]; the fp32
+ *     row scales are replicated and live outside the flat buffer
+ *     (weight_sharding, section "loading", quantised variants).
+ *   - Activations X are bfloat16, row-major [M, in] with a leading dimension.
+ *   - "Device pointer" arguments are HIP device addresses of the current
+ *     device; pointer *arrays* (chunk lists, source lists, partial lists) are
+ *     host arrays of device pointers, read during the call only.
+ *   - The caller owns every buffer.  The library borrows device buffers until
+ *     the work it enqueued on the given stream has finished, and never
+ *     allocates device memory in any entry point below.
+ *   - Every call checks all of its arguments before it enqueues anything:
+ *     on error nothing has been enqueued, the call returns a negative status
+ *     and swr_last_error() describes the problem.  No call falls back to a
+ *     different algorithm or to the host.
+ *   - Streams: any hipStream_t of the current device, or 0 for the null
+ *     stream.  Kernels are enqueued asynchronously.
+ */
+#ifndef SWR_H
+#define SWR_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------------ types */
+
+enum swr_dtype { SWR_BF16 = 0, SWR_FP8_E4M3FN = 1 };
+
+enum swr_status {
+  SWR_OK = 0,
+  SWR_E_INVALID = -1,  /* bad argument value, null pointer, unknown dtype   */
+  SWR_E_ALIGN = -2,    /* a pointer or size is not 16-byte aligned          */
+  SWR_E_CAPACITY = -3, /* a destination or workspace is too small           */
+  SWR_E_SHAPE = -4,    /* inconsistent or unsupported shapes                */
+  SWR_E_HIP = -5,      /* the HIP runtime reported an error                 */
+  SWR_E_SEQUENCE = -6  /* planner calls out of the documented order         */
+};
+
+#define SWR_MAX_CHUNKS 64   /* N, chunks per layer                           */
+#define SWR_MAX_WEIGHTS 64  /* weights per layer                             */
+#define SWR_ITEM_ALIGN 16   /* every item starts on a 16-byte boundary       */
+
+typedef struct swr_weight_desc {
+  int64_t out_features;
+  int64_t in_features;
+  int32_t dtype;    /* enum swr_dtype */
+  int32_t reserved; /* must be 0 */
+} swr_weight_desc;
+
+typedef struct swr_view_desc {
+  int64_t offset;       /* o_j: byte offset of the item in T (multiple of 16) */
+  int64_t nbytes;       /* s_j = out * in * element size                      */
+  int64_t out_features;
+  int64_t in_features;
+  int32_t dtype;
+  int32_t reserved;
+} swr_view_desc;
+
+typedef struct swr_layout {
+  int64_t payload_bytes; /* end of the last item                           */
+  int64_t total_bytes;   /* |T|: payload rounded up to a multiple of 16*N  */
+  int64_t chunk_bytes;   /* C = |T| / N, a multiple of 16                  */
+  int32_t n_weights;
+  int32_t n_chunks;      /* N */
+} swr_layout;
+
+/* ------------------------------------------------------- flat layout (a1) */
+
+/*
+ * swr_plan_layer -- host only, no device work.
+ * weight_sharding, section "one AllGather per layer: flat layout", steps 1-2:
+ * the layer's weights are laid end to end in the given order; each item
+ * starts at the first 16-byte boundary at or after the previous item's end
+ * (offsets relative to the start of T); |T| is the payload rounded up to a
+ * multiple of 16*N; C = |T| / N.  Bytes between items and after the payload
+ * are padding.
+ *   w[n_weights]         weights in packing order (1 <= n_weights <= 64,
+ *                        out, in >= 1, dtype BF16 or FP8_E4M3FN, reserved 0)
+ *   n_chunks             N, 1 <= N <= 64
+ *   views_out[n_weights] receives (o_j, s_j, out_j, in_j, dtype_j)
+ *   layout_out           receives payload, |T|, C, n_weights, N
+ * Errors: SWR_E_INVALID for null pointers or out-of-range counts/dtypes,
+ *         SWR_E_SHAPE for non-positive sizes or sizes that overflow int64.
+ */
+int swr_plan_layer(const swr_weight_desc* w, int32_t n_weights, int32_t n_chunks,
+                   swr_view_desc* views_out, swr_layout* layout_out);
+
+/* ------------------------------------------------------------- pack (a2) */
+
+/*
+ * swr_pack_layer -- enqueue on `stream`.
+ * weight_sharding, section "flat layout", steps 1-2, and section "loading"
+ * (the one-time re-layout into flat chunks): writes every byte of
+ * T = [W_0 | pad | W_1 | pad | ... | pad] into the N chunk buffers, chunk i
+ * receiving T[i*C, (i+1)*C).  Padding bytes are written as zero.
+ *   layout, views     as returned by swr_plan_layer (views[layout->n_weights])
+ *   src_dev[n]        device pointers to the full weights, row-major, each
+ *                     16-byte aligned and s_j bytes long
+ *   chunk_dev[N]      device pointers, each 16-byte aligned, >= C bytes
+ * Errors: SWR_E_INVALID (null/inconsistent layout), SWR_E_ALIGN, SWR_E_HIP.
+ */
+int swr_pack_layer(const swr_layout* layout, const swr_view_desc* views,
+                   const void* const* src_dev, void* const* chunk_dev, hipStream_t stream);
+
+/* ------------------------------------------------------- reassembly (a3) */
+
+/*
+ * swr_reassemble_into_slot -- enqueue on `side`.
+ * weight_sharding, section "flat layout" step 3 (one gather per layer gives
+ * every rank the whole T) and section "lookahead and ping-pong slot" (the
+ * gather waits on a gate event, its completion is an event the consumer
+ * waits on).  On one GPU the gather is the copy
+ *     slot[i*C, (i+1)*C) = chunk_dev[i]   for i = 0..N-1.
+ *   chunk_dev[N]   device pointers, 16-byte aligned, C bytes each (N <= 64)
+ *   chunk_bytes    C, a positive multiple of 16
+ *   slot           device pointer, 16-byte aligned, slot_bytes >= N*C
+ *   self_rank      the rank whose chunk is local (0 <= self_rank < N); it only
+ *                  changes the transfer count below
+ *   gate           if non-null, `side` waits for it before the copy
+ *   ready          if non-null, recorded on `side` after the copy
+ *   remote_bytes   if non-null, *remote_bytes += (N-1)*C, the bytes a rank
+ *                  receives from its peers (weight_sharding, cost section)
+ * Errors: SWR_E_INVALID, SWR_E_ALIGN, SWR_E_CAPACITY (slot too small),
+ *         SWR_E_HIP.
+ */
+int swr_reassemble_into_slot(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
+                             void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
+                             hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes);
+
+/* ------------------------------------------------------------ GEMMs (a5-a8) */
+
+/*
+ * swr_proj_forward -- enqueue on `stream`.
+ * One projection through a view (weight_sharding, section "flat layout"
+ * step 4: the GEMM sees the full W):
+ *     Y[m, o] = s[o] * sum_k X[m, k] * W[o, k]
+ * accumulated in fp32; the result is rounded once to bf16 (round to nearest
+ * even) unless y_fp32 is set.
+ *   W          device pointer, 16-byte aligned, [out_f, in_f] of `dtype`
+ *   row_scale  device pointer to fp32 [out_f], 16-byte aligned; NULL means
+ *              s = 1 (must be non-NULL for FP8 weights)
+ *   X          device pointer, bf16 [M, ldx] (the first in_f columns of each
+ *              row are read), 16-byte aligned, ldx >= in_f
+ *   Y          device pointer, bf16 or fp32 [M, ldy], 16-byte aligned,
+ *              ldy >= out_f; the first out_f columns of each row are written
+ *   workspace  NULL, or a 256-byte aligned device buffer of workspace_bytes
+ *              used for split-K partial sums; with NULL every row tile is
+ *              reduced over the whole K by one workgroup.  A non-NULL
+ *              workspace smaller than swr_proj_workspace_bytes() is an error.
+ *   Shapes: any out_f, in_f >= 1 and M >= 0 (M == 0 enqueues nothing).  The
+ *   matrix-core streaming kernel runs when in_f and ldx are multiples of 64
+ *   and 8; other shapes (odd projections) run a plain one-output-per-thread
+ *   kernel.
+ * Errors: SWR_E_INVALID, SWR_E_ALIGN, SWR_E_SHAPE, SWR_E_CAPACITY, SWR_E_HIP.
+ */
+int swr_proj_forward(const void* W, int32_t dtype, const float* row_scale, int64_t out_f,
+                     int64_t in_f, const void* X, int64_t ldx, int64_t M, void* Y, int32_t y_fp32,
+                     int64_t ldy, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Split-K scratch bytes swr_proj_forward can use for these sizes (0 when it
+ * does not split K), or a negative status.  Host only. */
+int64_t swr_proj_workspace_bytes(int64_t M, int64_t out_f, int64_t in_f, int32_t dtype);
+
+/*
+ * swr_mlp_forward -- enqueue on `stream`.
+ * The shared-expert MLP (vLLM PR #50656 report, test code: gate_up holds the
+ * gate rows then the up rows; the activation is SiLU of the gate half times
+ * the up half):
+ *     G = X @ W_gate_up^T * s_gu        fp32, [M, 2I]
+ *     h = bf16( silu(G[:, :I]) * G[:, I:] ),  silu(z) = z / (1 + exp(-z))
+ *     Y = bf16( (h @ W_down^T) * s_d )
+ *   W_gate_up  [2I, H] of dtype, W_down [H, I] of dtype, 16-byte aligned
+ *   s_gu, s_d  fp32 [2I] and [H] row scales (NULL means 1; required for FP8)
+ *   X          bf16 [M, H] contiguous; Y bf16 [M, H] contiguous; both 16-byte
+ *              aligned
+ *   workspace  device buffer of at least swr_mlp_workspace_bytes(M, H, I,
+ *              dtype) bytes, 256-byte aligned; it holds h and any split-K
+ *              partial sums and is overwritten
+ *   H, I       >= 1; the fused matrix-core path needs H, I multiples of 64
+ *              (and I of 32), other sizes run the plain kernel
+ * Errors: SWR_E_INVALID, SWR_E_ALIGN, SWR_E_SHAPE, SWR_E_CAPACITY, SWR_E_HIP.
+ */
+int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const void* W_down,
+                    const float* s_d, int32_t dtype, int64_t H, int64_t I, const void* X,
+                    int64_t M, void* Y, void* workspace, int64_t workspace_bytes,
+                    hipStream_t stream);
+
+/* Workspace bytes swr_mlp_forward needs for these sizes (>= 0), or a negative
+ * status for invalid sizes.  Host only. */
+int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int32_t dtype);
+
+/*
+ * swr_sum_partials -- enqueue on `stream`.
+ * Sharded-matrices notes (copecc.github.io), local matmul case 3: when the
+ * contraction dimension is split, each shard yields a partial result and
+ * the full result is their sum:
+ *     out[i] = parts[0][i] + parts[1][i] + ... + parts[n-1][i]
+ * added in fp32 in that fixed order, stored as fp32 or rounded to bf16.
+ *   parts[n]   device pointers to fp32 arrays of `count` elements, 16-byte
+ *              aligned (1 <= n <= 64)
+ *   out        device pointer, fp32 or bf16 [count], 16-byte aligned
+ * Errors: SWR_E_INVALID, SWR_E_ALIGN, SWR_E_HIP.
+ */
+int swr_sum_partials(const float* const* parts, int32_t n, int64_t count, void* out,
+                     int32_t out_bf16, hipStream_t stream);
+
+/* ------------------------------------------------------ scheduler (a9) */
+
+/*
+ * The lookahead / ping-pong planner (weight_sharding, sections "lookahead
+ * and ping-pong slot", "implementation in SGLang" and "CUDA graph and the
+ * draft model").  Per forward over layers [start, end):
+ *     swr_planner_reset(p);                  records the forward-start event
+ *     swr_planner_pre_dispatch(p, start);    side: gather(start) -> slot 0
+ *     for l in [start, end):
+ *         swr_planner_maybe_dispatch(p, l+1);  side: wait gate, gather(l+1)
+ *                                              into slot (l+1-start) % 2,
+ *                                              record ready(l+1); no-op if
+ *                                              l+1 is outside [start, end)
+ *         swr_planner_wait_ready_once(p, l, &slot);  compute waits ready(l)
+ *                                              at most once per forward
+ *         ... the layer's GEMMs on `compute`, reading views of *slot ...
+ *         swr_planner_update_done_event(p, l);  records done(l) on compute
+ * The gate of gather(l) is done(l-2), the last reader of the same slot, or
+ * the forward-start event when l-2 < start.  At most two layers' full
+ * weights exist at any time.  The planner owns its hipEvents; it borrows the
+ * streams, slots and chunk buffers.  Calls are not thread-safe.
+ */
+typedef struct swr_planner swr_planner;
+
+/* Trace op codes reported by swr_planner_trace (quadruples op, stream, layer, slot). */
+enum swr_trace_op {
+  SWR_OP_RECORD_START = 1, SWR_OP_WAIT_START = 2, SWR_OP_WAIT_DONE = 3, SWR_OP_COPY = 4,
+  SWR_OP_RECORD_READY = 5, SWR_OP_WAIT_READY = 6, SWR_OP_RECORD_DONE = 7
+};
+enum swr_trace_stream { SWR_STREAM_COMPUTE = 0, SWR_STREAM_SIDE = 1 };
+
+/* start < end; slot_a, slot_b device pointers (16-byte aligned, slot_bytes
+ * each); compute and side must be different streams.  Errors:
+ * SWR_E_INVALID, SWR_E_ALIGN, SWR_E_HIP (event creation). */
+int swr_planner_create(int32_t start, int32_t end, hipStream_t compute, hipStream_t side,
+                       void* slot_a, void* slot_b, int64_t slot_bytes, swr_planner** out);
+
+/* Register layer `layer`'s chunks (host array of N device pointers, C bytes
+ * each).  N*C must fit in slot_bytes (else SWR_E_CAPACITY). */
+int swr_planner_set_layer(swr_planner* p, int32_t layer, const void* const* chunk_dev,
+                          int32_t n_chunks, int64_t chunk_bytes);
+
+int swr_planner_reset(swr_planner* p);
+/* SWR_E_SEQUENCE if reset() was not called, or `layer` != start. */
+int swr_planner_pre_dispatch(swr_planner* p, int32_t layer);
+/* No-op (SWR_OK) outside [start, end); SWR_E_SEQUENCE if `layer` was already
+ * dispatched in this forward or layer-1 was not dispatched. */
+int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer);
+/* Makes `compute` wait for ready(layer) the first time it is called for
+ * `layer` in this forward; later calls only return the slot.  *slot_out gets
+ * the slot base (views are slot + o_j).  SWR_E_SEQUENCE if `layer` was not
+ * dispatched. */
+int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void** slot_out);
+/* SWR_E_SEQUENCE if wait_ready_once(layer) was not called first. */
+int swr_planner_update_done_event(swr_planner* p, int32_t layer);
+/* Bytes received from peers so far (sum of (N-1)*C over gathers), and the
+ * number of gathers issued, since creation. */
+int swr_planner_counters(const swr_planner* p, int64_t* remote_bytes, int64_t* gathers);
+/* Copies up to `cap` ops (4 int32 each: op, stream, layer, slot; -1 where
+ * not applicable) recorded since the last reset into ops; *n = total count. */
+int swr_planner_trace(const swr_planner* p, int32_t* ops, int32_t cap, int32_t* n);
+void swr_planner_destroy(swr_planner* p);
+
+/* ------------------------------------------------------------- errors */
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* swr_last_error(void);
+
+/* Library version string. */
+const char* swr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWR_H */

@@ -1,0 +1,328 @@
+"""Python binding of libswr: sharded weight reassembly on one MI355X (gfx950).
+
+Argument marshalling only.  Every step of the path runs in the HIP library
+(``libswr.so``, built in-tree by ``sharded_weight_reassembly_amd.build``);
+PyTorch supplies device memory and streams.  The functions carry the names
+of the C entry points in ``include/swr.h`` without the ``swr_`` prefix.
+
+If the library has not been built, importing the binding's functions raises
+ImportError: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch  # loaded first: libswr binds to the HIP runtime torch has loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libswr.so")
+
+BF16 = 0
+FP8_E4M3FN = 1
+DTYPES = {"bf16": BF16, "fp8_e4m3fn": FP8_E4M3FN}
+ELEM_BYTES = {BF16: 2, FP8_E4M3FN: 1}
+
+OK, E_INVALID, E_ALIGN, E_CAPACITY, E_SHAPE, E_HIP, E_SEQUENCE = 0, -1, -2, -3, -4, -5, -6
+STATUS_NAMES = {0: "SWR_OK", -1: "SWR_E_INVALID", -2: "SWR_E_ALIGN", -3: "SWR_E_CAPACITY", -4: "SWR_E_SHAPE",
+                -5: "SWR_E_HIP", -6: "SWR_E_SEQUENCE"}
+
+TRACE_OPS = {1: "record_start", 2: "wait_start", 3: "wait_done", 4: "copy", 5: "record_ready", 6: "wait_ready",
+             7: "record_done"}
+TRACE_STREAMS = {0: "compute", 1: "side"}
+
+# Every function include/swr.h declares.
+EXPORTS = (
+    "swr_plan_layer", "swr_pack_layer", "swr_reassemble_into_slot", "swr_proj_forward",
+    "swr_proj_workspace_bytes", "swr_mlp_forward", "swr_mlp_workspace_bytes", "swr_sum_partials",
+    "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
+    "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
+    "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_last_error", "swr_version",
+)
+
+
+class SwrError(RuntimeError):
+    def __init__(self, fn: str, code: int, message: str):
+        super().__init__(f"{fn} failed with {STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.fn = fn
+
+
+class WeightDesc(ctypes.Structure):
+    _fields_ = [("out_features", ctypes.c_int64), ("in_features", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class ViewDesc(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("nbytes", ctypes.c_int64), ("out_features", ctypes.c_int64),
+                ("in_features", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("payload_bytes", ctypes.c_int64), ("total_bytes", ctypes.c_int64), ("chunk_bytes", ctypes.c_int64),
+                ("n_weights", ctypes.c_int32), ("n_chunks", ctypes.c_int32)]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32, _i64 = ctypes.c_int32, ctypes.c_int64
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises ImportError if it was never built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sharded_weight_reassembly_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "swr_plan_layer": (_i32, [ctypes.POINTER(WeightDesc), _i32, _i32, ctypes.POINTER(ViewDesc),
+                                  ctypes.POINTER(Layout)]),
+        "swr_pack_layer": (_i32, [ctypes.POINTER(Layout), ctypes.POINTER(ViewDesc), ctypes.POINTER(_vp),
+                                  ctypes.POINTER(_vp), _vp]),
+        "swr_reassemble_into_slot": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i64, _i32, _vp, _vp, _vp,
+                                            ctypes.POINTER(_i64)]),
+        "swr_proj_forward": (_i32, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp]),
+        "swr_proj_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
+        "swr_mlp_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
+        "swr_mlp_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
+        "swr_sum_partials": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i32, _vp]),
+        "swr_planner_create": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]),
+        "swr_planner_set_layer": (_i32, [_vp, _i32, ctypes.POINTER(_vp), _i32, _i64]),
+        "swr_planner_reset": (_i32, [_vp]),
+        "swr_planner_pre_dispatch": (_i32, [_vp, _i32]),
+        "swr_planner_maybe_dispatch": (_i32, [_vp, _i32]),
+        "swr_planner_wait_ready_once": (_i32, [_vp, _i32, ctypes.POINTER(_vp)]),
+        "swr_planner_update_done_event": (_i32, [_vp, _i32]),
+        "swr_planner_counters": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+        "swr_planner_trace": (_i32, [_vp, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
+        "swr_planner_destroy": (None, [_vp]),
+        "swr_last_error": (ctypes.c_char_p, []),
+        "swr_version": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc < 0:
+        raise SwrError(fn, rc, lib().swr_last_error().decode())
+    return rc
+
+
+def _ptr(x) -> int | None:
+    """Device address of a tensor (or an int address, or None)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if isinstance(x, torch.Tensor):
+        if not x.is_cuda:
+            raise ValueError("expected a device tensor")
+        return x.data_ptr()
+    raise TypeError(f"cannot take a device address of {type(x)!r}")
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _event(e) -> int | None:
+    if e is None or isinstance(e, int):
+        return e
+    return e.cuda_event
+
+
+def _ptr_array(items) -> ctypes.Array:
+    arr = (_vp * len(items))()
+    for i, t in enumerate(items):
+        arr[i] = _ptr(t)
+    return arr
+
+
+def _dtype(d) -> int:
+    return DTYPES[d] if isinstance(d, str) else int(d)
+
+
+# --------------------------------------------------------------- flat layout
+
+def plan_layer(weights: Sequence[tuple[int, int, object]], n_chunks: int) -> tuple[list[dict], dict]:
+    """[(out, in, dtype)] -> (views, layout); dtype is "bf16"/"fp8_e4m3fn" or its code."""
+    n = len(weights)
+    descs = (WeightDesc * max(n, 1))()
+    for i, (o, k, d) in enumerate(weights):
+        descs[i] = WeightDesc(int(o), int(k), _dtype(d), 0)
+    views = (ViewDesc * max(n, 1))()
+    lay = Layout()
+    _check("swr_plan_layer", lib().swr_plan_layer(descs, n, int(n_chunks), views, ctypes.byref(lay)))
+    vs = [dict(offset=v.offset, nbytes=v.nbytes, out_features=v.out_features, in_features=v.in_features,
+               dtype=v.dtype) for v in views[:n]]
+    layout = dict(payload_bytes=lay.payload_bytes, total_bytes=lay.total_bytes, chunk_bytes=lay.chunk_bytes,
+                  n_weights=lay.n_weights, n_chunks=lay.n_chunks)
+    return vs, layout
+
+
+def _layout_struct(layout: dict) -> Layout:
+    return Layout(layout["payload_bytes"], layout["total_bytes"], layout["chunk_bytes"], layout["n_weights"],
+                  layout["n_chunks"])
+
+
+def _views_struct(views: list[dict]) -> ctypes.Array:
+    arr = (ViewDesc * max(len(views), 1))()
+    for i, v in enumerate(views):
+        arr[i] = ViewDesc(v["offset"], v["nbytes"], v["out_features"], v["in_features"], v["dtype"], 0)
+    return arr
+
+
+def pack_layer(layout: dict, views: list[dict], src, chunks, stream=None) -> None:
+    """Write T (weights + zero padding) into the N chunk buffers."""
+    lay = _layout_struct(layout)
+    _check("swr_pack_layer", lib().swr_pack_layer(ctypes.byref(lay), _views_struct(views), _ptr_array(src),
+                                                  _ptr_array(chunks), _stream(stream)))
+
+
+def reassemble_into_slot(chunks, chunk_bytes: int, slot, slot_bytes: int | None = None, self_rank: int = 0,
+                         stream=None, gate=None, ready=None) -> int:
+    """Gather the N chunks into `slot`; returns the bytes counted as received from peers."""
+    if slot_bytes is None:
+        slot_bytes = slot.numel() * slot.element_size()
+    remote = _i64(0)
+    _check("swr_reassemble_into_slot",
+           lib().swr_reassemble_into_slot(_ptr_array(chunks), len(chunks), int(chunk_bytes), _ptr(slot),
+                                          int(slot_bytes), int(self_rank), _stream(stream), _event(gate),
+                                          _event(ready), ctypes.byref(remote)))
+    return remote.value
+
+
+def view(slot: torch.Tensor, v: dict) -> torch.Tensor:
+    """Zero-copy view of weight v inside a uint8 slot tensor (narrow + view)."""
+    raw = slot.narrow(0, v["offset"], v["nbytes"])
+    if v["dtype"] == BF16:
+        return raw.view(torch.bfloat16).view(v["out_features"], v["in_features"])
+    return raw.view(v["out_features"], v["in_features"])
+
+
+# --------------------------------------------------------------------- GEMMs
+
+def proj_workspace_bytes(m: int, out_f: int, in_f: int, dtype) -> int:
+    return _check("swr_proj_workspace_bytes", lib().swr_proj_workspace_bytes(m, out_f, in_f, _dtype(dtype)))
+
+
+def proj_forward(w, dtype, row_scale, out_f: int, in_f: int, x: torch.Tensor, y: torch.Tensor, m: int | None = None,
+                 ldx: int | None = None, ldy: int | None = None, y_fp32: bool | None = None, workspace=None,
+                 workspace_bytes: int | None = None, stream=None) -> None:
+    """Y[m, o] = s[o] * sum_k X[m, k] W[o, k]; `w` is a tensor or a device address (a view)."""
+    if m is None:
+        m = x.shape[0]
+    if ldx is None:
+        ldx = x.stride(0) if x.dim() == 2 else in_f
+    if ldy is None:
+        ldy = y.stride(0) if y.dim() == 2 else out_f
+    if y_fp32 is None:
+        y_fp32 = y.dtype == torch.float32
+    if workspace is not None and workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("swr_proj_forward",
+           lib().swr_proj_forward(_ptr(w), _dtype(dtype), _ptr(row_scale), int(out_f), int(in_f), _ptr(x), int(ldx),
+                                  int(m), _ptr(y), int(bool(y_fp32)), int(ldy), _ptr(workspace),
+                                  int(workspace_bytes or 0), _stream(stream)))
+
+
+def mlp_workspace_bytes(m: int, hidden: int, inter: int, dtype) -> int:
+    return _check("swr_mlp_workspace_bytes", lib().swr_mlp_workspace_bytes(m, hidden, inter, _dtype(dtype)))
+
+
+def mlp_forward(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter: int, x: torch.Tensor, y: torch.Tensor,
+                workspace: torch.Tensor, m: int | None = None, stream=None) -> None:
+    """Y = bf16((bf16(silu(G[:, :I]) * G[:, I:]) @ W_down^T) * s_d),  G = X @ W_gate_up^T * s_gu."""
+    if m is None:
+        m = x.shape[0]
+    _check("swr_mlp_forward",
+           lib().swr_mlp_forward(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), _dtype(dtype), int(hidden),
+                                 int(inter), _ptr(x), int(m), _ptr(y), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sum_partials(parts, out: torch.Tensor, count: int | None = None, stream=None) -> None:
+    """out = parts[0] + ... + parts[n-1] (fp32, in order); out fp32 or bf16."""
+    if count is None:
+        count = out.numel()
+    _check("swr_sum_partials", lib().swr_sum_partials(_ptr_array(parts), len(parts), int(count), _ptr(out),
+                                                      int(out.dtype == torch.bfloat16), _stream(stream)))
+
+
+# ------------------------------------------------------------------ planner
+
+class Planner:
+    """Lookahead / ping-pong scheduler over layers [start, end) (owns its events)."""
+
+    def __init__(self, start: int, end: int, compute, side, slot_a: torch.Tensor, slot_b: torch.Tensor,
+                 slot_bytes: int | None = None):
+        if slot_bytes is None:
+            slot_bytes = min(slot_a.numel() * slot_a.element_size(), slot_b.numel() * slot_b.element_size())
+        h = _vp()
+        _check("swr_planner_create", lib().swr_planner_create(int(start), int(end), _stream(compute), _stream(side),
+                                                              _ptr(slot_a), _ptr(slot_b), int(slot_bytes),
+                                                              ctypes.byref(h)))
+        self._h = h
+        self.start, self.end = start, end
+        self._keep = (slot_a, slot_b)
+
+    def set_layer(self, layer: int, chunks, chunk_bytes: int) -> None:
+        _check("swr_planner_set_layer", lib().swr_planner_set_layer(self._h, int(layer), _ptr_array(chunks),
+                                                                    len(chunks), int(chunk_bytes)))
+
+    def reset(self) -> None:
+        _check("swr_planner_reset", lib().swr_planner_reset(self._h))
+
+    def pre_dispatch(self, layer: int) -> None:
+        _check("swr_planner_pre_dispatch", lib().swr_planner_pre_dispatch(self._h, int(layer)))
+
+    def maybe_dispatch(self, layer: int) -> None:
+        _check("swr_planner_maybe_dispatch", lib().swr_planner_maybe_dispatch(self._h, int(layer)))
+
+    def wait_ready_once(self, layer: int) -> int:
+        out = _vp()
+        _check("swr_planner_wait_ready_once", lib().swr_planner_wait_ready_once(self._h, int(layer), ctypes.byref(out)))
+        return out.value
+
+    def update_done_event(self, layer: int) -> None:
+        _check("swr_planner_update_done_event", lib().swr_planner_update_done_event(self._h, int(layer)))
+
+    def counters(self) -> tuple[int, int]:
+        rb, g = _i64(0), _i64(0)
+        _check("swr_planner_counters", lib().swr_planner_counters(self._h, ctypes.byref(rb), ctypes.byref(g)))
+        return rb.value, g.value
+
+    def trace(self) -> list[tuple]:
+        n = _i32(0)
+        _check("swr_planner_trace", lib().swr_planner_trace(self._h, None, 0, ctypes.byref(n)))
+        buf = (_i32 * (4 * max(n.value, 1)))()
+        _check("swr_planner_trace", lib().swr_planner_trace(self._h, buf, n.value, ctypes.byref(n)))
+        return [(TRACE_OPS[buf[4 * i]], TRACE_STREAMS[buf[4 * i + 1]], buf[4 * i + 2], buf[4 * i + 3])
+                for i in range(n.value)]
+
+    def close(self) -> None:
+        if self._h:
+            lib().swr_planner_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def version() -> str:
+    return lib().swr_version().decode()

@@ -1,0 +1,174 @@
+// C ABI of the GEMM entry points: argument checks, plan selection and the
+// workspace layout.  Every check happens before anything is enqueued.
+#include "swr_internal.h"
+
+using swr::aligned;
+using swr::fail;
+
+namespace {
+
+constexpr int64_t kWorkspaceAlign = 256;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+bool valid_dtype(int32_t d) { return d == SWR_BF16 || d == SWR_FP8_E4M3FN; }
+
+// A 256-byte aligned stand-in pointer: plans made with it assume the fast
+// (aligned) kernel, which needs the most scratch.
+const void* kAlignedProbe = reinterpret_cast<const void*>(uintptr_t(1) << 20);
+
+swr::GemmProblem mlp_gate_up(const void* W, const float* s, int32_t dtype, int64_t H, int64_t I, const void* X,
+                             int64_t M, void* h) {
+  swr::GemmProblem p{};
+  p.W = W;
+  p.dtype = dtype;
+  p.scale = s;
+  p.X = X;
+  p.ldx = H;
+  p.M = M;
+  p.rows = 2 * I;
+  p.K = H;
+  p.Y = h;
+  p.ldy = I;
+  p.mode = swr::OUT_SILU_BF16;
+  return p;
+}
+
+swr::GemmProblem mlp_down(const void* W, const float* s, int32_t dtype, int64_t H, int64_t I, const void* h,
+                          int64_t M, void* Y) {
+  swr::GemmProblem p{};
+  p.W = W;
+  p.dtype = dtype;
+  p.scale = s;
+  p.X = h;
+  p.ldx = I;
+  p.M = M;
+  p.rows = H;
+  p.K = I;
+  p.Y = Y;
+  p.ldy = H;
+  p.mode = swr::OUT_BF16;
+  return p;
+}
+
+int64_t h_bytes(int64_t M, int64_t I) { return round_up(M * I * 2, kWorkspaceAlign); }
+
+int check_sizes(const char* fn, int64_t M, int64_t a, int64_t b) {
+  const int64_t kLimit = INT64_C(1) << 40;
+  if (M < 0 || a < 1 || b < 1 || M > kLimit || a > kLimit || b > kLimit || (M > 0 && a > kLimit / M) ||
+      (M > 0 && b > kLimit / M) || a > kLimit / b)
+    return fail(SWR_E_SHAPE, "%s: unsupported sizes M=%lld, %lld, %lld", fn, (long long)M, (long long)a, (long long)b);
+  return SWR_OK;
+}
+
+}  // namespace
+
+extern "C" int64_t swr_proj_workspace_bytes(int64_t M, int64_t out_f, int64_t in_f, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(SWR_E_INVALID, "swr_proj_workspace_bytes: unknown dtype %d", dtype);
+  if (int rc = check_sizes("swr_proj_workspace_bytes", M, out_f, in_f)) return rc;
+  swr::GemmProblem p{};
+  p.W = kAlignedProbe;
+  p.dtype = dtype;
+  p.X = kAlignedProbe;
+  p.ldx = round_up(in_f, 8);
+  p.M = M;
+  p.rows = out_f;
+  p.K = in_f;
+  p.mode = swr::OUT_BF16;
+  swr::clear_error();
+  return swr::plan_gemm(p).partial_bytes;
+}
+
+extern "C" int swr_proj_forward(const void* W, int32_t dtype, const float* row_scale, int64_t out_f, int64_t in_f,
+                                const void* X, int64_t ldx, int64_t M, void* Y, int32_t y_fp32, int64_t ldy,
+                                void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "swr_proj_forward";
+  if (!W || !X || !Y) return fail(SWR_E_INVALID, "%s: null pointer", fn);
+  if (!valid_dtype(dtype)) return fail(SWR_E_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (dtype == SWR_FP8_E4M3FN && !row_scale) return fail(SWR_E_INVALID, "%s: FP8 weights need row scales", fn);
+  if (int rc = check_sizes(fn, M, out_f, in_f)) return rc;
+  if (ldx < in_f || ldy < out_f) return fail(SWR_E_SHAPE, "%s: ldx=%lld < in or ldy=%lld < out", fn,
+                                             (long long)ldx, (long long)ldy);
+  if (!aligned(W, 16) || !aligned(X, 16) || !aligned(Y, 16) || (row_scale && !aligned(row_scale, 16)))
+    return fail(SWR_E_ALIGN, "%s: W, X, Y and row_scale must be 16-byte aligned", fn);
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+    return fail(SWR_E_INVALID, "%s: workspace_bytes=%lld with workspace=%p", fn, (long long)workspace_bytes, workspace);
+  if (workspace && !aligned(workspace, kWorkspaceAlign))
+    return fail(SWR_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  swr::GemmProblem p{};
+  p.W = W;
+  p.dtype = dtype;
+  p.scale = row_scale;
+  p.X = X;
+  p.ldx = ldx;
+  p.M = M;
+  p.rows = out_f;
+  p.K = in_f;
+  p.Y = Y;
+  p.ldy = ldy;
+  p.mode = y_fp32 ? swr::OUT_F32 : swr::OUT_BF16;
+  swr::GemmPlan plan = swr::plan_gemm(p);
+  if (plan.partial_bytes > 0 && !workspace) {
+    // no scratch given: one K split per row tile (same kernel, no partials)
+    plan.ksplit = 1;
+    plan.kper = in_f;
+    plan.partial_bytes = 0;
+  }
+  if (plan.partial_bytes > workspace_bytes)
+    return fail(SWR_E_CAPACITY, "%s: workspace holds %lld bytes, needs %lld", fn, (long long)workspace_bytes,
+                (long long)plan.partial_bytes);
+  if (M == 0) {
+    swr::clear_error();
+    return SWR_OK;
+  }
+  const hipError_t e = swr::launch_gemm(p, plan, static_cast<float*>(workspace), stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_proj_forward: launch");
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(SWR_E_INVALID, "swr_mlp_workspace_bytes: unknown dtype %d", dtype);
+  if (int rc = check_sizes("swr_mlp_workspace_bytes", M, H, 2 * I)) return rc;
+  const int64_t pg =
+      swr::plan_gemm(mlp_gate_up(kAlignedProbe, nullptr, dtype, H, I, kAlignedProbe, M, nullptr)).partial_bytes;
+  const int64_t pd =
+      swr::plan_gemm(mlp_down(kAlignedProbe, nullptr, dtype, H, I, kAlignedProbe, M, nullptr)).partial_bytes;
+  swr::clear_error();
+  return h_bytes(M, I) + round_up(pg > pd ? pg : pd, kWorkspaceAlign);
+}
+
+extern "C" int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
+                               int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y,
+                               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "swr_mlp_forward";
+  if (!W_gate_up || !W_down || !X || !Y || !workspace) return fail(SWR_E_INVALID, "%s: null pointer", fn);
+  if (!valid_dtype(dtype)) return fail(SWR_E_INVALID, "%s: unknown dtype %d", fn, dtype);
+  if (dtype == SWR_FP8_E4M3FN && (!s_gu || !s_d)) return fail(SWR_E_INVALID, "%s: FP8 weights need row scales", fn);
+  if (int rc = check_sizes(fn, M, H, 2 * I)) return rc;
+  if (!aligned(W_gate_up, 16) || !aligned(W_down, 16) || !aligned(X, 16) || !aligned(Y, 16) ||
+      (s_gu && !aligned(s_gu, 16)) || (s_d && !aligned(s_d, 16)))
+    return fail(SWR_E_ALIGN, "%s: weights, scales, X and Y must be 16-byte aligned", fn);
+  if (!aligned(workspace, kWorkspaceAlign)) return fail(SWR_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  const int64_t need = swr_mlp_workspace_bytes(M, H, I, dtype);
+  if (need < 0) return int(need);
+  if (workspace_bytes < need)
+    return fail(SWR_E_CAPACITY, "%s: workspace holds %lld bytes, needs %lld", fn, (long long)workspace_bytes,
+                (long long)need);
+  if (M == 0) {
+    swr::clear_error();
+    return SWR_OK;
+  }
+  void* h = workspace;
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + h_bytes(M, I));
+  const swr::GemmProblem gu = mlp_gate_up(W_gate_up, s_gu, dtype, H, I, X, M, h);
+  const swr::GemmProblem dn = mlp_down(W_down, s_d, dtype, H, I, h, M, Y);
+  const swr::GemmPlan pg = swr::plan_gemm(gu);
+  const swr::GemmPlan pd = swr::plan_gemm(dn);
+  hipError_t e = swr::launch_gemm(gu, pg, partial, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_mlp_forward: gate_up launch");
+  e = swr::launch_gemm(dn, pd, partial, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_mlp_forward: down launch");
+  swr::clear_error();
+  return SWR_OK;
+}

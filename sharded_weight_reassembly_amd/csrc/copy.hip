@@ -1,0 +1,262 @@
+// Byte-moving kernels of the path: the one-time pack into flat chunks, the
+// per-layer reassembly of the chunks into a workspace slot, and the fixed-order
+// sum of split-contraction partials.  All three are HBM-bound streams of
+// 16-byte vectors; none of them does arithmetic on weight values.
+#include "swr_internal.h"
+
+namespace swr {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ----------------------------------------------------------------- reassembly
+//
+// weight_sharding, flat layout step 3: after the gather every rank holds the
+// whole T, i.e. slot[i*C, (i+1)*C) = chunk_i.  Grid: (blocks per chunk, N).
+// Each workgroup copies one contiguous span of one chunk with 16-byte loads
+// and stores, kUnroll vectors in flight per thread.
+constexpr int kCopyUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void reassemble_kernel(ChunkPtrs chunks, u32x4* __restrict__ slot,
+                                                              int64_t chunk_vecs, int64_t span_vecs) {
+  const int c = blockIdx.y;
+  const u32x4* __restrict__ src = static_cast<const u32x4*>(chunks.p[c]);
+  u32x4* __restrict__ dst = slot + int64_t(c) * chunk_vecs;
+  const int64_t begin = int64_t(blockIdx.x) * span_vecs;
+  const int64_t end = min(begin + span_vecs, chunk_vecs);
+  const int64_t step = int64_t(kThreads) * kCopyUnroll;
+  int64_t i = begin + threadIdx.x;
+  // full tiles: every vector of the tile is in range
+  for (; i + (kCopyUnroll - 1) * kThreads < end; i += step) {
+    u32x4 v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * kThreads);
+  }
+  for (; i < end; i += kThreads) dst[i] = src[i];
+}
+
+// --------------------------------------------------------------------- pack
+//
+// weight_sharding, flat layout steps 1-2 and the loading section's one-time
+// re-layout: every 16-byte vector of T is taken from the weight whose byte
+// range covers it (or is zero padding) and written to chunk p / C at p % C.
+// Item offsets and C are multiples of 16, so a vector never spans two items
+// or two chunks; only an item's last vector can be partly padding.
+__global__ __launch_bounds__(kThreads) void pack_kernel(PackPlan plan) {
+  const int64_t nvec = plan.total_bytes / 16;
+  for (int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x; v < nvec;
+       v += int64_t(gridDim.x) * kThreads) {
+    const int64_t p = v * 16;
+    // largest j with off[j] <= p (offsets are increasing)
+    int lo = 0, hi = plan.n_weights - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (plan.off[mid] <= p)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    uint4 out = make_uint4(0, 0, 0, 0);
+    const int64_t rel = p - plan.off[lo];
+    if (rel >= 0 && rel < plan.size[lo]) {
+      const uint8_t* s = static_cast<const uint8_t*>(plan.src[lo]) + rel;
+      if (rel + 16 <= plan.size[lo]) {
+        out = *reinterpret_cast<const uint4*>(s);
+      } else {
+        uint8_t b[16];
+        const int64_t n = plan.size[lo] - rel;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) b[t] = (t < n) ? s[t] : uint8_t(0);
+        out = *reinterpret_cast<const uint4*>(b);
+      }
+    }
+    const int64_t ci = p / plan.chunk_bytes;
+    uint8_t* dst = static_cast<uint8_t*>(plan.chunk[ci]) + (p - ci * plan.chunk_bytes);
+    *reinterpret_cast<uint4*>(dst) = out;
+  }
+}
+
+// ------------------------------------------------------------- sum partials
+//
+// Sharded-matrices notes, local matmul case 3: split-contraction partials add
+// up to the full product.  Added in fp32 in shard order 0..n-1.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 ha = static_cast<__bf16>(a);
+  const __bf16 hb = static_cast<__bf16>(b);
+  return uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
+}
+
+__global__ __launch_bounds__(kThreads) void sum_partials_kernel(PartPtrs parts, int n, int64_t count,
+                                                                void* __restrict__ out, int out_bf16) {
+  const int64_t nvec = count / 4;
+  for (int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x; v < nvec;
+       v += int64_t(gridDim.x) * kThreads) {
+    f32x4 acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[0]) + v);
+    for (int j = 1; j < n; ++j) acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[j]) + v);
+    if (out_bf16) {
+      uint2 o = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+      reinterpret_cast<uint2*>(out)[v] = o;
+    } else {
+      reinterpret_cast<f32x4*>(out)[v] = acc;
+    }
+  }
+  // scalar tail (count % 4 elements), done by the first workgroup
+  if (blockIdx.x == 0) {
+    const int64_t i = nvec * 4 + threadIdx.x;
+    if (i < count) {
+      float acc = parts.p[0][i];
+      for (int j = 1; j < n; ++j) acc += parts.p[j][i];
+      if (out_bf16)
+        reinterpret_cast<__bf16*>(out)[i] = static_cast<__bf16>(acc);
+      else
+        reinterpret_cast<float*>(out)[i] = acc;
+    }
+  }
+}
+
+int grid_for(int64_t work_items, int per_block_items) {
+  int64_t g = (work_items + per_block_items - 1) / per_block_items;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return int(g);
+}
+
+}  // namespace
+
+hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chunk_bytes, void* slot,
+                             hipStream_t stream) {
+  const int64_t chunk_vecs = chunk_bytes / 16;
+  // ~64 KiB per workgroup: thousands of workgroups for MB-sized chunks
+  const int64_t target_span = 4096;
+  int64_t blocks = (chunk_vecs + target_span - 1) / target_span;
+  if (blocks < 1) blocks = 1;
+  const int64_t span = (chunk_vecs + blocks - 1) / blocks;
+  const dim3 grid = dim3(unsigned(blocks), unsigned(n_chunks));
+  hipLaunchKernelGGL(reassemble_kernel, grid, dim3(kThreads), 0, stream, chunks, static_cast<u32x4*>(slot),
+                     chunk_vecs, span);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const PackPlan& plan, hipStream_t stream) {
+  const int grid = grid_for(plan.total_bytes / 16, kThreads * 4);
+  hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(kThreads), 0, stream, plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_partials(const PartPtrs& parts, int n, int64_t count, void* out, bool out_bf16,
+                               hipStream_t stream) {
+  const int grid = grid_for(count / 4 + 1, kThreads * 4);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(grid), dim3(kThreads), 0, stream, parts, n, count, out,
+                     out_bf16 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace swr
+
+// ====================================================================== C ABI
+
+using swr::aligned;
+using swr::fail;
+
+extern "C" int swr_pack_layer(const swr_layout* layout, const swr_view_desc* views,
+                              const void* const* src_dev, void* const* chunk_dev, hipStream_t stream) {
+  if (!layout || !views || !src_dev || !chunk_dev) return fail(SWR_E_INVALID, "swr_pack_layer: null pointer");
+  const int nw = layout->n_weights, nc = layout->n_chunks;
+  if (nw < 1 || nw > SWR_MAX_WEIGHTS || nc < 1 || nc > SWR_MAX_CHUNKS)
+    return fail(SWR_E_INVALID, "swr_pack_layer: n_weights=%d n_chunks=%d out of range", nw, nc);
+  if (layout->total_bytes <= 0 || layout->total_bytes % (16 * int64_t(nc)) != 0 ||
+      layout->chunk_bytes * nc != layout->total_bytes)
+    return fail(SWR_E_INVALID, "swr_pack_layer: inconsistent layout (|T|=%lld, C=%lld, N=%d)",
+                (long long)layout->total_bytes, (long long)layout->chunk_bytes, nc);
+  swr::PackPlan plan{};
+  int64_t prev_end = 0;
+  for (int j = 0; j < nw; ++j) {
+    const swr_view_desc& v = views[j];
+    if (v.offset % 16 != 0 || v.offset < prev_end || v.nbytes <= 0 || v.offset + v.nbytes > layout->payload_bytes)
+      return fail(SWR_E_INVALID, "swr_pack_layer: view %d (offset %lld, %lld bytes) does not fit the layout", j,
+                  (long long)v.offset, (long long)v.nbytes);
+    if (!src_dev[j]) return fail(SWR_E_INVALID, "swr_pack_layer: src_dev[%d] is null", j);
+    if (!aligned(src_dev[j], 16)) return fail(SWR_E_ALIGN, "swr_pack_layer: src_dev[%d] not 16-byte aligned", j);
+    plan.src[j] = src_dev[j];
+    plan.off[j] = v.offset;
+    plan.size[j] = v.nbytes;
+    prev_end = v.offset + v.nbytes;
+  }
+  if (layout->payload_bytes > layout->total_bytes)
+    return fail(SWR_E_INVALID, "swr_pack_layer: payload larger than |T|");
+  for (int i = 0; i < nc; ++i) {
+    if (!chunk_dev[i]) return fail(SWR_E_INVALID, "swr_pack_layer: chunk_dev[%d] is null", i);
+    if (!aligned(chunk_dev[i], 16)) return fail(SWR_E_ALIGN, "swr_pack_layer: chunk_dev[%d] not 16-byte aligned", i);
+    plan.chunk[i] = chunk_dev[i];
+  }
+  plan.chunk_bytes = layout->chunk_bytes;
+  plan.total_bytes = layout->total_bytes;
+  plan.n_weights = nw;
+  plan.n_chunks = nc;
+  const hipError_t e = swr::launch_pack(plan, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_pack_layer: launch");
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_reassemble_into_slot(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
+                                        void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
+                                        hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes) {
+  if (!chunk_dev || !slot) return fail(SWR_E_INVALID, "swr_reassemble_into_slot: null pointer");
+  if (n_chunks < 1 || n_chunks > SWR_MAX_CHUNKS)
+    return fail(SWR_E_INVALID, "swr_reassemble_into_slot: n_chunks=%d outside [1, %d]", n_chunks, SWR_MAX_CHUNKS);
+  if (chunk_bytes <= 0 || chunk_bytes % 16 != 0)
+    return fail(SWR_E_ALIGN, "swr_reassemble_into_slot: chunk_bytes=%lld is not a positive multiple of 16",
+                (long long)chunk_bytes);
+  if (self_rank < 0 || self_rank >= n_chunks)
+    return fail(SWR_E_INVALID, "swr_reassemble_into_slot: self_rank=%d outside [0, %d)", self_rank, n_chunks);
+  if (slot_bytes < chunk_bytes * n_chunks)
+    return fail(SWR_E_CAPACITY, "swr_reassemble_into_slot: slot holds %lld bytes, layer needs %lld",
+                (long long)slot_bytes, (long long)(chunk_bytes * n_chunks));
+  if (!aligned(slot, 16)) return fail(SWR_E_ALIGN, "swr_reassemble_into_slot: slot not 16-byte aligned");
+  swr::ChunkPtrs ptrs{};
+  for (int i = 0; i < n_chunks; ++i) {
+    if (!chunk_dev[i]) return fail(SWR_E_INVALID, "swr_reassemble_into_slot: chunk_dev[%d] is null", i);
+    if (!aligned(chunk_dev[i], 16))
+      return fail(SWR_E_ALIGN, "swr_reassemble_into_slot: chunk_dev[%d] not 16-byte aligned", i);
+    ptrs.p[i] = chunk_dev[i];
+  }
+  hipError_t e;
+  if (gate) {
+    e = hipStreamWaitEvent(side, gate, 0);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_reassemble_into_slot: wait gate");
+  }
+  e = swr::launch_reassemble(ptrs, n_chunks, chunk_bytes, slot, side);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_reassemble_into_slot: launch");
+  if (ready) {
+    e = hipEventRecord(ready, side);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_reassemble_into_slot: record ready");
+  }
+  if (remote_bytes) *remote_bytes += int64_t(n_chunks - 1) * chunk_bytes;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_sum_partials(const float* const* parts, int32_t n, int64_t count, void* out, int32_t out_bf16,
+                                hipStream_t stream) {
+  if (!parts || !out) return fail(SWR_E_INVALID, "swr_sum_partials: null pointer");
+  if (n < 1 || n > SWR_MAX_CHUNKS) return fail(SWR_E_INVALID, "swr_sum_partials: n=%d outside [1, 64]", n);
+  if (count < 0) return fail(SWR_E_INVALID, "swr_sum_partials: negative count");
+  if (!aligned(out, 16)) return fail(SWR_E_ALIGN, "swr_sum_partials: out not 16-byte aligned");
+  swr::PartPtrs ptrs{};
+  for (int j = 0; j < n; ++j) {
+    if (!parts[j]) return fail(SWR_E_INVALID, "swr_sum_partials: parts[%d] is null", j);
+    if (!aligned(parts[j], 16)) return fail(SWR_E_ALIGN, "swr_sum_partials: parts[%d] not 16-byte aligned", j);
+    ptrs.p[j] = parts[j];
+  }
+  if (count == 0) {
+    swr::clear_error();
+    return SWR_OK;
+  }
+  const hipError_t e = swr::launch_sum_partials(ptrs, n, count, out, out_bf16 != 0, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_sum_partials: launch");
+  swr::clear_error();
+  return SWR_OK;
+}

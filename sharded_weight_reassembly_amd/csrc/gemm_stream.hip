@@ -1,0 +1,469 @@
+// Weight-streaming GEMM for decode-shaped (skinny) activations on gfx950.
+//
+//   Y[m, o] = s[o] * sum_k X[m, k] * W[o, k]        W: out x in, K contiguous
+//
+// At M <= 64 tokens the work is bound by reading W from HBM once (264 MB per
+// shared-expert layer), so the kernel is organised around that stream:
+//   * a workgroup owns RT 16-row tiles of W and a K range; its 4 waves split
+//     the range in 64-element steps (wave w takes steps w, w+4, ...), so the
+//     workgroup reads 4 * 64 contiguous K of every row at a time;
+//   * every lane loads 16 contiguous weight bytes per row tile per step
+//     (lane = 16 rows x 4 K-groups), two steps ahead of the MFMAs;
+//   * FP8 E4M3FN codes are widened to BF16 in registers (exact: every E4M3FN
+//     value is a BF16 value) and multiplied on the matrix cores with
+//     v_mfma_f32_16x16x32_bf16 against the BF16 activations, fp32 accumulate.
+//     The A and B operands use the same K permutation, so any K order inside
+//     a step is consistent;
+//   * the per-row scale is applied once to the fp32 sum (the weight-sharding
+//     page's loading section keeps FP8 scales outside the flat buffer);
+//   * the 4 waves' partial sums are added in LDS; with more than one K split
+//     per row tile the workgroups write fp32 partials that a small finalize
+//     kernel adds in split order.
+// The MLP's gate_up projection runs in a fused mode: a workgroup owns gate
+// rows j..j+8RT and the matching up rows I+j..I+j+8RT, and writes
+// h = bf16(silu(G_gate) * G_up) directly (vLLM PR #50656 report, test code:
+// gate rows first, SiLU of the gate half times the up half).
+#include "swr_internal.h"
+
+namespace swr {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kStepK = 64;  // K elements per wave step
+
+struct StreamArgs {
+  const uint8_t* W;
+  const float* scale;
+  const uint16_t* X;
+  int64_t ldx;
+  int64_t M;
+  int64_t rows;
+  int64_t K;
+  int64_t kper;   // K per workgroup split
+  int64_t inter;  // I in SILU mode
+  void* Y;
+  int64_t ldy;
+  float* partial;  // [ksplit][M][rows] when ksplit > 1
+  int mode;
+  int ksplit;
+};
+
+__device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0];
+  r[1] = a[1];
+  r[2] = b[0];
+  r[3] = b[1];
+  r[4] = c[0];
+  r[5] = c[1];
+  r[6] = d[0];
+  r[7] = d[1];
+  return r;
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+
+// Per-lane weight data of one step for one 16-row tile: 16 K elements.
+template <bool FP8>
+struct WFrag;
+template <>
+struct WFrag<true> {
+  u32x4 v;
+};
+template <>
+struct WFrag<false> {
+  u32x4 v[2];
+};
+
+template <bool FP8>
+__device__ inline void load_w(WFrag<FP8>& f, const uint8_t* p);
+template <>
+__device__ inline void load_w<true>(WFrag<true>& f, const uint8_t* p) {
+  f.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+template <>
+__device__ inline void load_w<false>(WFrag<false>& f, const uint8_t* p) {
+  f.v[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  f.v[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + 1);
+}
+
+template <bool FP8>
+__device__ inline void to_operands(const WFrag<FP8>& f, bf16x8& a0, bf16x8& a1);
+template <>
+__device__ inline void to_operands<true>(const WFrag<true>& f, bf16x8& a0, bf16x8& a1) {
+  a0 = fp8x8_to_bf16(f.v[0], f.v[1]);
+  a1 = fp8x8_to_bf16(f.v[2], f.v[3]);
+}
+template <>
+__device__ inline void to_operands<false>(const WFrag<false>& f, bf16x8& a0, bf16x8& a1) {
+  a0 = as_bf16x8(f.v[0]);
+  a1 = as_bf16x8(f.v[1]);
+}
+
+template <int MT, int RT, bool FP8>
+struct Step {
+  WFrag<FP8> w[RT];
+  u32x4 x[MT][2];
+};
+
+template <int MT, int RT, bool FP8>
+__device__ inline void load_step(Step<MT, RT, FP8>& st, const uint8_t* const (&wp)[RT],
+                                 const uint16_t* const (&xp)[MT], int64_t k) {
+  constexpr int64_t eb = FP8 ? 1 : 2;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) load_w<FP8>(st.w[t], wp[t] + k * eb);
+#pragma unroll
+  for (int b = 0; b < MT; ++b) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(xp[b] + k);
+    st.x[b][0] = p[0];
+    st.x[b][1] = p[1];
+  }
+}
+
+template <int MT, int RT, bool FP8>
+__device__ inline void mma_step(const Step<MT, RT, FP8>& st, f32x4 (&acc)[RT][MT]) {
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    bf16x8 a0, a1;
+    to_operands<FP8>(st.w[t], a0, a1);
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(st.x[b][0]), acc[t][b], 0, 0, 0);
+      acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(st.x[b][1]), acc[t][b], 0, 0, 0);
+    }
+  }
+}
+
+// Output row of tile t, lane-row r (0..15) of this workgroup.
+template <int RT>
+__device__ inline int64_t tile_row(const StreamArgs& a, int t) {
+  if (a.mode == OUT_SILU_BF16) {
+    constexpr int half = RT / 2;
+    const int64_t j0 = int64_t(blockIdx.x) * 16 * half;
+    return t < half ? j0 + t * 16 : a.inter + j0 + (t - half) * 16;
+  }
+  return int64_t(blockIdx.x) * 16 * RT + t * 16;
+}
+
+__device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, const float (&v)[4], bool bf16_out) {
+  if (bf16_out) {
+    uint16_t* y = static_cast<uint16_t*>(a.Y) + tok * a.ldy + row;
+    if (row + 4 <= a.rows && ((reinterpret_cast<uintptr_t>(y) & 7) == 0)) {
+      uint2 o;
+      o.x = uint32_t(bf16_bits(v[0])) | (uint32_t(bf16_bits(v[1])) << 16);
+      o.y = uint32_t(bf16_bits(v[2])) | (uint32_t(bf16_bits(v[3])) << 16);
+      *reinterpret_cast<uint2*>(y) = o;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (row + i < a.rows) y[i] = bf16_bits(v[i]);
+    }
+  } else {
+    float* y = static_cast<float*>(a.Y) + tok * a.ldy + row;
+    if (row + 4 <= a.rows && ((reinterpret_cast<uintptr_t>(y) & 15) == 0)) {
+      *reinterpret_cast<float4*>(y) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (row + i < a.rows) y[i] = v[i];
+    }
+  }
+}
+
+template <int MT, int RT, bool FP8>
+__global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) {
+  constexpr int64_t eb = FP8 ? 1 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int64_t k_begin = int64_t(blockIdx.y) * a.kper;
+  const int64_t k_end = min(a.K, k_begin + a.kper);
+  const int nsub = int((k_end - k_begin) / kStepK);
+  const int64_t tok0 = int64_t(blockIdx.z) * 16 * MT;
+
+  const uint8_t* wp[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    int64_t r = tile_row<RT>(a, t) + r16;
+    r = min(r, a.rows - 1);  // rows past the end are loaded from the last row and never stored
+    wp[t] = a.W + (r * a.K + k_begin + grp * 16) * eb;
+  }
+  const uint16_t* xp[MT];
+#pragma unroll
+  for (int b = 0; b < MT; ++b) {
+    const int64_t m = min(tok0 + b * 16 + r16, a.M - 1);
+    xp[b] = a.X + m * a.ldx + k_begin + grp * 16;
+  }
+
+  f32x4 acc[RT][MT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int b = 0; b < MT; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // two steps in flight per wave
+  Step<MT, RT, FP8> s0, s1;
+  int s = wave;
+  if (s < nsub) load_step<MT, RT, FP8>(s0, wp, xp, int64_t(s) * kStepK);
+  if (s + kWaves < nsub) load_step<MT, RT, FP8>(s1, wp, xp, int64_t(s + kWaves) * kStepK);
+  for (; s < nsub; s += 2 * kWaves) {
+    mma_step<MT, RT, FP8>(s0, acc);
+    if (s + 2 * kWaves < nsub) load_step<MT, RT, FP8>(s0, wp, xp, int64_t(s + 2 * kWaves) * kStepK);
+    if (s + kWaves < nsub) {
+      mma_step<MT, RT, FP8>(s1, acc);
+      if (s + 3 * kWaves < nsub) load_step<MT, RT, FP8>(s1, wp, xp, int64_t(s + 3 * kWaves) * kStepK);
+    }
+  }
+
+  // ---- add the 4 waves' sums in LDS: red[wave][t][b][v][lane]
+  __shared__ float red[kWaves][RT][MT][4][64];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int b = 0; b < MT; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][t][b][v][lane] = acc[t][b][v];
+  __syncthreads();
+
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  const int tiles_out = silu_mode ? RT / 2 : RT;
+  const int items = tiles_out * MT * 64;
+  for (int q = threadIdx.x; q < items; q += kThreads) {
+    const int ql = q & 63;
+    const int b = (q >> 6) % MT;
+    const int t = (q >> 6) / MT;
+    const int64_t tok = tok0 + b * 16 + (ql & 15);
+    if (tok >= a.M) continue;
+    const int64_t row = tile_row<RT>(a, t) + 4 * (ql >> 4);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += red[w][t][b][i][ql];
+      v[i] = sum;
+    }
+    if (silu_mode) {
+      const int64_t urow = tile_row<RT>(a, t + RT / 2) + 4 * (ql >> 4);
+      float u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += red[w][t + RT / 2][b][i][ql];
+        u[i] = sum;
+      }
+      if (a.ksplit > 1) {
+        float* pg = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pg[row + i] = v[i];
+          pg[urow + i] = u[i];
+        }
+        continue;
+      }
+      float h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = v[i] * (a.scale ? a.scale[row + i] : 1.f);
+        const float up = u[i] * (a.scale ? a.scale[urow + i] : 1.f);
+        h[i] = silu(g) * up;
+      }
+      // h is [M, ldy] with I columns; `row` is the gate index j
+      StreamArgs hb = a;
+      hb.rows = a.inter;
+      store4(hb, tok, row, h, true);
+      continue;
+    }
+    if (a.ksplit > 1) {
+      float* pr = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
+      for (int i = 0; i < 4; ++i)
+        if (row + i < a.rows) pr[row + i] = v[i];
+      continue;
+    }
+    if (a.scale) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= (row + i < a.rows) ? a.scale[row + i] : 0.f;
+    }
+    store4(a, tok, row, v, a.mode == OUT_BF16);
+  }
+}
+
+// Adds the split-K partials in split order and applies scale / SiLU / rounding.
+// One thread per (token, 4 consecutive output columns).
+__global__ __launch_bounds__(kThreads) void splitk_finalize_kernel(StreamArgs a) {
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  const int64_t cols = silu_mode ? a.inter : a.rows;
+  const int64_t groups = (cols + 3) / 4;
+  const int64_t total = a.M * groups;
+  for (int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x; q < total; q += int64_t(gridDim.x) * kThreads) {
+    const int64_t tok = q / groups;
+    const int64_t c0 = (q % groups) * 4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.ksplit; ++s) {
+      const float* p = a.partial + (int64_t(s) * a.M + tok) * a.rows;
+      for (int i = 0; i < 4; ++i) {
+        if (c0 + i < cols) {
+          v[i] += p[c0 + i];
+          if (silu_mode) u[i] += p[a.inter + c0 + i];
+        }
+      }
+    }
+    if (silu_mode) {
+      for (int i = 0; i < 4; ++i) {
+        if (c0 + i >= cols) continue;
+        const float g = v[i] * (a.scale ? a.scale[c0 + i] : 1.f);
+        const float up = u[i] * (a.scale ? a.scale[a.inter + c0 + i] : 1.f);
+        v[i] = silu(g) * up;
+      }
+      StreamArgs hb = a;
+      hb.rows = a.inter;
+      store4(hb, tok, c0, v, true);
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (a.scale && c0 + i < cols) v[i] *= a.scale[c0 + i];
+      store4(a, tok, c0, v, a.mode == OUT_BF16);
+    }
+  }
+}
+
+// Any shape and alignment; one thread per output.  Used only when K is not a
+// multiple of 64 or an operand is not 16-byte aligned (odd projections).
+__global__ __launch_bounds__(kThreads) void generic_gemm_kernel(StreamArgs a, int fp8) {
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  const int64_t cols = silu_mode ? a.inter : a.rows;
+  const int64_t total = a.M * cols;
+  for (int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x; q < total; q += int64_t(gridDim.x) * kThreads) {
+    const int64_t tok = q / cols;
+    const int64_t c = q % cols;
+    const uint16_t* x = a.X + tok * a.ldx;
+    auto dot = [&](int64_t row) {
+      float acc = 0.f;
+      for (int64_t k = 0; k < a.K; ++k) {
+        float w;
+        if (fp8) {
+          const uint32_t code = a.W[row * a.K + k];
+          w = static_cast<float>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(code, 1.0f, false)[0]);
+        } else {
+          w = __builtin_bit_cast(float, uint32_t(reinterpret_cast<const uint16_t*>(a.W)[row * a.K + k]) << 16);
+        }
+        const float xv = __builtin_bit_cast(float, uint32_t(x[k]) << 16);
+        acc = fmaf(xv, w, acc);
+      }
+      return acc * (a.scale ? a.scale[row] : 1.f);
+    };
+    float y;
+    if (silu_mode) {
+      y = silu(dot(c)) * dot(a.inter + c);
+    } else {
+      y = dot(c);
+    }
+    if (a.mode == OUT_F32)
+      static_cast<float*>(a.Y)[tok * a.ldy + c] = y;
+    else
+      static_cast<uint16_t*>(a.Y)[tok * a.ldy + c] = bf16_bits(y);
+  }
+}
+
+template <int MT, int RT, bool FP8>
+hipError_t launch_stream(const StreamArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((stream_gemm_kernel<MT, RT, FP8>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int RT, bool FP8>
+hipError_t dispatch_mt(int mt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
+  switch (mt) {
+    case 1:
+      return launch_stream<1, RT, FP8>(a, grid, stream);
+    case 2:
+      return launch_stream<2, RT, FP8>(a, grid, stream);
+    default:
+      return launch_stream<4, RT, FP8>(a, grid, stream);
+  }
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(const GemmProblem& p) {
+  GemmPlan plan{};
+  const bool silu_mode = p.mode == OUT_SILU_BF16;
+  const int64_t inter = silu_mode ? p.rows / 2 : 0;
+  const bool fast = p.K % kStepK == 0 && aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0 &&
+                    (!silu_mode || inter % 32 == 0);
+  if (!fast) {
+    plan.kind = 1;
+    plan.ksplit = 1;
+    plan.kper = p.K;
+    return plan;
+  }
+  plan.kind = 0;
+  plan.mt = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
+  plan.rt = 4;
+  const int64_t row_blocks = silu_mode ? inter / (8 * plan.rt) : (p.rows + 16 * plan.rt - 1) / (16 * plan.rt);
+  const int64_t k256 = (p.K + 255) / 256;
+  int64_t ks = 1;
+  if (p.M <= 64) {
+    const int64_t target = 512;  // about two workgroups per CU
+    ks = (target + row_blocks - 1) / row_blocks;
+    if (ks > k256) ks = k256;
+    if (ks < 1) ks = 1;
+  }
+  const int64_t per = (k256 + ks - 1) / ks;
+  plan.kper = per * 256;
+  plan.ksplit = int((p.K + plan.kper - 1) / plan.kper);
+  plan.partial_bytes = plan.ksplit > 1 ? int64_t(plan.ksplit) * p.M * p.rows * 4 : 0;
+  return plan;
+}
+
+hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream) {
+  StreamArgs a{};
+  a.W = static_cast<const uint8_t*>(p.W);
+  a.scale = p.scale;
+  a.X = static_cast<const uint16_t*>(p.X);
+  a.ldx = p.ldx;
+  a.M = p.M;
+  a.rows = p.rows;
+  a.K = p.K;
+  a.kper = plan.kper;
+  a.inter = p.mode == OUT_SILU_BF16 ? p.rows / 2 : 0;
+  a.Y = p.Y;
+  a.ldy = p.ldy;
+  a.partial = partial;
+  a.mode = p.mode;
+  a.ksplit = plan.ksplit;
+  const bool fp8 = p.dtype == SWR_FP8_E4M3FN;
+  if (plan.kind == 1) {
+    const int64_t cols = p.mode == OUT_SILU_BF16 ? a.inter : p.rows;
+    int64_t g = (p.M * cols + kThreads - 1) / kThreads;
+    if (g > 65536) g = 65536;
+    hipLaunchKernelGGL(generic_gemm_kernel, dim3(unsigned(g)), dim3(kThreads), 0, stream, a, fp8 ? 1 : 0);
+    return hipGetLastError();
+  }
+  const int64_t row_blocks = p.mode == OUT_SILU_BF16 ? a.inter / (8 * plan.rt)
+                                                      : (p.rows + 16 * plan.rt - 1) / (16 * plan.rt);
+  const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
+  const dim3 grid = dim3(unsigned(row_blocks), unsigned(plan.ksplit), unsigned(tok_blocks));
+  hipError_t e = fp8 ? dispatch_mt<4, true>(plan.mt, a, grid, stream) : dispatch_mt<4, false>(plan.mt, a, grid, stream);
+  if (e != hipSuccess || plan.ksplit == 1) return e;
+  const int64_t cols = p.mode == OUT_SILU_BF16 ? a.inter : p.rows;
+  int64_t g = (p.M * ((cols + 3) / 4) + kThreads - 1) / kThreads;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(splitk_finalize_kernel, dim3(unsigned(g)), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace swr

@@ -1,0 +1,254 @@
+// Lookahead / ping-pong planner (weight_sharding, zdszero.github.io):
+//   * section "lookahead and ping-pong slot": the gather of layer l+1 runs on a
+//     side stream while layer l computes; layer l+1 waits on the gather's
+//     ready event; two slots alternate by layer, so the gather of l+1 first
+//     waits for the done event of l-1, the last reader of that slot;
+//   * section "implementation in SGLang": reset(), pre_dispatch(start), and
+//     per layer maybe_dispatch(i+1), the layer, update_done_event(i);
+//   * section "CUDA graph and the draft model": the compute stream waits at
+//     most once per layer (wait_ready_once) and the sequence is fixed at init.
+// A gather with no earlier layer in the forward is gated by a forward-start
+// event recorded by reset() on the compute stream.
+#include <vector>
+
+#include "swr_internal.h"
+
+using swr::fail;
+
+struct swr_planner {
+  int32_t start = 0, end = 0;
+  hipStream_t compute = nullptr, side = nullptr;
+  void* slot[2] = {nullptr, nullptr};
+  int64_t slot_bytes = 0;
+
+  struct Layer {
+    std::vector<const void*> chunks;
+    int64_t chunk_bytes = 0;
+  };
+  std::vector<Layer> layers;
+  hipEvent_t start_evt = nullptr;
+  std::vector<hipEvent_t> ready, done;
+
+  // per-forward state
+  bool reset_called = false;
+  std::vector<uint8_t> dispatched, waited, finished;
+
+  int64_t remote_bytes = 0;
+  int64_t gathers = 0;
+  std::vector<int32_t> trace;
+
+  int idx(int32_t layer) const { return layer - start; }
+  bool in_range(int32_t layer) const { return layer >= start && layer < end; }
+  int slot_of(int32_t layer) const { return (layer - start) & 1; }
+  void log(int32_t op, int32_t stream, int32_t layer, int32_t slot_id) {
+    trace.push_back(op);
+    trace.push_back(stream);
+    trace.push_back(layer);
+    trace.push_back(slot_id);
+  }
+};
+
+namespace {
+
+void destroy_events(swr_planner* p) {
+  if (p->start_evt) (void)hipEventDestroy(p->start_evt);
+  for (hipEvent_t e : p->ready)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->done)
+    if (e) (void)hipEventDestroy(e);
+}
+
+// Side stream: gate, gather of `layer` into its slot, ready record.
+int dispatch(swr_planner* p, int32_t layer) {
+  const int i = p->idx(layer);
+  const swr_planner::Layer& L = p->layers[i];
+  if (L.chunks.empty()) return fail(SWR_E_SEQUENCE, "planner: layer %d has no chunks (swr_planner_set_layer)", layer);
+  hipEvent_t gate;
+  const int32_t prev = layer - 2;  // last reader of the slot this gather overwrites
+  if (prev >= p->start) {
+    if (!p->finished[p->idx(prev)])
+      return fail(SWR_E_SEQUENCE, "planner: gather of layer %d needs done(%d), which was not recorded", layer, prev);
+    gate = p->done[p->idx(prev)];
+  } else {
+    gate = p->start_evt;
+  }
+  const int s = p->slot_of(layer);
+  int64_t remote = 0;
+  const int rc = swr_reassemble_into_slot(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s],
+                                          p->slot_bytes, 0, p->side, gate, p->ready[i], &remote);
+  if (rc != SWR_OK) return rc;
+  if (prev >= p->start)
+    p->log(SWR_OP_WAIT_DONE, SWR_STREAM_SIDE, prev, -1);
+  else
+    p->log(SWR_OP_WAIT_START, SWR_STREAM_SIDE, -1, -1);
+  p->log(SWR_OP_COPY, SWR_STREAM_SIDE, layer, s);
+  p->log(SWR_OP_RECORD_READY, SWR_STREAM_SIDE, layer, -1);
+  p->dispatched[i] = 1;
+  p->remote_bytes += remote;
+  p->gathers += 1;
+  return SWR_OK;
+}
+
+}  // namespace
+
+extern "C" int swr_planner_create(int32_t start, int32_t end, hipStream_t compute, hipStream_t side, void* slot_a,
+                                  void* slot_b, int64_t slot_bytes, swr_planner** out) {
+  if (!out || !slot_a || !slot_b) return fail(SWR_E_INVALID, "swr_planner_create: null pointer");
+  *out = nullptr;
+  if (end <= start || start < 0) return fail(SWR_E_INVALID, "swr_planner_create: empty range [%d, %d)", start, end);
+  if (end - start > (1 << 20)) return fail(SWR_E_INVALID, "swr_planner_create: too many layers");
+  if (compute == side) return fail(SWR_E_INVALID, "swr_planner_create: compute and side must be different streams");
+  if (slot_bytes <= 0) return fail(SWR_E_INVALID, "swr_planner_create: slot_bytes must be positive");
+  if (!swr::aligned(slot_a, 16) || !swr::aligned(slot_b, 16))
+    return fail(SWR_E_ALIGN, "swr_planner_create: slots must be 16-byte aligned");
+  swr_planner* p = new swr_planner();
+  p->start = start;
+  p->end = end;
+  p->compute = compute;
+  p->side = side;
+  p->slot[0] = slot_a;
+  p->slot[1] = slot_b;
+  p->slot_bytes = slot_bytes;
+  const int n = end - start;
+  p->layers.resize(n);
+  p->ready.assign(n, nullptr);
+  p->done.assign(n, nullptr);
+  p->dispatched.assign(n, 0);
+  p->waited.assign(n, 0);
+  p->finished.assign(n, 0);
+  hipError_t e = hipEventCreateWithFlags(&p->start_evt, hipEventDisableTiming);
+  for (int i = 0; e == hipSuccess && i < n; ++i) {
+    e = hipEventCreateWithFlags(&p->ready[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->done[i], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    destroy_events(p);
+    delete p;
+    return swr::hip_fail(e, "swr_planner_create: hipEventCreate");
+  }
+  *out = p;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_layer(swr_planner* p, int32_t layer, const void* const* chunk_dev, int32_t n_chunks,
+                                     int64_t chunk_bytes) {
+  if (!p || !chunk_dev) return fail(SWR_E_INVALID, "swr_planner_set_layer: null pointer");
+  if (!p->in_range(layer))
+    return fail(SWR_E_INVALID, "swr_planner_set_layer: layer %d outside [%d, %d)", layer, p->start, p->end);
+  if (n_chunks < 1 || n_chunks > SWR_MAX_CHUNKS)
+    return fail(SWR_E_INVALID, "swr_planner_set_layer: n_chunks=%d outside [1, 64]", n_chunks);
+  if (chunk_bytes <= 0 || chunk_bytes % 16)
+    return fail(SWR_E_ALIGN, "swr_planner_set_layer: chunk_bytes must be a positive multiple of 16");
+  if (chunk_bytes * n_chunks > p->slot_bytes)
+    return fail(SWR_E_CAPACITY, "swr_planner_set_layer: layer %d needs %lld bytes, slots hold %lld", layer,
+                (long long)(chunk_bytes * n_chunks), (long long)p->slot_bytes);
+  for (int i = 0; i < n_chunks; ++i) {
+    if (!chunk_dev[i]) return fail(SWR_E_INVALID, "swr_planner_set_layer: chunk %d is null", i);
+    if (!swr::aligned(chunk_dev[i], 16)) return fail(SWR_E_ALIGN, "swr_planner_set_layer: chunk %d misaligned", i);
+  }
+  swr_planner::Layer& L = p->layers[p->idx(layer)];
+  L.chunks.assign(chunk_dev, chunk_dev + n_chunks);
+  L.chunk_bytes = chunk_bytes;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_reset(swr_planner* p) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_reset: null pointer");
+  const hipError_t e = hipEventRecord(p->start_evt, p->compute);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_reset: record start");
+  std::fill(p->dispatched.begin(), p->dispatched.end(), 0);
+  std::fill(p->waited.begin(), p->waited.end(), 0);
+  std::fill(p->finished.begin(), p->finished.end(), 0);
+  p->trace.clear();
+  p->log(SWR_OP_RECORD_START, SWR_STREAM_COMPUTE, -1, -1);
+  p->reset_called = true;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_pre_dispatch(swr_planner* p, int32_t layer) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_pre_dispatch: null pointer");
+  if (!p->reset_called) return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: call swr_planner_reset first");
+  if (layer != p->start)
+    return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: layer %d is not the first layer %d", layer, p->start);
+  if (p->dispatched[0]) return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: already dispatched");
+  const int rc = dispatch(p, layer);
+  if (rc == SWR_OK) swr::clear_error();
+  return rc;
+}
+
+extern "C" int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_maybe_dispatch: null pointer");
+  if (!p->in_range(layer)) {
+    swr::clear_error();
+    return SWR_OK;
+  }
+  if (!p->reset_called) return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: call swr_planner_reset first");
+  if (p->dispatched[p->idx(layer)])
+    return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d already dispatched in this forward", layer);
+  if (layer > p->start && !p->dispatched[p->idx(layer - 1)])
+    return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d before layer %d", layer, layer - 1);
+  const int rc = dispatch(p, layer);
+  if (rc == SWR_OK) swr::clear_error();
+  return rc;
+}
+
+extern "C" int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void** slot_out) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_wait_ready_once: null pointer");
+  if (!p->in_range(layer))
+    return fail(SWR_E_INVALID, "swr_planner_wait_ready_once: layer %d outside [%d, %d)", layer, p->start, p->end);
+  const int i = p->idx(layer);
+  if (!p->dispatched[i]) return fail(SWR_E_SEQUENCE, "swr_planner_wait_ready_once: layer %d not dispatched", layer);
+  if (!p->waited[i]) {
+    const hipError_t e = hipStreamWaitEvent(p->compute, p->ready[i], 0);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_wait_ready_once: wait");
+    p->waited[i] = 1;
+    p->log(SWR_OP_WAIT_READY, SWR_STREAM_COMPUTE, layer, p->slot_of(layer));
+  }
+  if (slot_out) *slot_out = p->slot[p->slot_of(layer)];
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_update_done_event: null pointer");
+  if (!p->in_range(layer))
+    return fail(SWR_E_INVALID, "swr_planner_update_done_event: layer %d outside [%d, %d)", layer, p->start, p->end);
+  const int i = p->idx(layer);
+  if (!p->waited[i])
+    return fail(SWR_E_SEQUENCE, "swr_planner_update_done_event: layer %d did not wait for its weights", layer);
+  const hipError_t e = hipEventRecord(p->done[i], p->compute);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record");
+  p->finished[i] = 1;
+  p->log(SWR_OP_RECORD_DONE, SWR_STREAM_COMPUTE, layer, -1);
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_counters(const swr_planner* p, int64_t* remote_bytes, int64_t* gathers) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_counters: null pointer");
+  if (remote_bytes) *remote_bytes = p->remote_bytes;
+  if (gathers) *gathers = p->gathers;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_trace(const swr_planner* p, int32_t* ops, int32_t cap, int32_t* n) {
+  if (!p || !n) return fail(SWR_E_INVALID, "swr_planner_trace: null pointer");
+  const int32_t count = int32_t(p->trace.size() / 4);
+  *n = count;
+  if (ops) {
+    const int32_t m = count < cap ? count : cap;
+    for (int32_t i = 0; i < 4 * m; ++i) ops[i] = p->trace[i];
+  }
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" void swr_planner_destroy(swr_planner* p) {
+  if (!p) return;
+  destroy_events(p);
+  delete p;
+}

@@ -1,0 +1,81 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swr.h"
+
+namespace swr {
+
+// Native 16-byte vectors (usable with the nontemporal load/store builtins).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Records a printf-style message as the calling thread's last error and
+// returns `code` so call sites can `return fail(...)`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int hip_fail(hipError_t e, const char* what);
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- copies
+struct ChunkPtrs {
+  const void* p[SWR_MAX_CHUNKS];
+};
+hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chunk_bytes, void* slot,
+                             hipStream_t stream);
+
+struct PackPlan {
+  const void* src[SWR_MAX_WEIGHTS];
+  int64_t off[SWR_MAX_WEIGHTS];
+  int64_t size[SWR_MAX_WEIGHTS];
+  void* chunk[SWR_MAX_CHUNKS];
+  int64_t chunk_bytes;
+  int64_t total_bytes;
+  int32_t n_weights;
+  int32_t n_chunks;
+};
+hipError_t launch_pack(const PackPlan& plan, hipStream_t stream);
+
+struct PartPtrs {
+  const float* p[SWR_MAX_CHUNKS];
+};
+hipError_t launch_sum_partials(const PartPtrs& parts, int n, int64_t count, void* out, bool out_bf16,
+                               hipStream_t stream);
+
+// ---------------------------------------------------------------- GEMMs
+enum OutMode { OUT_BF16 = 0, OUT_F32 = 1, OUT_SILU_BF16 = 2 };
+
+// One weight-streaming GEMM  Y[m, o] = s[o] * sum_k X[m, k] W[o, k]  (or, in
+// OUT_SILU_BF16 mode, h[m, j] = silu(G[m, j]) * G[m, I + j] with G the scaled
+// product over 2I rows).  The plan fixes the kernel shape and split-K.
+struct GemmProblem {
+  const void* W;
+  int dtype;
+  const float* scale;  // may be null
+  const void* X;       // bf16
+  int64_t ldx;
+  int64_t M;
+  int64_t rows;  // output rows of W (2I in SILU mode)
+  int64_t K;
+  void* Y;
+  int64_t ldy;
+  int mode;
+};
+
+struct GemmPlan {
+  int kind;      // 0 = streaming MFMA kernel, 1 = generic kernel
+  int mt;        // 16-token blocks per workgroup (1, 2, 4)
+  int rt;        // 16-row tiles per workgroup
+  int ksplit;    // workgroups along K
+  int64_t kper;  // K elements per split (multiple of 256)
+  int64_t partial_bytes;  // fp32 split-K scratch needed (0 if ksplit == 1)
+};
+
+GemmPlan plan_gemm(const GemmProblem& p);
+// Enqueues the GEMM; `partial` must hold plan.partial_bytes bytes.
+hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream);
+
+}  // namespace swr

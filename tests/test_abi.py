@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/swr.h declares;
+* swr_plan_layer (host only) agrees with the oracle's flat layout;
+* argument errors come back as status codes before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+import sharded_weight_reassembly_amd as swr
+from oracle import layout as olayout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "swr.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swr_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _declared()
+    assert len(names) >= 20
+    L = swr.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(swr.EXPORTS)
+
+
+def test_version_string():
+    assert "gfx950" in swr.version()
+
+
+@pytest.mark.parametrize("ws,n", [
+    ([(512, 128, "bf16"), (128, 256, "bf16"), (100, 128, "bf16")], 4),
+    ([(512, 128, "bf16"), (100, 127, "bf16"), (128, 256, "bf16"), (3, 5, "fp8_e4m3fn")], 3),
+    ([(28672, 6144, "fp8_e4m3fn"), (6144, 14336, "fp8_e4m3fn")], 16),
+])
+def test_plan_matches_oracle(ws, n):
+    views, lay = swr.plan_layer(ws, n)
+    ref = olayout.plan_layer(ws, n)
+    assert [v["offset"] for v in views] == ref["offsets"]
+    assert [v["nbytes"] for v in views] == ref["sizes"]
+    assert lay["total_bytes"] == ref["total"] and lay["chunk_bytes"] == ref["chunk"]
+    assert lay["payload_bytes"] == ref["payload"] and lay["n_chunks"] == n and lay["n_weights"] == len(ws)
+
+
+@settings(max_examples=200, deadline=None)
+@given(ws=st.lists(st.tuples(st.integers(1, 3000), st.integers(1, 3000), st.sampled_from(["bf16", "fp8_e4m3fn"])),
+                   min_size=1, max_size=64),
+       n=st.integers(1, 64))
+def test_plan_matches_oracle_random(ws, n):
+    views, lay = swr.plan_layer(ws, n)
+    ref = olayout.plan_layer(ws, n)
+    assert [v["offset"] for v in views] == ref["offsets"]
+    assert (lay["total_bytes"], lay["chunk_bytes"], lay["payload_bytes"]) == (ref["total"], ref["chunk"], ref["payload"])
+
+
+@pytest.mark.parametrize("ws,n,code", [
+    ([], 4, swr.E_INVALID),
+    ([(4, 4, "bf16")], 0, swr.E_INVALID),
+    ([(4, 4, "bf16")], 65, swr.E_INVALID),
+    ([(0, 4, "bf16")], 4, swr.E_SHAPE),
+    ([(4, -1, "bf16")], 4, swr.E_SHAPE),
+    ([(4, 4, 7)], 4, swr.E_INVALID),
+    ([(1 << 40, 1 << 20, "bf16")], 4, swr.E_SHAPE),
+    ([(4, 4, "bf16")] * 65, 4, swr.E_INVALID),
+])
+def test_plan_errors(ws, n, code):
+    with pytest.raises(swr.SwrError) as e:
+        swr.plan_layer(ws, n)
+    assert e.value.code == code
+    assert swr.lib().swr_last_error().decode()
+
+
+def _vp_array(vals):
+    arr = (ctypes.c_void_p * max(len(vals), 1))()
+    for i, v in enumerate(vals):
+        arr[i] = v
+    return arr
+
+
+def test_reassemble_argument_errors_before_enqueue():
+    L = swr.lib()
+    good = 1 << 20
+    chunks = _vp_array([good, good + 4096])
+    # null slot
+    assert L.swr_reassemble_into_slot(chunks, 2, 4096, None, 8192, 0, None, None, None, None) == swr.E_INVALID
+    # chunk size not a multiple of 16
+    assert L.swr_reassemble_into_slot(chunks, 2, 4008, good, 8192, 0, None, None, None, None) == swr.E_ALIGN
+    # slot too small
+    assert L.swr_reassemble_into_slot(chunks, 2, 4096, good, 8191, 0, None, None, None, None) == swr.E_CAPACITY
+    # misaligned slot
+    assert L.swr_reassemble_into_slot(chunks, 2, 4096, good + 8, 8192, 0, None, None, None, None) == swr.E_ALIGN
+    # misaligned chunk
+    bad = _vp_array([good, good + 4])
+    assert L.swr_reassemble_into_slot(bad, 2, 4096, good, 8192, 0, None, None, None, None) == swr.E_ALIGN
+    # self rank out of range, too many chunks
+    assert L.swr_reassemble_into_slot(chunks, 2, 4096, good, 8192, 2, None, None, None, None) == swr.E_INVALID
+    assert L.swr_reassemble_into_slot(_vp_array([good] * 65), 65, 16, good, 1 << 20, 0, None, None, None,
+                                      None) == swr.E_INVALID
+
+
+def test_gemm_argument_errors_before_enqueue():
+    L = swr.lib()
+    a = 1 << 20
+    # FP8 without scales
+    assert L.swr_proj_forward(a, swr.FP8_E4M3FN, None, 64, 64, a, 64, 4, a, 0, 64, None, 0, None) == swr.E_INVALID
+    # misaligned X
+    assert L.swr_proj_forward(a, swr.BF16, None, 64, 64, a + 2, 64, 4, a, 0, 64, None, 0, None) == swr.E_ALIGN
+    # ldx too small
+    assert L.swr_proj_forward(a, swr.BF16, None, 64, 64, a, 32, 4, a, 0, 64, None, 0, None) == swr.E_SHAPE
+    # unknown dtype
+    assert L.swr_proj_forward(a, 3, None, 64, 64, a, 64, 4, a, 0, 64, None, 0, None) == swr.E_INVALID
+    # workspace too small for the MLP
+    need = swr.mlp_workspace_bytes(4, 128, 256, "bf16")
+    assert need >= 4 * 256 * 2
+    assert L.swr_mlp_forward(a, None, a, None, swr.BF16, 128, 256, a, 4, a, a, need - 1, None) == swr.E_CAPACITY
+    assert L.swr_mlp_forward(a, None, a, None, swr.BF16, 128, 256, a, 4, a, a + 16, need, None) == swr.E_ALIGN
+    assert L.swr_mlp_workspace_bytes(4, 0, 256, swr.BF16) == swr.E_SHAPE
+
+
+def test_mlp_workspace_covers_h():
+    for m in (1, 8, 32, 64, 100):
+        for dt in ("bf16", "fp8_e4m3fn"):
+            need = swr.mlp_workspace_bytes(m, 6144, 14336, dt)
+            assert need >= m * 14336 * 2 and need % 256 == 0
+
+
+def test_planner_errors_without_gpu_work():
+    L = swr.lib()
+    h = ctypes.c_void_p()
+    a = 1 << 20
+    assert L.swr_planner_create(3, 3, 1, 2, a, a, 4096, ctypes.byref(h)) == swr.E_INVALID
+    assert L.swr_planner_create(0, 4, 1, 1, a, a, 4096, ctypes.byref(h)) == swr.E_INVALID
+    assert L.swr_planner_create(0, 4, 1, 2, a + 8, a, 4096, ctypes.byref(h)) == swr.E_ALIGN
+    assert L.swr_planner_create(0, 4, 1, 2, None, a, 4096, ctypes.byref(h)) == swr.E_INVALID
+    assert L.swr_planner_reset(None) == swr.E_INVALID

@@ -1,0 +1,124 @@
+"""GPU parity: swr_mlp_forward (gate_up -> SiLU*up -> down) against the oracle.
+
+vLLM PR #50656 report, test code: gate rows then up rows; SiLU of the gate
+half times the up half; then the down projection.  Bar: max|y - y_ref| <=
+1e-2 * max(1, max|y_ref| of the row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import sharded_weight_reassembly_amd as swr
+import synth
+from oracle import gemm, numerics
+
+from gpu_util import DEV, assert_close_rows, bf16, f32, note, u8, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _mlp(gu, d, hidden, inter, x_bits, m=None):
+    m = x_bits.shape[0] if m is None else m
+    dt = gu.dtype
+    y = torch.full((max(m, 1), hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+    nb = swr.mlp_workspace_bytes(m, hidden, inter, dt)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    swr.mlp_forward(u8(gu.raw()), f32(gu.scale) if gu.scale is not None else None, u8(d.raw()),
+                    f32(d.scale) if d.scale is not None else None, dt, hidden, inter, bf16(x_bits), y, ws, m=m)
+    torch.cuda.synchronize()
+    return y[:m]
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+@pytest.mark.parametrize("hidden,inter", [(128, 256), (256, 96), (512, 1024), (192, 320)])
+@pytest.mark.parametrize("m", [1, 4, 16, 33, 64, 100])
+def test_mlp_parity(dt, hidden, inter, m):
+    note(f"mlp h={hidden} i={inter} {dt} m={m}")
+    gu = synth.weight(synth.seed_for(13, 0, 0), 2 * inter, hidden, dt)
+    d = synth.weight(synth.seed_for(13, 0, 1), hidden, inter, dt)
+    x = synth.activations(synth.seed_for(13, 0, 50), m, hidden)
+    y = _mlp(gu, d, hidden, inter, x)
+    _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter)
+    assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} {dt} m={m}")
+
+
+def test_tiny_config_mlp_and_projection():
+    """The tiny workload: hidden 128, intermediate 256, BF16, 4 tokens, N=4 chunks,
+    run through views of the reassembled slot."""
+    wl = synth.TINY
+    note("tiny workload through slot views")
+    ws = wl.layer_weights(0)
+    shp = [(o, i, d) for _, o, i, d in wl.weights]
+    views, lay = swr.plan_layer(shp, wl.n_chunks)
+    chunks = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(wl.n_chunks)]
+    swr.pack_layer(lay, views, [u8(w.raw()) for w in ws], chunks)
+    slot = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=DEV)
+    swr.reassemble_into_slot(chunks, lay["chunk_bytes"], slot)
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, 128)
+    xd = bf16(x)
+    y = torch.empty((4, 128), dtype=torch.bfloat16, device=DEV)
+    wsp = torch.empty(swr.mlp_workspace_bytes(4, 128, 256, "bf16"), dtype=torch.uint8, device=DEV)
+    base = slot.data_ptr()
+    swr.mlp_forward(base + views[0]["offset"], None, base + views[1]["offset"], None, "bf16", 128, 256, xd, y, wsp)
+    yp = torch.empty((4, 100), dtype=torch.bfloat16, device=DEV)
+    swr.proj_forward(base + views[2]["offset"], "bf16", None, 100, 128, xd, yp)
+    torch.cuda.synchronize()
+    _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", 128, 256)
+    assert_close_rows(values(y), ref, what="tiny mlp")
+    refp = gemm.proj_f64(x, ws[2].raw(), "bf16", 100, 128)
+    assert_close_rows(values(yp), refp, what="tiny proj")
+
+
+def test_intermediate_slices_add_up_on_gpu():
+    """The PR report's equivalence: the MLP over intermediate slices [r*s, (r+1)*s)
+    (gate rows, matching up rows, down columns) summed over r equals the full
+    MLP; here the slices run through mlp_forward with fp32-exact slicing of the
+    inputs and the sum is checked against the oracle's full MLP."""
+    note("intermediate-slice partials")
+    hidden, inter, ranks = 256, 512, 4
+    dt = synth.FP8
+    gu = synth.weight(21, 2 * inter, hidden, dt)
+    d = synth.weight(22, hidden, inter, dt)
+    x = synth.activations(23, 12, hidden)
+    sh = inter // ranks
+    total = np.zeros((12, hidden))
+    for r in range(ranks):
+        rows = np.r_[r * sh:(r + 1) * sh, inter + r * sh:inter + (r + 1) * sh]
+        gu_r = synth.Weight(2 * sh, hidden, dt, np.ascontiguousarray(gu.data[rows]), gu.scale[rows])
+        d_r = synth.Weight(hidden, sh, dt, np.ascontiguousarray(d.data[:, r * sh:(r + 1) * sh]), d.scale)
+        total += values(_mlp(gu_r, d_r, hidden, sh, x))
+    _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter)
+    assert_close_rows(total, ref, rel=2e-2, what="sum of slices")
+
+
+@pytest.fixture(scope="module")
+def shared_expert_layer():
+    wl = synth.SHARED_EXPERT_DECODE
+    gu, d = wl.layer_weights(0)
+    x = synth.activations(synth.seed_for(2, 0, 50), 64, wl.hidden)
+    return wl, gu, d, x
+
+
+@pytest.mark.parametrize("m", [1, 8, 32, 64])
+def test_full_size_shared_expert_mlp(shared_expert_layer, m):
+    """Hidden 6144, intermediate 14336, FP8 E4M3FN with row scales; sampled output columns."""
+    wl, gu, d, x = shared_expert_layer
+    note(f"full-size shared-expert MLP m={m}")
+    y = values(_mlp(gu, d, wl.hidden, wl.intermediate, x[:m]))
+    _check_full(wl, gu, d, x, m, y)
+
+
+_FULL_REF = {}
+
+
+def _check_full(wl, gu, d, x, m, y):
+    # The oracle's G needs every gate/up row; computed once at M=64 (rows of
+    # X are independent, so smaller M are row prefixes).
+    if "h" not in _FULL_REF:
+        g = gemm.proj_f64(x, gu.raw(), gu.dtype, 2 * wl.intermediate, wl.hidden, gu.scale)
+        with np.errstate(over="ignore"):
+            _FULL_REF["h"] = numerics.f64_to_bf16_bits(numerics.silu(g[:, :wl.intermediate]) * g[:, wl.intermediate:])
+    h = _FULL_REF["h"][:m]
+    cols = np.sort(np.random.default_rng(1).choice(wl.hidden, size=512, replace=False))
+    ref = gemm.proj_f64(h, np.ascontiguousarray(d.data[cols]), d.dtype, len(cols), wl.intermediate, d.scale[cols])
+    assert_close_rows(y[:, cols], ref, what=f"shared expert m={m}")

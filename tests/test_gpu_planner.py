@@ -1,0 +1,133 @@
+"""GPU checks of the lookahead / ping-pong planner (weight_sharding,
+zdszero.github.io, sections on lookahead and ping-pong slots, on the SGLang
+implementation and on CUDA graphs).
+
+* The planner's recorded launch/wait sequence equals the oracle's model and
+  passes the oracle's happens-before checker.
+* A pipelined forward over several layers, with each layer's compute delayed
+  on the compute stream, produces every layer's oracle output: if a gather
+  overwrote a slot still being read, some layer would read another layer's
+  weights.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sharded_weight_reassembly_amd as swr
+import synth
+from oracle import accounting, gemm
+from oracle import scheduler as osch
+
+from gpu_util import DEV, assert_close_rows, bf16, note, u8, values
+
+pytestmark = pytest.mark.gpu
+
+
+def _layers(wl, n_layers, n_chunks):
+    layers = []
+    for layer in range(n_layers):
+        ws = wl.layer_weights(layer)
+        shp = [(o, i, d) for _, o, i, d in wl.weights]
+        views, lay = swr.plan_layer(shp, n_chunks)
+        chunks = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(n_chunks)]
+        swr.pack_layer(lay, views, [u8(w.raw()) for w in ws], chunks)
+        layers.append(dict(ws=ws, views=views, lay=lay, chunks=chunks))
+    torch.cuda.synchronize()
+    return layers
+
+
+def _forward(planner, layers, start, x_dev, outs, ws_buf, delay=None):
+    wl = synth.TINY
+    planner.reset()
+    planner.pre_dispatch(start)
+    for i in range(start, start + len(layers)):
+        planner.maybe_dispatch(i + 1)
+        base = planner.wait_ready_once(i)
+        assert planner.wait_ready_once(i) == base  # second call: no new wait
+        if delay is not None:
+            delay()  # keeps the compute stream busy so an ungated gather would overlap
+        L = layers[i - start]
+        swr.mlp_forward(base + L["views"][0]["offset"], None, base + L["views"][1]["offset"], None, "bf16",
+                        wl.hidden, wl.intermediate, x_dev, outs[i - start], ws_buf)
+        planner.update_done_event(i)
+
+
+@pytest.mark.parametrize("start,n_layers", [(0, 1), (0, 2), (1, 5)])
+def test_trace_matches_model_and_outputs_match_oracle(start, n_layers):
+    note(f"planner start={start} layers={n_layers}")
+    wl = synth.TINY
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    compute = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    p = swr.Planner(start, start + n_layers, compute, side, slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(start + i, L["chunks"], L["lay"]["chunk_bytes"])
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    a = torch.randn(2048, 2048, device=DEV)
+
+    def delay():
+        for _ in range(4):
+            torch.mm(a, a)
+
+    traces = []
+    for _ in range(3):  # back-to-back forwards reuse the slots
+        _forward(p, layers, start, xd, outs, wsb, delay)
+        traces.append(p.trace())
+    torch.cuda.synchronize()
+    expected = osch.expected_trace(start, start + n_layers)
+    for t in traces:
+        assert t == expected
+    assert osch.check_trace(traces) == []
+    for i, L in enumerate(layers):
+        ws = L["ws"]
+        _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)
+        assert_close_rows(values(outs[i]), ref, what=f"layer {start + i}")
+    remote, gathers = p.counters()
+    assert gathers == 3 * n_layers
+    assert remote == 3 * n_layers * accounting.transfer_bytes(total, wl.n_chunks)
+    p.close()
+
+
+def test_sequence_errors():
+    wl = synth.TINY
+    layers = _layers(wl, 2, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(0, 2, torch.cuda.current_stream(), torch.cuda.Stream(), slot_a, slot_b)
+    with pytest.raises(swr.SwrError) as e:
+        p.pre_dispatch(0)  # before reset
+    assert e.value.code == swr.E_SEQUENCE
+    p.reset()
+    with pytest.raises(swr.SwrError) as e:
+        p.pre_dispatch(0)  # layer 0 has no chunks yet
+    assert e.value.code == swr.E_SEQUENCE
+    for i, L in enumerate(layers):
+        p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.reset()
+    with pytest.raises(swr.SwrError) as e:
+        p.wait_ready_once(1)  # not dispatched
+    assert e.value.code == swr.E_SEQUENCE
+    p.pre_dispatch(0)
+    with pytest.raises(swr.SwrError) as e:
+        p.update_done_event(0)  # did not wait
+    assert e.value.code == swr.E_SEQUENCE
+    p.maybe_dispatch(2)  # outside the range: no-op
+    with pytest.raises(swr.SwrError) as e:
+        p.set_layer(0, layers[0]["chunks"], 1 << 40)
+    assert e.value.code == swr.E_CAPACITY
+    torch.cuda.synchronize()
+    p.close()
+
+
+def test_slot_memory_account():
+    """Two slots sized by the largest layer: R/N + 2 max|T_l| per rank."""
+    wl = synth.TINY
+    sizes = [swr.plan_layer([(o, i, d) for _, o, i, d in wl.weights], n)[1]["total_bytes"] for n in (4, 4, 4)]
+    assert accounting.weight_shard_memory(sizes, 4) == sum(sizes) // 4 + 2 * max(sizes)
