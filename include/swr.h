@@ -276,6 +276,16 @@ int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer);
 int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void** slot_out);
 /* SWR_E_SEQUENCE if wait_ready_once(layer) was not called first. */
 int swr_planner_update_done_event(swr_planner* p, int32_t layer);
+/* Timing of the gathers.  swr_planner_set_timing(p, capacity) with
+ * capacity > 0 makes every later dispatch record two timing events on the side
+ * stream around its copy (after the gate wait, before the ready record), in a
+ * ring of `capacity` event pairs; 0 turns timing off.  Either way the
+ * launch/wait sequence is the same.  swr_planner_gather_times writes the copy
+ * durations (milliseconds) of the timed dispatches still in the ring, oldest
+ * first, at most `cap` of them, and sets *n to the number written; every one
+ * of those copies must have finished (else SWR_E_HIP). */
+int swr_planner_set_timing(swr_planner* p, int32_t capacity);
+int swr_planner_gather_times(const swr_planner* p, float* ms, int32_t cap, int32_t* n);
 /* Bytes received from peers so far (sum of (N-1)*C over gathers), and the
  * number of gathers issued, since creation. */
 int swr_planner_counters(const swr_planner* p, int64_t* remote_bytes, int64_t* gathers);

@@ -38,7 +38,8 @@ EXPORTS = (
     "swr_proj_workspace_bytes", "swr_mlp_forward", "swr_mlp_workspace_bytes", "swr_sum_partials",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
-    "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_last_error", "swr_version",
+    "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
+    "swr_planner_gather_times", "swr_last_error", "swr_version",
 )
 
 
@@ -99,6 +100,8 @@ def lib() -> ctypes.CDLL:
         "swr_planner_counters": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
         "swr_planner_trace": (_i32, [_vp, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
         "swr_planner_destroy": (None, [_vp]),
+        "swr_planner_set_timing": (_i32, [_vp, _i32]),
+        "swr_planner_gather_times": (_i32, [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]),
         "swr_last_error": (ctypes.c_char_p, []),
         "swr_version": (ctypes.c_char_p, []),
     }
@@ -298,6 +301,17 @@ class Planner:
 
     def update_done_event(self, layer: int) -> None:
         _check("swr_planner_update_done_event", lib().swr_planner_update_done_event(self._h, int(layer)))
+
+    def set_timing(self, capacity: int) -> None:
+        """Time the copies of the next dispatches in a ring of `capacity` event pairs (0: off)."""
+        _check("swr_planner_set_timing", lib().swr_planner_set_timing(self._h, int(capacity)))
+
+    def gather_times(self, cap: int = 1 << 16) -> list[float]:
+        """Copy durations (ms) of the timed dispatches still in the ring, oldest first."""
+        n = _i32(0)
+        buf = (ctypes.c_float * max(cap, 1))()
+        _check("swr_planner_gather_times", lib().swr_planner_gather_times(self._h, buf, int(cap), ctypes.byref(n)))
+        return list(buf[:n.value])
 
     def counters(self) -> tuple[int, int]:
         rb, g = _i64(0), _i64(0)

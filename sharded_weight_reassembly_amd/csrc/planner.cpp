@@ -28,6 +28,10 @@ struct swr_planner {
   std::vector<Layer> layers;
   hipEvent_t start_evt = nullptr;
   std::vector<hipEvent_t> ready, done;
+  // optional timing events around each gather's copy (after the gate wait):
+  // a ring of event pairs, one pair per timed dispatch
+  std::vector<hipEvent_t> t0, t1;
+  int64_t timed_dispatches = 0;
 
   // per-forward state
   bool reset_called = false;
@@ -56,6 +60,10 @@ void destroy_events(swr_planner* p) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->done)
     if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->t0)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->t1)
+    if (e) (void)hipEventDestroy(e);
 }
 
 // Side stream: gate, gather of `layer` into its slot, ready record.
@@ -74,8 +82,26 @@ int dispatch(swr_planner* p, int32_t layer) {
   }
   const int s = p->slot_of(layer);
   int64_t remote = 0;
-  const int rc = swr_reassemble_into_slot(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s],
-                                          p->slot_bytes, 0, p->side, gate, p->ready[i], &remote);
+  int rc;
+  if (p->t0.empty()) {
+    rc = swr_reassemble_into_slot(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s],
+                                  p->slot_bytes, 0, p->side, gate, p->ready[i], &remote);
+  } else {
+    // same sequence with timing records between the gate wait and the ready record
+    const size_t r = size_t(p->timed_dispatches % int64_t(p->t0.size()));
+    hipError_t e = hipStreamWaitEvent(p->side, gate, 0);
+    if (e != hipSuccess) return swr::hip_fail(e, "planner: wait gate");
+    e = hipEventRecord(p->t0[r], p->side);
+    if (e != hipSuccess) return swr::hip_fail(e, "planner: record timing start");
+    rc = swr_reassemble_into_slot(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s],
+                                  p->slot_bytes, 0, p->side, nullptr, nullptr, &remote);
+    if (rc == SWR_OK) {
+      e = hipEventRecord(p->t1[r], p->side);
+      if (e == hipSuccess) e = hipEventRecord(p->ready[i], p->side);
+      if (e != hipSuccess) return swr::hip_fail(e, "planner: record timing end / ready");
+      p->timed_dispatches += 1;
+    }
+  }
   if (rc != SWR_OK) return rc;
   if (prev >= p->start)
     p->log(SWR_OP_WAIT_DONE, SWR_STREAM_SIDE, prev, -1);
@@ -223,6 +249,51 @@ extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
   if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record");
   p->finished[i] = 1;
   p->log(SWR_OP_RECORD_DONE, SWR_STREAM_COMPUTE, layer, -1);
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_timing(swr_planner* p, int32_t capacity) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_set_timing: null pointer");
+  if (capacity < 0 || capacity > (1 << 16))
+    return fail(SWR_E_INVALID, "swr_planner_set_timing: capacity %d outside [0, 65536]", capacity);
+  for (hipEvent_t e : p->t0)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->t1)
+    if (e) (void)hipEventDestroy(e);
+  p->t0.assign(capacity, nullptr);
+  p->t1.assign(capacity, nullptr);
+  p->timed_dispatches = 0;
+  hipError_t e = hipSuccess;
+  for (int i = 0; e == hipSuccess && i < capacity; ++i) {
+    e = hipEventCreate(&p->t0[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->t1[i]);
+  }
+  if (e != hipSuccess) {
+    for (hipEvent_t x : p->t0)
+      if (x) (void)hipEventDestroy(x);
+    for (hipEvent_t x : p->t1)
+      if (x) (void)hipEventDestroy(x);
+    p->t0.clear();
+    p->t1.clear();
+    return swr::hip_fail(e, "swr_planner_set_timing: hipEventCreate");
+  }
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_gather_times(const swr_planner* p, float* ms, int32_t cap, int32_t* n) {
+  if (!p || !n || (cap > 0 && !ms)) return fail(SWR_E_INVALID, "swr_planner_gather_times: null pointer");
+  const int64_t ring = int64_t(p->t0.size());
+  const int64_t avail = p->timed_dispatches < ring ? p->timed_dispatches : ring;
+  const int64_t count = avail < cap ? avail : cap;
+  *n = int32_t(count);
+  const int64_t first = p->timed_dispatches - avail;  // oldest dispatch still in the ring
+  for (int64_t k = 0; k < count; ++k) {
+    const size_t r = size_t((first + k) % ring);
+    const hipError_t e = hipEventElapsedTime(&ms[k], p->t0[r], p->t1[r]);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_gather_times: hipEventElapsedTime");
+  }
   swr::clear_error();
   return SWR_OK;
 }
