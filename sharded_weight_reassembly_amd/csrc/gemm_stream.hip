@@ -23,6 +23,9 @@
 // rows j..j+8RT and the matching up rows I+j..I+j+8RT, and writes
 // h = bf16(silu(G_gate) * G_up) directly (vLLM PR #50656 report, test code:
 // gate rows first, SiLU of the gate half times the up half).
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "swr_internal.h"
 
 namespace swr {
@@ -33,7 +36,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kStepK = 64;  // K elements per wave step
+constexpr int kStepK = 64;    // K elements per wave step (stream kernel)
+constexpr int kStageK = 256;  // K elements per stage (staged kernel)
 
 struct StreamArgs {
   const uint8_t* W;
@@ -180,6 +184,78 @@ __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, con
   }
 }
 
+// Second half of every streaming GEMM workgroup: the 4 waves' fp32 sums for
+// RT row tiles x MT token blocks sit in LDS as red[wave][t][b][v][lane]
+// (lane = 16 * (row / 4) + token, v = row % 4 within the MFMA output tile);
+// each thread adds them for one token and 4 consecutive rows and applies the
+// output mode (scale, SiLU*up, bf16 rounding) or writes a split-K partial.
+template <int MT, int RT>
+__device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_t tok0) {
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  const int tiles_out = silu_mode ? RT / 2 : RT;
+  const int items = tiles_out * MT * 64;
+  auto at = [&](int w, int t, int b, int i, int ql) { return red[(((w * RT + t) * MT + b) * 4 + i) * 64 + ql]; };
+  for (int q = threadIdx.x; q < items; q += kThreads) {
+    const int ql = q & 63;
+    const int b = (q >> 6) % MT;
+    const int t = (q >> 6) / MT;
+    const int64_t tok = tok0 + b * 16 + (ql & 15);
+    if (tok >= a.M) continue;
+    const int64_t row = tile_row<RT>(a, t) + 4 * (ql >> 4);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += at(w, t, b, i, ql);
+      v[i] = sum;
+    }
+    if (silu_mode) {
+      const int64_t urow = tile_row<RT>(a, t + RT / 2) + 4 * (ql >> 4);
+      float u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += at(w, t + RT / 2, b, i, ql);
+        u[i] = sum;
+      }
+      if (a.ksplit > 1) {
+        float* pg = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pg[row + i] = v[i];
+          pg[urow + i] = u[i];
+        }
+        continue;
+      }
+      float h[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float g = v[i] * (a.scale ? a.scale[row + i] : 1.f);
+        const float up = u[i] * (a.scale ? a.scale[urow + i] : 1.f);
+        h[i] = silu(g) * up;
+      }
+      // h is [M, ldy] with I columns; `row` is the gate index j
+      StreamArgs hb = a;
+      hb.rows = a.inter;
+      store4(hb, tok, row, h, true);
+      continue;
+    }
+    if (a.ksplit > 1) {
+      float* pr = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
+      for (int i = 0; i < 4; ++i)
+        if (row + i < a.rows) pr[row + i] = v[i];
+      continue;
+    }
+    if (a.scale) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= (row + i < a.rows) ? a.scale[row + i] : 0.f;
+    }
+    store4(a, tok, row, v, a.mode == OUT_BF16);
+  }
+}
+
 template <int MT, int RT, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) {
   constexpr int64_t eb = FP8 ? 1 : 2;
@@ -228,77 +304,205 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
   }
 
   // ---- add the 4 waves' sums in LDS: red[wave][t][b][v][lane]
-  __shared__ float red[kWaves][RT][MT][4][64];
+  __shared__ float red[kWaves * RT * MT * 4 * 64];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
     for (int b = 0; b < MT; ++b)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][t][b][v][lane] = acc[t][b][v];
+      for (int v = 0; v < 4; ++v) red[(((wave * RT + t) * MT + b) * 4 + v) * 64 + lane] = acc[t][b][v];
   __syncthreads();
+  finish_tile<MT, RT>(a, red, tok0);
+}
 
-  const bool silu_mode = a.mode == OUT_SILU_BF16;
-  const int tiles_out = silu_mode ? RT / 2 : RT;
-  const int items = tiles_out * MT * 64;
-  for (int q = threadIdx.x; q < items; q += kThreads) {
-    const int ql = q & 63;
-    const int b = (q >> 6) % MT;
-    const int t = (q >> 6) / MT;
-    const int64_t tok = tok0 + b * 16 + (ql & 15);
-    if (tok >= a.M) continue;
-    const int64_t row = tile_row<RT>(a, t) + 4 * (ql >> 4);
-    float v[4];
+// ---------------------------------------------------------------------------
+// Staged variant (K a multiple of 256).  Same arithmetic and output modes as
+// stream_gemm_kernel; the difference is how weight bytes reach the MFMAs:
+//   * a K stage is 256 elements; the workgroup's RB = 16*RTL rows x 256 K of
+//     W are loaded with consecutive threads on consecutive 16-byte pieces of a
+//     row, so one wave instruction reads 4 rows x 256 B (fp8) or 2 rows x
+//     512 B (bf16) -- long runs per DRAM page instead of 16 rows x 64 B;
+//   * loads run D stages ahead in registers (about 64 KB of weights in
+//     flight per workgroup): HBM latency under full load is several
+//     microseconds, so a skinny GEMM is bound by bytes in flight per CU;
+//   * each stage passes through a double-buffered LDS tile whose 16-byte
+//     pieces are XOR-swizzled by row (piece c of row r sits at
+//     r * CPR + (c ^ (r % 16))), so the MFMA fragment reads (16 rows, one
+//     piece each) hit 16 distinct bank groups;
+//   * the 4 waves split each stage's 4 groups of 64 K and add their sums in
+//     LDS at the end.
+template <int MT, int RTL, bool FP8>
+struct StagedShape {
+  static constexpr int EB = FP8 ? 1 : 2;
+  static constexpr int CPR = kStageK * EB / 16;        // 16-byte pieces per row per stage
+  static constexpr int TILE = 16 * RTL * kStageK * EB;  // bytes of W per stage
+  static constexpr int NV = TILE / (16 * kThreads);     // W pieces per thread per stage
+  // A ring slot holds one stage's W pieces (4*NV VGPRs) and this lane's X
+  // fragments (8*MT VGPRs); D slots fit in about 160 VGPRs next to the
+  // accumulators.  U unrolls the loop over a whole number of rings and LDS
+  // buffer pairs.
+  static constexpr int SLOT = 4 * NV + 8 * MT;
+  static constexpr int BUDGET = 176 - 4 * RTL * MT;
+  static constexpr int D0 = BUDGET / SLOT;
+  static constexpr int D = D0 < 2 ? 2 : (D0 > 10 ? 10 : D0);
+  static constexpr int U = (D % 2 == 0) ? D : 2 * D;
+};
+
+template <int MT, int RTL, bool FP8>
+__global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) {
+  using S = StagedShape<MT, RTL, FP8>;
+  constexpr int EB = S::EB, CPR = S::CPR, TILE = S::TILE, NV = S::NV, D = S::D, U = S::U;
+  static_assert(NV >= 1 && TILE % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
+  constexpr int RED = kWaves * RTL * MT * 4 * 64 * 4;
+  constexpr int LDS = 2 * TILE > RED ? 2 * TILE : RED;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int64_t k_begin = int64_t(blockIdx.y) * a.kper;
+  const int64_t k_end = min(a.K, k_begin + a.kper);
+  const int nst = int((k_end - k_begin) / kStageK);
+  const int64_t tok0 = int64_t(blockIdx.z) * 16 * MT;
+
+  // W pieces this thread moves each stage: byte offset in W and swizzled LDS
+  // slot.  Loads go through a buffer resource over the whole matrix, so a
+  // prefetch past this workgroup's last stage is given an out-of-range offset
+  // and returns zeros without touching memory: the loop has no branches
+  // around its loads and the compiler's wait counts stay exact.
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.W), 0, int(a.rows * a.K * EB), 0x00020000);
+  int wsrc[NV];
+  int wdst[NV];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += red[w][t][b][i][ql];
-      v[i] = sum;
-    }
-    if (silu_mode) {
-      const int64_t urow = tile_row<RT>(a, t + RT / 2) + 4 * (ql >> 4);
-      float u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += red[w][t + RT / 2][b][i][ql];
-        u[i] = sum;
-      }
-      if (a.ksplit > 1) {
-        float* pg = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pg[row + i] = v[i];
-          pg[urow + i] = u[i];
-        }
-        continue;
-      }
-      float h[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = v[i] * (a.scale ? a.scale[row + i] : 1.f);
-        const float up = u[i] * (a.scale ? a.scale[urow + i] : 1.f);
-        h[i] = silu(g) * up;
-      }
-      // h is [M, ldy] with I columns; `row` is the gate index j
-      StreamArgs hb = a;
-      hb.rows = a.inter;
-      store4(hb, tok, row, h, true);
-      continue;
-    }
-    if (a.ksplit > 1) {
-      float* pr = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
-      for (int i = 0; i < 4; ++i)
-        if (row + i < a.rows) pr[row + i] = v[i];
-      continue;
-    }
-    if (a.scale) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= (row + i < a.rows) ? a.scale[row + i] : 0.f;
-    }
-    store4(a, tok, row, v, a.mode == OUT_BF16);
+  for (int j = 0; j < NV; ++j) {
+    const int v = j * kThreads + tid;
+    const int row = v / CPR;
+    const int piece = v % CPR;
+    int64_t r = tile_row<RTL>(a, row / 16) + (row % 16);
+    r = min(r, a.rows - 1);  // rows past the end are loaded from the last row and never stored
+    wsrc[j] = int((r * a.K + k_begin) * EB + piece * 16);
+    wdst[j] = (row * CPR + (piece ^ (row & 15))) * 16;
   }
+  // MFMA A-fragment slots of this lane: wave w handles pieces 4w..4w+3 (fp8)
+  int aoff[RTL][2];
+#pragma unroll
+  for (int t = 0; t < RTL; ++t) {
+    const int row = t * 16 + r16;
+    if (FP8) {
+      const int piece = 4 * wave + grp;
+      aoff[t][0] = (row * CPR + (piece ^ r16)) * 16;
+      aoff[t][1] = aoff[t][0];
+    } else {
+      const int p0 = 2 * (4 * wave + grp);
+      aoff[t][0] = (row * CPR + (p0 ^ r16)) * 16;
+      aoff[t][1] = (row * CPR + ((p0 + 1) ^ r16)) * 16;
+    }
+  }
+  // X fragments of this lane (token row clamped to M-1), also through a buffer resource
+  const __amdgpu_buffer_rsrc_t xres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, int(a.M * a.ldx * 2), 0x00020000);
+  int xsrc[MT];
+#pragma unroll
+  for (int b = 0; b < MT; ++b) {
+    const int64_t m = min(tok0 + b * 16 + r16, a.M - 1);
+    xsrc[b] = int((m * a.ldx + k_begin + (4 * wave + grp) * 16) * 2);
+  }
+
+  f32x4 acc[RTL][MT];
+#pragma unroll
+  for (int t = 0; t < RTL; ++t)
+#pragma unroll
+    for (int b = 0; b < MT; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int kOutOfRange = 0x7FFFFFF0;
+  u32x4 wr[D][NV];
+  u32x4 xr[D][MT][2];
+  auto load_w = [&](u32x4(&r)[NV], int st) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int off = st < nst ? wsrc[j] + st * (kStageK * EB) : kOutOfRange;
+      r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 2 /* nt */));
+    }
+  };
+  auto store_w = [&](int buf, const u32x4(&r)[NV]) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) *reinterpret_cast<u32x4*>(lds + buf * TILE + wdst[j]) = r[j];
+  };
+  auto load_x = [&](u32x4(&x)[MT][2], int st) {
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int off = st < nst ? xsrc[b] + st * (kStageK * 2) : kOutOfRange;
+      x[b][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+      x[b][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off + 16, 0, 0));
+    }
+  };
+  auto compute = [&](int buf, const u32x4(&x)[MT][2]) {
+#pragma unroll
+    for (int t = 0; t < RTL; ++t) {
+      bf16x8 a0, a1;
+      if (FP8) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + buf * TILE + aoff[t][0]);
+        a0 = fp8x8_to_bf16(v[0], v[1]);
+        a1 = fp8x8_to_bf16(v[2], v[3]);
+      } else {
+        a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + buf * TILE + aoff[t][0]));
+        a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + buf * TILE + aoff[t][1]));
+      }
+#pragma unroll
+      for (int b = 0; b < MT; ++b) {
+        acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[b][0]), acc[t][b], 0, 0, 0);
+        acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[b][1]), acc[t][b], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue: stages 0..D-1 in flight (past-the-end ones read nothing)
+  // (issued in slot order, which is also the order the loop refills slots,
+  // so the wait counts at the loop head are the same on entry and on repeat)
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    load_w(wr[j], j);
+    load_x(xr[j], j);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Stage s uses ring slot s % D and LDS buffer s % 2.  The loop is unrolled
+  // over U stages so every register index is a compile-time constant.  A slot
+  // is refilled with stage s + D right after its W pieces went to LDS, so the
+  // wait for stage s covers only loads issued D stages earlier.  Full groups of
+  // U stages run without any branch (one loop back-edge keeps the compiler's
+  // wait counts exact); the last partial group runs in a separate tail.
+  auto step = [&](const int j, const int s) {
+    const int slot = j % D;
+    store_w(j & 1, wr[slot]);  // LDS buffer j&1 was last read two stages ago, before the last barrier
+    __syncthreads();
+    load_w(wr[slot], s + D);
+    compute(j & 1, xr[slot]);
+    load_x(xr[slot], s + D);
+  };
+  int s0 = 0;
+  for (; s0 + U <= nst; s0 += U) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) step(j, s0 + j);
+  }
+#pragma unroll
+  for (int j = 0; j < U; ++j)
+    if (s0 + j < nst) step(j, s0 + j);
+  __syncthreads();  // every wave is done with the W tiles before LDS is reused
+
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int t = 0; t < RTL; ++t)
+#pragma unroll
+    for (int b = 0; b < MT; ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(((wave * RTL + t) * MT + b) * 4 + v) * 64 + lane] = acc[t][b][v];
+  __syncthreads();
+  finish_tile<MT, RTL>(a, red, tok0);
 }
 
 // Adds the split-K partials in split order and applies scale / SiLU / rounding.
@@ -398,36 +602,126 @@ hipError_t dispatch_mt(int mt, const StreamArgs& a, dim3 grid, hipStream_t strea
 
 }  // namespace
 
+namespace {
+
+int64_t row_blocks_of(const GemmProblem& p, int rt) {
+  if (p.mode == OUT_SILU_BF16) return (p.rows / 2) / (8 * rt);
+  return (p.rows + 16 * rt - 1) / (16 * rt);
+}
+
+// Fills ksplit/kper/partial_bytes for `ks` K splits of `granule`-element pieces.
+void set_split(GemmPlan& plan, const GemmProblem& p, int64_t ks, int64_t granule) {
+  const int64_t units = (p.K + granule - 1) / granule;
+  if (ks > units) ks = units;
+  if (ks < 1) ks = 1;
+  const int64_t per = (units + ks - 1) / ks;
+  plan.kper = per * granule;
+  plan.ksplit = int((p.K + plan.kper - 1) / plan.kper);
+  plan.partial_bytes = plan.ksplit > 1 ? int64_t(plan.ksplit) * p.M * p.rows * 4 : 0;
+}
+
+}  // namespace
+
+bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
+  const bool silu_mode = p.mode == OUT_SILU_BF16;
+  const int64_t inter = silu_mode ? p.rows / 2 : 0;
+  if (plan.kind == 1) return true;
+  if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
+  if (plan.mt != 1 && plan.mt != 2 && plan.mt != 4) return false;
+  if (plan.rt != 1 && plan.rt != 2 && plan.rt != 4) return false;
+  if (silu_mode && (plan.rt < 2 || inter % (8 * plan.rt) != 0)) return false;
+  if (plan.kind == 0) return p.K % kStepK == 0 && plan.rt == 4 && plan.kper % 256 == 0;
+  if (plan.kind == 2)
+    return p.K % kStageK == 0 && plan.kper % kStageK == 0 && p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31);
+  return false;
+}
+
 GemmPlan plan_gemm(const GemmProblem& p) {
   GemmPlan plan{};
   const bool silu_mode = p.mode == OUT_SILU_BF16;
   const int64_t inter = silu_mode ? p.rows / 2 : 0;
-  const bool fast = p.K % kStepK == 0 && aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0 &&
-                    (!silu_mode || inter % 32 == 0);
-  if (!fast) {
+  const bool aligned_ok = aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0;
+  plan.mt = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
+  const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
+  const int64_t w_bytes = p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2);
+  if (aligned_ok && p.K % kStageK == 0 && (!silu_mode || inter % 16 == 0) && w_bytes < (INT64_C(1) << 31)) {
+    // Staged kernel.  Row block and K split from a sweep of the shared-expert
+    // shapes on MI355X: 32-row blocks when one 16-token block suffices, 64-row
+    // blocks otherwise (fewer activation re-reads per weight byte); K is split
+    // only while fewer than 160 workgroups would run and each split keeps at
+    // least 4 stages (the split-K finalize costs about as much as a 1/8 split).
+    plan.kind = 2;
+    if (silu_mode)
+      plan.rt = inter % 32 == 0 ? 4 : 2;
+    else
+      plan.rt = plan.mt == 1 ? 2 : 4;
+    const int64_t wgs = row_blocks_of(p, plan.rt) * tok_blocks;
+    const int64_t stages = p.K / kStageK;
+    int64_t ks = 1;
+    if (p.M <= 64)
+      while (wgs * ks < 160 && stages / (2 * ks) >= 4) ks *= 2;
+    set_split(plan, p, ks, kStageK);
+  } else if (aligned_ok && p.K % kStepK == 0 && (!silu_mode || inter % 32 == 0)) {
+    plan.kind = 0;
+    plan.rt = 4;
+    int64_t ks = 1;
+    if (p.M <= 64) ks = (512 + row_blocks_of(p, 4) - 1) / row_blocks_of(p, 4);
+    set_split(plan, p, ks, 256);
+  } else {
     plan.kind = 1;
     plan.ksplit = 1;
     plan.kper = p.K;
     return plan;
   }
-  plan.kind = 0;
-  plan.mt = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
-  plan.rt = 4;
-  const int64_t row_blocks = silu_mode ? inter / (8 * plan.rt) : (p.rows + 16 * plan.rt - 1) / (16 * plan.rt);
-  const int64_t k256 = (p.K + 255) / 256;
-  int64_t ks = 1;
-  if (p.M <= 64) {
-    const int64_t target = 512;  // about two workgroups per CU
-    ks = (target + row_blocks - 1) / row_blocks;
-    if (ks > k256) ks = k256;
-    if (ks < 1) ks = 1;
+#ifdef SWR_TUNING
+  // tuning builds only: SWR_PLAN / SWR_PLAN_SILU = "kind,rt,ks" override the heuristic
+  if (const char* env = getenv(silu_mode ? "SWR_PLAN_SILU" : "SWR_PLAN")) {
+    int kind, rt, ks;
+    if (sscanf(env, "%d,%d,%d", &kind, &rt, &ks) == 3) {
+      GemmPlan t = plan;
+      t.kind = kind;
+      t.rt = rt;
+      set_split(t, p, ks, kind == 2 ? kStageK : 256);
+      if (plan_is_valid(p, t)) plan = t;
+    }
   }
-  const int64_t per = (k256 + ks - 1) / ks;
-  plan.kper = per * 256;
-  plan.ksplit = int((p.K + plan.kper - 1) / plan.kper);
-  plan.partial_bytes = plan.ksplit > 1 ? int64_t(plan.ksplit) * p.M * p.rows * 4 : 0;
+#endif
   return plan;
 }
+
+namespace {
+
+template <int MT, int RTL, bool FP8>
+hipError_t launch_staged(const StreamArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((staged_gemm_kernel<MT, RTL, FP8>), grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int MT, bool FP8>
+hipError_t dispatch_staged_rt(int rt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
+  switch (rt) {
+    case 1:
+      return launch_staged<MT, 1, FP8>(a, grid, stream);
+    case 2:
+      return launch_staged<MT, 2, FP8>(a, grid, stream);
+    default:
+      return launch_staged<MT, 4, FP8>(a, grid, stream);
+  }
+}
+
+template <bool FP8>
+hipError_t dispatch_staged(int mt, int rt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
+  switch (mt) {
+    case 1:
+      return dispatch_staged_rt<1, FP8>(rt, a, grid, stream);
+    case 2:
+      return dispatch_staged_rt<2, FP8>(rt, a, grid, stream);
+    default:
+      return dispatch_staged_rt<4, FP8>(rt, a, grid, stream);
+  }
+}
+
+}  // namespace
 
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream) {
   StreamArgs a{};
@@ -453,11 +747,15 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
     hipLaunchKernelGGL(generic_gemm_kernel, dim3(unsigned(g)), dim3(kThreads), 0, stream, a, fp8 ? 1 : 0);
     return hipGetLastError();
   }
-  const int64_t row_blocks = p.mode == OUT_SILU_BF16 ? a.inter / (8 * plan.rt)
-                                                      : (p.rows + 16 * plan.rt - 1) / (16 * plan.rt);
+  const int64_t row_blocks = row_blocks_of(p, plan.rt);
   const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
   const dim3 grid = dim3(unsigned(row_blocks), unsigned(plan.ksplit), unsigned(tok_blocks));
-  hipError_t e = fp8 ? dispatch_mt<4, true>(plan.mt, a, grid, stream) : dispatch_mt<4, false>(plan.mt, a, grid, stream);
+  hipError_t e;
+  if (plan.kind == 2)
+    e = fp8 ? dispatch_staged<true>(plan.mt, plan.rt, a, grid, stream)
+            : dispatch_staged<false>(plan.mt, plan.rt, a, grid, stream);
+  else
+    e = fp8 ? dispatch_mt<4, true>(plan.mt, a, grid, stream) : dispatch_mt<4, false>(plan.mt, a, grid, stream);
   if (e != hipSuccess || plan.ksplit == 1) return e;
   const int64_t cols = p.mode == OUT_SILU_BF16 ? a.inter : p.rows;
   int64_t g = (p.M * ((cols + 3) / 4) + kThreads - 1) / kThreads;

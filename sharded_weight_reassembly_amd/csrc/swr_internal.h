@@ -66,7 +66,7 @@ struct GemmProblem {
 };
 
 struct GemmPlan {
-  int kind;      // 0 = streaming MFMA kernel, 1 = generic kernel
+  int kind;      // 0 = streaming MFMA kernel, 1 = generic kernel, 2 = LDS-staged MFMA kernel
   int mt;        // 16-token blocks per workgroup (1, 2, 4)
   int rt;        // 16-row tiles per workgroup
   int ksplit;    // workgroups along K
@@ -75,6 +75,7 @@ struct GemmPlan {
 };
 
 GemmPlan plan_gemm(const GemmProblem& p);
+bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan);
 // Enqueues the GEMM; `partial` must hold plan.partial_bytes bytes.
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream);
 
