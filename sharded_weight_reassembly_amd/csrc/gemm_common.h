@@ -1,0 +1,66 @@
+// Device-side pieces shared by the GEMM kernels (streaming and tiled).
+#pragma once
+
+#include "swr_internal.h"
+
+namespace swr {
+
+// Arguments of every GEMM kernel (plain pointers and sizes).
+struct StreamArgs {
+  const uint8_t* W;
+  const float* scale;
+  const uint16_t* X;
+  int64_t ldx;
+  int64_t M;
+  int64_t rows;
+  int64_t K;
+  int64_t kper;   // K per workgroup split
+  int64_t inter;  // I in SILU mode
+  void* Y;
+  int64_t ldy;
+  float* partial;  // [ksplit][M][rows] when ksplit > 1
+  int mode;
+  int ksplit;
+};
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kStepK = 64;    // K elements per wave step (stream kernel)
+constexpr int kStageK = 256;  // K elements per stage (staged kernel)
+constexpr int kTileK = 64;    // K elements per tile (tiled prefill kernel)
+
+
+__device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0];
+  r[1] = a[1];
+  r[2] = b[0];
+  r[3] = b[1];
+  r[4] = c[0];
+  r[5] = c[1];
+  r[6] = d[0];
+  r[7] = d[1];
+  return r;
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
+
+}  // namespace
+
+// Tiled MFMA GEMM for prefill-sized M (gemm_tile.hip).  bn is 256 or 128.
+hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream);
+
+}  // namespace swr

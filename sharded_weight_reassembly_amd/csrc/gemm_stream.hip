@@ -26,58 +26,10 @@
 #include <stdio.h>
 #include <stdlib.h>
 
-#include "swr_internal.h"
+#include "gemm_common.h"
 
 namespace swr {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kStepK = 64;    // K elements per wave step (stream kernel)
-constexpr int kStageK = 256;  // K elements per stage (staged kernel)
-
-struct StreamArgs {
-  const uint8_t* W;
-  const float* scale;
-  const uint16_t* X;
-  int64_t ldx;
-  int64_t M;
-  int64_t rows;
-  int64_t K;
-  int64_t kper;   // K per workgroup split
-  int64_t inter;  // I in SILU mode
-  void* Y;
-  int64_t ldy;
-  float* partial;  // [ksplit][M][rows] when ksplit > 1
-  int mode;
-  int ksplit;
-};
-
-__device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  bf16x8 r;
-  r[0] = a[0];
-  r[1] = a[1];
-  r[2] = b[0];
-  r[3] = b[1];
-  r[4] = c[0];
-  r[5] = c[1];
-  r[6] = d[0];
-  r[7] = d[1];
-  return r;
-}
-
-__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
-
-__device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }
 
 // Per-lane weight data of one step for one 16-row tile: 16 K elements.
 template <bool FP8>
@@ -631,6 +583,7 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   if (plan.rt != 1 && plan.rt != 2 && plan.rt != 4) return false;
   if (silu_mode && (plan.rt < 2 || inter % (8 * plan.rt) != 0)) return false;
   if (plan.kind == 0) return p.K % kStepK == 0 && plan.rt == 4 && plan.kper % 256 == 0;
+  if (plan.kind == 3) return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
   if (plan.kind == 2)
     return p.K % kStageK == 0 && plan.kper % kStageK == 0 && p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31);
   return false;
@@ -644,6 +597,20 @@ GemmPlan plan_gemm(const GemmProblem& p) {
   plan.mt = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
   const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
   const int64_t w_bytes = p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2);
+  if (aligned_ok && p.M > 64 && p.K % kTileK == 0) {
+    // Prefill-sized M: the tiled MFMA kernel.  256-row weight tiles when they
+    // still give at least two waves of workgroups over the 256 CUs.
+    plan.kind = 3;
+    const int64_t tiles_m = (p.M + 255) / 256;
+    const int64_t cols = silu_mode ? inter : p.rows;
+    const int64_t t256 = tiles_m * ((cols + (silu_mode ? 127 : 255)) / (silu_mode ? 128 : 256));
+    plan.rt = t256 >= 512 ? 256 : 128;
+    plan.mt = 16;
+    plan.ksplit = 1;
+    plan.kper = p.K;
+    plan.partial_bytes = 0;
+    return plan;
+  }
   if (aligned_ok && p.K % kStageK == 0 && (!silu_mode || inter % 16 == 0) && w_bytes < (INT64_C(1) << 31)) {
     // Staged kernel.  Row block and K split from a sweep of the shared-expert
     // shapes on MI355X: 32-row blocks when one 16-token block suffices, 64-row
@@ -747,6 +714,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
     hipLaunchKernelGGL(generic_gemm_kernel, dim3(unsigned(g)), dim3(kThreads), 0, stream, a, fp8 ? 1 : 0);
     return hipGetLastError();
   }
+  if (plan.kind == 3) return launch_tile_gemm(a, plan.rt, fp8, stream);
   const int64_t row_blocks = row_blocks_of(p, plan.rt);
   const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
   const dim3 grid = dim3(unsigned(row_blocks), unsigned(plan.ksplit), unsigned(tok_blocks));

@@ -66,9 +66,9 @@ struct GemmProblem {
 };
 
 struct GemmPlan {
-  int kind;      // 0 = streaming MFMA kernel, 1 = generic kernel, 2 = LDS-staged MFMA kernel
+  int kind;      // 0 streaming MFMA, 1 generic, 2 LDS-staged MFMA (decode), 3 tiled MFMA (prefill)
   int mt;        // 16-token blocks per workgroup (1, 2, 4)
-  int rt;        // 16-row tiles per workgroup
+  int rt;        // 16-row tiles per workgroup (kind 3: weight rows per tile, 128 or 256)
   int ksplit;    // workgroups along K
   int64_t kper;  // K elements per split (multiple of 256)
   int64_t partial_bytes;  // fp32 split-K scratch needed (0 if ksplit == 1)

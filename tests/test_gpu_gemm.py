@@ -172,3 +172,34 @@ def test_full_size_projection_layer_sampled_rows():
         sub = np.ascontiguousarray(w.data[cols])
         ref = gemm.proj_f64(x, sub, w.dtype, len(cols), k, w.scale[cols])
         assert_close_rows(values(y)[:, cols], ref, what=f"projection {j} [{o}x{k}]")
+
+
+@pytest.mark.parametrize("o,k,dt,m", [
+    (1000, 512, synth.FP8, 300),     # row tail and token tail in the tiled kernel
+    (2048, 1024, synth.BF16, 513),
+    (384, 192, synth.FP8, 257),      # 3 K tiles, 128-row weight tiles
+    (4096, 256, synth.BF16, 1024),   # 256-row weight tiles
+])
+def test_tiled_prefill_parity(o, k, dt, m):
+    note(f"tiled proj o={o} k={k} {dt} m={m}")
+    w = synth.weight(synth.seed_for(14, 0, o % 89), o, k, dt)
+    x = synth.activations(synth.seed_for(14, 0, 50), m, k)
+    y = values(_run_proj(w, x))
+    ref = gemm.proj_f64(x, w.raw(), dt, o, k, w.scale)
+    assert_close_rows(y, ref, what=f"tiled {o}x{k} {dt} m={m}")
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+@pytest.mark.parametrize("hidden,inter,m", [(256, 320, 300), (512, 1024, 600), (128, 256, 4096)])
+def test_tiled_prefill_mlp(dt, hidden, inter, m):
+    note(f"tiled mlp h={hidden} i={inter} {dt} m={m}")
+    gu = synth.weight(synth.seed_for(15, 0, 0), 2 * inter, hidden, dt)
+    d = synth.weight(synth.seed_for(15, 0, 1), hidden, inter, dt)
+    x = synth.activations(synth.seed_for(15, 0, 50), m, hidden)
+    y = torch.empty((m, hidden), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(swr.mlp_workspace_bytes(m, hidden, inter, dt), dtype=torch.uint8, device=DEV)
+    swr.mlp_forward(u8(gu.raw()), f32(gu.scale) if gu.scale is not None else None, u8(d.raw()),
+                    f32(d.scale) if d.scale is not None else None, dt, hidden, inter, bf16(x), y, ws)
+    torch.cuda.synchronize()
+    _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter)
+    assert_close_rows(values(y), ref, what=f"tiled mlp {hidden}/{inter} {dt} m={m}")

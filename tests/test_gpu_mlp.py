@@ -122,3 +122,18 @@ def _check_full(wl, gu, d, x, m, y):
     cols = np.sort(np.random.default_rng(1).choice(wl.hidden, size=512, replace=False))
     ref = gemm.proj_f64(h, np.ascontiguousarray(d.data[cols]), d.dtype, len(cols), wl.intermediate, d.scale[cols])
     assert_close_rows(y[:, cols], ref, what=f"shared expert m={m}")
+
+
+@pytest.mark.parametrize("m", [4096, 16384])
+def test_prefill_shared_expert_sampled_tokens(shared_expert_layer, m):
+    """Prefill-shaped MLP (M = 4096 / 16384 tokens, hidden 6144, intermediate 14336,
+    FP8 weights): the oracle recomputes 24 sampled tokens completely."""
+    wl, gu, d, _ = shared_expert_layer
+    note(f"prefill shared-expert MLP m={m}")
+    x = synth.activations(synth.seed_for(4, 0, 50), m, wl.hidden)
+    y = values(_mlp(gu, d, wl.hidden, wl.intermediate, x))
+    toks = np.sort(np.random.default_rng(m).choice(m, 24, replace=False))
+    _, _, ref = gemm.mlp_f64(np.ascontiguousarray(x[toks]), gu.raw(), gu.scale, d.raw(), d.scale, gu.dtype,
+                             wl.hidden, wl.intermediate)
+    assert_close_rows(y[toks], ref, what=f"prefill m={m}")
+    assert np.isfinite(y).all()
