@@ -48,6 +48,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--isolated-reps", type=int, default=10)
+    ap.add_argument("--calibration-copy-mib", type=int, default=256,
+                    help="size of a plain device copy run at the end; rocprofv3 --pmc runs use it to scale "
+                         "FETCH_SIZE/WRITE_SIZE into bytes")
     return ap.parse_args()
 
 
@@ -110,6 +113,9 @@ def main() -> int:
     planner = swr.Planner(0, L, compute, side, slot_a, slot_b)
     for layer in range(L):
         planner.set_layer(layer, chunks[layer], C)
+    if L % 2 == 0:
+        # forwards run back to back: each gathers the next one's first layer during its last layer
+        planner.set_cyclic(True)
     o_gu, o_d = views[0]["offset"], views[1]["offset"]
 
     def forward(m: int, gemm_events=None) -> None:
@@ -153,6 +159,9 @@ def main() -> int:
     gathers = planner.gather_times()
     planner.set_timing(0)
     assert len(gathers) == args.steps * len(tokens) * L
+    # (in cyclic mode the first timed forward's first layer was gathered during warmup, and
+    # the last timed forward gathers one layer for a forward that does not run; the count is
+    # the same)
     gather_ms = {m: [] for m in tokens}
     k = 0
     for s in range(args.steps):
@@ -204,6 +213,28 @@ def main() -> int:
     iso_gather_ms = e0.elapsed_time(e1) / (args.isolated_reps * L)
     del full
 
+    # ---------------------------------------------------------------- serial reference
+    # the same gathers and MLPs back to back on one stream (no side stream, no overlap):
+    # on one GPU both share the HBM, so this shows what the overlap costs or gains
+    serial_ms = {}
+    with torch.cuda.stream(compute):
+        for m in tokens:
+            def serial_forward():
+                for layer in range(L):
+                    s_ = slot_a if layer % 2 == 0 else slot_b
+                    swr.reassemble_into_slot(chunks[layer], C, s_, stream=compute)
+                    b = s_.data_ptr()
+                    swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
+                                    xs[m], ys[m], wsp[m], stream=compute)
+            serial_forward()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(compute)
+            for _ in range(args.isolated_reps):
+                serial_forward()
+            e1.record(compute)
+            torch.cuda.synchronize()
+            serial_ms[m] = e0.elapsed_time(e1) / args.isolated_reps
+
     # ---------------------------------------------------------------- roofline
     def mlp_alg_bytes(m: int) -> int:
         # weights + scales + X read + h write + h read + Y write
@@ -229,8 +260,10 @@ def main() -> int:
         k["frac"] = k["achieved"] / k["peak"]
     dominant = "reassemble_into_slot" if gather_total_est >= gemm_total else "mlp_forward"
     dk = per_kernel[dominant]
+    for name, k in per_kernel.items():
+        k["traffic"] = measured_traffic(name)
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 1), "peak": dk["peak"], "unit": dk["unit"],
-                "frac": round(dk["frac"], 4), "traffic": None, "kernel": dominant}
+                "frac": round(dk["frac"], 4), "traffic": dk["traffic"], "kernel": dominant}
 
     per_m = {}
     for m in tokens:
@@ -246,7 +279,18 @@ def main() -> int:
             "isolated_weight_GBps": round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9, 1),
             "isolated_weight_frac": round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "isolated_tokens_per_s": round(m / (L * iso_gemm[m] * 1e-3), 1),
+            "serial_reference_ms_per_forward": round(serial_ms[m], 4),
         }
+
+    # a plain device-to-device copy of known size (read + write of the same
+    # byte count), the reference that hardware byte counters are scaled by
+    if args.calibration_copy_mib > 0:
+        src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -282,6 +326,26 @@ def main() -> int:
     print(json.dumps(result), flush=True)
     planner.close()
     return 0
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by the counter's reading for a plain
+    copy of known size), or None if there is none or the kernel's sources changed
+    since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_shared_expert_decode.json")
+    try:
+        rec = json.load(open(path))[kernel]
+        h = hashlib.sha256()
+        for f in rec["sources"]:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        if h.hexdigest()[:16] != rec["source_sha"]:
+            return None
+        return int(rec["bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, H, I, x_all, tokens) -> dict:

@@ -248,7 +248,8 @@ typedef struct swr_planner swr_planner;
 /* Trace op codes reported by swr_planner_trace (quadruples op, stream, layer, slot). */
 enum swr_trace_op {
   SWR_OP_RECORD_START = 1, SWR_OP_WAIT_START = 2, SWR_OP_WAIT_DONE = 3, SWR_OP_COPY = 4,
-  SWR_OP_RECORD_READY = 5, SWR_OP_WAIT_READY = 6, SWR_OP_RECORD_DONE = 7
+  SWR_OP_RECORD_READY = 5, SWR_OP_WAIT_READY = 6, SWR_OP_RECORD_DONE = 7,
+  SWR_OP_COPY_NEXT = 8 /* cyclic mode: the next forward's first layer */
 };
 enum swr_trace_stream { SWR_STREAM_COMPUTE = 0, SWR_STREAM_SIDE = 1 };
 
@@ -266,8 +267,9 @@ int swr_planner_set_layer(swr_planner* p, int32_t layer, const void* const* chun
 int swr_planner_reset(swr_planner* p);
 /* SWR_E_SEQUENCE if reset() was not called, or `layer` != start. */
 int swr_planner_pre_dispatch(swr_planner* p, int32_t layer);
-/* No-op (SWR_OK) outside [start, end); SWR_E_SEQUENCE if `layer` was already
- * dispatched in this forward or layer-1 was not dispatched. */
+/* No-op (SWR_OK) outside [start, end) (except layer == end in cyclic mode);
+ * SWR_E_SEQUENCE if `layer` was already dispatched in this forward or layer-1
+ * was not dispatched. */
 int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer);
 /* Makes `compute` wait for ready(layer) the first time it is called for
  * `layer` in this forward; later calls only return the slot.  *slot_out gets
@@ -276,6 +278,16 @@ int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer);
 int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void** slot_out);
 /* SWR_E_SEQUENCE if wait_ready_once(layer) was not called first. */
 int swr_planner_update_done_event(swr_planner* p, int32_t layer);
+/* Cyclic mode, for a model that runs the same layers forward after forward.
+ * The pages move the draft model's first-layer gather out of the loop so it
+ * overlaps other work (weight_sharding, "CUDA graph and the draft model");
+ * here maybe_dispatch(end) gathers the NEXT forward's first layer into slot 0,
+ * gated by done(end - 2), the last reader of slot 0 when the layer count is
+ * even.  The next forward's pre_dispatch(start) then enqueues nothing and its
+ * wait_ready_once(start) waits for that gather.  The trace shows the early
+ * gather as SWR_OP_COPY_NEXT.  SWR_E_INVALID for an odd number of layers. */
+int swr_planner_set_cyclic(swr_planner* p, int32_t enabled);
+
 /* Timing of the gathers.  swr_planner_set_timing(p, capacity) with
  * capacity > 0 makes every later dispatch record two timing events on the side
  * stream around its copy (after the gate wait, before the ready record), in a

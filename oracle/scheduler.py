@@ -17,9 +17,18 @@ i.e. layer l uses slot (l - start) mod 2; a gather with no previous layer in
 this forward is gated by a forward-start event that reset() records on the
 compute stream (it covers the previous forward's readers).
 
+Cyclic forwards (the same layers run again and again, with an even number of
+layers): the draft-model part of the page's CUDA-graph section moves a first
+layer's gather out of the loop so that it overlaps other work.  Here
+maybe_dispatch(end) gathers the *next* forward's first layer into slot 0 --
+free once done(end - 2) is recorded, since the last layer uses slot 1 -- and
+the next forward skips its own pre_dispatch gather.
+
 An op is a tuple (name, stream, layer, slot) with names
-  record_start  wait_start  wait_done  copy  record_ready  wait_ready  record_done
-and layer/slot -1 where they do not apply.  ``check_trace`` is an independent
+  record_start  wait_start  wait_done  copy  copy_next  record_ready
+  wait_ready  record_done
+and layer/slot -1 where they do not apply; ``copy_next`` is a gather made in
+one forward for the next one.  ``check_trace`` is an independent
 happens-before checker: it does not reuse ``expected_trace``.
 """
 from __future__ import annotations
@@ -31,11 +40,16 @@ def slot_of(layer: int, start: int) -> int:
     return (layer - start) % 2
 
 
-def expected_trace(start: int, end: int) -> list[tuple]:
-    """Launch/wait sequence of one forward over layers [start, end)."""
+def expected_trace(start: int, end: int, prefetched: bool = False, prefetch_next: bool = False) -> list[tuple]:
+    """Launch/wait sequence of one forward over layers [start, end).
+
+    prefetched: the previous forward already gathered layer `start` (cyclic mode);
+    prefetch_next: this forward gathers the next forward's layer `start`."""
     ops: list[tuple] = [("record_start", COMPUTE, -1, -1)]
     if end <= start:
         return ops
+    if prefetch_next and ((end - start) % 2 or end - start < 2):
+        raise ValueError("cyclic prefetch needs an even number of layers")
 
     def dispatch(layer: int) -> None:
         prev = layer - 2  # the last reader of the slot this gather overwrites
@@ -46,10 +60,17 @@ def expected_trace(start: int, end: int) -> list[tuple]:
         ops.append(("copy", SIDE, layer, slot_of(layer, start)))
         ops.append(("record_ready", SIDE, layer, -1))
 
-    dispatch(start)  # pre_dispatch(start)
+    if not prefetched:
+        dispatch(start)  # pre_dispatch(start)
     for layer in range(start, end):
         if layer + 1 < end:
             dispatch(layer + 1)  # maybe_dispatch(layer + 1)
+        elif prefetch_next:
+            # maybe_dispatch(end): the next forward's first layer into slot 0,
+            # whose last reader in this forward is layer end - 2
+            ops.append(("wait_done", SIDE, end - 2, -1))
+            ops.append(("copy_next", SIDE, start, 0))
+            ops.append(("record_ready", SIDE, start, -1))
         ops.append(("wait_ready", COMPUTE, layer, slot_of(layer, start)))
         ops.append(("record_done", COMPUTE, layer, -1))
     return ops
@@ -117,6 +138,8 @@ def check_trace(forwards: list[list[tuple]]) -> list[str]:
                     reading[layer] = slot
             elif name == "copy":
                 add("copy", stream, layer, slot, f)
+            elif name == "copy_next":
+                add("copy", stream, layer, slot, f + 1)  # feeds the next forward
             else:
                 problems.append(f"unknown op {op}")
         for layer, n in waits.items():

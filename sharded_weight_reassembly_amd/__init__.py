@@ -29,7 +29,7 @@ STATUS_NAMES = {0: "SWR_OK", -1: "SWR_E_INVALID", -2: "SWR_E_ALIGN", -3: "SWR_E_
                 -5: "SWR_E_HIP", -6: "SWR_E_SEQUENCE"}
 
 TRACE_OPS = {1: "record_start", 2: "wait_start", 3: "wait_done", 4: "copy", 5: "record_ready", 6: "wait_ready",
-             7: "record_done"}
+             7: "record_done", 8: "copy_next"}
 TRACE_STREAMS = {0: "compute", 1: "side"}
 
 # Every function include/swr.h declares.
@@ -39,7 +39,7 @@ EXPORTS = (
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
-    "swr_planner_gather_times", "swr_last_error", "swr_version",
+    "swr_planner_gather_times", "swr_planner_set_cyclic", "swr_last_error", "swr_version",
 )
 
 
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
         "swr_planner_trace": (_i32, [_vp, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
         "swr_planner_destroy": (None, [_vp]),
         "swr_planner_set_timing": (_i32, [_vp, _i32]),
+        "swr_planner_set_cyclic": (_i32, [_vp, _i32]),
         "swr_planner_gather_times": (_i32, [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]),
         "swr_last_error": (ctypes.c_char_p, []),
         "swr_version": (ctypes.c_char_p, []),
@@ -301,6 +302,10 @@ class Planner:
 
     def update_done_event(self, layer: int) -> None:
         _check("swr_planner_update_done_event", lib().swr_planner_update_done_event(self._h, int(layer)))
+
+    def set_cyclic(self, enabled: bool) -> None:
+        """Gather the next forward's first layer during the last layer (even layer counts)."""
+        _check("swr_planner_set_cyclic", lib().swr_planner_set_cyclic(self._h, int(bool(enabled))))
 
     def set_timing(self, capacity: int) -> None:
         """Time the copies of the next dispatches in a ring of `capacity` event pairs (0: off)."""

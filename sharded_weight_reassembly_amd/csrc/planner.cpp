@@ -9,6 +9,12 @@
 //     most once per layer (wait_ready_once) and the sequence is fixed at init.
 // A gather with no earlier layer in the forward is gated by a forward-start
 // event recorded by reset() on the compute stream.
+//
+// Cyclic mode (the same layers run forward after forward, an even number of
+// them): like the draft model's first-layer prefetch in the CUDA-graph
+// section, maybe_dispatch(end) gathers the next forward's first layer into
+// slot 0 -- free once done(end - 2) is recorded, since the last layer reads
+// slot 1 -- so the next forward starts without an exposed gather.
 #include <vector>
 
 #include "swr_internal.h"
@@ -32,6 +38,10 @@ struct swr_planner {
   // a ring of event pairs, one pair per timed dispatch
   std::vector<hipEvent_t> t0, t1;
   int64_t timed_dispatches = 0;
+
+  // cyclic first-layer prefetch
+  bool cyclic = false;
+  bool next_prefetched = false;  // the next forward's first layer is already gathered
 
   // per-forward state
   bool reset_called = false;
@@ -66,13 +76,15 @@ void destroy_events(swr_planner* p) {
     if (e) (void)hipEventDestroy(e);
 }
 
-// Side stream: gate, gather of `layer` into its slot, ready record.
-int dispatch(swr_planner* p, int32_t layer) {
+// Side stream: gate, gather of `layer` into its slot, ready record.  With
+// `for_next`, the gather is the next forward's first layer (cyclic mode): its
+// slot's last reader in this forward is layer end - 2.
+int dispatch(swr_planner* p, int32_t layer, bool for_next = false) {
   const int i = p->idx(layer);
   const swr_planner::Layer& L = p->layers[i];
   if (L.chunks.empty()) return fail(SWR_E_SEQUENCE, "planner: layer %d has no chunks (swr_planner_set_layer)", layer);
   hipEvent_t gate;
-  const int32_t prev = layer - 2;  // last reader of the slot this gather overwrites
+  const int32_t prev = for_next ? p->end - 2 : layer - 2;  // last reader of the slot this gather overwrites
   if (prev >= p->start) {
     if (!p->finished[p->idx(prev)])
       return fail(SWR_E_SEQUENCE, "planner: gather of layer %d needs done(%d), which was not recorded", layer, prev);
@@ -107,9 +119,12 @@ int dispatch(swr_planner* p, int32_t layer) {
     p->log(SWR_OP_WAIT_DONE, SWR_STREAM_SIDE, prev, -1);
   else
     p->log(SWR_OP_WAIT_START, SWR_STREAM_SIDE, -1, -1);
-  p->log(SWR_OP_COPY, SWR_STREAM_SIDE, layer, s);
+  p->log(for_next ? SWR_OP_COPY_NEXT : SWR_OP_COPY, SWR_STREAM_SIDE, layer, s);
   p->log(SWR_OP_RECORD_READY, SWR_STREAM_SIDE, layer, -1);
-  p->dispatched[i] = 1;
+  if (for_next)
+    p->next_prefetched = true;
+  else
+    p->dispatched[i] = 1;
   p->remote_bytes += remote;
   p->gathers += 1;
   return SWR_OK;
@@ -187,6 +202,10 @@ extern "C" int swr_planner_reset(swr_planner* p) {
   std::fill(p->dispatched.begin(), p->dispatched.end(), 0);
   std::fill(p->waited.begin(), p->waited.end(), 0);
   std::fill(p->finished.begin(), p->finished.end(), 0);
+  if (p->next_prefetched) {  // gathered by the previous forward
+    p->dispatched[0] = 1;
+    p->next_prefetched = false;
+  }
   p->trace.clear();
   p->log(SWR_OP_RECORD_START, SWR_STREAM_COMPUTE, -1, -1);
   p->reset_called = true;
@@ -199,7 +218,13 @@ extern "C" int swr_planner_pre_dispatch(swr_planner* p, int32_t layer) {
   if (!p->reset_called) return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: call swr_planner_reset first");
   if (layer != p->start)
     return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: layer %d is not the first layer %d", layer, p->start);
-  if (p->dispatched[0]) return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: already dispatched");
+  if (p->dispatched[0]) {
+    if (p->cyclic) {  // already gathered by the previous forward
+      swr::clear_error();
+      return SWR_OK;
+    }
+    return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: already dispatched");
+  }
   const int rc = dispatch(p, layer);
   if (rc == SWR_OK) swr::clear_error();
   return rc;
@@ -207,6 +232,13 @@ extern "C" int swr_planner_pre_dispatch(swr_planner* p, int32_t layer) {
 
 extern "C" int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer) {
   if (!p) return fail(SWR_E_INVALID, "swr_planner_maybe_dispatch: null pointer");
+  if (layer == p->end && p->cyclic && p->reset_called && !p->next_prefetched) {
+    if (!p->dispatched[p->idx(p->end - 1)])
+      return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: next forward before layer %d", p->end - 1);
+    const int rc = dispatch(p, p->start, true);
+    if (rc == SWR_OK) swr::clear_error();
+    return rc;
+  }
   if (!p->in_range(layer)) {
     swr::clear_error();
     return SWR_OK;
@@ -249,6 +281,16 @@ extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
   if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record");
   p->finished[i] = 1;
   p->log(SWR_OP_RECORD_DONE, SWR_STREAM_COMPUTE, layer, -1);
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_cyclic(swr_planner* p, int32_t enabled) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_set_cyclic: null pointer");
+  if (enabled && ((p->end - p->start) % 2 != 0 || p->end - p->start < 2))
+    return fail(SWR_E_INVALID, "swr_planner_set_cyclic: needs an even number of layers (have %d)", p->end - p->start);
+  p->cyclic = enabled != 0;
+  if (!p->cyclic) p->next_prefetched = false;
   swr::clear_error();
   return SWR_OK;
 }

@@ -131,3 +131,61 @@ def test_slot_memory_account():
     wl = synth.TINY
     sizes = [swr.plan_layer([(o, i, d) for _, o, i, d in wl.weights], n)[1]["total_bytes"] for n in (4, 4, 4)]
     assert accounting.weight_shard_memory(sizes, 4) == sum(sizes) // 4 + 2 * max(sizes)
+
+
+@pytest.mark.parametrize("start,n_layers", [(0, 2), (1, 4)])
+def test_cyclic_prefetch_on_gpu(start, n_layers):
+    """Cyclic mode: each forward gathers the next forward's first layer during its
+    last layer; traces equal the oracle's model, outputs equal the oracle's."""
+    note(f"planner cyclic start={start} layers={n_layers}")
+    wl = synth.TINY
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(start, start + n_layers, torch.cuda.current_stream(), torch.cuda.Stream(), slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(start + i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_cyclic(True)
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    a = torch.randn(2048, 2048, device=DEV)
+
+    def delay():
+        for _ in range(4):
+            torch.mm(a, a)
+
+    traces, outs_all = [], []
+    for _ in range(4):
+        outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+        _forward(p, layers, start, xd, outs, wsb, delay)
+        traces.append(p.trace())
+        outs_all.append(outs)
+    torch.cuda.synchronize()
+    end = start + n_layers
+    assert traces[0] == osch.expected_trace(start, end, prefetched=False, prefetch_next=True)
+    for t in traces[1:]:
+        assert t == osch.expected_trace(start, end, prefetched=True, prefetch_next=True)
+    assert osch.check_trace(traces) == []
+    for outs in outs_all:
+        for i, L in enumerate(layers):
+            ws = L["ws"]
+            _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)
+            assert_close_rows(values(outs[i]), ref, what=f"cyclic layer {start + i}")
+    _, gathers = p.counters()
+    assert gathers == 4 * n_layers + 1  # one per layer per forward, plus the last forward's early gather
+    p.set_cyclic(False)
+    p.close()
+
+
+def test_cyclic_needs_even_layers():
+    wl = synth.TINY
+    layers = _layers(wl, 1, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(0, 3, torch.cuda.current_stream(), torch.cuda.Stream(), slot, torch.empty_like(slot))
+    with pytest.raises(swr.SwrError) as e:
+        p.set_cyclic(True)
+    assert e.value.code == swr.E_INVALID
+    p.close()

@@ -66,3 +66,25 @@ def test_wrong_slot_is_caught():
 
 def test_empty_range():
     assert sch.expected_trace(5, 5) == [("record_start", "compute", -1, -1)]
+
+
+@pytest.mark.parametrize("start,end", [(0, 2), (1, 9), (0, 16)])
+def test_cyclic_prefetch_is_race_free(start, end):
+    first = sch.expected_trace(start, end, prefetched=False, prefetch_next=True)
+    mid = sch.expected_trace(start, end, prefetched=True, prefetch_next=True)
+    last = sch.expected_trace(start, end, prefetched=True, prefetch_next=False)
+    assert sch.check_trace([first, mid, mid, last]) == []
+    # the next forward issues no gather of its first layer
+    assert not any(op[0] == "copy" and op[2] == start for op in mid)
+
+
+def test_cyclic_prefetch_needs_its_gate_and_even_layers():
+    first = sch.expected_trace(0, 4, prefetch_next=True)
+    mid = sch.expected_trace(0, 4, prefetched=True)
+    i = first.index(("copy_next", "side", 0, 0))
+    no_gate = first[:i - 1] + first[i:]
+    assert any("race" in p for p in sch.check_trace([no_gate, mid]))
+    # a forward that believes its first layer was prefetched when it was not
+    assert sch.check_trace([sch.expected_trace(0, 4), mid])
+    with pytest.raises(ValueError):
+        sch.expected_trace(0, 3, prefetch_next=True)
