@@ -136,12 +136,12 @@ __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, con
   }
 }
 
-// Second half of every streaming GEMM workgroup: the 4 waves' fp32 sums for
-// RT row tiles x MT token blocks sit in LDS as red[wave][t][b][v][lane]
+// Second half of every streaming GEMM workgroup: NPART partial fp32 sums for
+// RT row tiles x MT token blocks sit in LDS as red[part][t][b][v][lane]
 // (lane = 16 * (row / 4) + token, v = row % 4 within the MFMA output tile);
 // each thread adds them for one token and 4 consecutive rows and applies the
 // output mode (scale, SiLU*up, bf16 rounding) or writes a split-K partial.
-template <int MT, int RT>
+template <int MT, int RT, int NPART = kWaves>
 __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_t tok0) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int tiles_out = silu_mode ? RT / 2 : RT;
@@ -159,7 +159,7 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
     for (int i = 0; i < 4; ++i) {
       float sum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) sum += at(w, t, b, i, ql);
+      for (int w = 0; w < NPART; ++w) sum += at(w, t, b, i, ql);
       v[i] = sum;
     }
     if (silu_mode) {
@@ -169,7 +169,7 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
       for (int i = 0; i < 4; ++i) {
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) sum += at(w, t + RT / 2, b, i, ql);
+        for (int w = 0; w < NPART; ++w) sum += at(w, t + RT / 2, b, i, ql);
         u[i] = sum;
       }
       if (a.ksplit > 1) {
@@ -269,43 +269,58 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 
 // ---------------------------------------------------------------------------
 // Staged variant (K a multiple of 256).  Same arithmetic and output modes as
-// stream_gemm_kernel; the difference is how weight bytes reach the MFMAs:
+// stream_gemm_kernel; the difference is how the operands reach the MFMAs:
 //   * a K stage is 256 elements; the workgroup's RB = 16*RTL rows x 256 K of
 //     W are loaded with consecutive threads on consecutive 16-byte pieces of a
 //     row, so one wave instruction reads 4 rows x 256 B (fp8) or 2 rows x
 //     512 B (bf16) -- long runs per DRAM page instead of 16 rows x 64 B;
-//   * loads run D stages ahead in registers (about 64 KB of weights in
-//     flight per workgroup): HBM latency under full load is several
-//     microseconds, so a skinny GEMM is bound by bytes in flight per CU;
+//   * HBM latency under full load is microseconds, so a skinny GEMM is bound
+//     by bytes in flight per CU: W pieces run DW stages ahead in a register
+//     ring (tens of KB per workgroup); the activation fragments, which come
+//     from L2, run one stage ahead in a ring of their own and are issued
+//     before the weight loads of the same stage, so waiting for them never
+//     drains the weight ring;
 //   * each stage passes through a double-buffered LDS tile whose 16-byte
 //     pieces are XOR-swizzled by row (piece c of row r sits at
 //     r * CPR + (c ^ (r % 16))), so the MFMA fragment reads (16 rows, one
 //     piece each) hit 16 distinct bank groups;
-//   * the 4 waves split each stage's 4 groups of 64 K and add their sums in
-//     LDS at the end.
+//   * wave w works on token block w % MT and on MT of the stage's 4 groups of
+//     64 K (group w / MT and on), so the accumulators stay RTL x 4 floats per
+//     lane at any token count; the 4 / MT waves that share a token block add
+//     their sums in LDS at the end.
+//   * loads go through buffer resources; a prefetch past the workgroup's last
+//     stage gets an out-of-range offset and reads nothing, so the unrolled
+//     main loop has no branches and the compiler's wait counts stay exact.
 template <int MT, int RTL, bool FP8>
 struct StagedShape {
   static constexpr int EB = FP8 ? 1 : 2;
   static constexpr int CPR = kStageK * EB / 16;        // 16-byte pieces per row per stage
   static constexpr int TILE = 16 * RTL * kStageK * EB;  // bytes of W per stage
   static constexpr int NV = TILE / (16 * kThreads);     // W pieces per thread per stage
-  // A ring slot holds one stage's W pieces (4*NV VGPRs) and this lane's X
-  // fragments (8*MT VGPRs); D slots fit in about 160 VGPRs next to the
-  // accumulators.  U unrolls the loop over a whole number of rings and LDS
-  // buffer pairs.
-  static constexpr int SLOT = 4 * NV + 8 * MT;
-  static constexpr int BUDGET = 176 - 4 * RTL * MT;
-  static constexpr int D0 = BUDGET / SLOT;
-  static constexpr int D = D0 < 2 ? 2 : (D0 > 10 ? 10 : D0);
-  static constexpr int U = (D % 2 == 0) ? D : 2 * D;
+  static constexpr int KQ = 4 / MT;                     // waves per token block (K groups)
+  static constexpr int XS = 8 * MT;                     // VGPRs of one stage of X fragments
+  static constexpr int WS = 4 * NV;                     // VGPRs of one stage of W pieces
+  // Ring depths in about 196 VGPRs next to the accumulators (two waves per
+  // SIMD leave 256).  One 16-token block: X is cheap, so W and X of a stage
+  // share a slot (D deep).  More tokens: X runs DX = 4 or 2 stages ahead in a
+  // ring of its own and W gets the rest, at most 112 VGPRs.
+  static constexpr int FREE = 196 - 4 * RTL;
+  static constexpr int DX0 = MT == 1 ? 0 : (MT == 2 && NV < 8 ? 4 : 2);
+  static constexpr int RING = MT == 1 ? (FREE < 140 ? FREE : 140) / (WS + XS)
+                                      : ((FREE - DX0 * XS) < 112 ? (FREE - DX0 * XS) : 112) / WS;
+  static constexpr int STEP = MT == 1 ? 2 : DX0;  // D must be a multiple of this (and even)
+  static constexpr int D1 = RING < STEP ? STEP : (RING > 12 ? 12 : RING);
+  static constexpr int D = D1 - (D1 % STEP);
+  static constexpr int DX = MT == 1 ? D : DX0;
 };
 
 template <int MT, int RTL, bool FP8>
 __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) {
   using S = StagedShape<MT, RTL, FP8>;
-  constexpr int EB = S::EB, CPR = S::CPR, TILE = S::TILE, NV = S::NV, D = S::D, U = S::U;
+  constexpr int EB = S::EB, CPR = S::CPR, TILE = S::TILE, NV = S::NV, D = S::D, DX = S::DX, KQ = S::KQ;
+  static_assert(D % DX == 0 && D % 2 == 0, "ring depths must nest");
   static_assert(NV >= 1 && TILE % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
-  constexpr int RED = kWaves * RTL * MT * 4 * 64 * 4;
+  constexpr int RED = KQ * RTL * MT * 4 * 64 * 4;
   constexpr int LDS = 2 * TILE > RED ? 2 * TILE : RED;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
 
@@ -314,17 +329,14 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
+  const int blk = wave % MT;  // token block of this wave
+  const int kq = wave / MT;   // its K groups: kq*MT .. kq*MT + MT - 1
 
   const int64_t k_begin = int64_t(blockIdx.y) * a.kper;
   const int64_t k_end = min(a.K, k_begin + a.kper);
   const int nst = int((k_end - k_begin) / kStageK);
   const int64_t tok0 = int64_t(blockIdx.z) * 16 * MT;
 
-  // W pieces this thread moves each stage: byte offset in W and swizzled LDS
-  // slot.  Loads go through a buffer resource over the whole matrix, so a
-  // prefetch past this workgroup's last stage is given an out-of-range offset
-  // and returns zeros without touching memory: the loop has no branches
-  // around its loads and the compiler's wait counts stay exact.
   const __amdgpu_buffer_rsrc_t wres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.W), 0, int(a.rows * a.K * EB), 0x00020000);
   int wsrc[NV];
@@ -339,40 +351,36 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
     wsrc[j] = int((r * a.K + k_begin) * EB + piece * 16);
     wdst[j] = (row * CPR + (piece ^ (row & 15))) * 16;
   }
-  // MFMA A-fragment slots of this lane: wave w handles pieces 4w..4w+3 (fp8)
-  int aoff[RTL][2];
+  // A-fragment LDS offsets for row tile 0 (tile t adds t * 16 rows): K group
+  // g4 = kq*MT + q (q < MT) covers pieces 4*g4 .. 4*g4+3 (fp8)
+  constexpr int kTileStride = 16 * CPR * 16;
+  int aoff[MT][2];
 #pragma unroll
-  for (int t = 0; t < RTL; ++t) {
-    const int row = t * 16 + r16;
+  for (int q = 0; q < MT; ++q) {
+    const int g4 = kq * MT + q;
     if (FP8) {
-      const int piece = 4 * wave + grp;
-      aoff[t][0] = (row * CPR + (piece ^ r16)) * 16;
-      aoff[t][1] = aoff[t][0];
+      const int piece = 4 * g4 + grp;
+      aoff[q][0] = (r16 * CPR + (piece ^ r16)) * 16;
+      aoff[q][1] = aoff[q][0];
     } else {
-      const int p0 = 2 * (4 * wave + grp);
-      aoff[t][0] = (row * CPR + (p0 ^ r16)) * 16;
-      aoff[t][1] = (row * CPR + ((p0 + 1) ^ r16)) * 16;
+      const int p0 = 2 * (4 * g4 + grp);
+      aoff[q][0] = (r16 * CPR + (p0 ^ r16)) * 16;
+      aoff[q][1] = (r16 * CPR + ((p0 + 1) ^ r16)) * 16;
     }
   }
-  // X fragments of this lane (token row clamped to M-1), also through a buffer resource
+  // X fragments of this lane: token row clamped to M-1, K group g4 at (4*g4 + grp)*16
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, int(a.M * a.ldx * 2), 0x00020000);
-  int xsrc[MT];
-#pragma unroll
-  for (int b = 0; b < MT; ++b) {
-    const int64_t m = min(tok0 + b * 16 + r16, a.M - 1);
-    xsrc[b] = int((m * a.ldx + k_begin + (4 * wave + grp) * 16) * 2);
-  }
+  const int64_t m_x = min(tok0 + blk * 16 + r16, a.M - 1);
+  const int xsrc = int((m_x * a.ldx + k_begin + (4 * kq * MT + grp) * 16) * 2);
 
-  f32x4 acc[RTL][MT];
+  f32x4 acc[RTL];
 #pragma unroll
-  for (int t = 0; t < RTL; ++t)
-#pragma unroll
-    for (int b = 0; b < MT; ++b) acc[t][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < RTL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int kOutOfRange = 0x7FFFFFF0;
   u32x4 wr[D][NV];
-  u32x4 xr[D][MT][2];
+  u32x4 xr[DX][MT][2];
   auto load_w = [&](u32x4(&r)[NV], int st) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -380,69 +388,68 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
       r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 2 /* nt */));
     }
   };
+  auto load_x = [&](u32x4(&x)[MT][2], int st) {
+#pragma unroll
+    for (int q = 0; q < MT; ++q) {
+      const int off = st < nst ? xsrc + (st * kStageK + q * 64) * 2 : kOutOfRange;
+      x[q][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+      x[q][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off + 16, 0, 0));
+    }
+  };
   auto store_w = [&](int buf, const u32x4(&r)[NV]) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) *reinterpret_cast<u32x4*>(lds + buf * TILE + wdst[j]) = r[j];
   };
-  auto load_x = [&](u32x4(&x)[MT][2], int st) {
-#pragma unroll
-    for (int b = 0; b < MT; ++b) {
-      const int off = st < nst ? xsrc[b] + st * (kStageK * 2) : kOutOfRange;
-      x[b][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
-      x[b][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off + 16, 0, 0));
-    }
-  };
   auto compute = [&](int buf, const u32x4(&x)[MT][2]) {
 #pragma unroll
-    for (int t = 0; t < RTL; ++t) {
-      bf16x8 a0, a1;
-      if (FP8) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(lds + buf * TILE + aoff[t][0]);
-        a0 = fp8x8_to_bf16(v[0], v[1]);
-        a1 = fp8x8_to_bf16(v[2], v[3]);
-      } else {
-        a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + buf * TILE + aoff[t][0]));
-        a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(lds + buf * TILE + aoff[t][1]));
-      }
+    for (int q = 0; q < MT; ++q)
 #pragma unroll
-      for (int b = 0; b < MT; ++b) {
-        acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[b][0]), acc[t][b], 0, 0, 0);
-        acc[t][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[b][1]), acc[t][b], 0, 0, 0);
+      for (int t = 0; t < RTL; ++t) {
+        bf16x8 a0, a1;
+        const uint8_t* base = lds + buf * TILE + t * kTileStride;
+        if (FP8) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(base + aoff[q][0]);
+          a0 = fp8x8_to_bf16(v[0], v[1]);
+          a1 = fp8x8_to_bf16(v[2], v[3]);
+        } else {
+          a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][0]));
+          a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][1]));
+        }
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[q][0]), acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[q][1]), acc[t], 0, 0, 0);
       }
-    }
   };
 
-  // prologue: stages 0..D-1 in flight (past-the-end ones read nothing)
-  // (issued in slot order, which is also the order the loop refills slots,
-  // so the wait counts at the loop head are the same on entry and on repeat)
+  // Stage s uses W slot s % D, X slot s % DX and LDS buffer s % 2.  Step s
+  // refills the W slot with stage s + D and then the X slot with stage s + DX,
+  // so the wait for X of a stage never reaches further than D - DX stages of
+  // weights ahead.  The prologue issues the same pattern for the virtual steps
+  // -D .. -1, so the wait counts at the loop head are the same on entry and on
+  // every repeat.
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     load_w(wr[j], j);
-    load_x(xr[j], j);
+    if (j + DX - D >= 0) load_x(xr[(j + DX - D) % DX], j + DX - D);
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // Stage s uses ring slot s % D and LDS buffer s % 2.  The loop is unrolled
-  // over U stages so every register index is a compile-time constant.  A slot
-  // is refilled with stage s + D right after its W pieces went to LDS, so the
-  // wait for stage s covers only loads issued D stages earlier.  Full groups of
-  // U stages run without any branch (one loop back-edge keeps the compiler's
-  // wait counts exact); the last partial group runs in a separate tail.
+  // The loop is unrolled D times so every register index is a compile-time
+  // constant.  Full groups of D stages run without any branch (one back edge
+  // keeps the wait counts exact); the last partial group runs in a tail.
   auto step = [&](const int j, const int s) {
-    const int slot = j % D;
-    store_w(j & 1, wr[slot]);  // LDS buffer j&1 was last read two stages ago, before the last barrier
+    store_w(j & 1, wr[j]);  // LDS buffer j&1 was last read two stages ago, before the last barrier
     __syncthreads();
-    load_w(wr[slot], s + D);
-    compute(j & 1, xr[slot]);
-    load_x(xr[slot], s + D);
+    load_w(wr[j], s + D);
+    compute(j & 1, xr[j % DX]);
+    load_x(xr[j % DX], s + DX);
   };
   int s0 = 0;
-  for (; s0 + U <= nst; s0 += U) {
+  for (; s0 + D <= nst; s0 += D) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) step(j, s0 + j);
+    for (int j = 0; j < D; ++j) step(j, s0 + j);
   }
 #pragma unroll
-  for (int j = 0; j < U; ++j)
+  for (int j = 0; j < D; ++j)
     if (s0 + j < nst) step(j, s0 + j);
   __syncthreads();  // every wave is done with the W tiles before LDS is reused
 
@@ -450,11 +457,9 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
 #pragma unroll
   for (int t = 0; t < RTL; ++t)
 #pragma unroll
-    for (int b = 0; b < MT; ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[(((wave * RTL + t) * MT + b) * 4 + v) * 64 + lane] = acc[t][b][v];
+    for (int v = 0; v < 4; ++v) red[(((kq * RTL + t) * MT + blk) * 4 + v) * 64 + lane] = acc[t][v];
   __syncthreads();
-  finish_tile<MT, RTL>(a, red, tok0);
+  finish_tile<MT, RTL, KQ>(a, red, tok0);
 }
 
 // Adds the split-K partials in split order and applies scale / SiLU / rounding.
@@ -580,7 +585,8 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   if (plan.kind == 1) return true;
   if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
   if (plan.mt != 1 && plan.mt != 2 && plan.mt != 4) return false;
-  if (plan.rt != 1 && plan.rt != 2 && plan.rt != 4) return false;
+  if (plan.rt != 1 && plan.rt != 2 && plan.rt != 4 && !(plan.kind == 2 && plan.rt == 8)) return false;
+  if (plan.rt == 8 && (plan.mt == 1 || p.dtype != SWR_FP8_E4M3FN)) return false;
   if (silu_mode && (plan.rt < 2 || inter % (8 * plan.rt) != 0)) return false;
   if (plan.kind == 0) return p.K % kStepK == 0 && plan.rt == 4 && plan.kper % 256 == 0;
   if (plan.kind == 3) return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
@@ -619,7 +625,9 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     // least 4 stages (the split-K finalize costs about as much as a 1/8 split).
     plan.kind = 2;
     if (silu_mode)
-      plan.rt = inter % 32 == 0 ? 4 : 2;
+      // 128-row blocks (64 gate + 64 up rows) pay off once X is reused by
+      // 32+ tokens: the X tile is then read from L2 half as often.
+      plan.rt = (plan.mt > 1 && p.dtype == SWR_FP8_E4M3FN && inter % 64 == 0) ? 8 : (inter % 32 == 0 ? 4 : 2);
     else
       plan.rt = plan.mt == 1 ? 2 : 4;
     const int64_t wgs = row_blocks_of(p, plan.rt) * tok_blocks;
@@ -671,6 +679,9 @@ hipError_t dispatch_staged_rt(int rt, const StreamArgs& a, dim3 grid, hipStream_
       return launch_staged<MT, 1, FP8>(a, grid, stream);
     case 2:
       return launch_staged<MT, 2, FP8>(a, grid, stream);
+    case 8:
+      if constexpr (FP8 && MT > 1) return launch_staged<MT, 8, FP8>(a, grid, stream);
+      return hipErrorInvalidValue;  // plan_is_valid rules this out
     default:
       return launch_staged<MT, 4, FP8>(a, grid, stream);
   }
