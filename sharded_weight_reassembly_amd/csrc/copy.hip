@@ -4,6 +4,8 @@
 // 16-byte vectors; none of them does arithmetic on weight values.
 #include <stdlib.h>
 
+#include <algorithm>
+
 #include "swr_internal.h"
 
 namespace swr {
@@ -28,19 +30,21 @@ __global__ __launch_bounds__(kThreads) void reassemble_kernel(ChunkPtrs chunks, 
   const int c = blockIdx.y;
   const u32x4* __restrict__ src = static_cast<const u32x4*>(chunks.p[c]);
   u32x4* __restrict__ dst = slot + int64_t(c) * chunk_vecs;
-  const int64_t begin = int64_t(blockIdx.x) * span_vecs;
-  const int64_t end = min(begin + span_vecs, chunk_vecs);
   const int64_t step = int64_t(kThreads) * kCopyUnroll;
-  int64_t i = begin + threadIdx.x;
-  // full tiles: every vector of the tile is in range
-  for (; i + (kCopyUnroll - 1) * kThreads < end; i += step) {
-    u32x4 v[kCopyUnroll];
+  // one span per workgroup when the grid covers the chunk; a smaller grid walks the spans
+  for (int64_t begin = int64_t(blockIdx.x) * span_vecs; begin < chunk_vecs; begin += int64_t(gridDim.x) * span_vecs) {
+    const int64_t end = min(begin + span_vecs, chunk_vecs);
+    int64_t i = begin + threadIdx.x;
+    // full tiles: every vector of the tile is in range
+    for (; i + (kCopyUnroll - 1) * kThreads < end; i += step) {
+      u32x4 v[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
+      for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * kThreads);
+      for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * kThreads);
+    }
+    for (; i < end; i += kThreads) dst[i] = src[i];
   }
-  for (; i < end; i += kThreads) dst[i] = src[i];
 }
 
 // --------------------------------------------------------------------- pack
@@ -140,6 +144,19 @@ hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chun
 #endif
   int64_t blocks = (chunk_vecs + span - 1) / span;
   if (blocks < 1) blocks = 1;
+#ifdef SWR_TUNING
+  if (const char* env = getenv("SWR_COPY_GRID")) blocks = std::min<int64_t>(blocks, atol(env));  // workgroups per chunk
+  if (const char* env = getenv("SWR_COPY_ENGINE")) {
+    if (atoi(env) == 1) {  // runtime device-to-device copies, one per chunk
+      for (int i = 0; i < n_chunks; ++i) {
+        const hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(slot) + int64_t(i) * chunk_bytes, chunks.p[i],
+                                            size_t(chunk_bytes), hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
+  }
+#endif
   const dim3 grid = dim3(unsigned(blocks), unsigned(n_chunks));
   hipLaunchKernelGGL(reassemble_kernel, grid, dim3(kThreads), 0, stream, chunks, static_cast<u32x4*>(slot),
                      chunk_vecs, span);

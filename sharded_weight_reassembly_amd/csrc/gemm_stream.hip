@@ -275,62 +275,86 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 //     row, so one wave instruction reads 4 rows x 256 B (fp8) or 2 rows x
 //     512 B (bf16) -- long runs per DRAM page instead of 16 rows x 64 B;
 //   * HBM latency under full load is microseconds, so a skinny GEMM is bound
-//     by bytes in flight per CU: W pieces run DW stages ahead in a register
-//     ring (tens of KB per workgroup); the activation fragments, which come
-//     from L2, run one stage ahead in a ring of their own and are issued
-//     before the weight loads of the same stage, so waiting for them never
-//     drains the weight ring;
+//     by bytes in flight per CU: W pieces run D stages ahead in a register
+//     ring (tens of KB per workgroup); the activations, which come from L2,
+//     run DX stages ahead in a ring of their own;
 //   * each stage passes through a double-buffered LDS tile whose 16-byte
 //     pieces are XOR-swizzled by row (piece c of row r sits at
 //     r * CPR + (c ^ (r % 16))), so the MFMA fragment reads (16 rows, one
 //     piece each) hit 16 distinct bank groups;
-//   * wave w works on token block w % MT and on MT of the stage's 4 groups of
-//     64 K (group w / MT and on), so the accumulators stay RTL x 4 floats per
-//     lane at any token count; the 4 / MT waves that share a token block add
-//     their sums in LDS at the end.
+//   * three ways to share a stage between the 4 waves:
+//     - token split (WK = false): wave w works on token block w % MT and on
+//       MT of the stage's 4 groups of 64 K (group w / MT and on); each wave
+//       reads and widens the W pieces of its K groups, so with MT token
+//       blocks every W piece is widened MT times;
+//     - K split (WK): wave w works on K group w for every token block, so
+//       each W piece is read from LDS and widened once; the wave loads its
+//       own X fragments (16 token rows x 64 B per instruction);
+//     - K split with X in LDS (WK and XL): the stage's X tile (16*MT token
+//       rows x 512 B) is loaded with row-contiguous 16-byte pieces, which
+//       keeps the L2 -> CU traffic of X in whole cache lines, and passes
+//       through a second double-buffered LDS tile (piece p of token row r at
+//       r * 32 + (p ^ (r % 16))); at 32+ tokens this traffic, not the weight
+//       stream, is what bounds the kernel once every workgroup re-reads X;
+//     in the K-split modes the 4 waves add their sums in LDS at the end.
 //   * loads go through buffer resources; a prefetch past the workgroup's last
 //     stage gets an out-of-range offset and reads nothing, so the unrolled
 //     main loop has no branches and the compiler's wait counts stay exact.
-template <int MT, int RTL, bool FP8>
+template <int MT, int RTL, bool FP8, bool WK, bool XL>
 struct StagedShape {
+  static_assert(!XL || WK, "X tiles in LDS go with K-split waves");
   static constexpr int EB = FP8 ? 1 : 2;
   static constexpr int CPR = kStageK * EB / 16;        // 16-byte pieces per row per stage
   static constexpr int TILE = 16 * RTL * kStageK * EB;  // bytes of W per stage
   static constexpr int NV = TILE / (16 * kThreads);     // W pieces per thread per stage
-  static constexpr int KQ = 4 / MT;                     // waves per token block (K groups)
-  static constexpr int XS = 8 * MT;                     // VGPRs of one stage of X fragments
+  static constexpr int XT = XL ? 16 * MT * kStageK * 2 : 0;  // bytes of X per stage in LDS
+  static constexpr int KQ = WK ? 4 : 4 / MT;            // waves that share a token block (K groups)
+  static constexpr int QN = WK ? 1 : MT;                // K groups per wave per stage
+  static constexpr int ACC = WK ? RTL * MT : RTL;       // 16x16 accumulator tiles per wave
+  static constexpr int XS = 8 * MT;                     // VGPRs of one stage of X (either layout)
   static constexpr int WS = 4 * NV;                     // VGPRs of one stage of W pieces
-  // Ring depths in about 196 VGPRs next to the accumulators (two waves per
-  // SIMD leave 256).  One 16-token block: X is cheap, so W and X of a stage
-  // share a slot (D deep).  More tokens: X runs DX = 4 or 2 stages ahead in a
-  // ring of its own and W gets the rest, at most 112 VGPRs.
-  static constexpr int FREE = 196 - 4 * RTL;
+  static constexpr int RED = KQ * RTL * MT * 4 * 64 * 4;  // bytes of the final cross-wave sum
+  static constexpr int LDS = (2 * TILE + 2 * XT) > RED ? (2 * TILE + 2 * XT) : RED;
+  // Two waves per SIMD (two workgroups per CU) where registers (about 196
+  // next to the accumulators) and LDS allow.  Otherwise one: the accumulators
+  // then sit in AGPRs and the rings get about 220 VGPRs (less the X
+  // fragments read from LDS).
+  static constexpr int OCC = (ACC >= 16 || LDS > 80 * 1024) ? 1 : 2;
+  static constexpr int FREE = OCC == 2 ? 196 - 4 * ACC : 220 - (XL ? 8 * MT : 0);
+  static constexpr int WCAP = OCC == 2 ? 112 : 128;
+  // One 16-token block: X is cheap, so W and X of a stage share a slot (D
+  // deep).  More tokens: X runs DX = 4 or 2 stages ahead in a ring of its own
+  // and W gets the rest, at most WCAP VGPRs.
   static constexpr int DX0 = MT == 1 ? 0 : (MT == 2 && NV < 8 ? 4 : 2);
   static constexpr int RING = MT == 1 ? (FREE < 140 ? FREE : 140) / (WS + XS)
-                                      : ((FREE - DX0 * XS) < 112 ? (FREE - DX0 * XS) : 112) / WS;
+                                      : ((FREE - DX0 * XS) < WCAP ? (FREE - DX0 * XS) : WCAP) / WS;
   static constexpr int STEP = MT == 1 ? 2 : DX0;  // D must be a multiple of this (and even)
   static constexpr int D1 = RING < STEP ? STEP : (RING > 12 ? 12 : RING);
   static constexpr int D = D1 - (D1 % STEP);
   static constexpr int DX = MT == 1 ? D : DX0;
 };
 
-template <int MT, int RTL, bool FP8>
-__global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) {
-  using S = StagedShape<MT, RTL, FP8>;
+template <int MT, int RTL, bool FP8, bool WK, bool XL>
+__global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC)) void staged_gemm_kernel(
+    StreamArgs a) {
+  using S = StagedShape<MT, RTL, FP8, WK, XL>;
   constexpr int EB = S::EB, CPR = S::CPR, TILE = S::TILE, NV = S::NV, D = S::D, DX = S::DX, KQ = S::KQ;
+  constexpr int QN = S::QN, XT = S::XT;
+  constexpr int XNV = XT / (16 * kThreads);  // X pieces per thread per stage (XL)
   static_assert(D % DX == 0 && D % 2 == 0, "ring depths must nest");
   static_assert(NV >= 1 && TILE % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
-  constexpr int RED = KQ * RTL * MT * 4 * 64 * 4;
-  constexpr int LDS = 2 * TILE > RED ? 2 * TILE : RED;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+  static_assert(!XL || XNV == 2 * MT, "X tile must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int grp = lane >> 4;
-  const int blk = wave % MT;  // token block of this wave
-  const int kq = wave / MT;   // its K groups: kq*MT .. kq*MT + MT - 1
+  // token split: token block wave % MT, K groups kq*MT .. kq*MT + MT - 1;
+  // K split: every token block, K group kq = wave
+  const int blk = WK ? 0 : wave % MT;
+  const int kq = WK ? wave : wave / MT;
 
   const int64_t k_begin = int64_t(blockIdx.y) * a.kper;
   const int64_t k_end = min(a.K, k_begin + a.kper);
@@ -352,12 +376,12 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
     wdst[j] = (row * CPR + (piece ^ (row & 15))) * 16;
   }
   // A-fragment LDS offsets for row tile 0 (tile t adds t * 16 rows): K group
-  // g4 = kq*MT + q (q < MT) covers pieces 4*g4 .. 4*g4+3 (fp8)
+  // g4 = kq*QN + q covers pieces 4*g4 .. 4*g4+3 (fp8)
   constexpr int kTileStride = 16 * CPR * 16;
-  int aoff[MT][2];
+  int aoff[QN][2];
 #pragma unroll
-  for (int q = 0; q < MT; ++q) {
-    const int g4 = kq * MT + q;
+  for (int q = 0; q < QN; ++q) {
+    const int g4 = kq * QN + q;
     if (FP8) {
       const int piece = 4 * g4 + grp;
       aoff[q][0] = (r16 * CPR + (piece ^ r16)) * 16;
@@ -368,19 +392,43 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
       aoff[q][1] = (r16 * CPR + ((p0 + 1) ^ r16)) * 16;
     }
   }
-  // X fragments of this lane: token row clamped to M-1, K group g4 at (4*g4 + grp)*16
   const __amdgpu_buffer_rsrc_t xres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, int(a.M * a.ldx * 2), 0x00020000);
-  const int64_t m_x = min(tok0 + blk * 16 + r16, a.M - 1);
-  const int xsrc = int((m_x * a.ldx + k_begin + (4 * kq * MT + grp) * 16) * 2);
-
-  f32x4 acc[RTL];
-#pragma unroll
-  for (int t = 0; t < RTL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   constexpr int kOutOfRange = 0x7FFFFFF0;
+  // Register-direct X (not XL): token split reads one token row, K group q at
+  // +q*64; K split reads one K group of token block b.  The lane's fragment
+  // is k = 16*grp .. 16*grp+15 of the group, token row r16 of the block.
+  constexpr int NXS = XL ? 1 : (WK ? MT : 1);
+  int xsrc[NXS];
+#pragma unroll
+  for (int b = 0; b < NXS; ++b) {
+    const int64_t m_x = min(tok0 + (blk + b) * 16 + r16, a.M - 1);
+    xsrc[b] = int((m_x * a.ldx + k_begin + (4 * kq * QN + grp) * 16) * 2);
+  }
+  // XL: piece i of a thread is piece (i*256 + tid) % 32 of token row
+  // (i*256 + tid) / 32 of the stage tile; rows past M read nothing.
+  int xg[XL ? XNV : 1];
+  int xdst[XL ? XNV : 1];
+  int xfrag[2];  // XL: LDS offsets of the lane's two X fragments in token block 0
+#pragma unroll
+  for (int i = 0; i < (XL ? XNV : 1); ++i) {
+    const int v = i * kThreads + tid;
+    const int row = v / 32, piece = v % 32;
+    xg[i] = tok0 + row < a.M ? int(((tok0 + row) * a.ldx + k_begin) * 2 + piece * 16) : -1;
+    xdst[i] = (row * 32 + (piece ^ (row & 15))) * 16;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int piece = 8 * kq + 2 * grp + h;
+    xfrag[h] = (r16 * 32 + (piece ^ r16)) * 16;
+  }
+
+  f32x4 acc[S::ACC];
+#pragma unroll
+  for (int t = 0; t < S::ACC; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
   u32x4 wr[D][NV];
-  u32x4 xr[DX][MT][2];
+  u32x4 xr[DX][MT][2];  // one stage of X: MT*2 pieces per lane in either layout
   auto load_w = [&](u32x4(&r)[NV], int st) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
@@ -390,34 +438,75 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
   };
   auto load_x = [&](u32x4(&x)[MT][2], int st) {
 #pragma unroll
-    for (int q = 0; q < MT; ++q) {
-      const int off = st < nst ? xsrc + (st * kStageK + q * 64) * 2 : kOutOfRange;
-      x[q][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
-      x[q][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off + 16, 0, 0));
-    }
+    for (int q = 0; q < MT; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int off;
+        if (XL) {
+          const int g = xg[2 * q + h];
+          off = (st < nst && g >= 0) ? g + st * kStageK * 2 : kOutOfRange;
+        } else {
+          off = st < nst ? (WK ? xsrc[q] + st * kStageK * 2 : xsrc[0] + (st * kStageK + q * 64) * 2) + 16 * h
+                         : kOutOfRange;
+        }
+        x[q][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+      }
   };
   auto store_w = [&](int buf, const u32x4(&r)[NV]) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) *reinterpret_cast<u32x4*>(lds + buf * TILE + wdst[j]) = r[j];
   };
-  auto compute = [&](int buf, const u32x4(&x)[MT][2]) {
+  auto store_x = [&](int buf, const u32x4(&x)[MT][2]) {
 #pragma unroll
     for (int q = 0; q < MT; ++q)
 #pragma unroll
+      for (int h = 0; h < 2; ++h)
+        *reinterpret_cast<u32x4*>(lds + 2 * TILE + buf * XT + xdst[2 * q + h]) = x[q][h];
+  };
+  // W fragment of row tile t, K group q (token-split) or of the wave's K group
+  auto w_frag = [&](int buf, int t, int q, bf16x8& a0, bf16x8& a1) {
+    const uint8_t* base = lds + buf * TILE + t * kTileStride;
+    if (FP8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(base + aoff[q][0]);
+      a0 = fp8x8_to_bf16(v[0], v[1]);
+      a1 = fp8x8_to_bf16(v[2], v[3]);
+    } else {
+      a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][0]));
+      a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][1]));
+    }
+  };
+  auto compute = [&](int buf, const u32x4(&x)[MT][2]) {
+    if (WK) {
+      // each W fragment is read and widened once and used by every token block
+      u32x4 xf[MT][2];
+#pragma unroll
+      for (int b = 0; b < MT; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          xf[b][h] = XL ? *reinterpret_cast<const u32x4*>(lds + 2 * TILE + buf * XT + b * 16 * 512 + xfrag[h])
+                        : x[b][h];
+#pragma unroll
       for (int t = 0; t < RTL; ++t) {
         bf16x8 a0, a1;
-        const uint8_t* base = lds + buf * TILE + t * kTileStride;
-        if (FP8) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(base + aoff[q][0]);
-          a0 = fp8x8_to_bf16(v[0], v[1]);
-          a1 = fp8x8_to_bf16(v[2], v[3]);
-        } else {
-          a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][0]));
-          a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][1]));
+        w_frag(buf, t, 0, a0, a1);
+#pragma unroll
+        for (int b = 0; b < MT; ++b) {
+          f32x4& c = acc[t * (WK ? MT : 1) + b];
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(xf[b][0]), c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(xf[b][1]), c, 0, 0, 0);
         }
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[q][0]), acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[q][1]), acc[t], 0, 0, 0);
       }
+    } else {
+#pragma unroll
+      for (int q = 0; q < MT; ++q)
+#pragma unroll
+        for (int t = 0; t < RTL; ++t) {
+          bf16x8 a0, a1;
+          w_frag(buf, t, q, a0, a1);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[q][0]), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[q][1]), acc[t], 0, 0, 0);
+        }
+    }
   };
 
   // Stage s uses W slot s % D, X slot s % DX and LDS buffer s % 2.  Step s
@@ -436,12 +525,19 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
   // The loop is unrolled D times so every register index is a compile-time
   // constant.  Full groups of D stages run without any branch (one back edge
   // keeps the wait counts exact); the last partial group runs in a tail.
+  // LDS buffer j&1 was last read two stages ago, before the last barrier.
   auto step = [&](const int j, const int s) {
-    store_w(j & 1, wr[j]);  // LDS buffer j&1 was last read two stages ago, before the last barrier
+    store_w(j & 1, wr[j]);
+    if (XL) store_x(j & 1, xr[j % DX]);
     __syncthreads();
     load_w(wr[j], s + D);
-    compute(j & 1, xr[j % DX]);
-    load_x(xr[j % DX], s + DX);
+    if (XL) {
+      load_x(xr[j % DX], s + DX);
+      compute(j & 1, xr[j % DX]);
+    } else {
+      compute(j & 1, xr[j % DX]);
+      load_x(xr[j % DX], s + DX);
+    }
   };
   int s0 = 0;
   for (; s0 + D <= nst; s0 += D) {
@@ -457,7 +553,10 @@ __global__ __launch_bounds__(kThreads, 2) void staged_gemm_kernel(StreamArgs a) 
 #pragma unroll
   for (int t = 0; t < RTL; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[(((kq * RTL + t) * MT + blk) * 4 + v) * 64 + lane] = acc[t][v];
+    for (int b = 0; b < (WK ? MT : 1); ++b)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        red[(((kq * RTL + t) * MT + blk + b) * 4 + v) * 64 + lane] = acc[t * (WK ? MT : 1) + b][v];
   __syncthreads();
   finish_tile<MT, RTL, KQ>(a, red, tok0);
 }
@@ -584,12 +683,22 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   const int64_t inter = silu_mode ? p.rows / 2 : 0;
   if (plan.kind == 1) return true;
   if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
+  if (plan.kind == 3)
+    return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
+  if (plan.kind == 5) {
+    // staged with K-split waves and X through LDS: 2 or 4 token blocks;
+    // 64-row blocks, 128 for FP8
+    if (plan.mt != 2 && plan.mt != 4) return false;
+    if (!(plan.rt == 4 || (plan.rt == 8 && p.dtype == SWR_FP8_E4M3FN))) return false;
+    if (silu_mode && inter % (8 * plan.rt) != 0) return false;
+    return p.K % kStageK == 0 && plan.kper % kStageK == 0 &&
+           p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31);
+  }
   if (plan.mt != 1 && plan.mt != 2 && plan.mt != 4) return false;
   if (plan.rt != 1 && plan.rt != 2 && plan.rt != 4 && !(plan.kind == 2 && plan.rt == 8)) return false;
   if (plan.rt == 8 && (plan.mt == 1 || p.dtype != SWR_FP8_E4M3FN)) return false;
   if (silu_mode && (plan.rt < 2 || inter % (8 * plan.rt) != 0)) return false;
   if (plan.kind == 0) return p.K % kStepK == 0 && plan.rt == 4 && plan.kper % 256 == 0;
-  if (plan.kind == 3) return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
   if (plan.kind == 2)
     return p.K % kStageK == 0 && plan.kper % kStageK == 0 && p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31);
   return false;
@@ -624,12 +733,19 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     // only while fewer than 160 workgroups would run and each split keeps at
     // least 4 stages (the split-K finalize costs about as much as a 1/8 split).
     plan.kind = 2;
+    const bool fp8 = p.dtype == SWR_FP8_E4M3FN;
     if (silu_mode)
       // 128-row blocks (64 gate + 64 up rows) pay off once X is reused by
       // 32+ tokens: the X tile is then read from L2 half as often.
-      plan.rt = (plan.mt > 1 && p.dtype == SWR_FP8_E4M3FN && inter % 64 == 0) ? 8 : (inter % 32 == 0 ? 4 : 2);
+      plan.rt = (plan.mt > 1 && fp8 && inter % 64 == 0) ? 8 : (inter % 32 == 0 ? 4 : 2);
     else
       plan.rt = plan.mt == 1 ? 2 : 4;
+    // 33-64 tokens of FP8 weights: K-split waves with X through LDS (each
+    // weight byte widened once, X read in whole cache lines)
+    if (plan.mt == 4 && fp8 && (!silu_mode || inter % 32 == 0)) {
+      plan.kind = 5;
+      if (silu_mode && inter % 64 != 0) plan.rt = 4;
+    }
     const int64_t wgs = row_blocks_of(p, plan.rt) * tok_blocks;
     const int64_t stages = p.K / kStageK;
     int64_t ks = 1;
@@ -656,7 +772,7 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       GemmPlan t = plan;
       t.kind = kind;
       t.rt = rt;
-      set_split(t, p, ks, kind == 2 ? kStageK : 256);
+      set_split(t, p, ks, (kind == 2 || kind == 5) ? kStageK : 256);
       if (plan_is_valid(p, t)) plan = t;
     }
   }
@@ -666,36 +782,41 @@ GemmPlan plan_gemm(const GemmProblem& p) {
 
 namespace {
 
-template <int MT, int RTL, bool FP8>
+template <int MT, int RTL, bool FP8, bool WK, bool XL>
 hipError_t launch_staged(const StreamArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((staged_gemm_kernel<MT, RTL, FP8>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((staged_gemm_kernel<MT, RTL, FP8, WK, XL>), grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int MT, bool FP8>
+// Instantiated (tile shape x sharing mode) combinations; plan_is_valid admits
+// exactly these.
+template <int MT, bool FP8, bool WK, bool XL>
 hipError_t dispatch_staged_rt(int rt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
   switch (rt) {
     case 1:
-      return launch_staged<MT, 1, FP8>(a, grid, stream);
+      if constexpr (!WK) return launch_staged<MT, 1, FP8, WK, XL>(a, grid, stream);
+      return hipErrorInvalidValue;
     case 2:
-      return launch_staged<MT, 2, FP8>(a, grid, stream);
+      if constexpr (!WK) return launch_staged<MT, 2, FP8, WK, XL>(a, grid, stream);
+      return hipErrorInvalidValue;
     case 8:
-      if constexpr (FP8 && MT > 1) return launch_staged<MT, 8, FP8>(a, grid, stream);
-      return hipErrorInvalidValue;  // plan_is_valid rules this out
+      if constexpr (FP8 && MT > 1) return launch_staged<MT, 8, FP8, WK, XL>(a, grid, stream);
+      return hipErrorInvalidValue;
     default:
-      return launch_staged<MT, 4, FP8>(a, grid, stream);
+      return launch_staged<MT, 4, FP8, WK, XL>(a, grid, stream);
   }
 }
 
-template <bool FP8>
+template <bool FP8, bool WK, bool XL>
 hipError_t dispatch_staged(int mt, int rt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
   switch (mt) {
     case 1:
-      return dispatch_staged_rt<1, FP8>(rt, a, grid, stream);
+      if constexpr (!WK) return dispatch_staged_rt<1, FP8, WK, XL>(rt, a, grid, stream);
+      return hipErrorInvalidValue;
     case 2:
-      return dispatch_staged_rt<2, FP8>(rt, a, grid, stream);
+      return dispatch_staged_rt<2, FP8, WK, XL>(rt, a, grid, stream);
     default:
-      return dispatch_staged_rt<4, FP8>(rt, a, grid, stream);
+      return dispatch_staged_rt<4, FP8, WK, XL>(rt, a, grid, stream);
   }
 }
 
@@ -731,8 +852,11 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
   const dim3 grid = dim3(unsigned(row_blocks), unsigned(plan.ksplit), unsigned(tok_blocks));
   hipError_t e;
   if (plan.kind == 2)
-    e = fp8 ? dispatch_staged<true>(plan.mt, plan.rt, a, grid, stream)
-            : dispatch_staged<false>(plan.mt, plan.rt, a, grid, stream);
+    e = fp8 ? dispatch_staged<true, false, false>(plan.mt, plan.rt, a, grid, stream)
+            : dispatch_staged<false, false, false>(plan.mt, plan.rt, a, grid, stream);
+  else if (plan.kind == 5)
+    e = fp8 ? dispatch_staged<true, true, true>(plan.mt, plan.rt, a, grid, stream)
+            : dispatch_staged<false, true, true>(plan.mt, plan.rt, a, grid, stream);
   else
     e = fp8 ? dispatch_mt<4, true>(plan.mt, a, grid, stream) : dispatch_mt<4, false>(plan.mt, a, grid, stream);
   if (e != hipSuccess || plan.ksplit == 1) return e;
