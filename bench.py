@@ -42,10 +42,14 @@ def log(msg: str) -> None:
 def parse() -> argparse.Namespace:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--workload", choices=["decode", "projections", "prefill", "sharded"], default="decode",
+                    help="decode (default, the headline): shared-expert decode MLP stack; projections: the "
+                         "replicated attention-projection layers at M=16; prefill: the shared-expert MLP at "
+                         "M=4096/16384; sharded: the sharded-matmul layouts (full, column shards, K shards)")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=str, default="1,8,32,64")
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: its own count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--isolated-reps", type=int, default=10)
     ap.add_argument("--calibration-copy-mib", type=int, default=256,
@@ -65,6 +69,10 @@ def main() -> int:
     if world != 1:
         print("bench.py must not be launched with more than one rank", file=sys.stderr)
         return 2
+    if args.workload != "decode":
+        import bench_workloads
+
+        return bench_workloads.run(args)
 
     import numpy as np
     import torch
@@ -79,7 +87,7 @@ def main() -> int:
     torch.cuda.set_device(dev)
     tokens = [int(t) for t in args.tokens.split(",")]
     wl = synth.SHARED_EXPERT_DECODE
-    H, I, N, L = wl.hidden, wl.intermediate, wl.n_chunks, args.layers
+    H, I, N, L = wl.hidden, wl.intermediate, wl.n_chunks, (args.layers or wl.layers)
     shp = [(o, i, d) for _, o, i, d in wl.weights]
     views, lay = swr.plan_layer(shp, N)
     T, C = lay["total_bytes"], lay["chunk_bytes"]
