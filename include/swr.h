@@ -55,6 +55,7 @@ enum swr_status {
 
 #define SWR_MAX_CHUNKS 64   /* N, chunks per layer                           */
 #define SWR_MAX_WEIGHTS 64  /* weights per layer                             */
+#define SWR_MAX_GROUP 16    /* projections per swr_proj_forward_grouped call */
 #define SWR_ITEM_ALIGN 16   /* every item starts on a 16-byte boundary       */
 
 typedef struct swr_weight_desc {
@@ -177,6 +178,43 @@ int swr_proj_forward(const void* W, int32_t dtype, const float* row_scale, int64
 /* Split-K scratch bytes swr_proj_forward can use for these sizes (0 when it
  * does not split K), or a negative status.  Host only. */
 int64_t swr_proj_workspace_bytes(int64_t M, int64_t out_f, int64_t in_f, int32_t dtype);
+
+/* One projection of a grouped call: a view of a reassembled slot with its own
+ * activations and output.  Fields as the arguments of swr_proj_forward. */
+typedef struct {
+  const void* W;          /* device, [out_features, in_features] of dtype, 16-byte aligned */
+  const float* row_scale; /* device fp32 [out_features] or NULL (s = 1; not for FP8)       */
+  const void* X;          /* device bf16 [M, ldx], 16-byte aligned                          */
+  void* Y;                /* device bf16 or fp32 [M, ldy], 16-byte aligned                  */
+  int64_t out_features, in_features, ldx, ldy;
+  int32_t dtype, y_fp32;
+} swr_proj_desc;
+
+/*
+ * swr_proj_forward_grouped -- enqueue on `stream`.
+ * The projections of one layer, all read through views of the same
+ * reassembled slot (weight_sharding, section "flat layout" step 4, and the
+ * section on targets: one gather per layer serves every projection in it).
+ * Each descriptor computes exactly what swr_proj_forward computes for it.
+ * When every projection can use the staged matrix-core kernel with the same
+ * dtype (K a multiple of 256, M <= 64, weights under 2 GiB, aligned) they
+ * run as ONE launch, which removes the per-launch ramp and tail that
+ * dominate small views; otherwise they are enqueued one after another.
+ *   descs      host array of n descriptors, 1 <= n <= SWR_MAX_GROUP; read
+ *              before the call returns
+ *   M          tokens, shared by all projections (M == 0 enqueues nothing)
+ *   workspace  as for swr_proj_forward, of at least
+ *              swr_proj_grouped_workspace_bytes(descs, n, M) bytes (0 when the
+ *              projections run as one launch)
+ * All descriptors are validated before anything is enqueued.
+ * Errors: SWR_E_INVALID, SWR_E_ALIGN, SWR_E_SHAPE, SWR_E_CAPACITY, SWR_E_HIP.
+ */
+int swr_proj_forward_grouped(const swr_proj_desc* descs, int32_t n, int64_t M, void* workspace,
+                             int64_t workspace_bytes, hipStream_t stream);
+
+/* Scratch bytes swr_proj_forward_grouped needs for these descriptors (0 when
+ * they run as one launch), or a negative status.  Host only. */
+int64_t swr_proj_grouped_workspace_bytes(const swr_proj_desc* descs, int32_t n, int64_t M);
 
 /*
  * swr_mlp_forward -- enqueue on `stream`.

@@ -35,7 +35,7 @@ TRACE_STREAMS = {0: "compute", 1: "side"}
 # Every function include/swr.h declares.
 EXPORTS = (
     "swr_plan_layer", "swr_pack_layer", "swr_reassemble_into_slot", "swr_proj_forward",
-    "swr_proj_workspace_bytes", "swr_mlp_forward", "swr_mlp_workspace_bytes", "swr_sum_partials",
+    "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward", "swr_mlp_workspace_bytes", "swr_sum_partials",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
@@ -65,6 +65,13 @@ class Layout(ctypes.Structure):
                 ("n_weights", ctypes.c_int32), ("n_chunks", ctypes.c_int32)]
 
 
+class ProjDesc(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("row_scale", ctypes.c_void_p), ("X", ctypes.c_void_p),
+                ("Y", ctypes.c_void_p), ("out_features", ctypes.c_int64), ("in_features", ctypes.c_int64),
+                ("ldx", ctypes.c_int64), ("ldy", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("y_fp32", ctypes.c_int32)]
+
+
 _lib = None
 _vp = ctypes.c_void_p
 _i32, _i64 = ctypes.c_int32, ctypes.c_int64
@@ -87,6 +94,8 @@ def lib() -> ctypes.CDLL:
                                             ctypes.POINTER(_i64)]),
         "swr_proj_forward": (_i32, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp]),
         "swr_proj_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
+        "swr_proj_forward_grouped": (_i32, [ctypes.POINTER(ProjDesc), _i32, _i64, _vp, _i64, _vp]),
+        "swr_proj_grouped_workspace_bytes": (_i64, [ctypes.POINTER(ProjDesc), _i32, _i64]),
         "swr_mlp_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
         "swr_mlp_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
         "swr_sum_partials": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i32, _vp]),
@@ -240,6 +249,38 @@ def proj_forward(w, dtype, row_scale, out_f: int, in_f: int, x: torch.Tensor, y:
            lib().swr_proj_forward(_ptr(w), _dtype(dtype), _ptr(row_scale), int(out_f), int(in_f), _ptr(x), int(ldx),
                                   int(m), _ptr(y), int(bool(y_fp32)), int(ldy), _ptr(workspace),
                                   int(workspace_bytes or 0), _stream(stream)))
+
+
+def _proj_descs(projs) -> ctypes.Array:
+    """projs: dicts with w, dtype, row_scale, out_f, in_f, x, y and optional ldx, ldy, y_fp32."""
+    arr = (ProjDesc * len(projs))()
+    for i, p in enumerate(projs):
+        x, y = p["x"], p["y"]
+        d = arr[i]
+        d.W, d.row_scale, d.X, d.Y = _ptr(p["w"]), _ptr(p.get("row_scale")), _ptr(x), _ptr(y)
+        d.out_features, d.in_features = int(p["out_f"]), int(p["in_f"])
+        d.ldx = int(p["ldx"]) if p.get("ldx") is not None else (x.stride(0) if isinstance(x, torch.Tensor) else
+                                                                  int(p["in_f"]))
+        d.ldy = int(p["ldy"]) if p.get("ldy") is not None else (y.stride(0) if isinstance(y, torch.Tensor) else
+                                                                  int(p["out_f"]))
+        y_fp32 = p.get("y_fp32")
+        if y_fp32 is None:
+            y_fp32 = isinstance(y, torch.Tensor) and y.dtype == torch.float32
+        d.dtype, d.y_fp32 = _dtype(p["dtype"]), int(bool(y_fp32))
+    return arr
+
+
+def proj_grouped_workspace_bytes(projs, m: int) -> int:
+    return _check("swr_proj_grouped_workspace_bytes",
+                  lib().swr_proj_grouped_workspace_bytes(_proj_descs(projs), len(projs), int(m)))
+
+
+def proj_forward_grouped(projs, m: int, workspace=None, stream=None) -> None:
+    """Every projection of `projs` as proj_forward would compute it, one launch where possible."""
+    nb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("swr_proj_forward_grouped",
+           lib().swr_proj_forward_grouped(_proj_descs(projs), len(projs), int(m), _ptr(workspace), nb,
+                                          _stream(stream)))
 
 
 def mlp_workspace_bytes(m: int, hidden: int, inter: int, dtype) -> int:

@@ -127,6 +127,114 @@ extern "C" int swr_proj_forward(const void* W, int32_t dtype, const float* row_s
   return SWR_OK;
 }
 
+namespace {
+
+// Checks one grouped descriptor like swr_proj_forward checks its arguments.
+int check_desc(const char* fn, const swr_proj_desc& d, int i, int64_t M) {
+  if (!d.W || !d.X || !d.Y) return fail(SWR_E_INVALID, "%s: descriptor %d has a null pointer", fn, i);
+  if (!valid_dtype(d.dtype)) return fail(SWR_E_INVALID, "%s: descriptor %d has unknown dtype %d", fn, i, d.dtype);
+  if (d.dtype == SWR_FP8_E4M3FN && !d.row_scale)
+    return fail(SWR_E_INVALID, "%s: descriptor %d: FP8 weights need row scales", fn, i);
+  if (int rc = check_sizes(fn, M, d.out_features, d.in_features)) return rc;
+  if (d.ldx < d.in_features || d.ldy < d.out_features)
+    return fail(SWR_E_SHAPE, "%s: descriptor %d: ldx=%lld < in or ldy=%lld < out", fn, i, (long long)d.ldx,
+                (long long)d.ldy);
+  if (!aligned(d.W, 16) || !aligned(d.X, 16) || !aligned(d.Y, 16) || (d.row_scale && !aligned(d.row_scale, 16)))
+    return fail(SWR_E_ALIGN, "%s: descriptor %d: W, X, Y and row_scale must be 16-byte aligned", fn, i);
+  return SWR_OK;
+}
+
+swr::GemmProblem desc_problem(const swr_proj_desc& d, int64_t M) {
+  swr::GemmProblem p{};
+  p.W = d.W;
+  p.dtype = d.dtype;
+  p.scale = d.row_scale;
+  p.X = d.X;
+  p.ldx = d.ldx;
+  p.M = M;
+  p.rows = d.out_features;
+  p.K = d.in_features;
+  p.Y = d.Y;
+  p.ldy = d.ldy;
+  p.mode = d.y_fp32 ? swr::OUT_F32 : swr::OUT_BF16;
+  return p;
+}
+
+// Validates the group; on success fills ps and returns the scratch the call
+// needs (0 for one grouped launch), else a negative status.
+int64_t plan_group(const char* fn, const swr_proj_desc* descs, int32_t n, int64_t M, swr::GemmProblem* ps,
+                   bool* one_launch, int* mt, int* rt) {
+  if (!descs) return fail(SWR_E_INVALID, "%s: null descriptor array", fn);
+  if (n < 1 || n > SWR_MAX_GROUP) return fail(SWR_E_INVALID, "%s: n=%d outside [1, %d]", fn, n, SWR_MAX_GROUP);
+  for (int i = 0; i < n; ++i) {
+    if (int rc = check_desc(fn, descs[i], i, M)) return rc;
+    ps[i] = desc_problem(descs[i], M);
+  }
+  *one_launch = swr::grouped_plan(ps, n, mt, rt);
+  if (*one_launch) return 0;
+  int64_t need = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t b = swr::plan_gemm(ps[i]).partial_bytes;
+    if (b > need) need = b;
+  }
+  return need;
+}
+
+}  // namespace
+
+extern "C" int64_t swr_proj_grouped_workspace_bytes(const swr_proj_desc* descs, int32_t n, int64_t M) {
+  swr::GemmProblem ps[SWR_MAX_GROUP];
+  bool one = false;
+  int mt = 0, rt = 0;
+  const int64_t need = plan_group("swr_proj_grouped_workspace_bytes", descs, n, M, ps, &one, &mt, &rt);
+  if (need >= 0) swr::clear_error();
+  return need;
+}
+
+extern "C" int swr_proj_forward_grouped(const swr_proj_desc* descs, int32_t n, int64_t M, void* workspace,
+                                        int64_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "swr_proj_forward_grouped";
+  swr::GemmProblem ps[SWR_MAX_GROUP];
+  bool one = false;
+  int mt = 0, rt = 0;
+  const int64_t need = plan_group(fn, descs, n, M, ps, &one, &mt, &rt);
+  if (need < 0) return int(need);
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+    return fail(SWR_E_INVALID, "%s: workspace_bytes=%lld with workspace=%p", fn, (long long)workspace_bytes, workspace);
+  if (workspace && !aligned(workspace, kWorkspaceAlign))
+    return fail(SWR_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  // separate launches: each projection as swr_proj_forward would plan it
+  swr::GemmPlan plans[SWR_MAX_GROUP];
+  if (!one) {
+    for (int i = 0; i < n; ++i) {
+      plans[i] = swr::plan_gemm(ps[i]);
+      if (plans[i].partial_bytes > 0 && !workspace) {
+        plans[i].ksplit = 1;
+        plans[i].kper = ps[i].K;
+        plans[i].partial_bytes = 0;
+      }
+      if (plans[i].partial_bytes > workspace_bytes)
+        return fail(SWR_E_CAPACITY, "%s: workspace holds %lld bytes, descriptor %d needs %lld", fn,
+                    (long long)workspace_bytes, i, (long long)plans[i].partial_bytes);
+    }
+  }
+  if (M == 0) {
+    swr::clear_error();
+    return SWR_OK;
+  }
+  if (one) {
+    const hipError_t e = swr::launch_grouped(ps, n, mt, rt, stream);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_proj_forward_grouped: launch");
+  } else {
+    for (int i = 0; i < n; ++i) {
+      const hipError_t e = swr::launch_gemm(ps[i], plans[i], static_cast<float*>(workspace), stream);
+      if (e != hipSuccess) return swr::hip_fail(e, "swr_proj_forward_grouped: launch");
+    }
+  }
+  swr::clear_error();
+  return SWR_OK;
+}
+
 extern "C" int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int32_t dtype) {
   if (!valid_dtype(dtype)) return fail(SWR_E_INVALID, "swr_mlp_workspace_bytes: unknown dtype %d", dtype);
   if (int rc = check_sizes("swr_mlp_workspace_bytes", M, H, 2 * I)) return rc;

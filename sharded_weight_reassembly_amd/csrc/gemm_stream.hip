@@ -104,13 +104,13 @@ __device__ inline void mma_step(const Step<MT, RT, FP8>& st, f32x4 (&acc)[RT][MT
 
 // Output row of tile t, lane-row r (0..15) of this workgroup.
 template <int RT>
-__device__ inline int64_t tile_row(const StreamArgs& a, int t) {
+__device__ inline int64_t tile_row(const StreamArgs& a, int t, int64_t bx) {
   if (a.mode == OUT_SILU_BF16) {
     constexpr int half = RT / 2;
-    const int64_t j0 = int64_t(blockIdx.x) * 16 * half;
+    const int64_t j0 = bx * 16 * half;
     return t < half ? j0 + t * 16 : a.inter + j0 + (t - half) * 16;
   }
-  return int64_t(blockIdx.x) * 16 * RT + t * 16;
+  return bx * 16 * RT + t * 16;
 }
 
 __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, const float (&v)[4], bool bf16_out) {
@@ -142,7 +142,7 @@ __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, con
 // each thread adds them for one token and 4 consecutive rows and applies the
 // output mode (scale, SiLU*up, bf16 rounding) or writes a split-K partial.
 template <int MT, int RT, int NPART = kWaves>
-__device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_t tok0) {
+__device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_t tok0, int64_t bx, int64_t split) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int tiles_out = silu_mode ? RT / 2 : RT;
   const int items = tiles_out * MT * 64;
@@ -153,7 +153,7 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
     const int t = (q >> 6) / MT;
     const int64_t tok = tok0 + b * 16 + (ql & 15);
     if (tok >= a.M) continue;
-    const int64_t row = tile_row<RT>(a, t) + 4 * (ql >> 4);
+    const int64_t row = tile_row<RT>(a, t, bx) + 4 * (ql >> 4);
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -163,7 +163,7 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
       v[i] = sum;
     }
     if (silu_mode) {
-      const int64_t urow = tile_row<RT>(a, t + RT / 2) + 4 * (ql >> 4);
+      const int64_t urow = tile_row<RT>(a, t + RT / 2, bx) + 4 * (ql >> 4);
       float u[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -173,7 +173,7 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
         u[i] = sum;
       }
       if (a.ksplit > 1) {
-        float* pg = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
+        float* pg = a.partial + (split * a.M + tok) * a.rows;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pg[row + i] = v[i];
@@ -195,7 +195,7 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
       continue;
     }
     if (a.ksplit > 1) {
-      float* pr = a.partial + (int64_t(blockIdx.y) * a.M + tok) * a.rows;
+      float* pr = a.partial + (split * a.M + tok) * a.rows;
       for (int i = 0; i < 4; ++i)
         if (row + i < a.rows) pr[row + i] = v[i];
       continue;
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
   const uint8_t* wp[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
-    int64_t r = tile_row<RT>(a, t) + r16;
+    int64_t r = tile_row<RT>(a, t, blockIdx.x) + r16;
     r = min(r, a.rows - 1);  // rows past the end are loaded from the last row and never stored
     wp[t] = a.W + (r * a.K + k_begin + grp * 16) * eb;
   }
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[(((wave * RT + t) * MT + b) * 4 + v) * 64 + lane] = acc[t][b][v];
   __syncthreads();
-  finish_tile<MT, RT>(a, red, tok0);
+  finish_tile<MT, RT>(a, red, tok0, blockIdx.x, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -334,9 +334,9 @@ struct StagedShape {
   static constexpr int DX = MT == 1 ? D : DX0;
 };
 
+// The body of a staged workgroup: row block bx, K split by, token block bz.
 template <int MT, int RTL, bool FP8, bool WK, bool XL>
-__global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC)) void staged_gemm_kernel(
-    StreamArgs a) {
+__device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, int64_t bz, uint8_t* lds) {
   using S = StagedShape<MT, RTL, FP8, WK, XL>;
   constexpr int EB = S::EB, CPR = S::CPR, TILE = S::TILE, NV = S::NV, D = S::D, DX = S::DX, KQ = S::KQ;
   constexpr int QN = S::QN, XT = S::XT;
@@ -344,7 +344,6 @@ __global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC))
   static_assert(D % DX == 0 && D % 2 == 0, "ring depths must nest");
   static_assert(NV >= 1 && TILE % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
   static_assert(!XL || XNV == 2 * MT, "X tile must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[S::LDS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -356,10 +355,10 @@ __global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC))
   const int blk = WK ? 0 : wave % MT;
   const int kq = WK ? wave : wave / MT;
 
-  const int64_t k_begin = int64_t(blockIdx.y) * a.kper;
+  const int64_t k_begin = by * a.kper;
   const int64_t k_end = min(a.K, k_begin + a.kper);
   const int nst = int((k_end - k_begin) / kStageK);
-  const int64_t tok0 = int64_t(blockIdx.z) * 16 * MT;
+  const int64_t tok0 = bz * 16 * MT;
 
   const __amdgpu_buffer_rsrc_t wres =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.W), 0, int(a.rows * a.K * EB), 0x00020000);
@@ -370,7 +369,7 @@ __global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC))
     const int v = j * kThreads + tid;
     const int row = v / CPR;
     const int piece = v % CPR;
-    int64_t r = tile_row<RTL>(a, row / 16) + (row % 16);
+    int64_t r = tile_row<RTL>(a, row / 16, bx) + (row % 16);
     r = min(r, a.rows - 1);  // rows past the end are loaded from the last row and never stored
     wsrc[j] = int((r * a.K + k_begin) * EB + piece * 16);
     wdst[j] = (row * CPR + (piece ^ (row & 15))) * 16;
@@ -558,7 +557,33 @@ __global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC))
       for (int v = 0; v < 4; ++v)
         red[(((kq * RTL + t) * MT + blk + b) * 4 + v) * 64 + lane] = acc[t * (WK ? MT : 1) + b][v];
   __syncthreads();
-  finish_tile<MT, RTL, KQ>(a, red, tok0);
+  finish_tile<MT, RTL, KQ>(a, red, tok0, bx, by);
+}
+
+template <int MT, int RTL, bool FP8, bool WK, bool XL>
+__global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL>::OCC)) void staged_gemm_kernel(
+    StreamArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StagedShape<MT, RTL, FP8, WK, XL>::LDS];
+  staged_body<MT, RTL, FP8, WK, XL>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
+
+// Several projections in one launch (the views of one reassembled layer):
+// workgroup x belongs to the group g with first[g] <= x < first[g + 1] and
+// runs that group's row block x - first[g].  No K split.
+struct GroupArgs {
+  StreamArgs g[kMaxGroup];
+  int first[kMaxGroup + 1];
+  int n;
+};
+
+template <int MT, int RTL, bool FP8>
+__global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, false, false>::OCC)) void grouped_staged_kernel(
+    GroupArgs ga) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StagedShape<MT, RTL, FP8, false, false>::LDS];
+  const int x = blockIdx.x;
+  int g = 0;
+  while (g + 1 < ga.n && x >= ga.first[g + 1]) ++g;
+  staged_body<MT, RTL, FP8, false, false>(ga.g[g], x - ga.first[g], 0, blockIdx.z, lds);
 }
 
 // Adds the split-K partials in split order and applies scale / SiLU / rounding.
@@ -822,7 +847,9 @@ hipError_t dispatch_staged(int mt, int rt, const StreamArgs& a, dim3 grid, hipSt
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream) {
+namespace {
+
+StreamArgs make_args(const GemmProblem& p, int64_t kper, int ksplit, float* partial) {
   StreamArgs a{};
   a.W = static_cast<const uint8_t*>(p.W);
   a.scale = p.scale;
@@ -831,13 +858,73 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
   a.M = p.M;
   a.rows = p.rows;
   a.K = p.K;
-  a.kper = plan.kper;
+  a.kper = kper;
   a.inter = p.mode == OUT_SILU_BF16 ? p.rows / 2 : 0;
   a.Y = p.Y;
   a.ldy = p.ldy;
   a.partial = partial;
   a.mode = p.mode;
-  a.ksplit = plan.ksplit;
+  a.ksplit = ksplit;
+  return a;
+}
+
+template <int MT, int RT, bool FP8>
+hipError_t launch_grouped_mt(const GroupArgs& ga, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((grouped_staged_kernel<MT, RT, FP8>), grid, dim3(kThreads), 0, stream, ga);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt) {
+  if (n < 1 || n > kMaxGroup) return false;
+  const int64_t M = ps[0].M;
+  if (M < 1 || M > 64) return false;
+  int64_t blocks = 0;
+  *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  *rt = *mt == 1 ? 2 : 4;
+  for (int i = 0; i < n; ++i) {
+    const GemmProblem& p = ps[i];
+    if (p.dtype != ps[0].dtype || p.M != M || p.mode == OUT_SILU_BF16) return false;
+    if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
+    if (p.K % kStageK != 0 || p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) >= (INT64_C(1) << 31)) return false;
+    blocks += (p.rows + 16 * *rt - 1) / (16 * *rt);
+  }
+  return blocks < (INT64_C(1) << 30);
+}
+
+hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStream_t stream) {
+  // longest K first: the last workgroups to start are the shortest
+  int order[kMaxGroup];
+  for (int i = 0; i < n; ++i) order[i] = i;
+  for (int i = 1; i < n; ++i)
+    for (int j = i; j > 0 && ps[order[j]].K > ps[order[j - 1]].K; --j) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  GroupArgs ga{};
+  ga.n = n;
+  int first = 0;
+  for (int i = 0; i < n; ++i) {
+    const GemmProblem& p = ps[order[i]];
+    ga.g[i] = make_args(p, p.K, 1, nullptr);
+    ga.first[i] = first;
+    first += int((p.rows + 16 * rt - 1) / (16 * rt));
+  }
+  ga.first[n] = first;
+  const int64_t tok_blocks = (ps[0].M + 16 * mt - 1) / (16 * mt);
+  const dim3 grid = dim3(unsigned(first), 1, unsigned(tok_blocks));
+  const bool fp8 = ps[0].dtype == SWR_FP8_E4M3FN;
+  if (mt == 1)
+    return fp8 ? launch_grouped_mt<1, 2, true>(ga, grid, stream) : launch_grouped_mt<1, 2, false>(ga, grid, stream);
+  if (mt == 2)
+    return fp8 ? launch_grouped_mt<2, 4, true>(ga, grid, stream) : launch_grouped_mt<2, 4, false>(ga, grid, stream);
+  return fp8 ? launch_grouped_mt<4, 4, true>(ga, grid, stream) : launch_grouped_mt<4, 4, false>(ga, grid, stream);
+}
+
+hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream) {
+  StreamArgs a = make_args(p, plan.kper, plan.ksplit, partial);
   const bool fp8 = p.dtype == SWR_FP8_E4M3FN;
   if (plan.kind == 1) {
     const int64_t cols = p.mode == OUT_SILU_BF16 ? a.inter : p.rows;

@@ -80,4 +80,11 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan);
 // Enqueues the GEMM; `partial` must hold plan.partial_bytes bytes.
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream);
 
+// Grouped projections (no SiLU mode): true when the n problems can run as one
+// staged launch (same dtype and token count, M <= 64, K a multiple of 256,
+// aligned); sets the token blocks and row tiles per workgroup.
+constexpr int kMaxGroup = SWR_MAX_GROUP;
+bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt);
+hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStream_t stream);
+
 }  // namespace swr

@@ -128,6 +128,50 @@ def test_gemm_argument_errors_before_enqueue():
     assert L.swr_mlp_workspace_bytes(4, 0, 256, swr.BF16) == swr.E_SHAPE
 
 
+def _descs(specs):
+    arr = (swr.ProjDesc * len(specs))()
+    for i, (w, s, x, y, o, k, ldx, ldy, dt) in enumerate(specs):
+        arr[i].W, arr[i].row_scale, arr[i].X, arr[i].Y = w, s, x, y
+        arr[i].out_features, arr[i].in_features, arr[i].ldx, arr[i].ldy = o, k, ldx, ldy
+        arr[i].dtype, arr[i].y_fp32 = dt, 0
+    return arr
+
+
+def test_grouped_projection_errors_before_enqueue():
+    L = swr.lib()
+    a = 1 << 20
+    ok = (a, a, a, a, 64, 256, 256, 64, swr.FP8_E4M3FN)
+    assert L.swr_proj_forward_grouped(None, 1, 4, None, 0, None) == swr.E_INVALID
+    assert L.swr_proj_forward_grouped(_descs([ok]), 0, 4, None, 0, None) == swr.E_INVALID
+    assert L.swr_proj_forward_grouped(_descs([ok] * 17), 17, 4, None, 0, None) == swr.E_INVALID
+    # the bad descriptor is the second one: nothing may be enqueued for the first
+    no_scale = (a, None, a, a, 64, 256, 256, 64, swr.FP8_E4M3FN)
+    assert L.swr_proj_forward_grouped(_descs([ok, no_scale]), 2, 4, None, 0, None) == swr.E_INVALID
+    misaligned = (a, a, a, a + 8, 64, 256, 256, 64, swr.FP8_E4M3FN)
+    assert L.swr_proj_forward_grouped(_descs([ok, misaligned]), 2, 4, None, 0, None) == swr.E_ALIGN
+    short_ldx = (a, a, a, a, 64, 256, 128, 64, swr.FP8_E4M3FN)
+    assert L.swr_proj_forward_grouped(_descs([ok, short_ldx]), 2, 4, None, 0, None) == swr.E_SHAPE
+    bad_dtype = (a, a, a, a, 64, 256, 256, 64, 7)
+    assert L.swr_proj_forward_grouped(_descs([bad_dtype]), 1, 4, None, 0, None) == swr.E_INVALID
+    assert L.swr_proj_forward_grouped(_descs([ok]), 1, 4, a + 16, 256, None) == swr.E_ALIGN
+
+
+def test_grouped_workspace_bytes():
+    L = swr.lib()
+    a = 1 << 20
+    stageable = [(a, a, a, a, 1000, 512, 512, 1000, swr.FP8_E4M3FN), (a, a, a, a, 300, 768, 768, 300, swr.FP8_E4M3FN)]
+    # one launch without any K split: no scratch
+    assert L.swr_proj_grouped_workspace_bytes(_descs(stageable), 2, 16) == 0
+    # K = 320 cannot be staged: separate launches, scratch of the largest single projection
+    mixed = stageable + [(a, a, a, a, 640, 320, 320, 640, swr.FP8_E4M3FN)]
+    need = L.swr_proj_grouped_workspace_bytes(_descs(mixed), 3, 16)
+    singles = [swr.proj_workspace_bytes(16, o, k, "fp8_e4m3fn") for (_, _, _, _, o, k, _, _, _) in mixed]
+    assert need == max(singles)
+    # tokens past the decode range: separate launches as well
+    assert L.swr_proj_grouped_workspace_bytes(_descs(stageable), 2, 65) == max(
+        swr.proj_workspace_bytes(65, o, k, "fp8_e4m3fn") for (_, _, _, _, o, k, _, _, _) in stageable)
+
+
 def test_mlp_workspace_covers_h():
     for m in (1, 8, 32, 64, 100):
         for dt in ("bf16", "fp8_e4m3fn"):

@@ -203,3 +203,92 @@ def test_tiled_prefill_mlp(dt, hidden, inter, m):
     torch.cuda.synchronize()
     _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter)
     assert_close_rows(values(y), ref, what=f"tiled mlp {hidden}/{inter} {dt} m={m}")
+
+
+def _grouped(ws, xs, m, y_fp32=False):
+    ys = [torch.full((max(m, 1), w.out_features), float("nan"), device=DEV,
+                     dtype=torch.float32 if y_fp32 else torch.bfloat16) for w in ws]
+    projs = [dict(w=u8(w.raw()), dtype=w.dtype, row_scale=f32(w.scale) if w.scale is not None else None,
+                  out_f=w.out_features, in_f=w.in_features, x=bf16(xs[w.in_features]), y=y)
+             for w, y in zip(ws, ys)]
+    nb = swr.proj_grouped_workspace_bytes(projs, m)
+    wsp = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV) if nb > 0 else None
+    swr.proj_forward_grouped(projs, m, workspace=wsp)
+    torch.cuda.synchronize()
+    return nb, [y[:m] for y in ys]
+
+
+GROUPS = [
+    # (shapes, dtype): K mixes and ragged row counts; all stageable -> one launch
+    ([(1000, 512), (300, 768), (64, 256), (2048, 1024)], synth.FP8),
+    ([(512, 256), (100, 512), (777, 768)], synth.BF16),
+    # K = 320 is not a multiple of 256: separate launches
+    ([(640, 320), (300, 768), (100, 127)], synth.FP8),
+]
+
+
+@pytest.mark.parametrize("gi", range(len(GROUPS)))
+@pytest.mark.parametrize("m", [1, 4, 16, 17, 33, 64, 65])
+def test_grouped_projection_parity(gi, m):
+    shapes, dt = GROUPS[gi]
+    note(f"grouped projections group={gi} m={m}")
+    ws = [synth.weight(synth.seed_for(16, gi, j), o, k, dt) for j, (o, k) in enumerate(shapes)]
+    xs = {k: synth.activations(synth.seed_for(16, gi, 50 + k % 97), m, k) for _, k in shapes}
+    nb, ys = _grouped(ws, xs, m)
+    if all(k % 256 == 0 for _, k in shapes) and m <= 64:
+        assert nb == 0  # one launch, no K split
+    for w, y in zip(ws, ys):
+        ref = gemm.proj_f64(xs[w.in_features], w.raw(), w.dtype, w.out_features, w.in_features, w.scale)
+        assert_close_rows(values(y), ref, what=f"grouped {w.out_features}x{w.in_features} {w.dtype} m={m}")
+
+
+def test_grouped_fp32_output_and_zero_tokens():
+    note("grouped fp32 output, M=0")
+    ws = [synth.weight(31, 320, 512, synth.FP8), synth.weight(32, 96, 256, synth.FP8)]
+    xs = {512: synth.activations(33, 9, 512), 256: synth.activations(34, 9, 256)}
+    _, ys = _grouped(ws, xs, 9, y_fp32=True)
+    for w, y in zip(ws, ys):
+        ref = gemm.proj_f64(xs[w.in_features], w.raw(), w.dtype, w.out_features, w.in_features, w.scale)
+        assert_close_rows(values(y), ref, what="grouped fp32")
+    y = torch.full((1, 320), 3.0, dtype=torch.bfloat16, device=DEV)
+    x = torch.zeros((1, 512), dtype=torch.bfloat16, device=DEV)
+    swr.proj_forward_grouped([dict(w=u8(ws[0].raw()), dtype=synth.FP8, row_scale=f32(ws[0].scale), out_f=320,
+                                   in_f=512, x=x, y=y)], 0)
+    torch.cuda.synchronize()
+    assert (y == 3.0).all()
+
+
+def test_full_size_projection_layer_grouped():
+    """The 8 FP8 projections of one replicated attention layer at M=16 in ONE
+    grouped call through views of one reassembled slot; the oracle recomputes
+    a sample of output columns of every projection."""
+    wl = synth.ATTN_PROJECTIONS
+    note("full-size projection layer M=16, grouped")
+    ws = wl.layer_weights(1)
+    shp = [(o, i, d) for _, o, i, d in wl.weights]
+    views, lay = swr.plan_layer(shp, wl.n_chunks)
+    src = [u8(w.raw()) for w in ws]
+    chunks = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(wl.n_chunks)]
+    swr.pack_layer(lay, views, src, chunks)
+    del src
+    slot = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=DEV)
+    swr.reassemble_into_slot(chunks, lay["chunk_bytes"], slot)
+    m = 16
+    xs, projs, ys = {}, [], []
+    for j, (w, v) in enumerate(zip(ws, views)):
+        k, o = w.in_features, w.out_features
+        if k not in xs:
+            xs[k] = synth.activations(synth.seed_for(3, 1, 50 + len(xs)), m, k)
+        y = torch.empty((m, o), dtype=torch.bfloat16, device=DEV)
+        ys.append(y)
+        projs.append(dict(w=slot.data_ptr() + v["offset"], dtype=w.dtype, row_scale=f32(w.scale), out_f=o, in_f=k,
+                          x=bf16(xs[k]), y=y))
+    assert swr.proj_grouped_workspace_bytes(projs, m) == 0  # one launch
+    swr.proj_forward_grouped(projs, m)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    for j, (w, y) in enumerate(zip(ws, ys)):
+        o, k = w.out_features, w.in_features
+        cols = np.sort(rng.choice(o, size=min(o, 96), replace=False))
+        ref = gemm.proj_f64(xs[k], np.ascontiguousarray(w.data[cols]), w.dtype, len(cols), k, w.scale[cols])
+        assert_close_rows(values(y)[:, cols], ref, what=f"grouped projection {j} [{o}x{k}]")
