@@ -243,6 +243,31 @@ def main() -> int:
             torch.cuda.synchronize()
             serial_ms[m] = e0.elapsed_time(e1) / args.isolated_reps
 
+    # ---------------------------------------------------------------- DMA-engine gather
+    # the same pipelined forwards with the gathers on the DMA engines (no compute
+    # units): the copy-engine path of the pages, at the smallest and largest M
+    dma = {}
+    planner.set_copy_engine(swr.ENGINE_DMA)
+    dma_steps = max(2, args.steps // 4)
+    for m in sorted({tokens[0], tokens[-1]}):
+        with torch.cuda.stream(compute):
+            forward(m)
+        torch.cuda.synchronize()
+        evd = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+               for _ in range(dma_steps)]
+        fwd_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dma_steps)]
+        with torch.cuda.stream(compute):
+            for s in range(dma_steps):
+                fwd_d[s][0].record(compute)
+                forward(m, evd[s])
+                fwd_d[s][1].record(compute)
+        torch.cuda.synchronize()
+        f = float(np.median([a.elapsed_time(b) for a, b in fwd_d]))
+        g = float(np.mean([a.elapsed_time(b) for row in evd for a, b in row]))
+        dma[str(m)] = {"pipelined_ms_per_forward": round(f, 4), "gemm_ms_per_layer_in_pipeline": round(g, 4),
+                       "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
+    planner.set_copy_engine(swr.ENGINE_KERNEL)
+
     # ---------------------------------------------------------------- roofline
     def mlp_alg_bytes(m: int) -> int:
         # weights + scales + X read + h write + h read + Y write
@@ -326,6 +351,7 @@ def main() -> int:
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "per_tokens": per_m,
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1),
+        "dma_engine_gather": dma,
         "roofline": roofline,
         "roofline_by_kernel": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                for k, v in per_kernel.items()},

@@ -145,6 +145,20 @@ int swr_reassemble_into_slot(const void* const* chunk_dev, int32_t n_chunks, int
                              void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
                              hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes);
 
+/*
+ * swr_reassemble_into_slot_dma -- the same gather, arguments, checks and
+ * events as swr_reassemble_into_slot, but the bytes move on the GPU's DMA
+ * engines (one device-to-device copy per chunk, hipMemcpyDeviceToDeviceNoCU)
+ * instead of a copy kernel.  weight_sharding, section on the NCCL policy /
+ * copy engine: a copy-engine gather leaves every compute unit to the layer's
+ * GEMMs.  On MI355X the DMA engines move far fewer bytes per second than the
+ * copy kernel; the trade is measured, not assumed.
+ * Errors: as swr_reassemble_into_slot.
+ */
+int swr_reassemble_into_slot_dma(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
+                                 void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
+                                 hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes);
+
 /* ------------------------------------------------------------ GEMMs (a5-a8) */
 
 /*
@@ -316,6 +330,19 @@ int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer);
 int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void** slot_out);
 /* SWR_E_SEQUENCE if wait_ready_once(layer) was not called first. */
 int swr_planner_update_done_event(swr_planner* p, int32_t layer);
+/* Gather engines of the planner (swr_planner_set_copy_engine). */
+#define SWR_ENGINE_KERNEL 0 /* swr_reassemble_into_slot (default)      */
+#define SWR_ENGINE_DMA 1    /* swr_reassemble_into_slot_dma            */
+
+/*
+ * swr_planner_set_copy_engine -- which gather the planner enqueues from now
+ * on: SWR_ENGINE_KERNEL (the copy kernel) or SWR_ENGINE_DMA (the DMA engines,
+ * weight_sharding section on the NCCL policy / copy engine).  The launch/wait
+ * sequence and the trace are the same for both.  Host only.
+ * Errors: SWR_E_INVALID (null planner, unknown engine).
+ */
+int swr_planner_set_copy_engine(swr_planner* p, int32_t engine);
+
 /* Cyclic mode, for a model that runs the same layers forward after forward.
  * The pages move the draft model's first-layer gather out of the loop so it
  * overlaps other work (weight_sharding, "CUDA graph and the draft model");

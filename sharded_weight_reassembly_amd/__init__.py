@@ -34,7 +34,8 @@ TRACE_STREAMS = {0: "compute", 1: "side"}
 
 # Every function include/swr.h declares.
 EXPORTS = (
-    "swr_plan_layer", "swr_pack_layer", "swr_reassemble_into_slot", "swr_proj_forward",
+    "swr_plan_layer", "swr_pack_layer", "swr_reassemble_into_slot", "swr_reassemble_into_slot_dma",
+    "swr_planner_set_copy_engine", "swr_proj_forward",
     "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward", "swr_mlp_workspace_bytes", "swr_sum_partials",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(_vp), _vp]),
         "swr_reassemble_into_slot": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i64, _i32, _vp, _vp, _vp,
                                             ctypes.POINTER(_i64)]),
+        "swr_reassemble_into_slot_dma": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i64, _i32, _vp, _vp, _vp,
+                                                ctypes.POINTER(_i64)]),
+        "swr_planner_set_copy_engine": (_i32, [_vp, _i32]),
         "swr_proj_forward": (_i32, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp]),
         "swr_proj_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
         "swr_proj_forward_grouped": (_i32, [ctypes.POINTER(ProjDesc), _i32, _i64, _vp, _i64, _vp]),
@@ -215,6 +219,22 @@ def reassemble_into_slot(chunks, chunk_bytes: int, slot, slot_bytes: int | None 
                                           int(slot_bytes), int(self_rank), _stream(stream), _event(gate),
                                           _event(ready), ctypes.byref(remote)))
     return remote.value
+
+
+def reassemble_into_slot_dma(chunks, chunk_bytes: int, slot, slot_bytes: int | None = None, self_rank: int = 0,
+                             stream=None, gate=None, ready=None) -> int:
+    """reassemble_into_slot on the DMA engines (no compute units)."""
+    if slot_bytes is None:
+        slot_bytes = slot.numel() * slot.element_size()
+    remote = _i64(0)
+    _check("swr_reassemble_into_slot_dma",
+           lib().swr_reassemble_into_slot_dma(_ptr_array(chunks), len(chunks), int(chunk_bytes), _ptr(slot),
+                                              int(slot_bytes), int(self_rank), _stream(stream), _event(gate),
+                                              _event(ready), ctypes.byref(remote)))
+    return remote.value
+
+
+ENGINE_KERNEL, ENGINE_DMA = 0, 1
 
 
 def view(slot: torch.Tensor, v: dict) -> torch.Tensor:
@@ -347,6 +367,10 @@ class Planner:
     def set_cyclic(self, enabled: bool) -> None:
         """Gather the next forward's first layer during the last layer (even layer counts)."""
         _check("swr_planner_set_cyclic", lib().swr_planner_set_cyclic(self._h, int(bool(enabled))))
+
+    def set_copy_engine(self, engine: int) -> None:
+        """ENGINE_KERNEL (the copy kernel, default) or ENGINE_DMA (the DMA engines)."""
+        _check("swr_planner_set_copy_engine", lib().swr_planner_set_copy_engine(self._h, int(engine)))
 
     def set_timing(self, capacity: int) -> None:
         """Time the copies of the next dispatches in a ring of `capacity` event pairs (0: off)."""

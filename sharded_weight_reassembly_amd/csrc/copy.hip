@@ -147,7 +147,7 @@ hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chun
 #ifdef SWR_TUNING
   if (const char* env = getenv("SWR_COPY_GRID")) blocks = std::min<int64_t>(blocks, atol(env));  // workgroups per chunk
   if (const char* env = getenv("SWR_COPY_ENGINE")) {
-    if (atoi(env) == 1) {  // runtime device-to-device copies, one per chunk
+    if (atoi(env) == 1) {  // the runtime's device-to-device copy (a blit kernel), one per chunk
       for (int i = 0; i < n_chunks; ++i) {
         const hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(slot) + int64_t(i) * chunk_bytes, chunks.p[i],
                                             size_t(chunk_bytes), hipMemcpyDeviceToDevice, stream);
@@ -225,42 +225,69 @@ extern "C" int swr_pack_layer(const swr_layout* layout, const swr_view_desc* vie
   return SWR_OK;
 }
 
-extern "C" int swr_reassemble_into_slot(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
-                                        void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
-                                        hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes) {
-  if (!chunk_dev || !slot) return fail(SWR_E_INVALID, "swr_reassemble_into_slot: null pointer");
+namespace {
+
+// Shared by both gather entry points: every argument is checked before the
+// gate wait, the copy and the ready record are enqueued on `side`.
+int reassemble(const char* fn, const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes, void* slot,
+               int64_t slot_bytes, int32_t self_rank, hipStream_t side, hipEvent_t gate, hipEvent_t ready,
+               int64_t* remote_bytes, bool dma) {
+  if (!chunk_dev || !slot) return fail(SWR_E_INVALID, "%s: null pointer", fn);
   if (n_chunks < 1 || n_chunks > SWR_MAX_CHUNKS)
-    return fail(SWR_E_INVALID, "swr_reassemble_into_slot: n_chunks=%d outside [1, %d]", n_chunks, SWR_MAX_CHUNKS);
+    return fail(SWR_E_INVALID, "%s: n_chunks=%d outside [1, %d]", fn, n_chunks, SWR_MAX_CHUNKS);
   if (chunk_bytes <= 0 || chunk_bytes % 16 != 0)
-    return fail(SWR_E_ALIGN, "swr_reassemble_into_slot: chunk_bytes=%lld is not a positive multiple of 16",
-                (long long)chunk_bytes);
+    return fail(SWR_E_ALIGN, "%s: chunk_bytes=%lld is not a positive multiple of 16", fn, (long long)chunk_bytes);
   if (self_rank < 0 || self_rank >= n_chunks)
-    return fail(SWR_E_INVALID, "swr_reassemble_into_slot: self_rank=%d outside [0, %d)", self_rank, n_chunks);
+    return fail(SWR_E_INVALID, "%s: self_rank=%d outside [0, %d)", fn, self_rank, n_chunks);
   if (slot_bytes < chunk_bytes * n_chunks)
-    return fail(SWR_E_CAPACITY, "swr_reassemble_into_slot: slot holds %lld bytes, layer needs %lld",
-                (long long)slot_bytes, (long long)(chunk_bytes * n_chunks));
-  if (!aligned(slot, 16)) return fail(SWR_E_ALIGN, "swr_reassemble_into_slot: slot not 16-byte aligned");
+    return fail(SWR_E_CAPACITY, "%s: slot holds %lld bytes, layer needs %lld", fn, (long long)slot_bytes,
+                (long long)(chunk_bytes * n_chunks));
+  if (!aligned(slot, 16)) return fail(SWR_E_ALIGN, "%s: slot not 16-byte aligned", fn);
   swr::ChunkPtrs ptrs{};
   for (int i = 0; i < n_chunks; ++i) {
-    if (!chunk_dev[i]) return fail(SWR_E_INVALID, "swr_reassemble_into_slot: chunk_dev[%d] is null", i);
-    if (!aligned(chunk_dev[i], 16))
-      return fail(SWR_E_ALIGN, "swr_reassemble_into_slot: chunk_dev[%d] not 16-byte aligned", i);
+    if (!chunk_dev[i]) return fail(SWR_E_INVALID, "%s: chunk_dev[%d] is null", fn, i);
+    if (!aligned(chunk_dev[i], 16)) return fail(SWR_E_ALIGN, "%s: chunk_dev[%d] not 16-byte aligned", fn, i);
     ptrs.p[i] = chunk_dev[i];
   }
   hipError_t e;
   if (gate) {
     e = hipStreamWaitEvent(side, gate, 0);
-    if (e != hipSuccess) return swr::hip_fail(e, "swr_reassemble_into_slot: wait gate");
+    if (e != hipSuccess) return swr::hip_fail(e, "reassembly: wait gate");
   }
-  e = swr::launch_reassemble(ptrs, n_chunks, chunk_bytes, slot, side);
-  if (e != hipSuccess) return swr::hip_fail(e, "swr_reassemble_into_slot: launch");
+  if (dma) {
+    // the DMA engines, no compute units: one device-to-device copy per chunk
+    for (int i = 0; i < n_chunks; ++i) {
+      e = hipMemcpyAsync(static_cast<uint8_t*>(slot) + int64_t(i) * chunk_bytes, chunk_dev[i], size_t(chunk_bytes),
+                         hipMemcpyDeviceToDeviceNoCU, side);
+      if (e != hipSuccess) return swr::hip_fail(e, "reassembly: DMA copy");
+    }
+  } else {
+    e = swr::launch_reassemble(ptrs, n_chunks, chunk_bytes, slot, side);
+    if (e != hipSuccess) return swr::hip_fail(e, "reassembly: launch");
+  }
   if (ready) {
     e = hipEventRecord(ready, side);
-    if (e != hipSuccess) return swr::hip_fail(e, "swr_reassemble_into_slot: record ready");
+    if (e != hipSuccess) return swr::hip_fail(e, "reassembly: record ready");
   }
   if (remote_bytes) *remote_bytes += int64_t(n_chunks - 1) * chunk_bytes;
   swr::clear_error();
   return SWR_OK;
+}
+
+}  // namespace
+
+extern "C" int swr_reassemble_into_slot(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
+                                        void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
+                                        hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes) {
+  return reassemble("swr_reassemble_into_slot", chunk_dev, n_chunks, chunk_bytes, slot, slot_bytes, self_rank, side,
+                    gate, ready, remote_bytes, false);
+}
+
+extern "C" int swr_reassemble_into_slot_dma(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
+                                            void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
+                                            hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes) {
+  return reassemble("swr_reassemble_into_slot_dma", chunk_dev, n_chunks, chunk_bytes, slot, slot_bytes, self_rank,
+                    side, gate, ready, remote_bytes, true);
 }
 
 extern "C" int swr_sum_partials(const float* const* parts, int32_t n, int64_t count, void* out, int32_t out_bf16,

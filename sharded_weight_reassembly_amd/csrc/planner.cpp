@@ -39,6 +39,9 @@ struct swr_planner {
   std::vector<hipEvent_t> t0, t1;
   int64_t timed_dispatches = 0;
 
+  // gather engine: 0 the copy kernel, 1 the DMA engines
+  int32_t engine = 0;
+
   // cyclic first-layer prefetch
   bool cyclic = false;
   bool next_prefetched = false;  // the next forward's first layer is already gathered
@@ -95,9 +98,10 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false) {
   const int s = p->slot_of(layer);
   int64_t remote = 0;
   int rc;
+  auto gather = p->engine == SWR_ENGINE_DMA ? swr_reassemble_into_slot_dma : swr_reassemble_into_slot;
   if (p->t0.empty()) {
-    rc = swr_reassemble_into_slot(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s],
-                                  p->slot_bytes, 0, p->side, gate, p->ready[i], &remote);
+    rc = gather(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s], p->slot_bytes, 0, p->side, gate,
+                p->ready[i], &remote);
   } else {
     // same sequence with timing records between the gate wait and the ready record
     const size_t r = size_t(p->timed_dispatches % int64_t(p->t0.size()));
@@ -105,8 +109,8 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false) {
     if (e != hipSuccess) return swr::hip_fail(e, "planner: wait gate");
     e = hipEventRecord(p->t0[r], p->side);
     if (e != hipSuccess) return swr::hip_fail(e, "planner: record timing start");
-    rc = swr_reassemble_into_slot(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s],
-                                  p->slot_bytes, 0, p->side, nullptr, nullptr, &remote);
+    rc = gather(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s], p->slot_bytes, 0, p->side,
+                nullptr, nullptr, &remote);
     if (rc == SWR_OK) {
       e = hipEventRecord(p->t1[r], p->side);
       if (e == hipSuccess) e = hipEventRecord(p->ready[i], p->side);
@@ -291,6 +295,15 @@ extern "C" int swr_planner_set_cyclic(swr_planner* p, int32_t enabled) {
     return fail(SWR_E_INVALID, "swr_planner_set_cyclic: needs an even number of layers (have %d)", p->end - p->start);
   p->cyclic = enabled != 0;
   if (!p->cyclic) p->next_prefetched = false;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_copy_engine(swr_planner* p, int32_t engine) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_set_copy_engine: null pointer");
+  if (engine != SWR_ENGINE_KERNEL && engine != SWR_ENGINE_DMA)
+    return fail(SWR_E_INVALID, "swr_planner_set_copy_engine: unknown engine %d", engine);
+  p->engine = engine;
   swr::clear_error();
   return SWR_OK;
 }

@@ -109,6 +109,18 @@ def test_reassemble_argument_errors_before_enqueue():
                                       None) == swr.E_INVALID
 
 
+def test_dma_reassemble_checks_like_the_kernel_path():
+    L = swr.lib()
+    good = 1 << 20
+    chunks = _vp_array([good, good + 4096])
+    for fn in (L.swr_reassemble_into_slot, L.swr_reassemble_into_slot_dma):
+        assert fn(None, 2, 4096, good, 8192, 0, None, None, None, None) == swr.E_INVALID
+        assert fn(chunks, 2, 4008, good, 8192, 0, None, None, None, None) == swr.E_ALIGN
+        assert fn(chunks, 2, 4096, good, 8191, 0, None, None, None, None) == swr.E_CAPACITY
+        assert fn(chunks, 2, 4096, good + 8, 8192, 0, None, None, None, None) == swr.E_ALIGN
+        assert fn(chunks, 2, 4096, good, 8192, 2, None, None, None, None) == swr.E_INVALID
+
+
 def test_gemm_argument_errors_before_enqueue():
     L = swr.lib()
     a = 1 << 20
@@ -188,3 +200,4 @@ def test_planner_errors_without_gpu_work():
     assert L.swr_planner_create(0, 4, 1, 2, a + 8, a, 4096, ctypes.byref(h)) == swr.E_ALIGN
     assert L.swr_planner_create(0, 4, 1, 2, None, a, 4096, ctypes.byref(h)) == swr.E_INVALID
     assert L.swr_planner_reset(None) == swr.E_INVALID
+    assert L.swr_planner_set_copy_engine(None, 0) == swr.E_INVALID

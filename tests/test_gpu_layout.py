@@ -114,3 +114,38 @@ def test_pack_rejects_misaligned_source():
     with pytest.raises(swr.SwrError) as e:
         swr.pack_layer(lay, views, [src.data_ptr() + 4], chunks)
     assert e.value.code == swr.E_ALIGN
+
+
+@pytest.mark.parametrize("shapes,n", [CASES[1], CASES[3], CASES[6]])
+def test_dma_gather_bit_exact(shapes, n):
+    """The DMA-engine gather writes exactly the copy kernel's bytes: T, and
+    nothing past |T|."""
+    note(f"dma gather shapes={[(o, i, d) for _, o, i, d in shapes][:4]} n={n}")
+    ws = [synth.weight(synth.seed_for(11, 1, t), o, i, d) for t, (_, o, i, d) in enumerate(shapes)]
+    shp = [(o, i, d) for _, o, i, d in shapes]
+    views, lay, chunks, _, _ = _pack_and_gather(shp, ws, n)
+    plan = olayout.plan_layer(shp, n)
+    t_ref, _ = olayout.pack_layer(plan, [w.raw() for w in ws])
+    slot = torch.full((lay["total_bytes"] + 4096,), 0x5A, dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    gate, ready = torch.cuda.Event(), torch.cuda.Event()
+    gate.record(torch.cuda.current_stream())
+    remote = swr.reassemble_into_slot_dma(chunks, lay["chunk_bytes"], slot, stream=side, gate=gate, ready=ready)
+    torch.cuda.current_stream().wait_event(ready)
+    got = slot.cpu().numpy()
+    assert np.array_equal(got[:lay["total_bytes"]], t_ref)
+    assert (got[lay["total_bytes"]:] == 0x5A).all(), "copy wrote past |T|"
+    assert remote == olayout.remote_bytes(plan)
+
+
+def test_dma_gather_full_size_layer():
+    """One 264 MB shared-expert layer gathered by the DMA engines equals T."""
+    wl = synth.SHARED_EXPERT_DECODE
+    note("full-size DMA gather 264 MB N=16")
+    ws = wl.layer_weights(1)
+    shp = [(o, i, d) for _, o, i, d in wl.weights]
+    views, lay, chunks, slot, _ = _pack_and_gather(shp, ws, wl.n_chunks)
+    slot2 = torch.zeros_like(slot)
+    swr.reassemble_into_slot_dma(chunks, lay["chunk_bytes"], slot2)
+    torch.cuda.synchronize()
+    assert torch.equal(slot2[:lay["total_bytes"]], slot[:lay["total_bytes"]])

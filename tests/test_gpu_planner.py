@@ -189,3 +189,54 @@ def test_cyclic_needs_even_layers():
         p.set_cyclic(True)
     assert e.value.code == swr.E_INVALID
     p.close()
+
+
+@pytest.mark.parametrize("start,n_layers,cyclic", [(0, 3, False), (1, 4, True)])
+def test_dma_engine_planner(start, n_layers, cyclic):
+    """The planner with the DMA-engine gather: same launch/wait sequence as the
+    copy kernel, and every layer's outputs equal the oracle's."""
+    note(f"planner dma engine start={start} layers={n_layers} cyclic={cyclic}")
+    wl = synth.TINY
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(start, start + n_layers, torch.cuda.current_stream(), torch.cuda.Stream(), slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(start + i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_copy_engine(swr.ENGINE_DMA)
+    with pytest.raises(swr.SwrError) as e:
+        p.set_copy_engine(7)
+    assert e.value.code == swr.E_INVALID
+    if cyclic:
+        p.set_cyclic(True)
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    a = torch.randn(2048, 2048, device=DEV)
+
+    def delay():
+        for _ in range(4):
+            torch.mm(a, a)
+
+    traces, outs_all = [], []
+    for _ in range(3):
+        outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+        _forward(p, layers, start, xd, outs, wsb, delay)
+        traces.append(p.trace())
+        outs_all.append(outs)
+    torch.cuda.synchronize()
+    end = start + n_layers
+    if cyclic:
+        assert traces[0] == osch.expected_trace(start, end, prefetched=False, prefetch_next=True)
+        assert all(t == osch.expected_trace(start, end, prefetched=True, prefetch_next=True) for t in traces[1:])
+    else:
+        assert all(t == osch.expected_trace(start, end) for t in traces)
+    assert osch.check_trace(traces) == []
+    for outs in outs_all:
+        for i, L in enumerate(layers):
+            ws = L["ws"]
+            _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)
+            assert_close_rows(values(outs[i]), ref, what=f"dma layer {start + i}")
+    p.set_cyclic(False)
+    p.close()
