@@ -126,19 +126,20 @@ def main() -> int:
         planner.set_cyclic(True)
     o_gu, o_d = views[0]["offset"], views[1]["offset"]
 
-    def forward(m: int, gemm_events=None) -> None:
-        planner.reset()
-        planner.pre_dispatch(0)
+    def forward(m: int, gemm_events=None, pl=None) -> None:
+        pl = planner if pl is None else pl
+        pl.reset()
+        pl.pre_dispatch(0)
         for layer in range(L):
-            planner.maybe_dispatch(layer + 1)
-            base = planner.wait_ready_once(layer)
+            pl.maybe_dispatch(layer + 1)
+            base = pl.wait_ready_once(layer)
             if gemm_events is not None:
                 gemm_events[layer][0].record(compute)
             swr.mlp_forward(base + o_gu, scales[layer][0], base + o_d, scales[layer][1], "fp8_e4m3fn", H, I, xs[m],
                             ys[m], wsp[m], stream=compute)
             if gemm_events is not None:
                 gemm_events[layer][1].record(compute)
-            planner.update_done_event(layer)
+            pl.update_done_event(layer)
 
     # ---------------------------------------------------------------- warmup
     with torch.cuda.stream(compute):
@@ -268,6 +269,44 @@ def main() -> int:
                        "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
     planner.set_copy_engine(swr.ENGINE_KERNEL)
 
+    # ---------------------------------------------------------------- graph replay
+    # one forward captured as a graph (weight_sharding, CUDA graph section) and
+    # replayed: a planner without the cross-forward prefetch, so every replay
+    # is self-contained, against the same planner run eagerly
+    graph = {}
+    gp = swr.Planner(0, L, compute, side, slot_a, slot_b)
+    for layer in range(L):
+        gp.set_layer(layer, chunks[layer], C)
+    reps = max(4, args.steps // 2)
+    for m in sorted({tokens[0], tokens[-1]}):
+        with torch.cuda.stream(compute):
+            forward(m, pl=gp)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(compute):
+            e0.record(compute)
+            for _ in range(reps):
+                forward(m, pl=gp)
+            e1.record(compute)
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=compute):
+            forward(m, pl=gp)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(compute):
+            e0.record(compute)
+            for _ in range(reps):
+                g.replay()
+            e1.record(compute)
+        torch.cuda.synchronize()
+        graph[str(m)] = {"eager_ms_per_forward": round(eager, 4),
+                         "graph_replay_ms_per_forward": round(e0.elapsed_time(e1) / reps, 4)}
+        del g
+    gp.close()
+
     # ---------------------------------------------------------------- roofline
     def mlp_alg_bytes(m: int) -> int:
         # weights + scales + X read + h write + h read + Y write
@@ -352,6 +391,7 @@ def main() -> int:
         "per_tokens": per_m,
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1),
         "dma_engine_gather": dma,
+        "graph_replay_no_prefetch": graph,
         "roofline": roofline,
         "roofline_by_kernel": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                for k, v in per_kernel.items()},

@@ -240,3 +240,51 @@ def test_dma_engine_planner(start, n_layers, cyclic):
             assert_close_rows(values(outs[i]), ref, what=f"dma layer {start + i}")
     p.set_cyclic(False)
     p.close()
+
+
+@pytest.mark.parametrize("engine", [swr.ENGINE_KERNEL, swr.ENGINE_DMA])
+def test_forward_captured_in_a_graph(engine):
+    """weight_sharding, CUDA graph section: the launch/wait sequence is fixed,
+    so one forward (gathers on the side stream, MLPs on the compute stream)
+    can be captured once and replayed.  Between replays both slots and every
+    output are overwritten with garbage by eager work; each replay must
+    gather again and reproduce the oracle's outputs."""
+    note(f"graph capture engine={engine}")
+    wl = synth.TINY
+    n_layers = 4
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    compute, side = torch.cuda.Stream(), torch.cuda.Stream()
+    p = swr.Planner(0, n_layers, compute, side, slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_copy_engine(engine)
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    refs = []
+    for L in layers:
+        ws = L["ws"]
+        refs.append(gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)[2])
+    with torch.cuda.stream(compute):
+        _forward(p, layers, 0, xd, outs, wsb)  # eager warm-up on the same streams
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=compute):
+        _forward(p, layers, 0, xd, outs, wsb)
+    assert p.trace() == osch.expected_trace(0, n_layers)  # the captured sequence is the model's
+    torch.cuda.synchronize()
+    for rep in range(4):
+        slot_a.fill_(0xFF)  # 0xFFFF as bf16 is NaN: a replay that skipped a gather would show it
+        slot_b.fill_(0xFF)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i in range(n_layers):
+            assert_close_rows(values(outs[i]), refs[i], what=f"graph replay {rep} layer {i}")
+    p.close()
