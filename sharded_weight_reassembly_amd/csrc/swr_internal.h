@@ -71,7 +71,8 @@ struct GemmPlan {
   int mt;        // 16-token blocks per workgroup (1, 2, 4)
   int rt;        // 16-row tiles per workgroup (kind 3: weight rows per tile, 128 or 256)
   int ksplit;    // workgroups along K
-  int64_t kper;  // K elements per split (multiple of 256)
+  int64_t kper;  // K elements per split (multiple of the stage length)
+  int sk;        // staged kinds: K elements per stage (256, or 512 for one FP8 token block)
   int64_t partial_bytes;  // fp32 split-K scratch needed (0 if ksplit == 1)
 };
 

@@ -49,6 +49,8 @@ SHAPES = [
     (64, 64, synth.FP8),
     (777, 320, synth.BF16),       # K = 5*64: not a multiple of 256
     (2048, 1024, synth.FP8),
+    (64, 8192, synth.FP8),        # few row blocks: 512-K stages with a 4-way K split at <= 16 tokens
+    (96, 16384, synth.FP8),       # 512-K stages, 8-way K split
 ]
 
 
