@@ -34,22 +34,25 @@ constexpr int kGroupM = 4;  // token blocks per XCD group
 
 __device__ inline int swz(int row, int piece) { return row * 8 + (piece ^ ((row >> 1) & 7)); }
 
-template <int BN, bool FP8>
-__global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
-  constexpr int WN = BN / 2;        // weight rows per wave
+template <int BN, bool FP8, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) {
+  constexpr int NT = 64 * WAVES;    // threads
+  constexpr int WGN = WAVES / 2;    // waves along the weight rows (2 along the tokens)
+  constexpr int WN = BN / WGN;      // weight rows per wave
   constexpr int TM = 4;             // 32-token MFMA tiles per wave (128 tokens)
   constexpr int TN = WN / 32;       // 32-row MFMA tiles per wave
   constexpr int A_BYTES = kTileM * kTileK * 2;
   constexpr int B_BYTES = BN * kTileK * 2;
-  constexpr int NA = A_BYTES / 16 / kThreads;             // X pieces per thread per step
-  constexpr int NB = FP8 ? BN * kTileK / 16 / kThreads     // fp8 pieces (16 codes) per thread
-                         : B_BYTES / 16 / kThreads;        // bf16 pieces per thread
+  constexpr int NA = A_BYTES / 16 / NT;             // X pieces per thread per step
+  constexpr int NB = FP8 ? BN * kTileK / 16 / NT     // fp8 pieces (16 codes) per thread
+                         : B_BYTES / 16 / NT;        // bf16 pieces per thread
+  static_assert(TN >= 1 && NA >= 1 && NB >= 1, "tile must split evenly over the workgroup");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const bool silu_mode = a.mode == OUT_SILU_BF16;
 
   // ---- tile numbering: XCD-contiguous ranges, grouped by token blocks
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
   int adst[NA];
 #pragma unroll
   for (int j = 0; j < NA; ++j) {
-    const int v = j * kThreads + tid;
+    const int v = j * NT + tid;
     const int row = v / 8, piece = v % 8;
     const int64_t m = min(m0 + row, a.M - 1);
     asrc[j] = a.X + m * a.ldx + piece * 8;
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
   int bdst[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int v = j * kThreads + tid;
+    const int v = j * NT + tid;
     if (FP8) {
       const int row = v / 4, q = v % 4;  // 16 codes = bf16 pieces 2q, 2q+1
       int64_t r = w_row(row);
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       if (FP8) {
-        const int v = j * kThreads + tid;
+        const int v = j * NT + tid;
         const int row = v / 4, q = v % 4;
         *reinterpret_cast<bf16x8*>(B + bdst[j]) = fp8x8_to_bf16(rb[j][0], rb[j][1]);
         *reinterpret_cast<bf16x8*>(B + swz(row, 2 * q + 1) * 16) = fp8x8_to_bf16(rb[j][2], rb[j][3]);
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
     }
   };
 
-  // ---- fragment read offsets (bytes within a buffer), for k-step 0; k-step ks adds 2 pieces
+  // ---- fragment reads: k-step ks of buffer buf into F (A rows then B rows)
   const int r32 = lane & 31, kg = lane >> 5;
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -143,36 +146,46 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
 #pragma unroll
     for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
 
-  auto compute = [&](int buf) {
+  bf16x8 F[2][TM + TN];  // two k-steps of fragments: the next one is read while the current one multiplies
+  auto read_frags = [&](int buf, int ks, bf16x8(&f)[TM + TN]) {
     const uint8_t* A = lds + buf * (A_BYTES + B_BYTES);
     const uint8_t* B = A + A_BYTES;
+    const int piece = ks * 2 + kg;
 #pragma unroll
-    for (int ks = 0; ks < kTileK / 16; ++ks) {
-      const int piece = ks * 2 + kg;
-      bf16x8 fa[TM], fb[TN];
+    for (int x = 0; x < TM; ++x) f[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, piece) * 16);
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
-        fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, piece) * 16);
+    for (int y = 0; y < TN; ++y)
+      f[TM + y] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, piece) * 16);
+  };
+  auto mfmas = [&](const bf16x8(&f)[TM + TN]) {
 #pragma unroll
-      for (int y = 0; y < TN; ++y)
-        fb[y] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, piece) * 16);
+    for (int x = 0; x < TM; ++x)
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
-#pragma unroll
-        for (int y = 0; y < TN; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-    }
+      for (int y = 0; y < TN; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[x], f[TM + y], acc[x][y], 0, 0, 0);
   };
 
   const int nk = int(a.K / kTileK);
   load(0);
   store(0);
   __syncthreads();
+  read_frags(0, 0, F[0]);
+  // Each k-step is a scheduling region of its own: the next k-step's LDS
+  // fragment reads (into the other register set) interleave with this
+  // k-step's MFMAs, and their wait lands at the start of the next region.
   for (int kt = 0; kt < nk; ++kt) {
     const bool more = kt + 1 < nk;
-    if (more) load(kt + 1);
-    compute(kt & 1);
-    if (more) store((kt + 1) & 1);
+    const int buf = kt & 1;
+    if (more) load(kt + 1);  // global loads, in flight during the MFMAs below
+#pragma unroll
+    for (int ks = 0; ks < kTileK / 16; ++ks) {
+      if (ks + 1 < kTileK / 16) read_frags(buf, ks + 1, F[(ks + 1) & 1]);
+      mfmas(F[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (more) store(buf ^ 1);  // the other buffer was last read before the previous barrier
     __syncthreads();
+    if (more) read_frags(buf ^ 1, 0, F[0]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: lane holds column c = l % 32 of each 32 x 32 tile, rows 8*(v/4) + 4*(l/32) + v%4
@@ -218,22 +231,25 @@ __global__ __launch_bounds__(kThreads, 1) void tile_gemm_kernel(StreamArgs a) {
   }
 }
 
-template <int BN, bool FP8>
+template <int BN, bool FP8, int WAVES>
 hipError_t launch_bn(const StreamArgs& a, hipStream_t stream) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
   const int64_t cols = silu_mode ? a.inter : a.rows;
   const int64_t col_tile = silu_mode ? BN / 2 : BN;
   const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
-  hipLaunchKernelGGL((tile_gemm_kernel<BN, FP8>), dim3(unsigned(tiles_m * tiles_n)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((tile_gemm_kernel<BN, FP8, WAVES>), dim3(unsigned(tiles_m * tiles_n)), dim3(64 * WAVES), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
-  if (bn == 256) return fp8 ? launch_bn<256, true>(a, stream) : launch_bn<256, false>(a, stream);
-  return fp8 ? launch_bn<128, true>(a, stream) : launch_bn<128, false>(a, stream);
+  // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
+  // waits on LDS and barriers are covered by the other's MFMAs
+  if (bn == 256) return fp8 ? launch_bn<256, true, 8>(a, stream) : launch_bn<256, false, 8>(a, stream);
+  return fp8 ? launch_bn<128, true, 4>(a, stream) : launch_bn<128, false, 4>(a, stream);
 }
 
 }  // namespace swr
