@@ -269,6 +269,58 @@ def main() -> int:
                        "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
     planner.set_copy_engine(swr.ENGINE_KERNEL)
 
+    # ---------------------------------------------------------------- tensor-parallel share
+    # The PR report's alternative to weight sharding: each of R ranks (its
+    # deployment's TP4) holds 1/R of the intermediate dimension and computes an
+    # fp32 partial of Y; the partials are all-reduced.  One GPU shows one
+    # rank's share at its real shape, timed over all ranks' shards of all
+    # layers (so no cache serves a later call), and the local reduce of R
+    # partials.
+    R = 4
+    sh = I // R
+    tmp = torch.empty(T, dtype=torch.uint8, device=dev)
+    shards = []
+    for layer in range(L):
+        swr.reassemble_into_slot(chunks[layer], C, tmp, stream=compute)
+        torch.cuda.synchronize()
+        gu_full = tmp[o_gu:o_gu + 2 * I * H].view(2 * I, H)
+        d_full = tmp[o_d:o_d + H * I].view(H, I)
+        for r in range(R):
+            rows = torch.cat([torch.arange(r * sh, (r + 1) * sh), torch.arange(I + r * sh, I + (r + 1) * sh)]).to(dev)
+            shards.append((gu_full.index_select(0, rows).contiguous(), scales[layer][0].index_select(0, rows).contiguous(),
+                           d_full[:, r * sh:(r + 1) * sh].contiguous(), scales[layer][1]))
+        torch.cuda.synchronize()
+    del tmp
+    rank_bytes = 2 * sh * H + H * sh + (2 * sh + H) * 4
+    tpres = {}
+    for m in sorted({tokens[0], tokens[-1]}):
+        parts = [torch.empty((m, H), dtype=torch.float32, device=dev) for _ in range(R)]
+        yt = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+        wst = torch.empty(swr.mlp_workspace_bytes(m, H, sh, "fp8_e4m3fn"), dtype=torch.uint8, device=dev)
+
+        def rank_pass(m=m, parts=parts, wst=wst):
+            for i, (g_r, sg_r, d_r, sd_r) in enumerate(shards):
+                swr.mlp_forward_partial(g_r, sg_r, d_r, sd_r, "fp8_e4m3fn", H, sh, xs[m], parts[i % R], wst,
+                                        stream=compute)
+
+        with torch.cuda.stream(compute):
+            rank_pass()
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record(compute)
+            rank_pass()
+            e1.record(compute)
+            for _ in range(L):
+                swr.sum_partials(parts, yt, stream=compute)
+            e2.record(compute)
+        torch.cuda.synchronize()
+        rank_ms = e0.elapsed_time(e1) / len(shards)
+        red_ms = e1.elapsed_time(e2) / L
+        tpres[str(m)] = {"rank_mlp_ms_per_layer": round(rank_ms, 4),
+                         "rank_weight_GBps": round(rank_bytes / (rank_ms * 1e-3) / 1e9, 1),
+                         "reduce_of_partials_ms": round(red_ms, 4),
+                         "weight_sharded_serial_ms_per_layer": round(serial_ms[m] / L, 4)}
+    del shards
+
     # ---------------------------------------------------------------- graph replay
     # one forward captured as a graph (weight_sharding, CUDA graph section) and
     # replayed: a planner without the cross-forward prefetch, so every replay
@@ -392,6 +444,7 @@ def main() -> int:
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1),
         "dma_engine_gather": dma,
         "graph_replay_no_prefetch": graph,
+        "tensor_parallel_share": {"ranks": R, "rank_weight_bytes_per_layer": rank_bytes, "per_tokens": tpres},
         "roofline": roofline,
         "roofline_by_kernel": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                for k, v in per_kernel.items()},

@@ -254,6 +254,28 @@ int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const void* W_down
                     int64_t M, void* Y, void* workspace, int64_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * swr_mlp_forward_partial -- enqueue on `stream`.
+ * One tensor-parallel rank's share of the shared-expert MLP (vLLM PR #50656
+ * report, the TP-sharded shared expert: each rank holds a slice of the
+ * intermediate dimension -- its gate rows, the matching up rows, and the
+ * matching columns of down -- and the ranks' outputs are summed by an
+ * all-reduce).  Computes what swr_mlp_forward computes for the slice, but Y
+ * is fp32 [M, H] and not rounded, so the partials of all ranks can be added
+ * (swr_sum_partials, rank order) and rounded once:
+ *     Y_r = (bf16(silu(G_r[:, :I_r]) * G_r[:, I_r:]) @ W_down_r^T) * s_d
+ *   W_gate_up  [2 I_r, H]: the rank's gate rows then its up rows, contiguous
+ *   W_down     [H, I_r]: the rank's columns of down, contiguous
+ *   s_d        the full down row scales (they multiply every partial)
+ *   Y          fp32 [M, H] contiguous, 16-byte aligned
+ *   workspace  as for swr_mlp_forward with I = I_r
+ * Errors: as swr_mlp_forward.
+ */
+int swr_mlp_forward_partial(const void* W_gate_up, const float* s_gu, const void* W_down,
+                            const float* s_d, int32_t dtype, int64_t H, int64_t I, const void* X,
+                            int64_t M, float* Y, void* workspace, int64_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Workspace bytes swr_mlp_forward needs for these sizes (>= 0), or a negative
  * status for invalid sizes.  Host only. */
 int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int32_t dtype);

@@ -36,7 +36,8 @@ TRACE_STREAMS = {0: "compute", 1: "side"}
 EXPORTS = (
     "swr_plan_layer", "swr_pack_layer", "swr_reassemble_into_slot", "swr_reassemble_into_slot_dma",
     "swr_planner_set_copy_engine", "swr_proj_forward",
-    "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward", "swr_mlp_workspace_bytes", "swr_sum_partials",
+    "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward",
+    "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
@@ -102,6 +103,7 @@ def lib() -> ctypes.CDLL:
         "swr_proj_grouped_workspace_bytes": (_i64, [ctypes.POINTER(ProjDesc), _i32, _i64]),
         "swr_mlp_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
         "swr_mlp_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
+        "swr_mlp_forward_partial": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
         "swr_sum_partials": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i32, _vp]),
         "swr_planner_create": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]),
         "swr_planner_set_layer": (_i32, [_vp, _i32, ctypes.POINTER(_vp), _i32, _i64]),
@@ -316,6 +318,17 @@ def mlp_forward(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter: int, x:
            lib().swr_mlp_forward(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), _dtype(dtype), int(hidden),
                                  int(inter), _ptr(x), int(m), _ptr(y), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mlp_forward_partial(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter: int, x: torch.Tensor,
+                        y: torch.Tensor, workspace: torch.Tensor, m: int | None = None, stream=None) -> None:
+    """One rank's fp32 partial of the MLP over its intermediate slice (no rounding of Y)."""
+    if m is None:
+        m = x.shape[0]
+    _check("swr_mlp_forward_partial",
+           lib().swr_mlp_forward_partial(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), _dtype(dtype),
+                                         int(hidden), int(inter), _ptr(x), int(m), _ptr(y), _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def sum_partials(parts, out: torch.Tensor, count: int | None = None, stream=None) -> None:

@@ -246,10 +246,12 @@ extern "C" int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int3
   return h_bytes(M, I) + round_up(pg > pd ? pg : pd, kWorkspaceAlign);
 }
 
-extern "C" int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
-                               int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y,
-                               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
-  const char* fn = "swr_mlp_forward";
+namespace {
+
+// The MLP of swr_mlp_forward; with y_fp32 the down GEMM writes fp32 (no rounding).
+int mlp_impl(const char* fn, const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
+             int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y, bool y_fp32, void* workspace,
+             int64_t workspace_bytes, hipStream_t stream) {
   if (!W_gate_up || !W_down || !X || !Y || !workspace) return fail(SWR_E_INVALID, "%s: null pointer", fn);
   if (!valid_dtype(dtype)) return fail(SWR_E_INVALID, "%s: unknown dtype %d", fn, dtype);
   if (dtype == SWR_FP8_E4M3FN && (!s_gu || !s_d)) return fail(SWR_E_INVALID, "%s: FP8 weights need row scales", fn);
@@ -270,13 +272,31 @@ extern "C" int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const v
   void* h = workspace;
   float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + h_bytes(M, I));
   const swr::GemmProblem gu = mlp_gate_up(W_gate_up, s_gu, dtype, H, I, X, M, h);
-  const swr::GemmProblem dn = mlp_down(W_down, s_d, dtype, H, I, h, M, Y);
+  swr::GemmProblem dn = mlp_down(W_down, s_d, dtype, H, I, h, M, Y);
+  if (y_fp32) dn.mode = swr::OUT_F32;
   const swr::GemmPlan pg = swr::plan_gemm(gu);
   const swr::GemmPlan pd = swr::plan_gemm(dn);
   hipError_t e = swr::launch_gemm(gu, pg, partial, stream);
-  if (e != hipSuccess) return swr::hip_fail(e, "swr_mlp_forward: gate_up launch");
+  if (e != hipSuccess) return swr::hip_fail(e, "mlp: gate_up launch");
   e = swr::launch_gemm(dn, pd, partial, stream);
-  if (e != hipSuccess) return swr::hip_fail(e, "swr_mlp_forward: down launch");
+  if (e != hipSuccess) return swr::hip_fail(e, "mlp: down launch");
   swr::clear_error();
   return SWR_OK;
+}
+
+}  // namespace
+
+extern "C" int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
+                               int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y,
+                               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+  return mlp_impl("swr_mlp_forward", W_gate_up, s_gu, W_down, s_d, dtype, H, I, X, M, Y, false, workspace,
+                  workspace_bytes, stream);
+}
+
+extern "C" int swr_mlp_forward_partial(const void* W_gate_up, const float* s_gu, const void* W_down,
+                                       const float* s_d, int32_t dtype, int64_t H, int64_t I, const void* X,
+                                       int64_t M, float* Y, void* workspace, int64_t workspace_bytes,
+                                       hipStream_t stream) {
+  return mlp_impl("swr_mlp_forward_partial", W_gate_up, s_gu, W_down, s_d, dtype, H, I, X, M, Y, true, workspace,
+                  workspace_bytes, stream);
 }

@@ -98,13 +98,26 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return uint32_t(__builtin_bit_cast(uint16_t, ha)) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
 }
 
+// One thread per 4 consecutive outputs.  The n partial vectors are loaded in
+// batches of 8 independent loads (all in flight at once) and added in shard
+// order, so the sum is the same as a plain left-to-right loop.
 __global__ __launch_bounds__(kThreads) void sum_partials_kernel(PartPtrs parts, int n, int64_t count,
                                                                 void* __restrict__ out, int out_bf16) {
+  constexpr int kBatch = 8;
   const int64_t nvec = count / 4;
   for (int64_t v = int64_t(blockIdx.x) * kThreads + threadIdx.x; v < nvec;
        v += int64_t(gridDim.x) * kThreads) {
-    f32x4 acc = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[0]) + v);
-    for (int j = 1; j < n; ++j) acc += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[j]) + v);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+      f32x4 p[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        p[u] = j0 + u < n ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(parts.p[j0 + u]) + v)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (j0 + u < n) acc = (j0 + u == 0) ? p[u] : acc + p[u];
+    }
     if (out_bf16) {
       uint2 o = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
       reinterpret_cast<uint2*>(out)[v] = o;
@@ -171,7 +184,7 @@ hipError_t launch_pack(const PackPlan& plan, hipStream_t stream) {
 
 hipError_t launch_sum_partials(const PartPtrs& parts, int n, int64_t count, void* out, bool out_bf16,
                                hipStream_t stream) {
-  const int grid = grid_for(count / 4 + 1, kThreads * 4);
+  const int grid = grid_for(count / 4 + 1, kThreads);
   hipLaunchKernelGGL(sum_partials_kernel, dim3(grid), dim3(kThreads), 0, stream, parts, n, count, out,
                      out_bf16 ? 1 : 0);
   return hipGetLastError();

@@ -137,3 +137,63 @@ def test_prefill_shared_expert_sampled_tokens(shared_expert_layer, m):
                              wl.hidden, wl.intermediate)
     assert_close_rows(y[toks], ref, what=f"prefill m={m}")
     assert np.isfinite(y).all()
+
+
+def _rank_shards(gu, d, inter, ranks, r):
+    """Rank r's contiguous weights of the tensor-parallel shared expert: its gate
+    rows then its up rows, and its columns of down."""
+    sh = inter // ranks
+    rows = np.r_[r * sh:(r + 1) * sh, inter + r * sh:inter + (r + 1) * sh]
+    gu_r = synth.Weight(2 * sh, gu.in_features, gu.dtype, np.ascontiguousarray(gu.data[rows]),
+                        None if gu.scale is None else gu.scale[rows])
+    d_r = synth.Weight(d.out_features, sh, d.dtype, np.ascontiguousarray(d.data[:, r * sh:(r + 1) * sh]), d.scale)
+    return gu_r, d_r
+
+
+def _tp_mlp(gu, d, hidden, inter, ranks, x_bits):
+    """Every rank's fp32 partial (swr_mlp_forward_partial) and their sum in rank
+    order rounded once (swr_sum_partials)."""
+    m = x_bits.shape[0]
+    parts = [torch.full((m, hidden), float("nan"), dtype=torch.float32, device=DEV) for _ in range(ranks)]
+    ws = torch.empty(swr.mlp_workspace_bytes(m, hidden, inter // ranks, gu.dtype), dtype=torch.uint8, device=DEV)
+    xd = bf16(x_bits)
+    for r in range(ranks):
+        gu_r, d_r = _rank_shards(gu, d, inter, ranks, r)
+        swr.mlp_forward_partial(u8(gu_r.raw()), f32(gu_r.scale) if gu_r.scale is not None else None, u8(d_r.raw()),
+                                f32(d_r.scale) if d_r.scale is not None else None, gu.dtype, hidden, inter // ranks,
+                                xd, parts[r], ws)
+        torch.cuda.synchronize()  # the rank's shard tensors go out of scope
+    y = torch.empty((m, hidden), dtype=torch.bfloat16, device=DEV)
+    swr.sum_partials(parts, y)
+    torch.cuda.synchronize()
+    return parts, y
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+@pytest.mark.parametrize("hidden,inter,ranks,m", [(256, 512, 4, 12), (512, 1024, 8, 33), (128, 256, 2, 1)])
+def test_tensor_parallel_partials(dt, hidden, inter, ranks, m):
+    """PR report, TP-sharded shared expert: each rank's fp32 partial equals the
+    oracle's contribution of its intermediate slice, and the rank-ordered sum
+    equals the full MLP."""
+    note(f"tp partials h={hidden} i={inter} ranks={ranks} {dt} m={m}")
+    gu = synth.weight(synth.seed_for(17, 0, 0), 2 * inter, hidden, dt)
+    d = synth.weight(synth.seed_for(17, 0, 1), hidden, inter, dt)
+    x = synth.activations(synth.seed_for(17, 0, 50), m, hidden)
+    parts, y = _tp_mlp(gu, d, hidden, inter, ranks, x)
+    sh = inter // ranks
+    for r in range(ranks):
+        ref = gemm.mlp_intermediate_slice_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter,
+                                              r * sh, (r + 1) * sh)
+        assert_close_rows(values(parts[r]), ref, what=f"rank {r} partial")
+    _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter)
+    assert_close_rows(values(y), ref, what="sum of rank partials")
+
+
+@pytest.mark.parametrize("m", [1, 64])
+def test_tensor_parallel_full_size(shared_expert_layer, m):
+    """The shared expert (hidden 6144, intermediate 14336, FP8) split over 16
+    ranks: the summed partials equal the oracle's MLP on sampled columns."""
+    wl, gu, d, x = shared_expert_layer
+    note(f"tp shared expert 16 ranks m={m}")
+    _, y = _tp_mlp(gu, d, wl.hidden, wl.intermediate, 16, x[:m])
+    _check_full(wl, gu, d, x, m, values(y))
