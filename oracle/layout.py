@@ -92,3 +92,61 @@ def remote_bytes(plan: dict, self_rank: int = 0) -> int:
     """Bytes a rank receives from its peers in one gather: every chunk but its own."""
     del self_rank  # every rank owns exactly one chunk of C bytes
     return (plan["n_chunks"] - 1) * plan["chunk"]
+
+
+# ---------------------------------------------------------------- row shards
+#
+# "weight_sharding", loading section: a tensor-parallel loader gives each of
+# N ranks a row shard of every weight (for a merged linear such as gate_up,
+# a row shard of each sub-block: the gate rows and the up rows are split
+# separately); weights whose rows do not divide by N stay whole on every
+# rank.  The one-time re-layout turns those row shards into the flat chunks
+# of the layout above.  Plainest reading: the re-layout's result is exactly
+# pack_layer of the whole weights, so the oracle rebuilds each whole weight
+# from its row shards and packs.
+
+
+def row_shards(raw: np.ndarray, out_features: int, in_features: int, dtype: str, sub_rows: list[int],
+               n: int) -> list[np.ndarray]:
+    """Rank r's row shard of one weight: for each sub-block b in order, its
+    rows [r*R_b/n, (r+1)*R_b/n), as contiguous bytes."""
+    if sum(sub_rows) != out_features or any(r % n for r in sub_rows):
+        raise ValueError("every sub-block's rows must split evenly over the ranks")
+    rows = np.asarray(raw, dtype=np.uint8).reshape(out_features, in_features * ELEM_BYTES[dtype])
+    starts = np.cumsum([0] + list(sub_rows))
+    out = []
+    for r in range(n):
+        parts = [rows[starts[b] + r * (sub_rows[b] // n):starts[b] + (r + 1) * (sub_rows[b] // n)]
+                 for b in range(len(sub_rows))]
+        out.append(np.ascontiguousarray(np.concatenate(parts)).reshape(-1))
+    return out
+
+
+def unshard_rows(shards: list[np.ndarray], out_features: int, in_features: int, dtype: str,
+                 sub_rows: list[int]) -> np.ndarray:
+    """The whole weight's bytes from its n row shards (inverse of row_shards)."""
+    n = len(shards)
+    row_bytes = in_features * ELEM_BYTES[dtype]
+    per_rank = [np.asarray(s, dtype=np.uint8).reshape(-1, row_bytes) for s in shards]
+    blocks = []
+    first = 0  # first row of sub-block b inside a rank's shard
+    for rb in sub_rows:
+        k = rb // n
+        blocks.extend(per_rank[r][first:first + k] for r in range(n))
+        first += k
+    whole = np.concatenate(blocks) if blocks else np.zeros((0, row_bytes), np.uint8)
+    assert whole.shape[0] == out_features
+    return whole.reshape(-1)
+
+
+def redistribute(plan: dict, weights: list[dict]) -> list[np.ndarray]:
+    """Flat chunks from per-weight row shards.  ``weights[j]`` holds
+    ``out_features``, ``in_features``, ``dtype`` and either ``whole`` (bytes of
+    a weight that stays whole) or ``shards`` plus ``sub_rows``."""
+    raws = []
+    for w in weights:
+        if "whole" in w:
+            raws.append(np.asarray(w["whole"], dtype=np.uint8).reshape(-1))
+        else:
+            raws.append(unshard_rows(w["shards"], w["out_features"], w["in_features"], w["dtype"], w["sub_rows"]))
+    return pack_layer(plan, raws)[1]

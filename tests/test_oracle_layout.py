@@ -137,3 +137,45 @@ def test_padding_is_zero():
     for off, size in zip(p["offsets"], p["sizes"]):
         mask[off:off + size] = True
     assert (t[~mask] == 0).all() and (~mask).sum() == p["total"] - sum(p["sizes"])
+
+
+# ---------------------------------------------------------------- row shards
+
+def test_row_shards_follow_the_split_rule():
+    """Rank r holds rows [r*R/n, (r+1)*R/n) of every sub-block, in order; a merged
+    [gate; up] weight is split per sub-block, not as one block."""
+    out_f, in_f, n = 8, 3, 2
+    raw = np.arange(out_f * in_f, dtype=np.uint8)
+    shards = layout.row_shards(raw, out_f, in_f, "fp8_e4m3fn", [4, 4], n)
+    rows = raw.reshape(out_f, in_f)
+    assert np.array_equal(shards[0].reshape(-1, in_f), rows[[0, 1, 4, 5]])
+    assert np.array_equal(shards[1].reshape(-1, in_f), rows[[2, 3, 6, 7]])
+    single = layout.row_shards(raw, out_f, in_f, "fp8_e4m3fn", [8], n)
+    assert np.array_equal(single[0].reshape(-1, in_f), rows[:4])
+    with pytest.raises(ValueError):
+        layout.row_shards(raw, out_f, in_f, "fp8_e4m3fn", [5, 3], n)
+
+
+@pytest.mark.parametrize("sub_rows,n", [([12], 1), ([12], 4), ([6, 6], 3), ([8, 4, 12], 4)])
+def test_unshard_inverts_row_shards(sub_rows, n):
+    out_f, in_f = sum(sub_rows), 7
+    raw = np.random.default_rng(n).integers(0, 256, out_f * in_f * 2, dtype=np.uint8)
+    shards = layout.row_shards(raw, out_f, in_f, "bf16", sub_rows, n)
+    assert sum(s.size for s in shards) == raw.size
+    assert np.array_equal(layout.unshard_rows(shards, out_f, in_f, "bf16", sub_rows), raw)
+
+
+def test_redistribute_equals_pack_of_whole_weights():
+    shp = [(16, 5, "bf16"), (12, 3, "fp8_e4m3fn"), (7, 9, "bf16")]
+    n = 4
+    plan = layout.plan_layer(shp, n)
+    rng = np.random.default_rng(3)
+    raws = [rng.integers(0, 256, o * i * layout.ELEM_BYTES[d], dtype=np.uint8) for o, i, d in shp]
+    ws = [dict(out_features=16, in_features=5, dtype="bf16", sub_rows=[8, 8],
+               shards=layout.row_shards(raws[0], 16, 5, "bf16", [8, 8], n)),
+          dict(out_features=12, in_features=3, dtype="fp8_e4m3fn", sub_rows=[12],
+               shards=layout.row_shards(raws[1], 12, 3, "fp8_e4m3fn", [12], n)),
+          dict(out_features=7, in_features=9, dtype="bf16", whole=raws[2])]  # 7 rows do not split over 4 ranks
+    chunks = layout.redistribute(plan, ws)
+    _, ref = layout.pack_layer(plan, raws)
+    assert all(np.array_equal(a, b) for a, b in zip(chunks, ref))
