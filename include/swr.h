@@ -56,6 +56,7 @@ enum swr_status {
 #define SWR_MAX_CHUNKS 64   /* N, chunks per layer                           */
 #define SWR_MAX_WEIGHTS 64  /* weights per layer                             */
 #define SWR_MAX_GROUP 16    /* projections per swr_proj_forward_grouped call */
+#define SWR_MAX_SUB 4       /* sub-blocks of a merged weight (row shards)    */
 #define SWR_ITEM_ALIGN 16   /* every item starts on a 16-byte boundary       */
 
 typedef struct swr_weight_desc {
@@ -119,6 +120,37 @@ int swr_plan_layer(const swr_weight_desc* w, int32_t n_weights, int32_t n_chunks
  */
 int swr_pack_layer(const swr_layout* layout, const swr_view_desc* views,
                    const void* const* src_dev, void* const* chunk_dev, hipStream_t stream);
+
+/* The row shards of one weight, as a tensor-parallel loader leaves them on
+ * the N ranks (weight_sharding, loading section).  A merged weight (gate_up
+ * = [gate rows; up rows]) is split per sub-block: rank r holds, for each
+ * sub-block b in order, the rows [r*R_b/N, (r+1)*R_b/N) of that sub-block,
+ * contiguous.  A weight whose rows do not divide by N stays whole. */
+typedef struct {
+  int32_t n_sub;                  /* sub-blocks, 1..SWR_MAX_SUB (ignored when replicated)   */
+  int32_t replicated;             /* nonzero: not row-sharded; src[0] holds the whole weight */
+  int64_t sub_rows[SWR_MAX_SUB];  /* rows of each sub-block; each a multiple of N, sum = out */
+  const void* src[SWR_MAX_CHUNKS];/* device, 16-byte aligned: rank r's shard (r < N)          */
+} swr_row_shards;
+
+/*
+ * swr_redistribute_row_shards -- enqueue on `stream`.
+ * The one-time re-layout of weight_sharding's loading section: from each
+ * weight's row shards, write the N flat chunks, byte for byte what
+ * swr_pack_layer writes from the whole weights (padding zero).  Chunk i
+ * takes its bytes from whichever rank shards hold the rows its byte window
+ * covers, so a chunk may straddle weights and shards.
+ *   layout, views  from swr_plan_layer (host memory)
+ *   shards         host array of layout->n_weights descriptors, read before
+ *                  the call returns
+ *   chunk_dev      N device buffers of >= chunk_bytes, 16-byte aligned
+ * One launch per weight.  Every argument is checked before the first launch.
+ * Errors: SWR_E_INVALID, SWR_E_ALIGN, SWR_E_SHAPE (rows not a multiple of N
+ * for a sharded weight, sub-blocks not adding up), SWR_E_HIP.
+ */
+int swr_redistribute_row_shards(const swr_layout* layout, const swr_view_desc* views,
+                                const swr_row_shards* shards, void* const* chunk_dev,
+                                hipStream_t stream);
 
 /* ------------------------------------------------------- reassembly (a3) */
 

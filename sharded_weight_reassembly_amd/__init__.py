@@ -34,7 +34,8 @@ TRACE_STREAMS = {0: "compute", 1: "side"}
 
 # Every function include/swr.h declares.
 EXPORTS = (
-    "swr_plan_layer", "swr_pack_layer", "swr_reassemble_into_slot", "swr_reassemble_into_slot_dma",
+    "swr_plan_layer", "swr_pack_layer", "swr_redistribute_row_shards", "swr_reassemble_into_slot",
+    "swr_reassemble_into_slot_dma",
     "swr_planner_set_copy_engine", "swr_proj_forward",
     "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward",
     "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials",
@@ -67,6 +68,14 @@ class Layout(ctypes.Structure):
                 ("n_weights", ctypes.c_int32), ("n_chunks", ctypes.c_int32)]
 
 
+MAX_CHUNKS, MAX_SUB = 64, 4
+
+
+class RowShards(ctypes.Structure):
+    _fields_ = [("n_sub", ctypes.c_int32), ("replicated", ctypes.c_int32), ("sub_rows", ctypes.c_int64 * MAX_SUB),
+                ("src", ctypes.c_void_p * MAX_CHUNKS)]
+
+
 class ProjDesc(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("row_scale", ctypes.c_void_p), ("X", ctypes.c_void_p),
                 ("Y", ctypes.c_void_p), ("out_features", ctypes.c_int64), ("in_features", ctypes.c_int64),
@@ -94,6 +103,8 @@ def lib() -> ctypes.CDLL:
                                   ctypes.POINTER(_vp), _vp]),
         "swr_reassemble_into_slot": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i64, _i32, _vp, _vp, _vp,
                                             ctypes.POINTER(_i64)]),
+        "swr_redistribute_row_shards": (_i32, [ctypes.POINTER(Layout), ctypes.POINTER(ViewDesc),
+                                               ctypes.POINTER(RowShards), ctypes.POINTER(_vp), _vp]),
         "swr_reassemble_into_slot_dma": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i64, _i32, _vp, _vp, _vp,
                                                 ctypes.POINTER(_i64)]),
         "swr_planner_set_copy_engine": (_i32, [_vp, _i32]),
@@ -208,6 +219,29 @@ def pack_layer(layout: dict, views: list[dict], src, chunks, stream=None) -> Non
     lay = _layout_struct(layout)
     _check("swr_pack_layer", lib().swr_pack_layer(ctypes.byref(lay), _views_struct(views), _ptr_array(src),
                                                   _ptr_array(chunks), _stream(stream)))
+
+
+def row_shards_struct(shards) -> ctypes.Array:
+    """shards[j]: dict with "src" (list of device tensors/addresses) and either
+    "replicated": True (src[0] is the whole weight) or "sub_rows"."""
+    arr = (RowShards * len(shards))()
+    for j, sh in enumerate(shards):
+        d = arr[j]
+        d.replicated = int(bool(sh.get("replicated", False)))
+        rows = list(sh.get("sub_rows", []))
+        d.n_sub = len(rows)
+        for b, r in enumerate(rows):
+            d.sub_rows[b] = int(r)
+        for r, t in enumerate(sh["src"]):
+            d.src[r] = _ptr(t)
+    return arr
+
+
+def redistribute_row_shards(layout: dict, views: list[dict], shards, chunks, stream=None) -> None:
+    """Flat chunks from every weight's row shards (the loader's one-time re-layout)."""
+    _check("swr_redistribute_row_shards",
+           lib().swr_redistribute_row_shards(ctypes.byref(_layout_struct(layout)), _views_struct(views),
+                                             row_shards_struct(shards), _ptr_array(chunks), _stream(stream)))
 
 
 def reassemble_into_slot(chunks, chunk_bytes: int, slot, slot_bytes: int | None = None, self_rank: int = 0,

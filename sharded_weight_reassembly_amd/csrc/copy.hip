@@ -88,6 +88,48 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackPlan plan) {
   }
 }
 
+// ----------------------------------------------------- row-shard re-layout
+//
+// weight_sharding, loading section: the one-time re-layout from a tensor-
+// parallel loader's row shards into the flat chunks.  One launch per weight
+// writes T[begin, end): the weight's bytes (each 16-byte vector gathered from
+// the rank shard that holds its row) and the zero padding up to the next item.
+// Rank r's shard holds, for each sub-block b of a merged weight in order, the
+// rows [r*R_b/N, (r+1)*R_b/N) of that sub-block.
+__device__ inline const uint8_t* shard_byte(const RedistArgs& a, int64_t rel) {
+  if (a.replicated) return a.src[0] + rel;
+  const int64_t row = rel / a.row_bytes;
+  const int64_t cb = rel - row * a.row_bytes;
+  int b = 0;
+  while (b + 1 < a.n_sub && row >= a.sub_start[b + 1]) ++b;
+  const int64_t per = (a.sub_start[b + 1] - a.sub_start[b]) / a.n;
+  const int64_t rr = row - a.sub_start[b];
+  const int64_t q = rr / per;
+  return a.src[q] + (a.sub_first[b] + (rr - q * per)) * a.row_bytes + cb;
+}
+
+__global__ __launch_bounds__(kThreads) void redistribute_kernel(RedistArgs a) {
+  for (int64_t p = a.begin + (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 16; p < a.end;
+       p += int64_t(gridDim.x) * kThreads * 16) {
+    const int64_t rel = p - a.off;
+    uint4 out = make_uint4(0, 0, 0, 0);
+    if (rel < a.size) {
+      const uint8_t* s0 = shard_byte(a, rel);
+      const bool one_row = (rel / a.row_bytes) == ((rel + 15) / a.row_bytes);
+      if (rel + 16 <= a.size && (a.replicated || one_row) && (reinterpret_cast<uintptr_t>(s0) & 15) == 0) {
+        out = *reinterpret_cast<const uint4*>(s0);
+      } else {
+        uint8_t b[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) b[t] = rel + t < a.size ? *shard_byte(a, rel + t) : uint8_t(0);
+        out = *reinterpret_cast<const uint4*>(b);
+      }
+    }
+    const int64_t ci = p / a.chunk_bytes;
+    *reinterpret_cast<uint4*>(static_cast<uint8_t*>(a.chunk[ci]) + (p - ci * a.chunk_bytes)) = out;
+  }
+}
+
 // ------------------------------------------------------------- sum partials
 //
 // Sharded-matrices notes, local matmul case 3: split-contraction partials add
@@ -182,6 +224,12 @@ hipError_t launch_pack(const PackPlan& plan, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_redistribute(const RedistArgs& a, hipStream_t stream) {
+  const int grid = grid_for((a.end - a.begin) / 16, kThreads * 4);
+  hipLaunchKernelGGL(redistribute_kernel, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_sum_partials(const PartPtrs& parts, int n, int64_t count, void* out, bool out_bf16,
                                hipStream_t stream) {
   const int grid = grid_for(count / 4 + 1, kThreads);
@@ -234,6 +282,85 @@ extern "C" int swr_pack_layer(const swr_layout* layout, const swr_view_desc* vie
   plan.n_chunks = nc;
   const hipError_t e = swr::launch_pack(plan, stream);
   if (e != hipSuccess) return swr::hip_fail(e, "swr_pack_layer: launch");
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_redistribute_row_shards(const swr_layout* layout, const swr_view_desc* views,
+                                           const swr_row_shards* shards, void* const* chunk_dev,
+                                           hipStream_t stream) {
+  const char* fn = "swr_redistribute_row_shards";
+  if (!layout || !views || !shards || !chunk_dev) return fail(SWR_E_INVALID, "%s: null pointer", fn);
+  const int nw = layout->n_weights, nc = layout->n_chunks;
+  if (nw < 1 || nw > SWR_MAX_WEIGHTS || nc < 1 || nc > SWR_MAX_CHUNKS)
+    return fail(SWR_E_INVALID, "%s: n_weights=%d n_chunks=%d out of range", fn, nw, nc);
+  if (layout->total_bytes <= 0 || layout->total_bytes % (16 * int64_t(nc)) != 0 ||
+      layout->chunk_bytes * nc != layout->total_bytes || layout->payload_bytes > layout->total_bytes)
+    return fail(SWR_E_INVALID, "%s: inconsistent layout", fn);
+  for (int i = 0; i < nc; ++i) {
+    if (!chunk_dev[i]) return fail(SWR_E_INVALID, "%s: chunk_dev[%d] is null", fn, i);
+    if (!aligned(chunk_dev[i], 16)) return fail(SWR_E_ALIGN, "%s: chunk_dev[%d] not 16-byte aligned", fn, i);
+  }
+  // every check before the first launch
+  int64_t prev_end = 0;
+  for (int j = 0; j < nw; ++j) {
+    const swr_view_desc& v = views[j];
+    const swr_row_shards& sh = shards[j];
+    const int64_t elem = v.dtype == SWR_FP8_E4M3FN ? 1 : 2;
+    if (v.offset % 16 != 0 || v.offset < prev_end || v.nbytes <= 0 || v.offset + v.nbytes > layout->payload_bytes ||
+        v.out_features * v.in_features * elem != v.nbytes)
+      return fail(SWR_E_INVALID, "%s: view %d does not fit the layout", fn, j);
+    prev_end = v.offset + v.nbytes;
+    if (sh.replicated) {
+      if (!sh.src[0]) return fail(SWR_E_INVALID, "%s: weight %d: src[0] is null", fn, j);
+      if (!aligned(sh.src[0], 16)) return fail(SWR_E_ALIGN, "%s: weight %d: src[0] not 16-byte aligned", fn, j);
+      continue;
+    }
+    if (sh.n_sub < 1 || sh.n_sub > SWR_MAX_SUB)
+      return fail(SWR_E_INVALID, "%s: weight %d: n_sub=%d outside [1, %d]", fn, j, sh.n_sub, SWR_MAX_SUB);
+    int64_t rows = 0;
+    for (int b = 0; b < sh.n_sub; ++b) {
+      if (sh.sub_rows[b] < 0 || sh.sub_rows[b] % nc != 0)
+        return fail(SWR_E_SHAPE, "%s: weight %d: sub-block %d has %lld rows, not a multiple of N=%d", fn, j, b,
+                    (long long)sh.sub_rows[b], nc);
+      rows += sh.sub_rows[b];
+    }
+    if (rows != v.out_features)
+      return fail(SWR_E_SHAPE, "%s: weight %d: sub-blocks hold %lld rows, the weight %lld", fn, j, (long long)rows,
+                  (long long)v.out_features);
+    for (int r = 0; r < nc; ++r) {
+      if (!sh.src[r]) return fail(SWR_E_INVALID, "%s: weight %d: src[%d] is null", fn, j, r);
+      if (!aligned(sh.src[r], 16)) return fail(SWR_E_ALIGN, "%s: weight %d: src[%d] not 16-byte aligned", fn, j, r);
+    }
+  }
+  // leading zero padding cannot occur: the first item starts at 0
+  for (int j = 0; j < nw; ++j) {
+    const swr_view_desc& v = views[j];
+    const swr_row_shards& sh = shards[j];
+    swr::RedistArgs a{};
+    a.begin = j == 0 ? 0 : v.offset;
+    a.end = j + 1 < nw ? views[j + 1].offset : layout->total_bytes;
+    a.off = v.offset;
+    a.size = v.nbytes;
+    a.row_bytes = v.nbytes / v.out_features;
+    a.chunk_bytes = layout->chunk_bytes;
+    a.n = nc;
+    a.replicated = sh.replicated ? 1 : 0;
+    a.n_sub = sh.replicated ? 1 : sh.n_sub;
+    int64_t start = 0, first = 0;
+    for (int b = 0; b < a.n_sub; ++b) {
+      a.sub_start[b] = start;
+      a.sub_first[b] = first;
+      const int64_t rb = sh.replicated ? v.out_features : sh.sub_rows[b];
+      start += rb;
+      first += rb / nc;
+    }
+    a.sub_start[a.n_sub] = start;
+    for (int r = 0; r < (sh.replicated ? 1 : nc); ++r) a.src[r] = static_cast<const uint8_t*>(sh.src[r]);
+    for (int i = 0; i < nc; ++i) a.chunk[i] = chunk_dev[i];
+    const hipError_t e = swr::launch_redistribute(a, stream);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_redistribute_row_shards: launch");
+  }
   swr::clear_error();
   return SWR_OK;
 }

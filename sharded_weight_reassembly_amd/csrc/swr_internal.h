@@ -24,6 +24,19 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 struct ChunkPtrs {
   const void* p[SWR_MAX_CHUNKS];
 };
+// One weight of the row-shard re-layout (see swr_redistribute_row_shards).
+struct RedistArgs {
+  const uint8_t* src[SWR_MAX_CHUNKS];  // rank shards (replicated: src[0] is the whole weight)
+  void* chunk[SWR_MAX_CHUNKS];
+  int64_t begin, end;                  // bytes of T written by this launch
+  int64_t off, size, row_bytes;        // the weight's item
+  int64_t sub_start[SWR_MAX_SUB + 1];  // first row of each sub-block in the weight
+  int64_t sub_first[SWR_MAX_SUB];      // first row of each sub-block inside a rank shard
+  int64_t chunk_bytes;
+  int32_t n_sub, replicated, n;
+};
+hipError_t launch_redistribute(const RedistArgs& a, hipStream_t stream);
+
 hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chunk_bytes, void* slot,
                              hipStream_t stream);
 

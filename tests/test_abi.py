@@ -109,6 +109,29 @@ def test_reassemble_argument_errors_before_enqueue():
                                       None) == swr.E_INVALID
 
 
+def test_redistribute_errors_before_enqueue():
+    L = swr.lib()
+    a = 1 << 20
+    shp = [(512, 128, "bf16"), (100, 128, "bf16")]
+    views, lay = swr.plan_layer(shp, 4)
+    lay_s, views_s = swr._layout_struct(lay), swr._views_struct(views)
+    chunks = _vp_array([a + i * lay["chunk_bytes"] for i in range(4)])
+
+    def call(shards):
+        return L.swr_redistribute_row_shards(ctypes.byref(lay_s), views_s, swr.row_shards_struct(shards), chunks,
+                                             None)
+
+    good = [dict(sub_rows=[256, 256], src=[a] * 4), dict(sub_rows=[100], src=[a] * 4)]
+    assert L.swr_redistribute_row_shards(None, views_s, swr.row_shards_struct(good), chunks, None) == swr.E_INVALID
+    # 100 rows over 4 ranks is fine; 102 rows would not be
+    assert call([good[0], dict(sub_rows=[98, 2], src=[a] * 4)]) == swr.E_SHAPE
+    assert call([dict(sub_rows=[256, 252], src=[a] * 4), good[1]]) == swr.E_SHAPE   # rows do not add up
+    assert call([dict(sub_rows=[], src=[a] * 4), good[1]]) == swr.E_INVALID         # no sub-blocks
+    assert call([good[0], dict(sub_rows=[100], src=[a, a, a + 8, a])]) == swr.E_ALIGN
+    assert call([good[0], dict(sub_rows=[100], src=[a, a, None, a])]) == swr.E_INVALID
+    assert call([good[0], dict(replicated=True, src=[None])]) == swr.E_INVALID
+
+
 def test_dma_reassemble_checks_like_the_kernel_path():
     L = swr.lib()
     good = 1 << 20

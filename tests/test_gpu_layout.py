@@ -149,3 +149,68 @@ def test_dma_gather_full_size_layer():
     swr.reassemble_into_slot_dma(chunks, lay["chunk_bytes"], slot2)
     torch.cuda.synchronize()
     assert torch.equal(slot2[:lay["total_bytes"]], slot[:lay["total_bytes"]])
+
+
+
+def _shard_specs(shapes, ws, n, merged=()):
+    """Row shards as the oracle's split rule makes them: weights listed in
+    `merged` are [gate; up] (two equal sub-blocks); weights whose rows do not
+    split over n stay whole."""
+    specs, oracle_ws = [], []
+    for j, ((_, o, i, d), w) in enumerate(zip(shapes, ws)):
+        sub = [o // 2, o // 2] if j in merged else [o]
+        if all(r % n == 0 for r in sub):
+            sh = olayout.row_shards(w.raw(), o, i, d, sub, n)
+            specs.append(dict(sub_rows=sub, src=[u8(x) for x in sh]))
+            oracle_ws.append(dict(out_features=o, in_features=i, dtype=d, sub_rows=sub, shards=sh))
+        else:
+            specs.append(dict(replicated=True, src=[u8(w.raw())]))
+            oracle_ws.append(dict(out_features=o, in_features=i, dtype=d, whole=w.raw()))
+    return specs, oracle_ws
+
+
+@pytest.mark.parametrize("shapes,n,merged", [
+    (synth.TINY_PADDED.weights, 4, (0,)),   # [100 x 127] bf16: 254-byte rows; [3 x 5] fp8 stays whole
+    (synth.TINY_PADDED.weights, 2, (0,)),
+    (synth.TINY_PADDED.weights, 1, ()),
+    (synth.TINY.weights, 4, (0,)),
+])
+def test_redistribute_row_shards_bit_exact(shapes, n, merged):
+    """weight_sharding, loading section: flat chunks written from the loader's
+    row shards equal the oracle's pack of the whole weights, byte for byte."""
+    note(f"redistribute shapes={[(o, i, d) for _, o, i, d in shapes]} n={n}")
+    ws = [synth.weight(synth.seed_for(18, 0, t), o, i, d) for t, (_, o, i, d) in enumerate(shapes)]
+    shp = [(o, i, d) for _, o, i, d in shapes]
+    views, lay = swr.plan_layer(shp, n)
+    specs, oracle_ws = _shard_specs(shapes, ws, n, merged)
+    chunks = [torch.full((lay["chunk_bytes"],), 0xA5, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    swr.redistribute_row_shards(lay, views, specs, chunks)
+    torch.cuda.synchronize()
+    plan = olayout.plan_layer(shp, n)
+    ref = olayout.redistribute(plan, oracle_ws)
+    _, packed = olayout.pack_layer(plan, [w.raw() for w in ws])
+    for i in range(n):
+        got = chunks[i].cpu().numpy()
+        assert np.array_equal(got, ref[i]), f"chunk {i}"
+        assert np.array_equal(got, packed[i]), f"chunk {i} vs pack"
+
+
+@pytest.mark.parametrize("wl,merged", [(synth.ATTN_PROJECTIONS, ()), (synth.SHARED_EXPERT_DECODE, (0,))])
+def test_redistribute_full_size_layer(wl, merged):
+    """A full-size layer at N=16: the projection layer ([1000 x 7168] stays
+    whole: 1000 rows do not split over 16 ranks) and the shared expert with
+    gate_up split per sub-block.  Chunks equal swr_pack_layer's."""
+    note(f"redistribute full-size {wl.name}")
+    n = wl.n_chunks
+    ws = wl.layer_weights(0)
+    shp = [(o, i, d) for _, o, i, d in wl.weights]
+    views, lay = swr.plan_layer(shp, n)
+    specs, _ = _shard_specs(wl.weights, ws, n, merged)
+    chunks = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(n)]
+    swr.redistribute_row_shards(lay, views, specs, chunks)
+    del specs
+    ref = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(n)]
+    swr.pack_layer(lay, views, [u8(w.raw()) for w in ws], ref)
+    torch.cuda.synchronize()
+    for i in range(n):
+        assert torch.equal(chunks[i], ref[i]), f"chunk {i}"
