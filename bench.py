@@ -51,6 +51,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--tokens", type=str, default="1,8,32,64")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: its own count)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--minimal", action="store_true",
+                    help="only the pipelined steps and isolated kernels (no serial, DMA, tensor-parallel or graph "
+                         "sections)")
     ap.add_argument("--isolated-reps", type=int, default=10)
     ap.add_argument("--calibration-copy-mib", type=int, default=256,
                     help="size of a plain device copy run at the end; rocprofv3 --pmc runs use it to scale "
@@ -222,142 +225,146 @@ def main() -> int:
     iso_gather_ms = e0.elapsed_time(e1) / (args.isolated_reps * L)
     del full
 
-    # ---------------------------------------------------------------- serial reference
-    # the same gathers and MLPs back to back on one stream (no side stream, no overlap):
-    # on one GPU both share the HBM, so this shows what the overlap costs or gains
-    serial_ms = {}
-    with torch.cuda.stream(compute):
-        for m in tokens:
-            def serial_forward():
-                for layer in range(L):
-                    s_ = slot_a if layer % 2 == 0 else slot_b
-                    swr.reassemble_into_slot(chunks[layer], C, s_, stream=compute)
-                    b = s_.data_ptr()
-                    swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
-                                    xs[m], ys[m], wsp[m], stream=compute)
-            serial_forward()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(compute)
-            for _ in range(args.isolated_reps):
+    # The sections below (serial reference, DMA-engine gather, tensor-parallel
+    # share, graph replay) are reports beside the headline; --minimal skips
+    # them, e.g. for hardware-counter runs that average over every MLP call.
+    serial_ms, dma, graph, tpres, R, rank_bytes = {}, {}, {}, {}, 4, 0
+    if not args.minimal:
+        # ---------------------------------------------------------------- serial reference
+        # the same gathers and MLPs back to back on one stream (no side stream, no overlap):
+        # on one GPU both share the HBM, so this shows what the overlap costs or gains
+        with torch.cuda.stream(compute):
+            for m in tokens:
+                def serial_forward():
+                    for layer in range(L):
+                        s_ = slot_a if layer % 2 == 0 else slot_b
+                        swr.reassemble_into_slot(chunks[layer], C, s_, stream=compute)
+                        b = s_.data_ptr()
+                        swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
+                                        xs[m], ys[m], wsp[m], stream=compute)
                 serial_forward()
-            e1.record(compute)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(compute)
+                for _ in range(args.isolated_reps):
+                    serial_forward()
+                e1.record(compute)
+                torch.cuda.synchronize()
+                serial_ms[m] = e0.elapsed_time(e1) / args.isolated_reps
+
+        # ---------------------------------------------------------------- DMA-engine gather
+        # the same pipelined forwards with the gathers on the DMA engines (no compute
+        # units): the copy-engine path of the pages, at the smallest and largest M
+        dma = {}
+        planner.set_copy_engine(swr.ENGINE_DMA)
+        dma_steps = max(2, args.steps // 4)
+        for m in sorted({tokens[0], tokens[-1]}):
+            with torch.cuda.stream(compute):
+                forward(m)
             torch.cuda.synchronize()
-            serial_ms[m] = e0.elapsed_time(e1) / args.isolated_reps
+            evd = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+                   for _ in range(dma_steps)]
+            fwd_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dma_steps)]
+            with torch.cuda.stream(compute):
+                for s in range(dma_steps):
+                    fwd_d[s][0].record(compute)
+                    forward(m, evd[s])
+                    fwd_d[s][1].record(compute)
+            torch.cuda.synchronize()
+            f = float(np.median([a.elapsed_time(b) for a, b in fwd_d]))
+            g = float(np.mean([a.elapsed_time(b) for row in evd for a, b in row]))
+            dma[str(m)] = {"pipelined_ms_per_forward": round(f, 4), "gemm_ms_per_layer_in_pipeline": round(g, 4),
+                           "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
+        planner.set_copy_engine(swr.ENGINE_KERNEL)
 
-    # ---------------------------------------------------------------- DMA-engine gather
-    # the same pipelined forwards with the gathers on the DMA engines (no compute
-    # units): the copy-engine path of the pages, at the smallest and largest M
-    dma = {}
-    planner.set_copy_engine(swr.ENGINE_DMA)
-    dma_steps = max(2, args.steps // 4)
-    for m in sorted({tokens[0], tokens[-1]}):
-        with torch.cuda.stream(compute):
-            forward(m)
-        torch.cuda.synchronize()
-        evd = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-               for _ in range(dma_steps)]
-        fwd_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(dma_steps)]
-        with torch.cuda.stream(compute):
-            for s in range(dma_steps):
-                fwd_d[s][0].record(compute)
-                forward(m, evd[s])
-                fwd_d[s][1].record(compute)
-        torch.cuda.synchronize()
-        f = float(np.median([a.elapsed_time(b) for a, b in fwd_d]))
-        g = float(np.mean([a.elapsed_time(b) for row in evd for a, b in row]))
-        dma[str(m)] = {"pipelined_ms_per_forward": round(f, 4), "gemm_ms_per_layer_in_pipeline": round(g, 4),
-                       "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
-    planner.set_copy_engine(swr.ENGINE_KERNEL)
+        # ---------------------------------------------------------------- tensor-parallel share
+        # The PR report's alternative to weight sharding: each of R ranks (its
+        # deployment's TP4) holds 1/R of the intermediate dimension and computes an
+        # fp32 partial of Y; the partials are all-reduced.  One GPU shows one
+        # rank's share at its real shape, timed over all ranks' shards of all
+        # layers (so no cache serves a later call), and the local reduce of R
+        # partials.
+        R = 4
+        sh = I // R
+        tmp = torch.empty(T, dtype=torch.uint8, device=dev)
+        shards = []
+        for layer in range(L):
+            swr.reassemble_into_slot(chunks[layer], C, tmp, stream=compute)
+            torch.cuda.synchronize()
+            gu_full = tmp[o_gu:o_gu + 2 * I * H].view(2 * I, H)
+            d_full = tmp[o_d:o_d + H * I].view(H, I)
+            for r in range(R):
+                rows = torch.cat([torch.arange(r * sh, (r + 1) * sh), torch.arange(I + r * sh, I + (r + 1) * sh)]).to(dev)
+                shards.append((gu_full.index_select(0, rows).contiguous(), scales[layer][0].index_select(0, rows).contiguous(),
+                               d_full[:, r * sh:(r + 1) * sh].contiguous(), scales[layer][1]))
+            torch.cuda.synchronize()
+        del tmp
+        rank_bytes = 2 * sh * H + H * sh + (2 * sh + H) * 4
+        tpres = {}
+        for m in sorted({tokens[0], tokens[-1]}):
+            parts = [torch.empty((m, H), dtype=torch.float32, device=dev) for _ in range(R)]
+            yt = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
+            wst = torch.empty(swr.mlp_workspace_bytes(m, H, sh, "fp8_e4m3fn"), dtype=torch.uint8, device=dev)
 
-    # ---------------------------------------------------------------- tensor-parallel share
-    # The PR report's alternative to weight sharding: each of R ranks (its
-    # deployment's TP4) holds 1/R of the intermediate dimension and computes an
-    # fp32 partial of Y; the partials are all-reduced.  One GPU shows one
-    # rank's share at its real shape, timed over all ranks' shards of all
-    # layers (so no cache serves a later call), and the local reduce of R
-    # partials.
-    R = 4
-    sh = I // R
-    tmp = torch.empty(T, dtype=torch.uint8, device=dev)
-    shards = []
-    for layer in range(L):
-        swr.reassemble_into_slot(chunks[layer], C, tmp, stream=compute)
-        torch.cuda.synchronize()
-        gu_full = tmp[o_gu:o_gu + 2 * I * H].view(2 * I, H)
-        d_full = tmp[o_d:o_d + H * I].view(H, I)
-        for r in range(R):
-            rows = torch.cat([torch.arange(r * sh, (r + 1) * sh), torch.arange(I + r * sh, I + (r + 1) * sh)]).to(dev)
-            shards.append((gu_full.index_select(0, rows).contiguous(), scales[layer][0].index_select(0, rows).contiguous(),
-                           d_full[:, r * sh:(r + 1) * sh].contiguous(), scales[layer][1]))
-        torch.cuda.synchronize()
-    del tmp
-    rank_bytes = 2 * sh * H + H * sh + (2 * sh + H) * 4
-    tpres = {}
-    for m in sorted({tokens[0], tokens[-1]}):
-        parts = [torch.empty((m, H), dtype=torch.float32, device=dev) for _ in range(R)]
-        yt = torch.empty((m, H), dtype=torch.bfloat16, device=dev)
-        wst = torch.empty(swr.mlp_workspace_bytes(m, H, sh, "fp8_e4m3fn"), dtype=torch.uint8, device=dev)
+            def rank_pass(m=m, parts=parts, wst=wst):
+                for i, (g_r, sg_r, d_r, sd_r) in enumerate(shards):
+                    swr.mlp_forward_partial(g_r, sg_r, d_r, sd_r, "fp8_e4m3fn", H, sh, xs[m], parts[i % R], wst,
+                                            stream=compute)
 
-        def rank_pass(m=m, parts=parts, wst=wst):
-            for i, (g_r, sg_r, d_r, sd_r) in enumerate(shards):
-                swr.mlp_forward_partial(g_r, sg_r, d_r, sd_r, "fp8_e4m3fn", H, sh, xs[m], parts[i % R], wst,
-                                        stream=compute)
+            with torch.cuda.stream(compute):
+                rank_pass()
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(compute)
+                rank_pass()
+                e1.record(compute)
+                for _ in range(L):
+                    swr.sum_partials(parts, yt, stream=compute)
+                e2.record(compute)
+            torch.cuda.synchronize()
+            rank_ms = e0.elapsed_time(e1) / len(shards)
+            red_ms = e1.elapsed_time(e2) / L
+            tpres[str(m)] = {"rank_mlp_ms_per_layer": round(rank_ms, 4),
+                             "rank_weight_GBps": round(rank_bytes / (rank_ms * 1e-3) / 1e9, 1),
+                             "reduce_of_partials_ms": round(red_ms, 4),
+                             "weight_sharded_serial_ms_per_layer": round(serial_ms[m] / L, 4)}
+        del shards
 
-        with torch.cuda.stream(compute):
-            rank_pass()
-            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-            e0.record(compute)
-            rank_pass()
-            e1.record(compute)
-            for _ in range(L):
-                swr.sum_partials(parts, yt, stream=compute)
-            e2.record(compute)
-        torch.cuda.synchronize()
-        rank_ms = e0.elapsed_time(e1) / len(shards)
-        red_ms = e1.elapsed_time(e2) / L
-        tpres[str(m)] = {"rank_mlp_ms_per_layer": round(rank_ms, 4),
-                         "rank_weight_GBps": round(rank_bytes / (rank_ms * 1e-3) / 1e9, 1),
-                         "reduce_of_partials_ms": round(red_ms, 4),
-                         "weight_sharded_serial_ms_per_layer": round(serial_ms[m] / L, 4)}
-    del shards
-
-    # ---------------------------------------------------------------- graph replay
-    # one forward captured as a graph (weight_sharding, CUDA graph section) and
-    # replayed: a planner without the cross-forward prefetch, so every replay
-    # is self-contained, against the same planner run eagerly
-    graph = {}
-    gp = swr.Planner(0, L, compute, side, slot_a, slot_b)
-    for layer in range(L):
-        gp.set_layer(layer, chunks[layer], C)
-    reps = max(4, args.steps // 2)
-    for m in sorted({tokens[0], tokens[-1]}):
-        with torch.cuda.stream(compute):
-            forward(m, pl=gp)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(compute):
-            e0.record(compute)
-            for _ in range(reps):
+        # ---------------------------------------------------------------- graph replay
+        # one forward captured as a graph (weight_sharding, CUDA graph section) and
+        # replayed: a planner without the cross-forward prefetch, so every replay
+        # is self-contained, against the same planner run eagerly
+        graph = {}
+        gp = swr.Planner(0, L, compute, side, slot_a, slot_b)
+        for layer in range(L):
+            gp.set_layer(layer, chunks[layer], C)
+        reps = max(4, args.steps // 2)
+        for m in sorted({tokens[0], tokens[-1]}):
+            with torch.cuda.stream(compute):
                 forward(m, pl=gp)
-            e1.record(compute)
-        torch.cuda.synchronize()
-        eager = e0.elapsed_time(e1) / reps
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=compute):
-            forward(m, pl=gp)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(compute):
-            e0.record(compute)
-            for _ in range(reps):
-                g.replay()
-            e1.record(compute)
-        torch.cuda.synchronize()
-        graph[str(m)] = {"eager_ms_per_forward": round(eager, 4),
-                         "graph_replay_ms_per_forward": round(e0.elapsed_time(e1) / reps, 4)}
-        del g
-    gp.close()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(compute):
+                e0.record(compute)
+                for _ in range(reps):
+                    forward(m, pl=gp)
+                e1.record(compute)
+            torch.cuda.synchronize()
+            eager = e0.elapsed_time(e1) / reps
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=compute):
+                forward(m, pl=gp)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(compute):
+                e0.record(compute)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(compute)
+            torch.cuda.synchronize()
+            graph[str(m)] = {"eager_ms_per_forward": round(eager, 4),
+                             "graph_replay_ms_per_forward": round(e0.elapsed_time(e1) / reps, 4)}
+            del g
+        gp.close()
 
     # ---------------------------------------------------------------- roofline
     def mlp_alg_bytes(m: int) -> int:
@@ -403,7 +410,7 @@ def main() -> int:
             "isolated_weight_GBps": round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9, 1),
             "isolated_weight_frac": round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "isolated_tokens_per_s": round(m / (L * iso_gemm[m] * 1e-3), 1),
-            "serial_reference_ms_per_forward": round(serial_ms[m], 4),
+            "serial_reference_ms_per_forward": round(serial_ms[m], 4) if m in serial_ms else None,
         }
 
     # a plain device-to-device copy of known size (read + write of the same
