@@ -152,11 +152,12 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
-    ev = {m: [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-               for _ in range(args.steps)] for m in tokens}
     fwd_ev = {m: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.steps)] for m in tokens}
-    # every copy of the timed steps gets a pair of timing events on the side stream
+    # The planner times every copy (events on the side stream around it) and
+    # every layer's compute (its begin record after the ready wait -- the last
+    # packet before the layer's kernels -- to a record after done): no event
+    # of the bench sits between a gate and the work it orders.
     planner.set_timing(args.steps * len(tokens) * L)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -164,13 +165,14 @@ def main() -> int:
         for s in range(args.steps):
             for m in tokens:
                 fwd_ev[m][s][0].record(compute)
-                forward(m, ev[m][s])
+                forward(m)
                 fwd_ev[m][s][1].record(compute)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gathers = planner.gather_times()
+    layer_spans = planner.layer_times()
     planner.set_timing(0)
-    assert len(gathers) == args.steps * len(tokens) * L
+    assert len(gathers) == args.steps * len(tokens) * L and len(layer_spans) == len(gathers)
     # (in cyclic mode the first timed forward's first layer was gathered during warmup, and
     # the last timed forward gathers one layer for a forward that does not run; the count is
     # the same)
@@ -180,8 +182,12 @@ def main() -> int:
         for m in tokens:
             gather_ms[m].extend(gathers[k:k + L])
             k += L
-    gemm_ms = {m: [ev[m][s][l][0].elapsed_time(ev[m][s][l][1]) for s in range(args.steps) for l in range(L)]
-               for m in tokens}
+    gemm_ms = {m: [] for m in tokens}
+    k = 0
+    for s in range(args.steps):
+        for m in tokens:
+            gemm_ms[m].extend(layer_spans[k:k + L])
+            k += L
     fwd_ms = {m: [fwd_ev[m][s][0].elapsed_time(fwd_ev[m][s][1]) for s in range(args.steps)] for m in tokens}
 
     ms_per_step = wall * 1e3 / args.steps
@@ -228,7 +234,7 @@ def main() -> int:
     # The sections below (serial reference, DMA-engine gather, tensor-parallel
     # share, graph replay) are reports beside the headline; --minimal skips
     # them, e.g. for hardware-counter runs that average over every MLP call.
-    serial_ms, dma, graph, tpres, R, rank_bytes = {}, {}, {}, {}, 4, 0
+    serial_ms, dma, graph, tpres, gate_begin, R, rank_bytes = {}, {}, {}, {}, {}, 4, 0
     if not args.minimal:
         # ---------------------------------------------------------------- serial reference
         # the same gathers and MLPs back to back on one stream (no side stream, no overlap):
@@ -275,6 +281,23 @@ def main() -> int:
             dma[str(m)] = {"pipelined_ms_per_forward": round(f, 4), "gemm_ms_per_layer_in_pipeline": round(g, 4),
                            "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
         planner.set_copy_engine(swr.ENGINE_KERNEL)
+
+        # ---------------------------------------------------------------- begin gate
+        # the same pipelined forwards with SWR_GATE_BEGIN (the gather of l+1
+        # waits for the compute stream to begin layer l), without timing events
+        gate_begin = {}
+        planner.set_gate(swr.GATE_BEGIN)
+        for m in tokens:
+            with torch.cuda.stream(compute):
+                forward(m)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(compute)
+                for _ in range(dma_steps * 2):
+                    forward(m)
+                e1.record(compute)
+            torch.cuda.synchronize()
+            gate_begin[str(m)] = {"pipelined_ms_per_forward": round(e0.elapsed_time(e1) / (dma_steps * 2), 4)}
+        planner.set_gate(swr.GATE_DONE)
 
         # ---------------------------------------------------------------- tensor-parallel share
         # The PR report's alternative to weight sharding: each of R ranks (its
@@ -450,6 +473,7 @@ def main() -> int:
         "per_tokens": per_m,
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1),
         "dma_engine_gather": dma,
+        "begin_gate": gate_begin,
         "graph_replay_no_prefetch": graph,
         "tensor_parallel_share": {"ranks": R, "rank_weight_bytes_per_layer": rank_bytes, "per_tokens": tpres},
         "roofline": roofline,

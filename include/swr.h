@@ -355,7 +355,9 @@ typedef struct swr_planner swr_planner;
 enum swr_trace_op {
   SWR_OP_RECORD_START = 1, SWR_OP_WAIT_START = 2, SWR_OP_WAIT_DONE = 3, SWR_OP_COPY = 4,
   SWR_OP_RECORD_READY = 5, SWR_OP_WAIT_READY = 6, SWR_OP_RECORD_DONE = 7,
-  SWR_OP_COPY_NEXT = 8 /* cyclic mode: the next forward's first layer */
+  SWR_OP_COPY_NEXT = 8, /* cyclic mode: the next forward's first layer */
+  SWR_OP_RECORD_BEGIN = 9, /* gate SWR_GATE_BEGIN: compute stream begins layer l (after its ready wait) */
+  SWR_OP_WAIT_BEGIN = 10   /* side stream waits for that record before a gather */
 };
 enum swr_trace_stream { SWR_STREAM_COMPUTE = 0, SWR_STREAM_SIDE = 1 };
 
@@ -384,6 +386,31 @@ int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer);
 int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void** slot_out);
 /* SWR_E_SEQUENCE if wait_ready_once(layer) was not called first. */
 int swr_planner_update_done_event(swr_planner* p, int32_t layer);
+/* Gate of the planner's gathers (swr_planner_set_gate). */
+#define SWR_GATE_DONE 0  /* gather(l+1) waits for done(l-1), as the pages (default)     */
+#define SWR_GATE_BEGIN 1 /* gather(l+1) waits for the compute stream to begin layer l */
+
+/*
+ * swr_planner_set_gate -- which compute-stream event gates each gather.
+ * weight_sharding, lookahead and ping-pong section: the gather of layer l+1
+ * may overwrite its slot once layer l-1, the slot's last reader, is done.
+ *   SWR_GATE_DONE   the gather waits for done(l-1) (the pages' gate).
+ *   SWR_GATE_BEGIN  the gather waits for an event recorded on the compute
+ *                   stream right after that stream's wait for ready(l), i.e.
+ *                   when layer l begins.  That point follows done(l-1) in
+ *                   stream order and the gather of layer l precedes it on the
+ *                   side stream, so the dependencies are the same; the gather
+ *                   is enqueued by swr_planner_wait_ready_once(l) instead of
+ *                   swr_planner_maybe_dispatch(l+1) (which then only marks it
+ *                   pending), and on one GPU the layer's GEMM workgroups are
+ *                   resident before the copy's many short workgroups arrive.
+ * The trace then shows SWR_OP_RECORD_BEGIN / SWR_OP_WAIT_BEGIN in place of
+ * SWR_OP_WAIT_DONE.  Host only.
+ * Errors: SWR_E_INVALID (null planner, unknown gate), SWR_E_SEQUENCE (a
+ * gather is pending).
+ */
+int swr_planner_set_gate(swr_planner* p, int32_t gate);
+
 /* Gather engines of the planner (swr_planner_set_copy_engine). */
 #define SWR_ENGINE_KERNEL 0 /* swr_reassemble_into_slot (default)      */
 #define SWR_ENGINE_DMA 1    /* swr_reassemble_into_slot_dma            */
@@ -407,16 +434,25 @@ int swr_planner_set_copy_engine(swr_planner* p, int32_t engine);
  * gather as SWR_OP_COPY_NEXT.  SWR_E_INVALID for an odd number of layers. */
 int swr_planner_set_cyclic(swr_planner* p, int32_t enabled);
 
-/* Timing of the gathers.  swr_planner_set_timing(p, capacity) with
- * capacity > 0 makes every later dispatch record two timing events on the side
- * stream around its copy (after the gate wait, before the ready record), in a
- * ring of `capacity` event pairs; 0 turns timing off.  Either way the
+/* Timing of the gathers and of the layers.  swr_planner_set_timing(p, capacity)
+ * with capacity > 0 makes every later dispatch record two timing events on the
+ * side stream around its copy (after the gate wait, before the ready record),
+ * and every later layer two on the compute stream (the begin record after its
+ * ready wait, and one after its done record), each in a ring of `capacity`
+ * event pairs; 0 turns timing off.  Either way the
  * launch/wait sequence is the same.  swr_planner_gather_times writes the copy
  * durations (milliseconds) of the timed dispatches still in the ring, oldest
  * first, at most `cap` of them, and sets *n to the number written; every one
  * of those copies must have finished (else SWR_E_HIP). */
 int swr_planner_set_timing(swr_planner* p, int32_t capacity);
 int swr_planner_gather_times(const swr_planner* p, float* ms, int32_t cap, int32_t* n);
+
+/* The compute span of each timed layer, oldest first: from the begin record
+ * (after the layer's ready wait, the last packet before its kernels) to the
+ * record after its done event, in ms.  Timing is on while set_timing's
+ * capacity is non-zero; the ring keeps the last `capacity` layers.  Host only;
+ * synchronise the compute stream first.  Errors: SWR_E_INVALID, SWR_E_HIP. */
+int swr_planner_layer_times(const swr_planner* p, float* ms, int32_t cap, int32_t* n);
 /* Bytes received from peers so far (sum of (N-1)*C over gathers), and the
  * number of gathers issued, since creation. */
 int swr_planner_counters(const swr_planner* p, int64_t* remote_bytes, int64_t* gathers);

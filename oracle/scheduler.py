@@ -24,9 +24,17 @@ maybe_dispatch(end) gathers the *next* forward's first layer into slot 0 --
 free once done(end - 2) is recorded, since the last layer uses slot 1 -- and
 the next forward skips its own pre_dispatch gather.
 
+Gate "begin" (a one-GPU variant, same dependencies): the gather of layer
+l+1 waits for an event recorded on the compute stream right after that
+stream's wait for ready(l) -- the moment layer l begins.  That point follows
+done(l-1) on the compute stream, and the gather of l precedes the gather of
+l+1 on the side stream, so the gather may start exactly when the page's gate
+allows; it is enqueued after the compute stream's ready wait instead of
+before it.
+
 An op is a tuple (name, stream, layer, slot) with names
   record_start  wait_start  wait_done  copy  copy_next  record_ready
-  wait_ready  record_done
+  wait_ready  record_done  record_begin  wait_begin
 and layer/slot -1 where they do not apply; ``copy_next`` is a gather made in
 one forward for the next one.  ``check_trace`` is an independent
 happens-before checker: it does not reuse ``expected_trace``.
@@ -40,16 +48,37 @@ def slot_of(layer: int, start: int) -> int:
     return (layer - start) % 2
 
 
-def expected_trace(start: int, end: int, prefetched: bool = False, prefetch_next: bool = False) -> list[tuple]:
+def expected_trace(start: int, end: int, prefetched: bool = False, prefetch_next: bool = False,
+                   gate: str = "done") -> list[tuple]:
     """Launch/wait sequence of one forward over layers [start, end).
 
     prefetched: the previous forward already gathered layer `start` (cyclic mode);
-    prefetch_next: this forward gathers the next forward's layer `start`."""
+    prefetch_next: this forward gathers the next forward's layer `start`;
+    gate: "done" (the page's gate) or "begin"."""
     ops: list[tuple] = [("record_start", COMPUTE, -1, -1)]
     if end <= start:
         return ops
     if prefetch_next and ((end - start) % 2 or end - start < 2):
         raise ValueError("cyclic prefetch needs an even number of layers")
+    if gate not in ("done", "begin"):
+        raise ValueError("gate is 'done' or 'begin'")
+    if gate == "begin":
+        if not prefetched:
+            ops += [("wait_start", SIDE, -1, -1), ("copy", SIDE, start, 0), ("record_ready", SIDE, start, -1)]
+        for layer in range(start, end):
+            ops.append(("wait_ready", COMPUTE, layer, slot_of(layer, start)))
+            nxt = layer + 1 < end
+            if nxt or prefetch_next:
+                ops.append(("record_begin", COMPUTE, layer, -1))
+                ops.append(("wait_begin", SIDE, layer, -1))
+                if nxt:
+                    ops.append(("copy", SIDE, layer + 1, slot_of(layer + 1, start)))
+                    ops.append(("record_ready", SIDE, layer + 1, -1))
+                else:
+                    ops.append(("copy_next", SIDE, start, 0))
+                    ops.append(("record_ready", SIDE, start, -1))
+            ops.append(("record_done", COMPUTE, layer, -1))
+        return ops
 
     def dispatch(layer: int) -> None:
         prev = layer - 2  # the last reader of the slot this gather overwrites
@@ -84,6 +113,8 @@ def _event(op: tuple):
         return ("ready", layer)
     if name in ("record_done", "wait_done"):
         return ("done", layer)
+    if name in ("record_begin", "wait_begin"):
+        return ("begin", layer)
     return None
 
 

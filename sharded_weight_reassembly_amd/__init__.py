@@ -29,20 +29,20 @@ STATUS_NAMES = {0: "SWR_OK", -1: "SWR_E_INVALID", -2: "SWR_E_ALIGN", -3: "SWR_E_
                 -5: "SWR_E_HIP", -6: "SWR_E_SEQUENCE"}
 
 TRACE_OPS = {1: "record_start", 2: "wait_start", 3: "wait_done", 4: "copy", 5: "record_ready", 6: "wait_ready",
-             7: "record_done", 8: "copy_next"}
+             7: "record_done", 8: "copy_next", 9: "record_begin", 10: "wait_begin"}
 TRACE_STREAMS = {0: "compute", 1: "side"}
 
 # Every function include/swr.h declares.
 EXPORTS = (
     "swr_plan_layer", "swr_pack_layer", "swr_redistribute_row_shards", "swr_reassemble_into_slot",
     "swr_reassemble_into_slot_dma",
-    "swr_planner_set_copy_engine", "swr_proj_forward",
+    "swr_planner_set_copy_engine", "swr_planner_set_gate", "swr_proj_forward",
     "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward",
     "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
-    "swr_planner_gather_times", "swr_planner_set_cyclic", "swr_last_error", "swr_version",
+    "swr_planner_gather_times", "swr_planner_layer_times", "swr_planner_set_cyclic", "swr_last_error", "swr_version",
 )
 
 
@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
         "swr_reassemble_into_slot_dma": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i64, _i32, _vp, _vp, _vp,
                                                 ctypes.POINTER(_i64)]),
         "swr_planner_set_copy_engine": (_i32, [_vp, _i32]),
+        "swr_planner_set_gate": (_i32, [_vp, _i32]),
         "swr_proj_forward": (_i32, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp]),
         "swr_proj_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
         "swr_proj_forward_grouped": (_i32, [ctypes.POINTER(ProjDesc), _i32, _i64, _vp, _i64, _vp]),
@@ -129,6 +130,7 @@ def lib() -> ctypes.CDLL:
         "swr_planner_set_timing": (_i32, [_vp, _i32]),
         "swr_planner_set_cyclic": (_i32, [_vp, _i32]),
         "swr_planner_gather_times": (_i32, [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]),
+        "swr_planner_layer_times": (_i32, [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]),
         "swr_last_error": (ctypes.c_char_p, []),
         "swr_version": (ctypes.c_char_p, []),
     }
@@ -271,6 +273,7 @@ def reassemble_into_slot_dma(chunks, chunk_bytes: int, slot, slot_bytes: int | N
 
 
 ENGINE_KERNEL, ENGINE_DMA = 0, 1
+GATE_DONE, GATE_BEGIN = 0, 1
 
 
 def view(slot: torch.Tensor, v: dict) -> torch.Tensor:
@@ -415,6 +418,10 @@ class Planner:
         """Gather the next forward's first layer during the last layer (even layer counts)."""
         _check("swr_planner_set_cyclic", lib().swr_planner_set_cyclic(self._h, int(bool(enabled))))
 
+    def set_gate(self, gate: int) -> None:
+        """GATE_DONE (gather(l+1) waits for done(l-1), default) or GATE_BEGIN (waits for layer l to begin)."""
+        _check("swr_planner_set_gate", lib().swr_planner_set_gate(self._h, int(gate)))
+
     def set_copy_engine(self, engine: int) -> None:
         """ENGINE_KERNEL (the copy kernel, default) or ENGINE_DMA (the DMA engines)."""
         _check("swr_planner_set_copy_engine", lib().swr_planner_set_copy_engine(self._h, int(engine)))
@@ -428,6 +435,13 @@ class Planner:
         n = _i32(0)
         buf = (ctypes.c_float * max(cap, 1))()
         _check("swr_planner_gather_times", lib().swr_planner_gather_times(self._h, buf, int(cap), ctypes.byref(n)))
+        return list(buf[:n.value])
+
+    def layer_times(self, cap: int = 1 << 16) -> list[float]:
+        """Compute spans (ms) of the timed layers still in the ring, oldest first (begin record to done)."""
+        n = _i32(0)
+        buf = (ctypes.c_float * max(cap, 1))()
+        _check("swr_planner_layer_times", lib().swr_planner_layer_times(self._h, buf, int(cap), ctypes.byref(n)))
         return list(buf[:n.value])
 
     def counters(self) -> tuple[int, int]:

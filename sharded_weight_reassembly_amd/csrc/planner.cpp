@@ -38,9 +38,23 @@ struct swr_planner {
   // a ring of event pairs, one pair per timed dispatch
   std::vector<hipEvent_t> t0, t1;
   int64_t timed_dispatches = 0;
+  // and around each layer's compute on the compute stream: c0 recorded when
+  // the layer begins (after its ready wait, the last packet before its
+  // kernels), c1 after its done record
+  std::vector<hipEvent_t> c0, c1;
+  int64_t timed_layers = 0;
+  std::vector<int64_t> layer_slot;  // ring slot of each layer's c0 in this forward
 
   // gather engine: 0 the copy kernel, 1 the DMA engines
   int32_t engine = 0;
+
+  // gate mode: each gather of layer l+1 waits for the compute stream to begin
+  // layer l (after its ready(l) wait) instead of done(l-1); the gather is
+  // enqueued by wait_ready_once(l)
+  bool gate_begin = false;
+  std::vector<hipEvent_t> begin;
+  int32_t pending = -1;       // layer whose gather waits for the next begin record
+  bool pending_next = false;  // the next forward's first layer waits likewise
 
   // cyclic first-layer prefetch
   bool cyclic = false;
@@ -73,22 +87,31 @@ void destroy_events(swr_planner* p) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->done)
     if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->begin)
+    if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->t0)
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->t1)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->c0)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->c1)
     if (e) (void)hipEventDestroy(e);
 }
 
 // Side stream: gate, gather of `layer` into its slot, ready record.  With
 // `for_next`, the gather is the next forward's first layer (cyclic mode): its
 // slot's last reader in this forward is layer end - 2.
-int dispatch(swr_planner* p, int32_t layer, bool for_next = false) {
+int dispatch(swr_planner* p, int32_t layer, bool for_next = false, hipEvent_t begin_gate = nullptr,
+             int32_t begin_layer = -1) {
   const int i = p->idx(layer);
   const swr_planner::Layer& L = p->layers[i];
   if (L.chunks.empty()) return fail(SWR_E_SEQUENCE, "planner: layer %d has no chunks (swr_planner_set_layer)", layer);
   hipEvent_t gate;
   const int32_t prev = for_next ? p->end - 2 : layer - 2;  // last reader of the slot this gather overwrites
-  if (prev >= p->start) {
+  if (begin_gate) {
+    gate = begin_gate;  // recorded on the compute stream after done(prev)
+  } else if (prev >= p->start) {
     if (!p->finished[p->idx(prev)])
       return fail(SWR_E_SEQUENCE, "planner: gather of layer %d needs done(%d), which was not recorded", layer, prev);
     gate = p->done[p->idx(prev)];
@@ -119,7 +142,9 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false) {
     }
   }
   if (rc != SWR_OK) return rc;
-  if (prev >= p->start)
+  if (begin_gate)
+    p->log(SWR_OP_WAIT_BEGIN, SWR_STREAM_SIDE, begin_layer, -1);
+  else if (prev >= p->start)
     p->log(SWR_OP_WAIT_DONE, SWR_STREAM_SIDE, prev, -1);
   else
     p->log(SWR_OP_WAIT_START, SWR_STREAM_SIDE, -1, -1);
@@ -158,6 +183,8 @@ extern "C" int swr_planner_create(int32_t start, int32_t end, hipStream_t comput
   p->layers.resize(n);
   p->ready.assign(n, nullptr);
   p->done.assign(n, nullptr);
+  p->begin.assign(n, nullptr);
+  p->layer_slot.assign(n, -1);
   p->dispatched.assign(n, 0);
   p->waited.assign(n, 0);
   p->finished.assign(n, 0);
@@ -165,6 +192,7 @@ extern "C" int swr_planner_create(int32_t start, int32_t end, hipStream_t comput
   for (int i = 0; e == hipSuccess && i < n; ++i) {
     e = hipEventCreateWithFlags(&p->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->done[i], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->begin[i], hipEventDisableTiming);
   }
   if (e != hipSuccess) {
     destroy_events(p);
@@ -210,6 +238,8 @@ extern "C" int swr_planner_reset(swr_planner* p) {
     p->dispatched[0] = 1;
     p->next_prefetched = false;
   }
+  p->pending = -1;
+  p->pending_next = false;
   p->trace.clear();
   p->log(SWR_OP_RECORD_START, SWR_STREAM_COMPUTE, -1, -1);
   p->reset_called = true;
@@ -239,6 +269,11 @@ extern "C" int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer) {
   if (layer == p->end && p->cyclic && p->reset_called && !p->next_prefetched) {
     if (!p->dispatched[p->idx(p->end - 1)])
       return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: next forward before layer %d", p->end - 1);
+    if (p->gate_begin) {  // enqueued by wait_ready_once(end - 1)
+      p->pending_next = true;
+      swr::clear_error();
+      return SWR_OK;
+    }
     const int rc = dispatch(p, p->start, true);
     if (rc == SWR_OK) swr::clear_error();
     return rc;
@@ -252,6 +287,13 @@ extern "C" int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer) {
     return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d already dispatched in this forward", layer);
   if (layer > p->start && !p->dispatched[p->idx(layer - 1)])
     return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d before layer %d", layer, layer - 1);
+  if (p->gate_begin && layer > p->start) {  // enqueued by wait_ready_once(layer - 1)
+    if (p->pending >= 0)
+      return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d is still pending", p->pending);
+    p->pending = layer;
+    swr::clear_error();
+    return SWR_OK;
+  }
   const int rc = dispatch(p, layer);
   if (rc == SWR_OK) swr::clear_error();
   return rc;
@@ -268,6 +310,35 @@ extern "C" int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void**
     if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_wait_ready_once: wait");
     p->waited[i] = 1;
     p->log(SWR_OP_WAIT_READY, SWR_STREAM_COMPUTE, layer, p->slot_of(layer));
+    const bool next_due = p->pending == layer + 1;
+    const bool first_due = p->pending_next && layer == p->end - 1;
+    const bool gate_due = p->gate_begin && (next_due || first_due);
+    // the begin record: a timing event when layers are timed, the gate of the
+    // pending gather in SWR_GATE_BEGIN mode, or both
+    hipEvent_t begin_ev = nullptr;
+    if (!p->c0.empty()) {
+      const int64_t r = p->timed_layers % int64_t(p->c0.size());
+      p->layer_slot[i] = r;
+      begin_ev = p->c0[size_t(r)];
+    } else if (gate_due) {
+      begin_ev = p->begin[i];
+    }
+    if (begin_ev) {
+      const hipError_t eb = hipEventRecord(begin_ev, p->compute);
+      if (eb != hipSuccess) return swr::hip_fail(eb, "swr_planner_wait_ready_once: record begin");
+    }
+    if (gate_due) {
+      p->log(SWR_OP_RECORD_BEGIN, SWR_STREAM_COMPUTE, layer, -1);
+      int rc;
+      if (next_due) {
+        p->pending = -1;
+        rc = dispatch(p, layer + 1, false, begin_ev, layer);
+      } else {
+        p->pending_next = false;
+        rc = dispatch(p, p->start, true, begin_ev, layer);
+      }
+      if (rc != SWR_OK) return rc;
+    }
   }
   if (slot_out) *slot_out = p->slot[p->slot_of(layer)];
   swr::clear_error();
@@ -281,8 +352,14 @@ extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
   const int i = p->idx(layer);
   if (!p->waited[i])
     return fail(SWR_E_SEQUENCE, "swr_planner_update_done_event: layer %d did not wait for its weights", layer);
-  const hipError_t e = hipEventRecord(p->done[i], p->compute);
+  hipError_t e = hipEventRecord(p->done[i], p->compute);
   if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record");
+  if (!p->c1.empty() && p->layer_slot[i] >= 0) {
+    e = hipEventRecord(p->c1[size_t(p->layer_slot[i])], p->compute);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record timing end");
+    p->layer_slot[i] = -1;
+    p->timed_layers += 1;
+  }
   p->finished[i] = 1;
   p->log(SWR_OP_RECORD_DONE, SWR_STREAM_COMPUTE, layer, -1);
   swr::clear_error();
@@ -295,6 +372,17 @@ extern "C" int swr_planner_set_cyclic(swr_planner* p, int32_t enabled) {
     return fail(SWR_E_INVALID, "swr_planner_set_cyclic: needs an even number of layers (have %d)", p->end - p->start);
   p->cyclic = enabled != 0;
   if (!p->cyclic) p->next_prefetched = false;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_gate(swr_planner* p, int32_t gate) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_set_gate: null pointer");
+  if (gate != SWR_GATE_DONE && gate != SWR_GATE_BEGIN)
+    return fail(SWR_E_INVALID, "swr_planner_set_gate: unknown gate %d", gate);
+  if (p->pending >= 0 || p->pending_next)
+    return fail(SWR_E_SEQUENCE, "swr_planner_set_gate: a gather is still pending");
+  p->gate_begin = gate == SWR_GATE_BEGIN;
   swr::clear_error();
   return SWR_OK;
 }
@@ -316,21 +404,30 @@ extern "C" int swr_planner_set_timing(swr_planner* p, int32_t capacity) {
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->t1)
     if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->c0)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : p->c1)
+    if (e) (void)hipEventDestroy(e);
   p->t0.assign(capacity, nullptr);
   p->t1.assign(capacity, nullptr);
+  p->c0.assign(capacity, nullptr);
+  p->c1.assign(capacity, nullptr);
+  std::fill(p->layer_slot.begin(), p->layer_slot.end(), -1);
   p->timed_dispatches = 0;
+  p->timed_layers = 0;
   hipError_t e = hipSuccess;
   for (int i = 0; e == hipSuccess && i < capacity; ++i) {
     e = hipEventCreate(&p->t0[i]);
     if (e == hipSuccess) e = hipEventCreate(&p->t1[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->c0[i]);
+    if (e == hipSuccess) e = hipEventCreate(&p->c1[i]);
   }
   if (e != hipSuccess) {
-    for (hipEvent_t x : p->t0)
-      if (x) (void)hipEventDestroy(x);
-    for (hipEvent_t x : p->t1)
-      if (x) (void)hipEventDestroy(x);
-    p->t0.clear();
-    p->t1.clear();
+    for (auto* v : {&p->t0, &p->t1, &p->c0, &p->c1}) {
+      for (hipEvent_t x : *v)
+        if (x) (void)hipEventDestroy(x);
+      v->clear();
+    }
     return swr::hip_fail(e, "swr_planner_set_timing: hipEventCreate");
   }
   swr::clear_error();
@@ -348,6 +445,22 @@ extern "C" int swr_planner_gather_times(const swr_planner* p, float* ms, int32_t
     const size_t r = size_t((first + k) % ring);
     const hipError_t e = hipEventElapsedTime(&ms[k], p->t0[r], p->t1[r]);
     if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_gather_times: hipEventElapsedTime");
+  }
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_layer_times(const swr_planner* p, float* ms, int32_t cap, int32_t* n) {
+  if (!p || !n || (cap > 0 && !ms)) return fail(SWR_E_INVALID, "swr_planner_layer_times: null pointer");
+  const int64_t ring = int64_t(p->c0.size());
+  const int64_t avail = p->timed_layers < ring ? p->timed_layers : ring;
+  const int64_t count = avail < cap ? avail : cap;
+  *n = int32_t(count);
+  const int64_t first = p->timed_layers - avail;
+  for (int64_t k = 0; k < count; ++k) {
+    const size_t r = size_t((first + k) % ring);
+    const hipError_t e = hipEventElapsedTime(&ms[k], p->c0[r], p->c1[r]);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_layer_times: hipEventElapsedTime");
   }
   swr::clear_error();
   return SWR_OK;

@@ -242,8 +242,9 @@ def test_dma_engine_planner(start, n_layers, cyclic):
     p.close()
 
 
-@pytest.mark.parametrize("engine", [swr.ENGINE_KERNEL, swr.ENGINE_DMA])
-def test_forward_captured_in_a_graph(engine):
+@pytest.mark.parametrize("engine,gate", [(swr.ENGINE_KERNEL, swr.GATE_DONE), (swr.ENGINE_DMA, swr.GATE_DONE),
+                                         (swr.ENGINE_KERNEL, swr.GATE_BEGIN)])
+def test_forward_captured_in_a_graph(engine, gate):
     """weight_sharding, CUDA graph section: the launch/wait sequence is fixed,
     so one forward (gathers on the side stream, MLPs on the compute stream)
     can be captured once and replayed.  Between replays both slots and every
@@ -261,6 +262,7 @@ def test_forward_captured_in_a_graph(engine):
     for i, L in enumerate(layers):
         p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
     p.set_copy_engine(engine)
+    p.set_gate(gate)
     x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
     xd = bf16(x)
     outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
@@ -275,7 +277,8 @@ def test_forward_captured_in_a_graph(engine):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=compute):
         _forward(p, layers, 0, xd, outs, wsb)
-    assert p.trace() == osch.expected_trace(0, n_layers)  # the captured sequence is the model's
+    # the captured sequence is the model's
+    assert p.trace() == osch.expected_trace(0, n_layers, gate="begin" if gate == swr.GATE_BEGIN else "done")
     torch.cuda.synchronize()
     for rep in range(4):
         slot_a.fill_(0xFF)  # 0xFFFF as bf16 is NaN: a replay that skipped a gather would show it
@@ -287,4 +290,87 @@ def test_forward_captured_in_a_graph(engine):
         torch.cuda.synchronize()
         for i in range(n_layers):
             assert_close_rows(values(outs[i]), refs[i], what=f"graph replay {rep} layer {i}")
+    p.close()
+
+
+@pytest.mark.parametrize("start,n_layers,cyclic", [(0, 3, False), (1, 4, True), (0, 2, False)])
+def test_begin_gate_on_gpu(start, n_layers, cyclic):
+    """SWR_GATE_BEGIN: each gather after the first waits for the compute stream
+    to begin the previous layer.  The trace equals the oracle's model of that
+    gate, passes the happens-before checker, and every layer's outputs equal
+    the oracle's with the compute stream delayed."""
+    note(f"planner begin gate start={start} layers={n_layers} cyclic={cyclic}")
+    wl = synth.TINY
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(start, start + n_layers, torch.cuda.current_stream(), torch.cuda.Stream(), slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(start + i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_gate(swr.GATE_BEGIN)
+    with pytest.raises(swr.SwrError) as e:
+        p.set_gate(5)
+    assert e.value.code == swr.E_INVALID
+    if cyclic:
+        p.set_cyclic(True)
+    p.set_timing(64)  # the begin record doubles as the layer's timing start
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    a = torch.randn(2048, 2048, device=DEV)
+
+    def delay():
+        for _ in range(4):
+            torch.mm(a, a)
+
+    traces, outs_all = [], []
+    for _ in range(3):
+        outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+        _forward(p, layers, start, xd, outs, wsb, delay)
+        traces.append(p.trace())
+        outs_all.append(outs)
+    torch.cuda.synchronize()
+    end = start + n_layers
+    if cyclic:
+        assert traces[0] == osch.expected_trace(start, end, prefetch_next=True, gate="begin")
+        assert all(t == osch.expected_trace(start, end, prefetched=True, prefetch_next=True, gate="begin")
+                   for t in traces[1:])
+    else:
+        assert all(t == osch.expected_trace(start, end, gate="begin") for t in traces)
+    assert osch.check_trace(traces) == []
+    for outs in outs_all:
+        for i, L in enumerate(layers):
+            ws = L["ws"]
+            _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)
+            assert_close_rows(values(outs[i]), ref, what=f"begin gate layer {start + i}")
+    times = p.layer_times()
+    assert len(times) == 3 * n_layers and all(t > 0 for t in times)
+    assert len(p.gather_times()) == (3 * n_layers + 1 if cyclic else 3 * n_layers)
+    p.set_timing(0)
+    p.set_cyclic(False)
+    p.close()
+
+
+def test_set_gate_refused_while_a_gather_is_pending():
+    wl = synth.TINY
+    layers = _layers(wl, 2, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(0, 2, torch.cuda.current_stream(), torch.cuda.Stream(), slot, torch.empty_like(slot))
+    for i, L in enumerate(layers):
+        p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_gate(swr.GATE_BEGIN)
+    p.reset()
+    p.pre_dispatch(0)
+    p.maybe_dispatch(1)  # pending until wait_ready_once(0)
+    with pytest.raises(swr.SwrError) as e:
+        p.set_gate(swr.GATE_DONE)
+    assert e.value.code == swr.E_SEQUENCE
+    p.wait_ready_once(0)
+    p.update_done_event(0)
+    p.wait_ready_once(1)
+    p.update_done_event(1)
+    p.set_gate(swr.GATE_DONE)
+    torch.cuda.synchronize()
     p.close()

@@ -88,3 +88,32 @@ def test_cyclic_prefetch_needs_its_gate_and_even_layers():
     assert sch.check_trace([sch.expected_trace(0, 4), mid])
     with pytest.raises(ValueError):
         sch.expected_trace(0, 3, prefetch_next=True)
+
+
+@pytest.mark.parametrize("start,end", [(0, 1), (0, 2), (1, 5), (3, 11)])
+def test_begin_gate_is_race_free(start, end):
+    t = sch.expected_trace(start, end, gate="begin")
+    assert sch.check_trace([t, t, t]) == []
+    # the same gathers and slots as the page's gate, in the same order
+    copies = lambda tr: [op for op in tr if op[0] in ("copy", "copy_next")]
+    assert copies(t) == copies(sch.expected_trace(start, end))
+
+
+@pytest.mark.parametrize("start,end", [(0, 2), (1, 9)])
+def test_begin_gate_cyclic_is_race_free(start, end):
+    first = sch.expected_trace(start, end, prefetch_next=True, gate="begin")
+    mid = sch.expected_trace(start, end, prefetched=True, prefetch_next=True, gate="begin")
+    last = sch.expected_trace(start, end, prefetched=True, gate="begin")
+    assert sch.check_trace([first, mid, mid, last]) == []
+
+
+def test_begin_gate_mistakes_are_caught():
+    t = sch.expected_trace(0, 6, gate="begin")
+    no_wait = [op for op in t if op[0] != "wait_begin"]
+    assert any("race" in p for p in sch.check_trace([no_wait]))
+    # gating the gather of l+1 on the begin of l-1 lets it overwrite the slot layer l-1 still reads
+    early = [("wait_begin", s, layer - 1, x) if (n == "wait_begin" and layer >= 1) else (n, s, layer, x)
+             for n, s, layer, x in t]
+    assert any("race" in p for p in sch.check_trace([early]))
+    with pytest.raises(ValueError):
+        sch.expected_trace(0, 4, gate="ready")
