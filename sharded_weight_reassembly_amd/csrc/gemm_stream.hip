@@ -141,13 +141,13 @@ __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, con
 // (lane = 16 * (row / 4) + token, v = row % 4 within the MFMA output tile);
 // each thread adds them for one token and 4 consecutive rows and applies the
 // output mode (scale, SiLU*up, bf16 rounding) or writes a split-K partial.
-template <int MT, int RT, int NPART = kWaves>
+template <int MT, int RT, int NPART = kWaves, int NT = kThreads>
 __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_t tok0, int64_t bx, int64_t split) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int tiles_out = silu_mode ? RT / 2 : RT;
   const int items = tiles_out * MT * 64;
   auto at = [&](int w, int t, int b, int i, int ql) { return red[(((w * RT + t) * MT + b) * 4 + i) * 64 + ql]; };
-  for (int q = threadIdx.x; q < items; q += kThreads) {
+  for (int q = threadIdx.x; q < items; q += NT) {
     const int ql = q & 63;
     const int b = (q >> 6) % MT;
     const int t = (q >> 6) / MT;
@@ -300,21 +300,26 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 //   * loads go through buffer resources; a prefetch past the workgroup's last
 //     stage gets an out-of-range offset and reads nothing, so the unrolled
 //     main loop has no branches and the compiler's wait counts stay exact.
-template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK>
+template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK, int NW = kWaves>
 struct StagedShape {
   static_assert(!XL || WK, "X tiles in LDS go with K-split waves");
   static_assert(SK == kStageK || (!WK && SK == 2 * kStageK), "longer stages only with token-split waves");
+  static_assert(NW == 4 || (NW == 8 && WK && XL && RTL % 2 == 0), "8 waves: K split, X in LDS, two row halves");
+  static constexpr int NT = 64 * NW;                   // threads per workgroup
+  static constexpr int RH = NW / 4;                    // row halves (8 waves: wave / 4 picks one)
+  static constexpr int RTW = RTL / RH;                 // row tiles per wave (K-split modes)
   static constexpr int EB = FP8 ? 1 : 2;
   static constexpr int G = SK / 64;                    // 64-K groups per stage
   static constexpr int CPR = SK * EB / 16;             // 16-byte pieces per row per stage
   static constexpr int TILE = 16 * RTL * SK * EB;      // bytes of W per stage
-  static constexpr int NV = TILE / (16 * kThreads);    // W pieces per thread per stage
+  static constexpr int NV = TILE / (16 * NT);          // W pieces per thread per stage
   static constexpr int XT = XL ? 16 * MT * SK * 2 : 0;  // bytes of X per stage in LDS
+  static constexpr int XNV = XT / (16 * NT);           // X pieces per thread per stage (XL)
   static constexpr int KQ = WK ? 4 : 4 / MT;           // waves that share a token block (K groups)
   static constexpr int QN = WK ? 1 : G * MT / 4;       // K groups per wave per stage
   static constexpr int XF = WK ? MT : QN;              // X fragment pairs per lane per stage
-  static constexpr int ACC = WK ? RTL * MT : RTL;      // 16x16 accumulator tiles per wave
-  static constexpr int XS = 8 * XF;                    // VGPRs of one stage of X (either layout)
+  static constexpr int ACC = WK ? RTW * MT : RTL;      // 16x16 accumulator tiles per wave
+  static constexpr int XS = XL ? 4 * XNV : 8 * XF;     // VGPRs of one stage of X in the ring
   static constexpr int WS = 4 * NV;                     // VGPRs of one stage of W pieces
   static constexpr int RED = KQ * RTL * MT * 4 * 64 * 4;  // bytes of the final cross-wave sum
   static constexpr int LDS = (2 * TILE + 2 * XT) > RED ? (2 * TILE + 2 * XT) : RED;
@@ -324,10 +329,13 @@ struct StagedShape {
   // fragments read from LDS).
   // One 16-token block over 32 or fewer rows (the down GEMM and small views
   // at decode) has few workgroups, so each keeps a deep ring instead.
+  // Eight waves (two per SIMD, one workgroup per CU): 256 registers per wave,
+  // the accumulators in AGPRs, and the rings get what the fragments leave.
   static constexpr bool DEEP = MT == 1 && RTL <= 2;
-  static constexpr int OCC = (DEEP || ACC >= 16 || LDS > 80 * 1024) ? 1 : 2;
-  static constexpr int FREE = OCC == 2 ? 196 - 4 * ACC : (DEEP ? 440 - 4 * ACC : 220 - (XL ? 8 * MT : 0));
-  static constexpr int WCAP = OCC == 2 ? 112 : 128;
+  static constexpr int OCC = (NW == 8 || DEEP || ACC >= 16 || LDS > 80 * 1024) ? 1 : 2;
+  static constexpr int FREE = NW == 8 ? 256 - 4 * ACC - 52 - 8 * MT - 16
+                                      : (OCC == 2 ? 196 - 4 * ACC : (DEEP ? 440 - 4 * ACC : 220 - (XL ? 8 * MT : 0)));
+  static constexpr int WCAP = OCC == 2 || NW == 8 ? 112 : 128;
   // One 16-token block: X is cheap, so W and X of a stage share a slot (D
   // deep).  More tokens: X runs DX = 4 or 2 stages ahead in a ring of its own
   // and W gets the rest, at most WCAP VGPRs.
@@ -343,15 +351,15 @@ struct StagedShape {
 };
 
 // The body of a staged workgroup: row block bx, K split by, token block bz.
-template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK>
+template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK, int NW = kWaves>
 __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, int64_t bz, uint8_t* lds) {
-  using S = StagedShape<MT, RTL, FP8, WK, XL, SK>;
+  using S = StagedShape<MT, RTL, FP8, WK, XL, SK, NW>;
   constexpr int EB = S::EB, CPR = S::CPR, TILE = S::TILE, NV = S::NV, D = S::D, DX = S::DX, KQ = S::KQ;
-  constexpr int QN = S::QN, XT = S::XT, XF = S::XF;
-  constexpr int XNV = XT / (16 * kThreads);  // X pieces per thread per stage (XL)
+  constexpr int QN = S::QN, XT = S::XT, XF = S::XF, NT = S::NT, RTW = S::RTW;
+  constexpr int XNV = S::XNV;
   static_assert(D % DX == 0 && D % 2 == 0, "ring depths must nest");
-  static_assert(NV >= 1 && TILE % (16 * kThreads) == 0, "tile must split evenly over the workgroup");
-  static_assert(!XL || XNV == 2 * MT, "X tile must split evenly over the workgroup");
+  static_assert(NV >= 1 && TILE % (16 * NT) == 0, "tile must split evenly over the workgroup");
+  static_assert(!XL || XNV * 16 * NT == XT, "X tile must split evenly over the workgroup");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -359,22 +367,29 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
   const int r16 = lane & 15;
   const int grp = lane >> 4;
   // token split: token block wave % MT, K groups kq*MT .. kq*MT + MT - 1;
-  // K split: every token block, K group kq = wave
+  // K split: every token block, K group kq = wave % 4, row tiles rh*RTW ..
+  // rh*RTW + RTW - 1 (rh = wave / 4: one half of the rows with 8 waves)
   const int blk = WK ? 0 : wave % MT;
-  const int kq = WK ? wave : wave / MT;
+  const int kq = WK ? wave % 4 : wave / MT;
+  const int rh = WK ? wave / 4 : 0;
 
   const int64_t k_begin = by * a.kper;
   const int64_t k_end = min(a.K, k_begin + a.kper);
   const int nst = int((k_end - k_begin) / SK);
   const int64_t tok0 = bz * 16 * MT;
 
-  const __amdgpu_buffer_rsrc_t wres =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.W), 0, int(a.rows * a.K * EB), 0x00020000);
+  // Buffer resources; a stage at or past nst is loaded through a copy with
+  // num_records = 0, so every lane reads nothing and gets zeros.  The stage
+  // offset goes in the scalar offset: the per-lane offsets stay constant.
+  const int w_records = int(a.rows * a.K * EB);
+  auto wres_at = [&](int st) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.W), 0, st < nst ? w_records : 0, 0x00020000);
+  };
   int wsrc[NV];
   int wdst[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int v = j * kThreads + tid;
+    const int v = j * NT + tid;
     const int row = v / CPR;
     const int piece = v % CPR;
     int64_t r = tile_row<RTL>(a, row / 16, bx) + (row % 16);
@@ -399,8 +414,11 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
       aoff[q][1] = (r16 * CPR + ((p0 + 1) ^ r16)) * 16;
     }
   }
-  const __amdgpu_buffer_rsrc_t xres =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, int(a.M * a.ldx * 2), 0x00020000);
+  const int x_records = int(a.M * a.ldx * 2);
+  auto xres_at = [&](int st) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, st < nst ? x_records : 0, 0x00020000);
+  };
+  // a lane offset at or past every buffer's end: that lane reads nothing
   constexpr int kOutOfRange = 0x7FFFFFF0;
   // Register-direct X (not XL): token split reads one token row, K group q at
   // +q*64; K split reads one K group of token block b.  The lane's fragment
@@ -412,16 +430,16 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
     const int64_t m_x = min(tok0 + (blk + b) * 16 + r16, a.M - 1);
     xsrc[b] = int((m_x * a.ldx + k_begin + (4 * kq * QN + grp) * 16) * 2);
   }
-  // XL: piece i of a thread is piece (i*256 + tid) % 32 of token row
-  // (i*256 + tid) / 32 of the stage tile; rows past M read nothing.
+  // XL: piece i of a thread is piece (i*NT + tid) % 32 of token row
+  // (i*NT + tid) / 32 of the stage tile; rows past M read nothing.
   int xg[XL ? XNV : 1];
   int xdst[XL ? XNV : 1];
   int xfrag[2];  // XL: LDS offsets of the lane's two X fragments in token block 0
 #pragma unroll
   for (int i = 0; i < (XL ? XNV : 1); ++i) {
-    const int v = i * kThreads + tid;
+    const int v = i * NT + tid;
     const int row = v / 32, piece = v % 32;
-    xg[i] = tok0 + row < a.M ? int(((tok0 + row) * a.ldx + k_begin) * 2 + piece * 16) : -1;
+    xg[i] = tok0 + row < a.M ? int(((tok0 + row) * a.ldx + k_begin) * 2 + piece * 16) : kOutOfRange;
     xdst[i] = (row * 32 + (piece ^ (row & 15))) * 16;
   }
 #pragma unroll
@@ -435,116 +453,134 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
   for (int t = 0; t < S::ACC; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 wr[D][NV];
-  u32x4 xr[DX][XF][2];  // one stage of X: XF*2 pieces per lane in either layout
+  // One stage of X per ring slot: XR pieces per lane -- the lane's share of
+  // the stage tile (XL), or its fragments, piece 2q+h = K group q, half h.
+  constexpr int XR = XL ? XNV : 2 * XF;
+  u32x4 xr[DX][XR];
   auto load_w = [&](u32x4(&r)[NV], int st) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const int off = st < nst ? wsrc[j] + st * (SK * EB) : kOutOfRange;
-      r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 2 /* nt */));
+      r[j] = __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(wres_at(st), wsrc[j], st * (SK * EB), 2 /* nt */));
     }
   };
-  auto load_x = [&](u32x4(&x)[XF][2], int st) {
+  auto load_x = [&](u32x4(&x)[XR], int st) {
 #pragma unroll
-    for (int q = 0; q < XF; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int off;
-        if (XL) {
-          const int g = xg[2 * q + h];
-          off = (st < nst && g >= 0) ? g + st * SK * 2 : kOutOfRange;
-        } else {
-          off = st < nst ? (WK ? xsrc[q] + st * SK * 2 : xsrc[0] + (st * SK + q * 64) * 2) + 16 * h
-                         : kOutOfRange;
-        }
-        x[q][h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
-      }
+    for (int i = 0; i < XR; ++i) {
+      const int q = i / 2, h = i % 2;
+      const int off = XL ? xg[i] : (WK ? xsrc[q] : xsrc[0] + q * 64 * 2) + 16 * h;
+      x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres_at(st), off, st * SK * 2, 0));
+    }
   };
   auto store_w = [&](int buf, const u32x4(&r)[NV]) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) *reinterpret_cast<u32x4*>(lds + buf * TILE + wdst[j]) = r[j];
   };
-  auto store_x = [&](int buf, const u32x4(&x)[XF][2]) {
+  auto store_x = [&](int buf, const u32x4(&x)[XR]) {
 #pragma unroll
-    for (int q = 0; q < XF; ++q)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        *reinterpret_cast<u32x4*>(lds + 2 * TILE + buf * XT + xdst[2 * q + h]) = x[q][h];
+    for (int i = 0; i < XR; ++i) *reinterpret_cast<u32x4*>(lds + 2 * TILE + buf * XT + xdst[i]) = x[i];
   };
-  // W fragment of row tile t, K group q (token-split) or of the wave's K group
-  auto w_frag = [&](int buf, int t, int q, bf16x8& a0, bf16x8& a1) {
+  // The raw W fragments of row tile t, K group q (token split) or of the
+  // wave's K group: one 16-byte LDS read for FP8, two for BF16.
+  constexpr int FV = FP8 ? 1 : 2;
+  auto w_read = [&](int buf, int t, int q, u32x4 (&v)[FV]) {
     const uint8_t* base = lds + buf * TILE + t * kTileStride;
+#pragma unroll
+    for (int h = 0; h < FV; ++h) v[h] = *reinterpret_cast<const u32x4*>(base + aoff[q][h]);
+  };
+  auto w_widen = [&](const u32x4 (&v)[FV], bf16x8& a0, bf16x8& a1) {
     if (FP8) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(base + aoff[q][0]);
-      a0 = fp8x8_to_bf16(v[0], v[1]);
-      a1 = fp8x8_to_bf16(v[2], v[3]);
+      a0 = fp8x8_to_bf16(v[0][0], v[0][1]);
+      a1 = fp8x8_to_bf16(v[0][2], v[0][3]);
     } else {
-      a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][0]));
-      a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(base + aoff[q][1]));
+      a0 = as_bf16x8(v[0]);
+      a1 = as_bf16x8(v[FV - 1]);
     }
   };
-  auto compute = [&](int buf, const u32x4(&x)[XF][2]) {
+  // The fragment reads of all row tiles are issued before the first
+  // conversion, so the LDS latency is paid once per K group rather than once
+  // per row tile.
+  auto compute = [&](int buf, const u32x4(&x)[XR]) {
     if (WK) {
-      // each W fragment is read and widened once and used by every token block
+      // each W fragment is read and widened once and used by every token
+      // block; the fragments are read in groups of at most 4 row tiles
+      constexpr int TG = RTW < 4 ? RTW : 4;
       u32x4 xf[MT][2];
 #pragma unroll
-      for (int b = 0; b < MT; ++b)
+      for (int t0 = 0; t0 < RTW; t0 += TG) {
+        u32x4 wv[TG][FV];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          xf[b][h] = XL ? *reinterpret_cast<const u32x4*>(lds + 2 * TILE + buf * XT + b * 16 * 512 + xfrag[h])
-                        : x[b][h];
+        for (int t = 0; t < TG; ++t) w_read(buf, rh * RTW + t0 + t, 0, wv[t]);
+        if (t0 == 0) {
 #pragma unroll
-      for (int t = 0; t < RTL; ++t) {
-        bf16x8 a0, a1;
-        w_frag(buf, t, 0, a0, a1);
+          for (int b = 0; b < MT; ++b)
 #pragma unroll
-        for (int b = 0; b < MT; ++b) {
-          f32x4& c = acc[t * (WK ? MT : 1) + b];
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(xf[b][0]), c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(xf[b][1]), c, 0, 0, 0);
+            for (int h = 0; h < 2; ++h)
+              xf[b][h] = XL ? *reinterpret_cast<const u32x4*>(lds + 2 * TILE + buf * XT + b * 16 * 512 + xfrag[h])
+                            : x[XL ? 0 : 2 * b + h];
+        }
+#pragma unroll
+        for (int t = 0; t < TG; ++t) {
+          bf16x8 a0, a1;
+          w_widen(wv[t], a0, a1);
+#pragma unroll
+          for (int b = 0; b < MT; ++b) {
+            f32x4& c = acc[(t0 + t) * MT + b];
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(xf[b][0]), c, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(xf[b][1]), c, 0, 0, 0);
+          }
         }
       }
     } else {
+      // token split: one K group's fragments at a time (QN groups per stage)
 #pragma unroll
-      for (int q = 0; q < QN; ++q)
+      for (int q = 0; q < QN; ++q) {
+        u32x4 wv[RTL][FV];
+#pragma unroll
+        for (int t = 0; t < RTL; ++t) w_read(buf, t, q, wv[t]);
 #pragma unroll
         for (int t = 0; t < RTL; ++t) {
           bf16x8 a0, a1;
-          w_frag(buf, t, q, a0, a1);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[q][0]), acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[q][1]), acc[t], 0, 0, 0);
+          w_widen(wv[t], a0, a1);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(x[2 * q]), acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(x[2 * q + 1]), acc[t], 0, 0, 0);
         }
+      }
     }
   };
 
-  // Stage s uses W slot s % D, X slot s % DX and LDS buffer s % 2.  Step s
-  // refills the W slot with stage s + D and then the X slot with stage s + DX,
-  // so the wait for X of a stage never reaches further than D - DX stages of
-  // weights ahead.  The prologue issues the same pattern for the virtual steps
-  // -D .. -1, so the wait counts at the loop head are the same on entry and on
-  // every repeat.
+  // Stage s uses W slot s % D, X slot s % DX and LDS buffer s % 2.  The
+  // prologue loads stages 0 .. D-1 and writes stage 0 to LDS.  Step s then
+  // reads stage s from LDS and multiplies it while the same waves write
+  // stage s + 1 into the other buffer and refill its register slot with stage
+  // s + 1 + D; one barrier per step closes both.  The LDS writes, the
+  // fragment reads and the MFMAs of a step thus overlap instead of running
+  // one after the other in every wave.
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     load_w(wr[j], j);
     if (j + DX - D >= 0) load_x(xr[(j + DX - D) % DX], j + DX - D);
     __builtin_amdgcn_sched_barrier(0);
   }
+  store_w(0, wr[0]);
+  if (XL) store_x(0, xr[0]);
+  load_w(wr[0], D);
+  if (XL) load_x(xr[0], DX);
+  __syncthreads();
 
   // The loop is unrolled D times so every register index is a compile-time
   // constant.  Full groups of D stages run without any branch (one back edge
   // keeps the wait counts exact); the last partial group runs in a tail.
-  // LDS buffer j&1 was last read two stages ago, before the last barrier.
+  // Stages past the end were loaded as zeros and are written but never read.
   auto step = [&](const int j, const int s) {
-    store_w(j & 1, wr[j]);
-    if (XL) store_x(j & 1, xr[j % DX]);
+    const int n = (j + 1) % D;  // register slot of stage s + 1
+    compute(j & 1, xr[j % DX]);
+    if (!XL) load_x(xr[j % DX], s + DX);
+    store_w((j + 1) & 1, wr[n]);
+    if (XL) store_x((j + 1) & 1, xr[n % DX]);
+    load_w(wr[n], s + 1 + D);
+    if (XL) load_x(xr[n % DX], s + 1 + DX);
     __syncthreads();
-    load_w(wr[j], s + D);
-    if (XL) {
-      load_x(xr[j % DX], s + DX);
-      compute(j & 1, xr[j % DX]);
-    } else {
-      compute(j & 1, xr[j % DX]);
-      load_x(xr[j % DX], s + DX);
-    }
   };
   int s0 = 0;
   for (; s0 + D <= nst; s0 += D) {
@@ -554,25 +590,25 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
 #pragma unroll
   for (int j = 0; j < D; ++j)
     if (s0 + j < nst) step(j, s0 + j);
-  __syncthreads();  // every wave is done with the W tiles before LDS is reused
 
   float* red = reinterpret_cast<float*>(lds);
+  constexpr int TW = WK ? RTW : RTL;
 #pragma unroll
-  for (int t = 0; t < RTL; ++t)
+  for (int t = 0; t < TW; ++t)
 #pragma unroll
     for (int b = 0; b < (WK ? MT : 1); ++b)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        red[(((kq * RTL + t) * MT + blk + b) * 4 + v) * 64 + lane] = acc[t * (WK ? MT : 1) + b][v];
+        red[(((kq * RTL + rh * TW + t) * MT + blk + b) * 4 + v) * 64 + lane] = acc[t * (WK ? MT : 1) + b][v];
   __syncthreads();
-  finish_tile<MT, RTL, KQ>(a, red, tok0, bx, by);
+  finish_tile<MT, RTL, KQ, NT>(a, red, tok0, bx, by);
 }
 
-template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK>
-__global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, WK, XL, SK>::OCC)) void staged_gemm_kernel(
+template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK, int NW = kWaves>
+__global__ __launch_bounds__(64 * NW, (StagedShape<MT, RTL, FP8, WK, XL, SK, NW>::OCC)) void staged_gemm_kernel(
     StreamArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[StagedShape<MT, RTL, FP8, WK, XL, SK>::LDS];
-  staged_body<MT, RTL, FP8, WK, XL, SK>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StagedShape<MT, RTL, FP8, WK, XL, SK, NW>::LDS];
+  staged_body<MT, RTL, FP8, WK, XL, SK, NW>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Several projections in one launch (the views of one reassembled layer):
@@ -718,9 +754,9 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
   if (plan.kind == 3)
     return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
-  if (plan.kind == 5) {
-    // staged with K-split waves and X through LDS: 2 or 4 token blocks;
-    // 64-row blocks, 128 for FP8
+  if (plan.kind == 5 || plan.kind == 6) {
+    // staged with K-split waves and X through LDS (kind 6: eight waves, two
+    // row halves): 2 or 4 token blocks; 64-row blocks, 128 for FP8
     if (plan.mt != 2 && plan.mt != 4) return false;
     if (!(plan.rt == 4 || (plan.rt == 8 && p.dtype == SWR_FP8_E4M3FN))) return false;
     if (silu_mode && inter % (8 * plan.rt) != 0) return false;
@@ -778,11 +814,14 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       plan.rt = (plan.mt > 1 && fp8 && inter % 64 == 0) ? 8 : (inter % 32 == 0 ? 4 : 2);
     else
       plan.rt = plan.mt == 1 ? 2 : 4;
-    // 33-64 tokens of FP8 weights: K-split waves with X through LDS (each
-    // weight byte widened once, X read in whole cache lines)
-    if (plan.mt == 4 && fp8 && (!silu_mode || inter % 32 == 0)) {
-      plan.kind = 5;
-      if (silu_mode && inter % 64 != 0) plan.rt = 4;
+    // 17-64 tokens of FP8 weights: eight K-split waves in two row halves
+    // with X through LDS (each weight byte widened once, X read in whole
+    // cache lines, two waves per SIMD to cover each other's waits); 128-row
+    // blocks.  Measured on the shared-expert shapes against four waves:
+    // gate_up 41.9 vs 55.8 us and down 35.4 vs 41.2 us at 64 tokens.
+    if (plan.mt >= 2 && fp8 && (!silu_mode || inter % 32 == 0)) {
+      plan.kind = 6;
+      plan.rt = (!silu_mode || inter % 64 == 0) ? 8 : 4;
     }
     // One FP8 token block outside the SiLU mode (the down GEMM, projections):
     // 512-K stages halve the per-stage fixed cost (LDS round trip, barrier,
@@ -818,7 +857,7 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       t.rt = rt;
       if (kind != 2) t.sk = kStageK;
       if (const char* sk_env = getenv("SWR_SK")) t.sk = atoi(sk_env);
-      set_split(t, p, ks, (kind == 2 || kind == 5) ? t.sk : 256);
+      set_split(t, p, ks, (kind == 2 || kind == 5 || kind == 6) ? t.sk : 256);
       if (plan_is_valid(p, t)) plan = t;
     }
   }
@@ -828,10 +867,26 @@ GemmPlan plan_gemm(const GemmProblem& p) {
 
 namespace {
 
-template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK>
+template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK, int NW = kWaves>
 hipError_t launch_staged(const StreamArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((staged_gemm_kernel<MT, RTL, FP8, WK, XL, SK>), grid, dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((staged_gemm_kernel<MT, RTL, FP8, WK, XL, SK, NW>), grid, dim3(64 * NW), 0, stream, a);
   return hipGetLastError();
+}
+
+// Eight-wave K-split kernels with X through LDS: 2 or 4 token blocks, 64
+// rows, or 128 rows of FP8 weights.
+template <bool FP8>
+hipError_t dispatch_staged8(int mt, int rt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
+  if (mt == 2) {
+    if (rt == 4) return launch_staged<2, 4, FP8, true, true, kStageK, 8>(a, grid, stream);
+    if constexpr (FP8)
+      if (rt == 8) return launch_staged<2, 8, FP8, true, true, kStageK, 8>(a, grid, stream);
+  } else if (mt == 4) {
+    if (rt == 4) return launch_staged<4, 4, FP8, true, true, kStageK, 8>(a, grid, stream);
+    if constexpr (FP8)
+      if (rt == 8) return launch_staged<4, 8, FP8, true, true, kStageK, 8>(a, grid, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Instantiated (tile shape x sharing mode x stage length) combinations;
@@ -981,6 +1036,9 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
   else if (plan.kind == 5)
     e = fp8 ? dispatch_staged<true, true, true>(plan.mt, plan.rt, plan.sk, a, grid, stream)
             : dispatch_staged<false, true, true>(plan.mt, plan.rt, plan.sk, a, grid, stream);
+  else if (plan.kind == 6)
+    e = fp8 ? dispatch_staged8<true>(plan.mt, plan.rt, a, grid, stream)
+            : dispatch_staged8<false>(plan.mt, plan.rt, a, grid, stream);
   else
     e = fp8 ? dispatch_mt<4, true>(plan.mt, a, grid, stream) : dispatch_mt<4, false>(plan.mt, a, grid, stream);
   if (e != hipSuccess || plan.ksplit == 1) return e;
