@@ -16,6 +16,7 @@ struct StreamArgs {
   int64_t K;
   int64_t kper;   // K per workgroup split
   int64_t inter;  // I in SILU mode
+  int64_t rb;     // output rows per row block (gate rows in SILU mode), a multiple of 4
   void* Y;
   int64_t ldy;
   float* partial;  // [ksplit][M][rows] when ksplit > 1

@@ -102,15 +102,25 @@ __device__ inline void mma_step(const Step<MT, RT, FP8>& st, f32x4 (&acc)[RT][MT
   }
 }
 
-// Output row of tile t, lane-row r (0..15) of this workgroup.
+// First weight row of tile t of row block bx.  A row block holds a.rb
+// output rows (gate rows and as many up rows in SILU mode), which may be
+// fewer than its RT tiles cover: rows past the block's end are masked.
 template <int RT>
 __device__ inline int64_t tile_row(const StreamArgs& a, int t, int64_t bx) {
   if (a.mode == OUT_SILU_BF16) {
     constexpr int half = RT / 2;
-    const int64_t j0 = bx * 16 * half;
+    const int64_t j0 = bx * a.rb;
     return t < half ? j0 + t * 16 : a.inter + j0 + (t - half) * 16;
   }
-  return bx * 16 * RT + t * 16;
+  return bx * a.rb + t * 16;
+}
+
+// End (exclusive) of the output rows of row block bx: weight rows for plain
+// modes, gate indices j in SILU mode (gate row j and up row I + j).
+__device__ inline int64_t block_row_end(const StreamArgs& a, int64_t bx) {
+  const int64_t end = (bx + 1) * a.rb;
+  const int64_t cols = a.mode == OUT_SILU_BF16 ? a.inter : a.rows;
+  return end < cols ? end : cols;
 }
 
 __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, const float (&v)[4], bool bf16_out) {
@@ -154,6 +164,8 @@ __device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_
     const int64_t tok = tok0 + b * 16 + (ql & 15);
     if (tok >= a.M) continue;
     const int64_t row = tile_row<RT>(a, t, bx) + 4 * (ql >> 4);
+    // masked rows of a short row block belong to the next block
+    if (row >= block_row_end(a, bx)) continue;
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -300,6 +312,23 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 //   * loads go through buffer resources; a prefetch past the workgroup's last
 //     stage gets an out-of-range offset and reads nothing, so the unrolled
 //     main loop has no branches and the compiler's wait counts stay exact.
+// Workgroups per CU of a staged kernel: two where registers (about 196 next
+// to the accumulators) and LDS allow, otherwise one -- the accumulators then
+// sit in AGPRs and the rings get about 220 VGPRs.  One 16-token block over 32
+// or fewer rows (the down GEMM and small views at decode) has few
+// workgroups, so each keeps a deep ring instead; eight waves fill a CU.
+constexpr int staged_occupancy(int MT, int RTL, bool FP8, bool WK, bool XL, int SK, int NW) {
+  const int EB = FP8 ? 1 : 2;
+  const int TILE = 16 * RTL * SK * EB;
+  const int XT = XL ? 16 * MT * SK * 2 : 0;
+  const int KQ = WK ? 4 : 4 / MT;
+  const int ACC = WK ? (RTL / (NW / 4)) * MT : RTL;
+  const int RED = KQ * RTL * MT * 4 * 64 * 4;
+  const int LDS = (2 * TILE + 2 * XT) > RED ? (2 * TILE + 2 * XT) : RED;
+  const bool DEEP = MT == 1 && RTL <= 2;
+  return (NW == 8 || DEEP || ACC >= 16 || LDS > 80 * 1024) ? 1 : 2;
+}
+
 template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK, int NW = kWaves>
 struct StagedShape {
   static_assert(!XL || WK, "X tiles in LDS go with K-split waves");
@@ -323,16 +352,10 @@ struct StagedShape {
   static constexpr int WS = 4 * NV;                     // VGPRs of one stage of W pieces
   static constexpr int RED = KQ * RTL * MT * 4 * 64 * 4;  // bytes of the final cross-wave sum
   static constexpr int LDS = (2 * TILE + 2 * XT) > RED ? (2 * TILE + 2 * XT) : RED;
-  // Two waves per SIMD (two workgroups per CU) where registers (about 196
-  // next to the accumulators) and LDS allow.  Otherwise one: the accumulators
-  // then sit in AGPRs and the rings get about 220 VGPRs (less the X
-  // fragments read from LDS).
-  // One 16-token block over 32 or fewer rows (the down GEMM and small views
-  // at decode) has few workgroups, so each keeps a deep ring instead.
-  // Eight waves (two per SIMD, one workgroup per CU): 256 registers per wave,
-  // the accumulators in AGPRs, and the rings get what the fragments leave.
+  // Register budget of the rings (VGPRs): with eight waves (two per SIMD)
+  // 256 registers per wave less the accumulators and fragments.
   static constexpr bool DEEP = MT == 1 && RTL <= 2;
-  static constexpr int OCC = (NW == 8 || DEEP || ACC >= 16 || LDS > 80 * 1024) ? 1 : 2;
+  static constexpr int OCC = staged_occupancy(MT, RTL, FP8, WK, XL, SK, NW);
   static constexpr int FREE = NW == 8 ? 256 - 4 * ACC - 52 - 8 * MT - 16
                                       : (OCC == 2 ? 196 - 4 * ACC : (DEEP ? 440 - 4 * ACC : 220 - (XL ? 8 * MT : 0)));
   static constexpr int WCAP = OCC == 2 || NW == 8 ? 112 : 128;
@@ -385,6 +408,8 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
   auto wres_at = [&](int st) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.W), 0, st < nst ? w_records : 0, 0x00020000);
   };
+  // a lane offset at or past every buffer's end: that lane reads nothing
+  constexpr int kOutOfRange = 0x7FFFFFF0;
   int wsrc[NV];
   int wdst[NV];
 #pragma unroll
@@ -392,9 +417,11 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
     const int v = j * NT + tid;
     const int row = v / CPR;
     const int piece = v % CPR;
-    int64_t r = tile_row<RTL>(a, row / 16, bx) + (row % 16);
-    r = min(r, a.rows - 1);  // rows past the end are loaded from the last row and never stored
-    wsrc[j] = int((r * a.K + k_begin) * EB + piece * 16);
+    const int64_t r = tile_row<RTL>(a, row / 16, bx) + (row % 16);
+    // rows past the row block (or the matrix) read nothing and are never stored
+    const bool up_tile = a.mode == OUT_SILU_BF16 && row / 16 >= RTL / 2;
+    const int64_t j_out = up_tile ? r - a.inter : r;
+    wsrc[j] = j_out < block_row_end(a, bx) ? int((r * a.K + k_begin) * EB + piece * 16) : kOutOfRange;
     wdst[j] = (row * CPR + (piece ^ (row & 15))) * 16;
   }
   // A-fragment LDS offsets for row tile 0 (tile t adds t * 16 rows): K group
@@ -418,8 +445,6 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
   auto xres_at = [&](int st) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, st < nst ? x_records : 0, 0x00020000);
   };
-  // a lane offset at or past every buffer's end: that lane reads nothing
-  constexpr int kOutOfRange = 0x7FFFFFF0;
   // Register-direct X (not XL): token split reads one token row, K group q at
   // +q*64; K split reads one K group of token block b.  The lane's fragment
   // is k = 16*grp .. 16*grp+15 of the group, token row r16 of the block.
@@ -729,9 +754,33 @@ hipError_t dispatch_mt(int mt, const StreamArgs& a, dim3 grid, hipStream_t strea
 
 namespace {
 
-int64_t row_blocks_of(const GemmProblem& p, int rt) {
-  if (p.mode == OUT_SILU_BF16) return (p.rows / 2) / (8 * rt);
-  return (p.rows + 16 * rt - 1) / (16 * rt);
+// Output rows of a full row block of rt tiles (gate rows in SILU mode).
+int64_t full_rows(const GemmProblem& p, int rt) { return p.mode == OUT_SILU_BF16 ? 8 * rt : 16 * rt; }
+
+int64_t row_blocks_of(const GemmProblem& p, int64_t rb) {
+  const int64_t cols = p.mode == OUT_SILU_BF16 ? p.rows / 2 : p.rows;
+  return (cols + rb - 1) / rb;
+}
+
+// Shortens the row blocks of a staged plan so that its workgroups fill whole
+// waves of the CUs: with `slots` workgroups resident at once, the count is
+// rounded up to a multiple of `slots` by giving each row block fewer rows (a
+// multiple of 4, at least half the tiles' rows).  A CU that would otherwise
+// idle in the last wave takes a share instead; the masked rows cost LDS and
+// matrix-core work but no HBM bytes.
+void fill_slots(GemmPlan& plan, const GemmProblem& p, int64_t tok_blocks, int64_t slots) {
+  const int64_t cols = p.mode == OUT_SILU_BF16 ? p.rows / 2 : p.rows;
+  const int64_t full = full_rows(p, plan.rt);
+  const int64_t per_block = tok_blocks * plan.ksplit;  // workgroups per row block
+  if (per_block < 1 || slots < 1) return;              // no tokens: nothing to launch
+  const int64_t wgs = row_blocks_of(p, full) * per_block;
+  const int64_t waves = (wgs + slots - 1) / slots;
+  const int64_t blocks = waves * slots / per_block;  // row blocks that fit in those waves
+  if (blocks <= row_blocks_of(p, full)) return;
+  int64_t rb = (cols + blocks - 1) / blocks;
+  rb = (rb + 3) / 4 * 4;
+  if (rb >= full || 2 * rb < full || row_blocks_of(p, rb) * per_block > waves * slots) return;
+  plan.rb = rb;
 }
 
 // Fills ksplit/kper/partial_bytes for `ks` K splits of `granule`-element pieces.
@@ -754,6 +803,10 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
   if (plan.kind == 3)
     return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
+  // row blocks: whole tiles (the streaming kind), or a multiple of 4 rows
+  // up to the tiles' rows (staged kinds)
+  const int64_t full = full_rows(p, plan.rt);
+  if (plan.kind == 0 ? plan.rb != full : (plan.rb < 4 || plan.rb % 4 != 0 || plan.rb > full)) return false;
   if (plan.kind == 5 || plan.kind == 6) {
     // staged with K-split waves and X through LDS (kind 6: eight waves, two
     // row halves): 2 or 4 token blocks; 64-row blocks, 128 for FP8
@@ -829,17 +882,23 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     // slower on gate_up.
     plan.sk = (plan.kind == 2 && plan.mt == 1 && fp8 && !silu_mode && p.K % (2 * kStageK) == 0) ? 2 * kStageK
                                                                                                  : kStageK;
-    const int64_t wgs = row_blocks_of(p, plan.rt) * tok_blocks;
+    plan.rb = full_rows(p, plan.rt);
+    const int64_t wgs = row_blocks_of(p, plan.rb) * tok_blocks;
     const int64_t stages = p.K / plan.sk;
     int64_t ks = 1;
     if (p.M <= 64)
       while (wgs * ks < 160 && stages / (2 * ks) >= 4) ks *= 2;
     set_split(plan, p, ks, plan.sk);
+    // every CU busy to the end: 256 CUs times the kernel's workgroups per CU
+    const int occ = plan.kind == 6 ? staged_occupancy(plan.mt, plan.rt, fp8, true, true, plan.sk, 8)
+                                   : staged_occupancy(plan.mt, plan.rt, fp8, false, false, plan.sk, kWaves);
+    fill_slots(plan, p, tok_blocks, 256 * int64_t(occ));
   } else if (aligned_ok && p.K % kStepK == 0 && (!silu_mode || inter % 32 == 0)) {
     plan.kind = 0;
     plan.rt = 4;
+    plan.rb = full_rows(p, 4);
     int64_t ks = 1;
-    if (p.M <= 64) ks = (512 + row_blocks_of(p, 4) - 1) / row_blocks_of(p, 4);
+    if (p.M <= 64) ks = (512 + row_blocks_of(p, plan.rb) - 1) / row_blocks_of(p, plan.rb);
     set_split(plan, p, ks, 256);
   } else {
     plan.kind = 1;
@@ -855,9 +914,17 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       GemmPlan t = plan;
       t.kind = kind;
       t.rt = rt;
+      t.rb = full_rows(p, rt);
+      if (const char* rb_env = getenv("SWR_RB")) t.rb = atoi(rb_env);
       if (kind != 2) t.sk = kStageK;
       if (const char* sk_env = getenv("SWR_SK")) t.sk = atoi(sk_env);
       set_split(t, p, ks, (kind == 2 || kind == 5 || kind == 6) ? t.sk : 256);
+      if (getenv("SWR_FILL") && (kind == 2 || kind == 6)) {
+        const bool f8 = p.dtype == SWR_FP8_E4M3FN;
+        const int occ = kind == 6 ? staged_occupancy(t.mt, t.rt, f8, true, true, t.sk, 8)
+                                  : staged_occupancy(t.mt, t.rt, f8, false, false, t.sk, kWaves);
+        fill_slots(t, p, tok_blocks, 256 * int64_t(occ));
+      }
       if (plan_is_valid(p, t)) plan = t;
     }
   }
@@ -941,7 +1008,7 @@ hipError_t dispatch_staged(int mt, int rt, int sk, const StreamArgs& a, dim3 gri
 
 namespace {
 
-StreamArgs make_args(const GemmProblem& p, int64_t kper, int ksplit, float* partial) {
+StreamArgs make_args(const GemmProblem& p, int64_t kper, int ksplit, float* partial, int64_t rb) {
   StreamArgs a{};
   a.W = static_cast<const uint8_t*>(p.W);
   a.scale = p.scale;
@@ -952,6 +1019,7 @@ StreamArgs make_args(const GemmProblem& p, int64_t kper, int ksplit, float* part
   a.K = p.K;
   a.kper = kper;
   a.inter = p.mode == OUT_SILU_BF16 ? p.rows / 2 : 0;
+  a.rb = rb;
   a.Y = p.Y;
   a.ldy = p.ldy;
   a.partial = partial;
@@ -1000,7 +1068,7 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
   int first = 0;
   for (int i = 0; i < n; ++i) {
     const GemmProblem& p = ps[order[i]];
-    ga.g[i] = make_args(p, p.K, 1, nullptr);
+    ga.g[i] = make_args(p, p.K, 1, nullptr, full_rows(p, rt));
     ga.first[i] = first;
     first += int((p.rows + 16 * rt - 1) / (16 * rt));
   }
@@ -1016,7 +1084,7 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
 }
 
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream) {
-  StreamArgs a = make_args(p, plan.kper, plan.ksplit, partial);
+  StreamArgs a = make_args(p, plan.kper, plan.ksplit, partial, plan.rb);
   const bool fp8 = p.dtype == SWR_FP8_E4M3FN;
   if (plan.kind == 1) {
     const int64_t cols = p.mode == OUT_SILU_BF16 ? a.inter : p.rows;
@@ -1026,7 +1094,7 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
     return hipGetLastError();
   }
   if (plan.kind == 3) return launch_tile_gemm(a, plan.rt, fp8, stream);
-  const int64_t row_blocks = row_blocks_of(p, plan.rt);
+  const int64_t row_blocks = row_blocks_of(p, plan.rb);
   const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
   const dim3 grid = dim3(unsigned(row_blocks), unsigned(plan.ksplit), unsigned(tok_blocks));
   hipError_t e;

@@ -84,6 +84,8 @@ struct GemmPlan {
                  // 6 as 5 with eight waves in two row halves
   int mt;        // 16-token blocks per workgroup (1, 2, 4)
   int rt;        // 16-row tiles per workgroup (kind 3: weight rows per tile, 128 or 256)
+  int64_t rb;    // output rows per row block, a multiple of 4 up to the rt tiles' rows
+                 // (gate rows in SILU mode); fewer masks the tiles' last rows
   int ksplit;    // workgroups along K
   int64_t kper;  // K elements per split (multiple of the stage length)
   int sk;        // staged kinds: K elements per stage (256, or 512 for one FP8 token block)

@@ -207,6 +207,22 @@ def test_grouped_workspace_bytes():
         swr.proj_workspace_bytes(65, o, k, "fp8_e4m3fn") for (_, _, _, _, o, k, _, _, _) in stageable)
 
 
+def test_planner_handles_every_token_count():
+    """The GEMM planner runs on the host before any launch: no token count or
+    shape of the workloads may trip it (zero tokens included)."""
+    L = swr.lib()
+    a = 1 << 20
+    shapes = [(6144, 14336), (28672, 6144), (24576, 7168), (1000, 7168), (100, 128), (320, 512), (96, 256)]
+    for m in (0, 1, 2, 8, 16, 17, 31, 32, 33, 63, 64, 65):
+        for out_f, in_f in shapes:
+            for dt in ("bf16", "fp8_e4m3fn"):
+                assert swr.proj_workspace_bytes(m, out_f, in_f, dt) >= 0
+        assert swr.mlp_workspace_bytes(m, 6144, 14336, "fp8_e4m3fn") >= 0
+    # zero tokens through the grouped entry: separate-launch planning, nothing enqueued
+    descs = _descs([(a, a, a, a, 320, 512, 512, 320, swr.FP8_E4M3FN)])
+    assert L.swr_proj_grouped_workspace_bytes(descs, 1, 0) >= 0
+
+
 def test_mlp_workspace_covers_h():
     for m in (1, 8, 32, 64, 100):
         for dt in ("bf16", "fp8_e4m3fn"):
