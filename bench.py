@@ -50,6 +50,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=str, default="1,8,32,64")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: its own count)")
+    ap.add_argument("--gate", choices=["done", "begin"], default="done",
+                    help="decode: what the gather of layer l+1 waits for -- layer l-1 being done (the pages' gate) "
+                         "or the compute stream beginning layer l")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--minimal", action="store_true",
                     help="only the pipelined steps and isolated kernels (no serial, DMA, tensor-parallel or graph "
@@ -127,6 +130,8 @@ def main() -> int:
     if L % 2 == 0:
         # forwards run back to back: each gathers the next one's first layer during its last layer
         planner.set_cyclic(True)
+    gate_of = {"begin": swr.GATE_BEGIN, "done": swr.GATE_DONE}
+    planner.set_gate(gate_of[args.gate])
     o_gu, o_d = views[0]["offset"], views[1]["offset"]
 
     def forward(m: int, gemm_events=None, pl=None) -> None:
@@ -282,11 +287,11 @@ def main() -> int:
                            "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
         planner.set_copy_engine(swr.ENGINE_KERNEL)
 
-        # ---------------------------------------------------------------- begin gate
-        # the same pipelined forwards with SWR_GATE_BEGIN (the gather of l+1
-        # waits for the compute stream to begin layer l), without timing events
-        gate_begin = {}
-        planner.set_gate(swr.GATE_BEGIN)
+        # ---------------------------------------------------------------- the other gate
+        # the same pipelined forwards with the other gate, without timing events
+        other = "done" if args.gate == "begin" else "begin"
+        gate_begin = {"gate": other}
+        planner.set_gate(gate_of[other])
         for m in tokens:
             with torch.cuda.stream(compute):
                 forward(m)
@@ -297,7 +302,7 @@ def main() -> int:
                 e1.record(compute)
             torch.cuda.synchronize()
             gate_begin[str(m)] = {"pipelined_ms_per_forward": round(e0.elapsed_time(e1) / (dma_steps * 2), 4)}
-        planner.set_gate(swr.GATE_DONE)
+        planner.set_gate(gate_of[args.gate])
 
         # ---------------------------------------------------------------- tensor-parallel share
         # The PR report's alternative to weight sharding: each of R ranks (its
@@ -357,6 +362,7 @@ def main() -> int:
         # is self-contained, against the same planner run eagerly
         graph = {}
         gp = swr.Planner(0, L, compute, side, slot_a, slot_b)
+        gp.set_gate(gate_of[args.gate])
         for layer in range(L):
             gp.set_layer(layer, chunks[layer], C)
         reps = max(4, args.steps // 2)
@@ -466,14 +472,14 @@ def main() -> int:
         "data": "synthetic: seeded N(0,0.02) weights quantised per row to E4M3FN, N(0,1) bf16 tokens",
         "config": {
             "workload": wl.name, "hidden": H, "intermediate": I, "layers": L, "n_chunks": N,
-            "tokens": tokens, "layer_bytes": T, "chunk_bytes": C, "slots": 2,
+            "tokens": tokens, "layer_bytes": T, "chunk_bytes": C, "slots": 2, "gate": args.gate,
             "step": "pipelined forward (side-stream reassembly + MLP) over all layers for every M",
         },
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "per_tokens": per_m,
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1),
         "dma_engine_gather": dma,
-        "begin_gate": gate_begin,
+        "other_gate": gate_begin,
         "graph_replay_no_prefetch": graph,
         "tensor_parallel_share": {"ranks": R, "rank_weight_bytes_per_layer": rank_bytes, "per_tokens": tpres},
         "roofline": roofline,
