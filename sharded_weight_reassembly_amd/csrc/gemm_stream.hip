@@ -282,10 +282,14 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 // ---------------------------------------------------------------------------
 // Staged variant (K a multiple of 256).  Same arithmetic and output modes as
 // stream_gemm_kernel; the difference is how the operands reach the MFMAs:
-//   * a K stage is 256 elements; the workgroup's RB = 16*RTL rows x 256 K of
-//     W are loaded with consecutive threads on consecutive 16-byte pieces of a
-//     row, so one wave instruction reads 4 rows x 256 B (fp8) or 2 rows x
-//     512 B (bf16) -- long runs per DRAM page instead of 16 rows x 64 B;
+//   * a K stage is 256 elements (512 for one FP8 token block outside the SiLU
+//     mode); the workgroup's 16*RTL rows x one stage of W are loaded with
+//     consecutive threads on consecutive 16-byte pieces of a row, so one wave
+//     instruction reads 4 rows x 256 B (fp8) or 2 rows x 512 B (bf16) -- long
+//     runs per DRAM page instead of 16 rows x 64 B;
+//   * a row block may hold fewer output rows than its tiles (StreamArgs::rb):
+//     rows past its end read nothing and are never stored, which lets the
+//     planner make the workgroup count fill whole waves of the CUs;
 //   * HBM latency under full load is microseconds, so a skinny GEMM is bound
 //     by bytes in flight per CU: W pieces run D stages ahead in a register
 //     ring (tens of KB per workgroup); the activations, which come from L2,
@@ -293,25 +297,28 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 //   * each stage passes through a double-buffered LDS tile whose 16-byte
 //     pieces are XOR-swizzled by row (piece c of row r sits at
 //     r * CPR + (c ^ (r % 16))), so the MFMA fragment reads (16 rows, one
-//     piece each) hit 16 distinct bank groups;
-//   * three ways to share a stage between the 4 waves:
-//     - token split (WK = false): wave w works on token block w % MT and on
-//       MT of the stage's 4 groups of 64 K (group w / MT and on); each wave
-//       reads and widens the W pieces of its K groups, so with MT token
-//       blocks every W piece is widened MT times;
-//     - K split (WK): wave w works on K group w for every token block, so
-//       each W piece is read from LDS and widened once; the wave loads its
-//       own X fragments (16 token rows x 64 B per instruction);
-//     - K split with X in LDS (WK and XL): the stage's X tile (16*MT token
-//       rows x 512 B) is loaded with row-contiguous 16-byte pieces, which
-//       keeps the L2 -> CU traffic of X in whole cache lines, and passes
-//       through a second double-buffered LDS tile (piece p of token row r at
-//       r * 32 + (p ^ (r % 16))); at 32+ tokens this traffic, not the weight
-//       stream, is what bounds the kernel once every workgroup re-reads X;
-//     in the K-split modes the 4 waves add their sums in LDS at the end.
-//   * loads go through buffer resources; a prefetch past the workgroup's last
-//     stage gets an out-of-range offset and reads nothing, so the unrolled
-//     main loop has no branches and the compiler's wait counts stay exact.
+//     piece each) hit 16 distinct bank groups; a step multiplies stage s out
+//     of one buffer while it writes stage s + 1 into the other;
+//   * two ways to share a stage between the waves:
+//     - token split (4 waves, WK = false): wave w works on token block w % MT
+//       and on MT of the stage's 4 groups of 64 K (group w / MT and on); each
+//       wave reads and widens the W pieces of its K groups, so with MT token
+//       blocks every W piece is widened MT times -- the mode for one token
+//       block, where it is a pure K split;
+//     - K split with X in LDS (WK and XL; 8 waves in two row halves for 2 or
+//       4 token blocks): wave w works on K group w % 4 of row half w / 4 for
+//       every token block, so each W piece is read from LDS and widened once;
+//       the stage's X tile (16*MT token rows x 512 B) is loaded with
+//       row-contiguous 16-byte pieces, which keeps the L2 -> CU traffic of X
+//       in whole cache lines, and passes through a second double-buffered LDS
+//       tile (piece p of token row r at r * 32 + (p ^ (r % 16))); two waves
+//       per SIMD cover each other's LDS and load latencies, and each holds
+//       half the accumulators;
+//     the waves of a K group add their sums in LDS at the end.
+//   * loads go through buffer resources with the stage offset in the scalar
+//     offset; a stage past the workgroup's last reads through a resource with
+//     no records and gets zeros, so the unrolled main loop has no branches and
+//     the compiler's wait counts stay exact.
 // Workgroups per CU of a staged kernel: two where registers (about 196 next
 // to the accumulators) and LDS allow, otherwise one -- the accumulators then
 // sit in AGPRs and the rings get about 220 VGPRs.  One 16-token block over 32
@@ -331,7 +338,7 @@ constexpr int staged_occupancy(int MT, int RTL, bool FP8, bool WK, bool XL, int 
 
 template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK = kStageK, int NW = kWaves>
 struct StagedShape {
-  static_assert(!XL || WK, "X tiles in LDS go with K-split waves");
+  static_assert(XL == WK, "K-split waves read X from LDS; token-split waves load their own");
   static_assert(SK == kStageK || (!WK && SK == 2 * kStageK), "longer stages only with token-split waves");
   static_assert(NW == 4 || (NW == 8 && WK && XL && RTL % 2 == 0), "8 waves: K split, X in LDS, two row halves");
   static constexpr int NT = 64 * NW;                   // threads per workgroup
@@ -445,16 +452,11 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
   auto xres_at = [&](int st) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, st < nst ? x_records : 0, 0x00020000);
   };
-  // Register-direct X (not XL): token split reads one token row, K group q at
-  // +q*64; K split reads one K group of token block b.  The lane's fragment
-  // is k = 16*grp .. 16*grp+15 of the group, token row r16 of the block.
-  constexpr int NXS = XL ? 1 : (WK ? MT : 1);
-  int xsrc[NXS];
-#pragma unroll
-  for (int b = 0; b < NXS; ++b) {
-    const int64_t m_x = min(tok0 + (blk + b) * 16 + r16, a.M - 1);
-    xsrc[b] = int((m_x * a.ldx + k_begin + (4 * kq * QN + grp) * 16) * 2);
-  }
+  // Register-direct X (token split): one token row, K group q at +q*64; the
+  // lane's fragment is k = 16*grp .. 16*grp+15 of the group, token row r16
+  // of the block.
+  const int64_t m_x = min(tok0 + blk * 16 + r16, a.M - 1);
+  const int xsrc = int((m_x * a.ldx + k_begin + (4 * kq * QN + grp) * 16) * 2);
   // XL: piece i of a thread is piece (i*NT + tid) % 32 of token row
   // (i*NT + tid) / 32 of the stage tile; rows past M read nothing.
   int xg[XL ? XNV : 1];
@@ -493,7 +495,7 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
 #pragma unroll
     for (int i = 0; i < XR; ++i) {
       const int q = i / 2, h = i % 2;
-      const int off = XL ? xg[i] : (WK ? xsrc[q] : xsrc[0] + q * 64 * 2) + 16 * h;
+      const int off = XL ? xg[i] : xsrc + q * 64 * 2 + 16 * h;
       x[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres_at(st), off, st * SK * 2, 0));
     }
   };
@@ -541,8 +543,7 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
           for (int b = 0; b < MT; ++b)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-              xf[b][h] = XL ? *reinterpret_cast<const u32x4*>(lds + 2 * TILE + buf * XT + b * 16 * 512 + xfrag[h])
-                            : x[XL ? 0 : 2 * b + h];
+              xf[b][h] = *reinterpret_cast<const u32x4*>(lds + 2 * TILE + buf * XT + b * 16 * 512 + xfrag[h]);
         }
 #pragma unroll
         for (int t = 0; t < TG; ++t) {
@@ -807,9 +808,9 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   // up to the tiles' rows (staged kinds)
   const int64_t full = full_rows(p, plan.rt);
   if (plan.kind == 0 ? plan.rb != full : (plan.rb < 4 || plan.rb % 4 != 0 || plan.rb > full)) return false;
-  if (plan.kind == 5 || plan.kind == 6) {
-    // staged with K-split waves and X through LDS (kind 6: eight waves, two
-    // row halves): 2 or 4 token blocks; 64-row blocks, 128 for FP8
+  if (plan.kind == 6) {
+    // staged with eight K-split waves in two row halves and X through LDS:
+    // 2 or 4 token blocks; 64-row blocks, 128 for FP8
     if (plan.mt != 2 && plan.mt != 4) return false;
     if (!(plan.rt == 4 || (plan.rt == 8 && p.dtype == SWR_FP8_E4M3FN))) return false;
     if (silu_mode && inter % (8 * plan.rt) != 0) return false;
@@ -918,7 +919,7 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       if (const char* rb_env = getenv("SWR_RB")) t.rb = atoi(rb_env);
       if (kind != 2) t.sk = kStageK;
       if (const char* sk_env = getenv("SWR_SK")) t.sk = atoi(sk_env);
-      set_split(t, p, ks, (kind == 2 || kind == 5 || kind == 6) ? t.sk : 256);
+      set_split(t, p, ks, (kind == 2 || kind == 6) ? t.sk : 256);
       if (getenv("SWR_FILL") && (kind == 2 || kind == 6)) {
         const bool f8 = p.dtype == SWR_FP8_E4M3FN;
         const int occ = kind == 6 ? staged_occupancy(t.mt, t.rt, f8, true, true, t.sk, 8)
@@ -1101,9 +1102,6 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
   if (plan.kind == 2)
     e = fp8 ? dispatch_staged<true, false, false>(plan.mt, plan.rt, plan.sk, a, grid, stream)
             : dispatch_staged<false, false, false>(plan.mt, plan.rt, plan.sk, a, grid, stream);
-  else if (plan.kind == 5)
-    e = fp8 ? dispatch_staged<true, true, true>(plan.mt, plan.rt, plan.sk, a, grid, stream)
-            : dispatch_staged<false, true, true>(plan.mt, plan.rt, plan.sk, a, grid, stream);
   else if (plan.kind == 6)
     e = fp8 ? dispatch_staged8<true>(plan.mt, plan.rt, a, grid, stream)
             : dispatch_staged8<false>(plan.mt, plan.rt, a, grid, stream);

@@ -80,8 +80,8 @@ struct GemmProblem {
 
 struct GemmPlan {
   int kind;      // 0 streaming MFMA, 1 generic, 2 LDS-staged MFMA (decode), 3 tiled MFMA (prefill),
-                 // 5 LDS-staged with waves split along K and X through LDS (decode, 33-64 tokens),
-                 // 6 as 5 with eight waves in two row halves
+                 // 6 LDS-staged with eight waves split along K in two row halves and X through
+                 // LDS (decode, 17-64 tokens)
   int mt;        // 16-token blocks per workgroup (1, 2, 4)
   int rt;        // 16-row tiles per workgroup (kind 3: weight rows per tile, 128 or 256)
   int64_t rb;    // output rows per row block, a multiple of 4 up to the rt tiles' rows
