@@ -65,6 +65,21 @@ def test_proj_parity(o, k, dt, m):
     assert_close_rows(values(y), ref, what=f"proj {o}x{k} {dt} m={m}")
 
 
+@pytest.mark.parametrize("o,k,m", [(4128, 512, 1), (4128, 512, 8), (7712, 2048, 17), (7712, 2048, 40),
+                                   (7712, 2048, 64)])
+def test_short_row_blocks(o, k, m):
+    """Shapes where the planner shortens row blocks to fill whole waves of CUs
+    and the last block is partial (4128 rows at <= 16 tokens: 20-row blocks,
+    the last of 8 rows; 7712 rows at 17-64 tokens: 64-row blocks of 128-row
+    tiles, the last of 32): every row is computed once and only once."""
+    note(f"short row blocks o={o} k={k} m={m}")
+    w = synth.weight(synth.seed_for(12, 1, o % 97), o, k, synth.FP8)
+    x = synth.activations(synth.seed_for(12, 1, 50), m, k)
+    y = _run_proj(w, x)
+    ref = gemm.proj_f64(x, w.raw(), synth.FP8, o, k, w.scale)
+    assert_close_rows(values(y), ref, what=f"short row blocks {o}x{k} m={m}")
+
+
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
 def test_bf16_output_is_rne_of_fp32_output(dt):
     note(f"rne check {dt}")

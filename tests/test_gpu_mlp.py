@@ -42,6 +42,20 @@ def test_mlp_parity(dt, hidden, inter, m):
     assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} {dt} m={m}")
 
 
+@pytest.mark.parametrize("hidden,inter,m", [(2048, 4128, 1), (2048, 4128, 40), (2048, 2144, 17), (2048, 2144, 64)])
+def test_short_row_blocks_silu(hidden, inter, m):
+    """gate_up shapes where the planner shortens row blocks (gate rows and the
+    matching up rows) to fill whole waves of CUs and the last block is
+    partial: 20 gate rows per block, the last of 8 (I = 4128) or 4 (I = 2144)."""
+    note(f"short silu row blocks h={hidden} i={inter} m={m}")
+    gu = synth.weight(synth.seed_for(13, 2, 0), 2 * inter, hidden, synth.FP8)
+    d = synth.weight(synth.seed_for(13, 2, 1), hidden, inter, synth.FP8)
+    x = synth.activations(synth.seed_for(13, 2, 50), m, hidden)
+    y = _mlp(gu, d, hidden, inter, x)
+    _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, synth.FP8, hidden, inter)
+    assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} m={m}")
+
+
 def test_tiny_config_mlp_and_projection():
     """The tiny workload: hidden 128, intermediate 256, BF16, 4 tokens, N=4 chunks,
     run through views of the reassembled slot."""
