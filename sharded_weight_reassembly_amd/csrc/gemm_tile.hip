@@ -4,17 +4,20 @@
 //
 // At thousands of tokens the weights are reused by every token block and the
 // product is bound by the matrix cores, so this is a classic LDS-tiled GEMM:
-//   * a workgroup (4 waves, 2 x 2) computes a 256-token x BN-row tile of Y;
-//     each wave a 128 x BN/2 sub-tile with v_mfma_f32_32x32x16_bf16 (tokens are
-//     the MFMA rows, weight rows the MFMA columns, so a lane's outputs run
-//     along a row of Y);
-//   * each 64-K step of X (bf16) and W is staged in LDS, double buffered, the
-//     next step's global loads in registers while the current one is
-//     multiplied; FP8 weight codes are widened to BF16 once, on the way into
-//     LDS (exact);
-//   * LDS rows are 128 B of 16-byte pieces; piece p of row r is stored at
-//     r * 8 + (p ^ ((r >> 1) & 7)), so the 32-row fragment reads of one MFMA
-//     hit distinct banks;
+//   * a workgroup computes a 256-token x BN-row tile of Y with 2 x WAVES/2
+//     waves; each wave a 128 x (2*BN/WAVES) sub-tile with
+//     v_mfma_f32_32x32x16_bf16 (tokens are the MFMA rows, weight rows the
+//     MFMA columns, so a lane's outputs run along a row of Y);
+//   * K advances in steps of 64; X is staged in LDS as bf16 rows of 128 B of
+//     16-byte pieces, piece p of row r at r * 8 + (p ^ ((r >> 1) & 7)), so the
+//     32-row fragment reads of one MFMA hit distinct banks;
+//   * BF16 weights: X and W of the next step are loaded into registers while
+//     the current step is multiplied, then written to a double-buffered LDS
+//     tile (tile_gemm_kernel);
+//   * FP8 weights: X and the raw FP8 codes go from memory straight into a
+//     three-stage LDS ring with buffer-to-LDS loads, two steps ahead of the
+//     MFMAs, with no staging registers (tile_gemm_fp8_kernel); the codes are
+//     widened to BF16 (exact) after the fragment read;
 //   * tiles are numbered so that each XCD (workgroups are dealt round-robin
 //     to the 8 XCDs) works through a compact group of 4 token blocks x all
 //     weight blocks, which keeps the X and W tiles of concurrently running
@@ -28,34 +31,22 @@ namespace swr {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kTileM = 256;
 constexpr int kGroupM = 4;  // token blocks per XCD group
 
 __device__ inline int swz(int row, int piece) { return row * 8 + (piece ^ ((row >> 1) & 7)); }
 
-template <int BN, bool FP8, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) {
-  constexpr int NT = 64 * WAVES;    // threads
-  constexpr int WGN = WAVES / 2;    // waves along the weight rows (2 along the tokens)
-  constexpr int WN = BN / WGN;      // weight rows per wave
-  constexpr int TM = 4;             // 32-token MFMA tiles per wave (128 tokens)
-  constexpr int TN = WN / 32;       // 32-row MFMA tiles per wave
-  constexpr int A_BYTES = kTileM * kTileK * 2;
-  constexpr int B_BYTES = BN * kTileK * 2;
-  constexpr int NA = A_BYTES / 16 / NT;             // X pieces per thread per step
-  constexpr int NB = FP8 ? BN * kTileK / 16 / NT     // fp8 pieces (16 codes) per thread
-                         : B_BYTES / 16 / NT;        // bf16 pieces per thread
-  static_assert(TN >= 1 && NA >= 1 && NB >= 1, "tile must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
+// Output tile of this workgroup: XCD-contiguous ranges, grouped by token blocks.
+struct TileCoord {
+  int64_t m0;      // first token
+  int64_t tile_n;  // weight-row block
+};
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
+template <int BN>
+__device__ inline TileCoord tile_coord(const StreamArgs& a) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
-
-  // ---- tile numbering: XCD-contiguous ranges, grouped by token blocks
   const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
   const int64_t cols = silu_mode ? a.inter : a.rows;  // output columns
   const int64_t col_tile = silu_mode ? BN / 2 : BN;
@@ -66,22 +57,92 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) 
   const int64_t group = t / (kGroupM * tiles_n);
   const int64_t first_m = group * kGroupM;
   const int64_t gsize = min<int64_t>(tiles_m - first_m, kGroupM);
-  const int64_t tile_m = first_m + (t % (kGroupM * tiles_n)) % gsize;
-  const int64_t tile_n = (t % (kGroupM * tiles_n)) / gsize;
+  TileCoord c;
+  c.m0 = (first_m + (t % (kGroupM * tiles_n)) % gsize) * kTileM;
+  c.tile_n = (t % (kGroupM * tiles_n)) / gsize;
+  return c;
+}
 
-  // weight row held by local B row c (0 <= c < BN)
-  auto w_row = [&](int c) -> int64_t {
-    if (silu_mode) {
-      const int half = c / WN;       // which wave column
-      const int c2 = c % WN;         // within the wave: first half gate, second half up
-      const int64_t j = tile_n * (BN / 2) + half * (WN / 2) + (c2 % (WN / 2));
-      return c2 < WN / 2 ? j : a.inter + j;
+// Weight row held by local B row c (0 <= c < BN) of weight block tile_n; WN
+// rows per wave column (SiLU mode: its first half gate rows, second half the
+// matching up rows).
+template <int BN, int WN>
+__device__ inline int64_t w_row(const StreamArgs& a, int64_t tile_n, int c) {
+  if (a.mode == OUT_SILU_BF16) {
+    const int half = c / WN;
+    const int c2 = c % WN;
+    const int64_t j = tile_n * (BN / 2) + half * (WN / 2) + (c2 % (WN / 2));
+    return c2 < WN / 2 ? j : a.inter + j;
+  }
+  return tile_n * BN + c;
+}
+
+// Epilogue: lane holds column c = l % 32 of each 32 x 32 tile, rows
+// 8*(v/4) + 4*(l/32) + v%4; scale, SiLU*up, rounding.
+template <int BN, int WN, int TM, int TN>
+__device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t tile_n,
+                                     int wm, int wn, int r32, int kg, const float* lds_scale = nullptr) {
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  const int tn_out = silu_mode ? TN / 2 : TN;
+#pragma unroll
+  for (int y = 0; y < tn_out; ++y) {
+    const int c = wn * WN + y * 32 + r32;                // local B row
+    const int64_t ocol = w_row<BN, WN>(a, tile_n, c);  // output column (gate index j in SiLU mode)
+    if (ocol >= (silu_mode ? a.inter : a.rows)) continue;
+    float sc = 1.f, su = 1.f;
+    if (lds_scale) {
+      // scales of local rows c and (SiLU mode) its up row c + WN / 2
+      sc = lds_scale[c];
+      if (silu_mode) su = lds_scale[c + WN / 2];
+    } else if (a.scale) {
+      sc = a.scale[ocol];
+      if (silu_mode) su = a.scale[a.inter + ocol];
     }
-    return tile_n * BN + c;
-  };
+#pragma unroll
+    for (int x = 0; x < TM; ++x) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * 128 + x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
+        if (m >= a.M) continue;
+        float out = acc[x][y][v] * sc;
+        if (silu_mode) {
+          const float u = acc[x][y + TN / 2][v] * su;
+          out = silu(out) * u;
+          static_cast<uint16_t*>(a.Y)[m * a.ldy + ocol] = bf16_bits(out);
+        } else if (a.mode == OUT_F32) {
+          static_cast<float*>(a.Y)[m * a.ldy + ocol] = out;
+        } else {
+          static_cast<uint16_t*>(a.Y)[m * a.ldy + ocol] = bf16_bits(out);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// BF16 weights: register-staged, double-buffered LDS.
+template <int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) {
+  constexpr int NT = 64 * WAVES;    // threads
+  constexpr int WGN = WAVES / 2;    // waves along the weight rows (2 along the tokens)
+  constexpr int WN = BN / WGN;      // weight rows per wave
+  constexpr int TM = 4;             // 32-token MFMA tiles per wave (128 tokens)
+  constexpr int TN = WN / 32;       // 32-row MFMA tiles per wave
+  constexpr int A_BYTES = kTileM * kTileK * 2;
+  constexpr int B_BYTES = BN * kTileK * 2;
+  constexpr int NA = A_BYTES / 16 / NT;  // X pieces per thread per step
+  constexpr int NB = B_BYTES / 16 / NT;  // W pieces per thread per step
+  static_assert(TN >= 1 && NA >= 1 && NB >= 1, "tile must split evenly over the workgroup");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const TileCoord tc = tile_coord<BN>(a);
+  const int64_t m0 = tc.m0;
 
   // ---- global -> register staging addresses
-  const int64_t m0 = tile_m * kTileM;
   const uint16_t* asrc[NA];
   int adst[NA];
 #pragma unroll
@@ -97,19 +158,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) 
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int v = j * NT + tid;
-    if (FP8) {
-      const int row = v / 4, q = v % 4;  // 16 codes = bf16 pieces 2q, 2q+1
-      int64_t r = w_row(row);
-      r = min(r, a.rows - 1);
-      bsrc[j] = a.W + r * a.K + q * 16;
-      bdst[j] = swz(row, 2 * q) * 16;  // piece 2q+1 goes to swz(row, 2q+1)
-    } else {
-      const int row = v / 8, piece = v % 8;
-      int64_t r = w_row(row);
-      r = min(r, a.rows - 1);
-      bsrc[j] = a.W + (r * a.K + piece * 8) * 2;
-      bdst[j] = swz(row, piece) * 16;
-    }
+    const int row = v / 8, piece = v % 8;
+    const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
+    bsrc[j] = a.W + (r * a.K + piece * 8) * 2;
+    bdst[j] = swz(row, piece) * 16;
   }
 
   u32x4 ra[NA], rb[NB];
@@ -118,7 +170,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) 
 #pragma unroll
     for (int j = 0; j < NA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(asrc[j] + k0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(bsrc[j] + k0 * (FP8 ? 1 : 2));
+    for (int j = 0; j < NB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(bsrc[j] + k0 * 2);
   };
   auto store = [&](int buf) {
     uint8_t* A = lds + buf * (A_BYTES + B_BYTES);
@@ -126,16 +178,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) 
 #pragma unroll
     for (int j = 0; j < NA; ++j) *reinterpret_cast<u32x4*>(A + adst[j]) = ra[j];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (FP8) {
-        const int v = j * NT + tid;
-        const int row = v / 4, q = v % 4;
-        *reinterpret_cast<bf16x8*>(B + bdst[j]) = fp8x8_to_bf16(rb[j][0], rb[j][1]);
-        *reinterpret_cast<bf16x8*>(B + swz(row, 2 * q + 1) * 16) = fp8x8_to_bf16(rb[j][2], rb[j][3]);
-      } else {
-        *reinterpret_cast<u32x4*>(B + bdst[j]) = rb[j];
-      }
-    }
+    for (int j = 0; j < NB; ++j) *reinterpret_cast<u32x4*>(B + bdst[j]) = rb[j];
   };
 
   // ---- fragment reads: k-step ks of buffer buf into F (A rows then B rows)
@@ -187,59 +230,211 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) 
     if (more) read_frags(buf ^ 1, 0, F[0]);
     __builtin_amdgcn_sched_barrier(0);
   }
-
-  // ---- epilogue: lane holds column c = l % 32 of each 32 x 32 tile, rows 8*(v/4) + 4*(l/32) + v%4
-  const int tn_out = silu_mode ? TN / 2 : TN;
-#pragma unroll
-  for (int y = 0; y < tn_out; ++y) {
-    const int c = wn * WN + y * 32 + r32;  // local B row
-    const int64_t orow = w_row(c);
-    int64_t ocol;  // output column
-    float sc = 1.f, su = 1.f;
-    bool col_ok;
-    if (silu_mode) {
-      ocol = orow;  // gate index j
-      col_ok = ocol < a.inter;
-      if (col_ok && a.scale) {
-        sc = a.scale[ocol];
-        su = a.scale[a.inter + ocol];
-      }
-    } else {
-      ocol = orow;
-      col_ok = ocol < a.rows;
-      if (col_ok && a.scale) sc = a.scale[ocol];
-    }
-    if (!col_ok) continue;
-#pragma unroll
-    for (int x = 0; x < TM; ++x) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 128 + x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
-        if (m >= a.M) continue;
-        float out = acc[x][y][v] * sc;
-        if (silu_mode) {
-          const float u = acc[x][y + TN / 2][v] * su;
-          out = silu(out) * u;
-          static_cast<uint16_t*>(a.Y)[m * a.ldy + ocol] = bf16_bits(out);
-        } else if (a.mode == OUT_F32) {
-          static_cast<float*>(a.Y)[m * a.ldy + ocol] = out;
-        } else {
-          static_cast<uint16_t*>(a.Y)[m * a.ldy + ocol] = bf16_bits(out);
-        }
-      }
-    }
-  }
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg);
 }
 
-template <int BN, bool FP8, int WAVES>
-hipError_t launch_bn(const StreamArgs& a, hipStream_t stream) {
+// ---------------------------------------------------------------------------
+// FP8 weights: both operands reach LDS by buffer-to-LDS loads (no staging
+// registers) through a three-stage ring, two k-steps ahead of the MFMAs.
+//   * X stage: 256 rows x 128 B (bf16), the swizzled layout above; a load
+//     instruction fills 1 KB = 8 rows, and each lane fetches the piece that
+//     belongs at its position (the swizzle is applied to the source address);
+//   * W stage: BN rows x 64 B of FP8 codes, piece q of row r at
+//     r * 4 + (q ^ ((r >> 2) & 3)); a load instruction fills 16 rows;
+//   * within each 32-K half s of a step, lane group g (0, 1) of an MFMA takes
+//     K = 32*s + 16*g + 8*h .. +7 in the MFMA pair h = 0, 1, for both
+//     operands: one 16-byte fragment read of 16 FP8 codes feeds both MFMAs
+//     of the pair (the sum over K does not depend on the order);
+//   * per step: wait until this wave's loads of step t have landed (loads
+//     complete in issue order), barrier, issue the loads of step t + 2 into
+//     the stage that step t - 1 read, multiply step t.
+constexpr int kStages = 3;
+
+__device__ inline int wswz(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
+
+// Raw buffer resource (base, no stride, num_records bytes) in scalar registers.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ inline u32x4s raw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4s r;
+  r[0] = uint32_t(p);
+  r[1] = uint32_t(p >> 32) & 0xFFFFu;  // stride 0
+  r[2] = uint32_t(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 16-byte buffer-to-LDS load per lane: lane l's bytes land at lds + 16*l
+// (the wave-uniform base goes in M0).  Written as assembly so that the
+// compiler adds no waits of its own for it: this kernel orders these loads
+// itself (wait_vm before each barrier).  NT selects the streaming hint.  M0
+// is set here and holds nothing else in this kernel (no other instruction in
+// it reads M0; checked in its ISA).
+template <bool NT>
+__device__ inline void lds_load16(const u32x4s& res, uint8_t* lds, int voffset, int soffset) {
+  // the base is the same in every lane of the wave
+  const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds)));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 :
+                 : "s"(base), "v"(voffset), "s"(res), "s"(soffset)
+                 : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(base), "v"(voffset), "s"(res), "s"(soffset)
+                 : "memory");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  // s_waitcnt with vmcnt = N and the other counters at their maximum
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs a) {
+  constexpr int WGN = WAVES / 2;
+  constexpr int WN = BN / WGN;
+  constexpr int TM = 4;
+  constexpr int TN = WN / 32;
+  constexpr int A_BYTES = kTileM * kTileK * 2;  // 32 KB
+  constexpr int B_BYTES = BN * kTileK;          // FP8 codes
+  constexpr int NA = A_BYTES / 1024 / WAVES;    // 1 KB loads of X per wave per stage
+  constexpr int NB = B_BYTES / 1024 / WAVES;    // 1 KB loads of W per wave per stage
+  static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
+                "stage must split into whole 1 KB loads per wave");
+  // one array per stage, so the compiler can tell the stages' loads apart
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[B_BYTES];
+  // The row scales of the workgroup's weight rows, for the epilogue.  Being
+  // the most aligned, this array sits at the start of LDS: a stage array
+  // there would have its reads wait for every load in flight, because the
+  // compiler cannot tell an access at the base of LDS from the others.
+  __shared__ __attribute__((aligned(4096))) float row_scale[BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const TileCoord tc = tile_coord<BN>(a);
+  const int64_t m0 = tc.m0;
+  for (int c = tid; c < BN; c += 64 * WAVES) {
+    const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
+    row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
+  }
+
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * 2);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K);
+  // Source offsets of this lane's pieces (step 0); rows past the end are
+  // read from the last row and never stored.
+  int aoff[NA], boff[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = (wave * NA + i) * 8 + lane / 8;
+    const int piece = (lane % 8) ^ ((row >> 1) & 7);
+    const int64_t m = min(m0 + row, a.M - 1);
+    aoff[i] = int((m * a.ldx + piece * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = (wave * NB + i) * 16 + lane / 4;
+    const int q = (lane % 4) ^ ((row >> 2) & 3);
+    const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
+    boff[i] = int(r * a.K + q * 16);
+  }
+  auto issue = [&](uint8_t* A, uint8_t* B, int kt) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kt * kTileK * 2);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_load16<true>(wres, B + (wave * NB + i) * 1024, boff[i], kt * kTileK);
+  };
+
+  const int r32 = lane & 31, kg = lane >> 5;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int x = 0; x < TM; ++x)
+#pragma unroll
+    for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
+
+  // one step of stage (A, B): two 32-K halves, each an MFMA pair
+  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 wraw[TN];
+#pragma unroll
+      for (int y = 0; y < TN; ++y) {
+        const int row = wn * WN + y * 32 + r32;
+        wraw[y] = *reinterpret_cast<const u32x4*>(B + wswz(row, 2 * s + kg) * 16);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 fa[TM], fb[TN];
+#pragma unroll
+        for (int x = 0; x < TM; ++x)
+          fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
+#pragma unroll
+        for (int y = 0; y < TN; ++y) fb[y] = fp8x8_to_bf16(wraw[y][2 * h], wraw[y][2 * h + 1]);
+#pragma unroll
+        for (int x = 0; x < TM; ++x)
+#pragma unroll
+          for (int y = 0; y < TN; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+      }
+    }
+  };
+
+  constexpr int kLoads = NA + NB;  // loads per wave per step
+  const int nk = int(a.K / kTileK);
+  // prologue: steps 0 and 1 in flight
+  issue(a0, b0, 0);
+  if (nk > 1) issue(a1, b1, 1);
+
+  // Step t uses stage t % 3; the loop is unrolled by the ring so every stage
+  // is a fixed array.  A step opens with the wait for its own loads (those
+  // of step t + 1 may stay in flight) and a barrier, which also frees the
+  // stage that step t - 1 read for the loads of step t + 2.
+  auto step = [&](const uint8_t* A, const uint8_t* B, uint8_t* An, uint8_t* Bn, int kt) {
+    if (kt + 1 < nk)
+      wait_vm<kLoads>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 2 < nk) issue(An, Bn, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(A, B);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  step(a0, b0, a2, b2, 0);
+  for (int kt = 1; kt < nk; kt += kStages) {
+    step(a1, b1, a0, b0, kt);
+    if (kt + 1 < nk) step(a2, b2, a1, b1, kt + 1);
+    if (kt + 2 < nk) step(a0, b0, a2, b2, kt + 2);
+  }
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
+}
+
+template <int BN>
+dim3 tile_grid(const StreamArgs& a) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
   const int64_t cols = silu_mode ? a.inter : a.rows;
   const int64_t col_tile = silu_mode ? BN / 2 : BN;
   const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
-  hipLaunchKernelGGL((tile_gemm_kernel<BN, FP8, WAVES>), dim3(unsigned(tiles_m * tiles_n)), dim3(64 * WAVES), 0,
-                     stream, a);
+  return dim3(unsigned(tiles_m * tiles_n));
+}
+
+template <int BN, int WAVES>
+hipError_t launch_bf16(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((tile_gemm_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int BN, int WAVES>
+hipError_t launch_fp8(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((tile_gemm_fp8_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -248,8 +443,8 @@ hipError_t launch_bn(const StreamArgs& a, hipStream_t stream) {
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
   // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
   // waits on LDS and barriers are covered by the other's MFMAs
-  if (bn == 256) return fp8 ? launch_bn<256, true, 8>(a, stream) : launch_bn<256, false, 8>(a, stream);
-  return fp8 ? launch_bn<128, true, 4>(a, stream) : launch_bn<128, false, 4>(a, stream);
+  if (bn == 256) return fp8 ? launch_fp8<256, 8>(a, stream) : launch_bf16<256, 8>(a, stream);
+  return fp8 ? launch_fp8<128, 4>(a, stream) : launch_bf16<128, 4>(a, stream);
 }
 
 }  // namespace swr
