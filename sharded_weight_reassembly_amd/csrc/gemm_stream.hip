@@ -146,77 +146,118 @@ __device__ inline void store4(const StreamArgs& a, int64_t tok, int64_t row, con
   }
 }
 
-// Second half of every streaming GEMM workgroup: NPART partial fp32 sums for
-// RT row tiles x MT token blocks sit in LDS as red[part][t][b][v][lane]
-// (lane = 16 * (row / 4) + token, v = row % 4 within the MFMA output tile);
-// each thread adds them for one token and 4 consecutive rows and applies the
-// output mode (scale, SiLU*up, bf16 rounding) or writes a split-K partial.
-template <int MT, int RT, int NPART = kWaves, int NT = kThreads>
-__device__ inline void finish_tile(const StreamArgs& a, const float* red, int64_t tok0, int64_t bx, int64_t split) {
+// Second half of every streaming GEMM workgroup.  NPART partial fp32 sums of
+// RT row tiles x MT token blocks sit in LDS token-major, red[part][token][row]
+// with a row stride of 16 * RT + 4 floats: a lane's four outputs of an MFMA
+// tile (rows 4 * (lane / 16) + 0..3, token lane % 16) are one 16-byte write,
+// and the 16 tokens of a write land 16 bytes apart, in distinct bank groups.
+template <int MT, int RT>
+struct Red {
+  static constexpr int RS = 16 * RT + 4;  // floats per token row
+  static constexpr int bytes(int nparts) { return nparts * MT * 16 * RS * 4; }
+};
+
+template <int MT, int RT>
+__device__ inline void red_put(float* red, int part, int t, int b, int lane, const f32x4& v) {
+  *reinterpret_cast<f32x4*>(red + (part * MT * 16 + b * 16 + (lane & 15)) * Red<MT, RT>::RS + t * 16 +
+                            4 * (lane >> 4)) = v;
+}
+
+// The output rows a thread finishes: row group rg = tid % G4 of its row block
+// (G4 = 4 per output tile), the same for every token it handles.  Their
+// scales are loaded here, before the cross-wave sum, so that the finish does
+// not wait on them.
+struct EpiRows {
+  int64_t row;   // first of 4 output rows (the gate index in SILU mode)
+  int64_t urow;  // first of the 4 matching up rows (SILU mode)
+  int col;       // offset of `row` in the LDS token row
+  bool live;     // inside the row block
+  f32x4 sg, su;  // scales of the 4 rows (ones for split-K partials)
+};
+
+template <int RT>
+__device__ inline int epi_groups(const StreamArgs& a) {
+  return (a.mode == OUT_SILU_BF16 ? RT / 2 : RT) * 4;
+}
+
+template <int RT>
+__device__ inline EpiRows epi_rows(const StreamArgs& a, int64_t bx) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
-  const int tiles_out = silu_mode ? RT / 2 : RT;
-  const int items = tiles_out * MT * 64;
-  auto at = [&](int w, int t, int b, int i, int ql) { return red[(((w * RT + t) * MT + b) * 4 + i) * 64 + ql]; };
-  for (int q = threadIdx.x; q < items; q += NT) {
-    const int ql = q & 63;
-    const int b = (q >> 6) % MT;
-    const int t = (q >> 6) / MT;
-    const int64_t tok = tok0 + b * 16 + (ql & 15);
-    if (tok >= a.M) continue;
-    const int64_t row = tile_row<RT>(a, t, bx) + 4 * (ql >> 4);
-    // masked rows of a short row block belong to the next block
-    if (row >= block_row_end(a, bx)) continue;
-    float v[4];
+  const int rg = threadIdx.x % epi_groups<RT>(a);
+  EpiRows e;
+  e.row = tile_row<RT>(a, rg / 4, bx) + 4 * (rg % 4);
+  e.urow = silu_mode ? tile_row<RT>(a, rg / 4 + RT / 2, bx) + 4 * (rg % 4) : 0;
+  e.col = 4 * rg;
+  // masked rows of a short row block belong to the next block
+  e.live = e.row < block_row_end(a, bx);
+  e.sg = f32x4{1.f, 1.f, 1.f, 1.f};
+  e.su = e.sg;
+  if (a.scale && a.ksplit == 1 && e.live) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < NPART; ++w) sum += at(w, t, b, i, ql);
-      v[i] = sum;
+      e.sg[i] = e.row + i < a.rows ? a.scale[e.row + i] : 0.f;
+      if (silu_mode) e.su[i] = a.scale[e.urow + i];
     }
+  }
+  return e;
+}
+
+// Adds the NPART partial sums for one token and 4 consecutive rows per item
+// and applies the output mode (scale, SiLU*up, bf16 rounding) or writes a
+// split-K partial.  Consecutive threads take consecutive row groups of one
+// token, so the global stores of a wave cover whole runs of a token's row.
+template <int MT, int RT, int NPART = kWaves, int NT = kThreads>
+__device__ inline void finish_tile(const StreamArgs& a, const float* red, const EpiRows& e, int64_t tok0,
+                                   int64_t split) {
+  if (!e.live) return;
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  constexpr int RS = Red<MT, RT>::RS;
+  const int g4 = epi_groups<RT>(a);
+  const int ucol = 8 * RT + e.col;  // the up rows sit RT / 2 tiles further
+  auto sum_at = [&](int tl, int col) {
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NPART; ++w) v += *reinterpret_cast<const f32x4*>(red + (w * MT * 16 + tl) * RS + col);
+    return v;
+  };
+  for (int tl = threadIdx.x / g4; tl < MT * 16; tl += NT / g4) {
+    const int64_t tok = tok0 + tl;
+    if (tok >= a.M) break;
+    const f32x4 g = sum_at(tl, e.col);
     if (silu_mode) {
-      const int64_t urow = tile_row<RT>(a, t + RT / 2, bx) + 4 * (ql >> 4);
-      float u[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < NPART; ++w) sum += at(w, t + RT / 2, b, i, ql);
-        u[i] = sum;
-      }
+      const f32x4 u = sum_at(tl, ucol);
       if (a.ksplit > 1) {
+        // SILU mode: rows = 2 I with I a multiple of 16, so these are aligned
         float* pg = a.partial + (split * a.M + tok) * a.rows;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pg[row + i] = v[i];
-          pg[urow + i] = u[i];
-        }
+        *reinterpret_cast<f32x4*>(pg + e.row) = g;
+        *reinterpret_cast<f32x4*>(pg + e.urow) = u;
         continue;
       }
       float h[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float g = v[i] * (a.scale ? a.scale[row + i] : 1.f);
-        const float up = u[i] * (a.scale ? a.scale[urow + i] : 1.f);
-        h[i] = silu(g) * up;
-      }
+      for (int i = 0; i < 4; ++i) h[i] = silu(g[i] * e.sg[i]) * (u[i] * e.su[i]);
       // h is [M, ldy] with I columns; `row` is the gate index j
       StreamArgs hb = a;
       hb.rows = a.inter;
-      store4(hb, tok, row, h, true);
+      store4(hb, tok, e.row, h, true);
       continue;
     }
-    if (a.ksplit > 1) {
-      float* pr = a.partial + (split * a.M + tok) * a.rows;
-      for (int i = 0; i < 4; ++i)
-        if (row + i < a.rows) pr[row + i] = v[i];
-      continue;
-    }
-    if (a.scale) {
+    float v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= (row + i < a.rows) ? a.scale[row + i] : 0.f;
+    for (int i = 0; i < 4; ++i) v[i] = g[i];
+    if (a.ksplit > 1) {
+      float* pr = a.partial + (split * a.M + tok) * a.rows + e.row;
+      if (e.row + 4 <= a.rows && (reinterpret_cast<uintptr_t>(pr) & 15) == 0) {
+        *reinterpret_cast<f32x4*>(pr) = g;
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (e.row + i < a.rows) pr[i] = v[i];
+      }
+      continue;
     }
-    store4(a, tok, row, v, a.mode == OUT_BF16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= e.sg[i];
+    store4(a, tok, e.row, v, a.mode == OUT_BF16);
   }
 }
 
@@ -258,6 +299,8 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
   int s = wave;
   if (s < nsub) load_step<MT, RT, FP8>(s0, wp, xp, int64_t(s) * kStepK);
   if (s + kWaves < nsub) load_step<MT, RT, FP8>(s1, wp, xp, int64_t(s + kWaves) * kStepK);
+  // output rows and their scales, loaded long before the finish needs them
+  const EpiRows e = epi_rows<RT>(a, blockIdx.x);
   for (; s < nsub; s += 2 * kWaves) {
     mma_step<MT, RT, FP8>(s0, acc);
     if (s + 2 * kWaves < nsub) load_step<MT, RT, FP8>(s0, wp, xp, int64_t(s + 2 * kWaves) * kStepK);
@@ -267,16 +310,14 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
     }
   }
 
-  // ---- add the 4 waves' sums in LDS: red[wave][t][b][v][lane]
-  __shared__ float red[kWaves * RT * MT * 4 * 64];
+  // ---- add the 4 waves' sums in LDS
+  __shared__ __attribute__((aligned(16))) float red[Red<MT, RT>::bytes(kWaves) / 4];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int b = 0; b < MT; ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[(((wave * RT + t) * MT + b) * 4 + v) * 64 + lane] = acc[t][b][v];
+    for (int b = 0; b < MT; ++b) red_put<MT, RT>(red, wave, t, b, lane, acc[t][b]);
   __syncthreads();
-  finish_tile<MT, RT>(a, red, tok0, blockIdx.x, blockIdx.y);
+  finish_tile<MT, RT>(a, red, e, tok0, blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -330,7 +371,7 @@ constexpr int staged_occupancy(int MT, int RTL, bool FP8, bool WK, bool XL, int 
   const int XT = XL ? 16 * MT * SK * 2 : 0;
   const int KQ = WK ? 4 : 4 / MT;
   const int ACC = WK ? (RTL / (NW / 4)) * MT : RTL;
-  const int RED = KQ * RTL * MT * 4 * 64 * 4;
+  const int RED = KQ * MT * 16 * (16 * RTL + 4) * 4;
   const int LDS = (2 * TILE + 2 * XT) > RED ? (2 * TILE + 2 * XT) : RED;
   const bool DEEP = MT == 1 && RTL <= 2;
   return (NW == 8 || DEEP || ACC >= 16 || LDS > 80 * 1024) ? 1 : 2;
@@ -357,7 +398,7 @@ struct StagedShape {
   static constexpr int ACC = WK ? RTW * MT : RTL;      // 16x16 accumulator tiles per wave
   static constexpr int XS = XL ? 4 * XNV : 8 * XF;     // VGPRs of one stage of X in the ring
   static constexpr int WS = 4 * NV;                     // VGPRs of one stage of W pieces
-  static constexpr int RED = KQ * RTL * MT * 4 * 64 * 4;  // bytes of the final cross-wave sum
+  static constexpr int RED = Red<MT, RTL>::bytes(KQ);  // bytes of the final cross-wave sum
   static constexpr int LDS = (2 * TILE + 2 * XT) > RED ? (2 * TILE + 2 * XT) : RED;
   // Register budget of the rings (VGPRs): with eight waves (two per SIMD)
   // 256 registers per wave less the accumulators and fragments.
@@ -588,6 +629,10 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
     if (j + DX - D >= 0) load_x(xr[(j + DX - D) % DX], j + DX - D);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // output rows and their scales, loaded behind the first stages (loads
+  // retire in order) and long before the finish needs them
+  const EpiRows e = epi_rows<RTL>(a, bx);
+  __builtin_amdgcn_sched_barrier(0);
   store_w(0, wr[0]);
   if (XL) store_x(0, xr[0]);
   load_w(wr[0], D);
@@ -623,11 +668,9 @@ __device__ inline void staged_body(const StreamArgs& a, int64_t bx, int64_t by, 
   for (int t = 0; t < TW; ++t)
 #pragma unroll
     for (int b = 0; b < (WK ? MT : 1); ++b)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        red[(((kq * RTL + rh * TW + t) * MT + blk + b) * 4 + v) * 64 + lane] = acc[t * (WK ? MT : 1) + b][v];
+      red_put<MT, RTL>(red, kq, rh * TW + t, blk + b, lane, acc[t * (WK ? MT : 1) + b]);
   __syncthreads();
-  finish_tile<MT, RTL, KQ, NT>(a, red, tok0, bx, by);
+  finish_tile<MT, RTL, KQ, NT>(a, red, e, tok0, by);
 }
 
 template <int MT, int RTL, bool FP8, bool WK, bool XL, int SK, int NW = kWaves>
@@ -657,39 +700,62 @@ __global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, false, false>:
 }
 
 // Adds the split-K partials in split order and applies scale / SiLU / rounding.
-// One thread per (token, 4 consecutive output columns).
+// One thread per (token, 4 consecutive output columns); where the partial rows
+// and the scales are 16-byte aligned each split is one 16-byte load.
 __global__ __launch_bounds__(kThreads) void splitk_finalize_kernel(StreamArgs a) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int64_t cols = silu_mode ? a.inter : a.rows;
   const int64_t groups = (cols + 3) / 4;
   const int64_t total = a.M * groups;
+  const bool vec = a.rows % 4 == 0 && cols % 4 == 0 && (reinterpret_cast<uintptr_t>(a.partial) & 15) == 0 &&
+                   (!a.scale || (reinterpret_cast<uintptr_t>(a.scale) & 15) == 0);
   for (int64_t q = int64_t(blockIdx.x) * kThreads + threadIdx.x; q < total; q += int64_t(gridDim.x) * kThreads) {
     const int64_t tok = q / groups;
     const int64_t c0 = (q % groups) * 4;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     float u[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.ksplit; ++s) {
-      const float* p = a.partial + (int64_t(s) * a.M + tok) * a.rows;
+    float sg[4] = {1.f, 1.f, 1.f, 1.f};
+    float su[4] = {1.f, 1.f, 1.f, 1.f};
+    if (vec) {
+      f32x4 gv = f32x4{0.f, 0.f, 0.f, 0.f}, uv = gv;
+      for (int s = 0; s < a.ksplit; ++s) {
+        const float* p = a.partial + (int64_t(s) * a.M + tok) * a.rows + c0;
+        gv += *reinterpret_cast<const f32x4*>(p);
+        if (silu_mode) uv += *reinterpret_cast<const f32x4*>(p + a.inter);
+      }
+      const f32x4 one = f32x4{1.f, 1.f, 1.f, 1.f};
+      const f32x4 gs = a.scale ? *reinterpret_cast<const f32x4*>(a.scale + c0) : one;
+      const f32x4 us = a.scale && silu_mode ? *reinterpret_cast<const f32x4*>(a.scale + a.inter + c0) : one;
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (c0 + i < cols) {
-          v[i] += p[c0 + i];
-          if (silu_mode) u[i] += p[a.inter + c0 + i];
+        v[i] = gv[i];
+        u[i] = uv[i];
+        sg[i] = gs[i];
+        su[i] = us[i];
+      }
+    } else {
+      for (int s = 0; s < a.ksplit; ++s) {
+        const float* p = a.partial + (int64_t(s) * a.M + tok) * a.rows;
+        for (int i = 0; i < 4; ++i) {
+          if (c0 + i < cols) {
+            v[i] += p[c0 + i];
+            if (silu_mode) u[i] += p[a.inter + c0 + i];
+          }
         }
+      }
+      for (int i = 0; i < 4; ++i) {
+        if (c0 + i >= cols || !a.scale) continue;
+        sg[i] = a.scale[c0 + i];
+        if (silu_mode) su[i] = a.scale[a.inter + c0 + i];
       }
     }
     if (silu_mode) {
-      for (int i = 0; i < 4; ++i) {
-        if (c0 + i >= cols) continue;
-        const float g = v[i] * (a.scale ? a.scale[c0 + i] : 1.f);
-        const float up = u[i] * (a.scale ? a.scale[a.inter + c0 + i] : 1.f);
-        v[i] = silu(g) * up;
-      }
+      for (int i = 0; i < 4; ++i) v[i] = silu(v[i] * sg[i]) * (u[i] * su[i]);
       StreamArgs hb = a;
       hb.rows = a.inter;
       store4(hb, tok, c0, v, true);
     } else {
-      for (int i = 0; i < 4; ++i)
-        if (a.scale && c0 + i < cols) v[i] *= a.scale[c0 + i];
+      for (int i = 0; i < 4; ++i) v[i] *= sg[i];
       store4(a, tok, c0, v, a.mode == OUT_BF16);
     }
   }
