@@ -8,16 +8,16 @@
 //     waves; each wave a 128 x (2*BN/WAVES) sub-tile with
 //     v_mfma_f32_32x32x16_bf16 (tokens are the MFMA rows, weight rows the
 //     MFMA columns, so a lane's outputs run along a row of Y);
-//   * K advances in steps of 64; X is staged in LDS as bf16 rows of 128 B of
-//     16-byte pieces, piece p of row r at r * 8 + (p ^ ((r >> 1) & 7)), so the
-//     32-row fragment reads of one MFMA hit distinct banks;
-//   * BF16 weights: X and W of the next step are loaded into registers while
-//     the current step is multiplied, then written to a double-buffered LDS
-//     tile (tile_gemm_kernel);
-//   * FP8 weights: X and the raw FP8 codes go from memory straight into a
-//     three-stage LDS ring with buffer-to-LDS loads, two steps ahead of the
-//     MFMAs, with no staging registers (tile_gemm_fp8_kernel); the codes are
-//     widened to BF16 (exact) after the fragment read;
+//   * both operands go from memory straight into an LDS ring with
+//     buffer-to-LDS loads (no staging registers), several steps ahead of the
+//     MFMAs; 16-byte pieces are XOR-swizzled by row, so the 32-row fragment
+//     reads of one MFMA hit distinct banks;
+//   * FP8 weights (tile_gemm_fp8_kernel): steps of 64 K, a three-stage ring
+//     two steps ahead; X rows of 128 B with piece p of row r at
+//     r * 8 + (p ^ ((r >> 1) & 7)), and the raw FP8 codes, widened to BF16
+//     (exact) after the fragment read;
+//   * BF16 weights (tile_gemm_bf16_kernel): steps of 32 K, a four-stage ring
+//     three steps ahead, rows of 64 B for both operands;
 //   * tiles are numbered so that each XCD (workgroups are dealt round-robin
 //     to the 8 XCDs) works through a compact group of 4 token blocks x all
 //     weight blocks, which keeps the X and W tiles of concurrently running
@@ -117,120 +117,6 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
       }
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// BF16 weights: register-staged, double-buffered LDS.
-template <int BN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_kernel(StreamArgs a) {
-  constexpr int NT = 64 * WAVES;    // threads
-  constexpr int WGN = WAVES / 2;    // waves along the weight rows (2 along the tokens)
-  constexpr int WN = BN / WGN;      // weight rows per wave
-  constexpr int TM = 4;             // 32-token MFMA tiles per wave (128 tokens)
-  constexpr int TN = WN / 32;       // 32-row MFMA tiles per wave
-  constexpr int A_BYTES = kTileM * kTileK * 2;
-  constexpr int B_BYTES = BN * kTileK * 2;
-  constexpr int NA = A_BYTES / 16 / NT;  // X pieces per thread per step
-  constexpr int NB = B_BYTES / 16 / NT;  // W pieces per thread per step
-  static_assert(TN >= 1 && NA >= 1 && NB >= 1, "tile must split evenly over the workgroup");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (A_BYTES + B_BYTES)];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const TileCoord tc = tile_coord<BN>(a);
-  const int64_t m0 = tc.m0;
-
-  // ---- global -> register staging addresses
-  const uint16_t* asrc[NA];
-  int adst[NA];
-#pragma unroll
-  for (int j = 0; j < NA; ++j) {
-    const int v = j * NT + tid;
-    const int row = v / 8, piece = v % 8;
-    const int64_t m = min(m0 + row, a.M - 1);
-    asrc[j] = a.X + m * a.ldx + piece * 8;
-    adst[j] = swz(row, piece) * 16;
-  }
-  const uint8_t* bsrc[NB];
-  int bdst[NB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int v = j * NT + tid;
-    const int row = v / 8, piece = v % 8;
-    const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
-    bsrc[j] = a.W + (r * a.K + piece * 8) * 2;
-    bdst[j] = swz(row, piece) * 16;
-  }
-
-  u32x4 ra[NA], rb[NB];
-  auto load = [&](int kt) {
-    const int64_t k0 = int64_t(kt) * kTileK;
-#pragma unroll
-    for (int j = 0; j < NA; ++j) ra[j] = *reinterpret_cast<const u32x4*>(asrc[j] + k0);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) rb[j] = *reinterpret_cast<const u32x4*>(bsrc[j] + k0 * 2);
-  };
-  auto store = [&](int buf) {
-    uint8_t* A = lds + buf * (A_BYTES + B_BYTES);
-    uint8_t* B = A + A_BYTES;
-#pragma unroll
-    for (int j = 0; j < NA; ++j) *reinterpret_cast<u32x4*>(A + adst[j]) = ra[j];
-#pragma unroll
-    for (int j = 0; j < NB; ++j) *reinterpret_cast<u32x4*>(B + bdst[j]) = rb[j];
-  };
-
-  // ---- fragment reads: k-step ks of buffer buf into F (A rows then B rows)
-  const int r32 = lane & 31, kg = lane >> 5;
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int x = 0; x < TM; ++x)
-#pragma unroll
-    for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
-
-  bf16x8 F[2][TM + TN];  // two k-steps of fragments: the next one is read while the current one multiplies
-  auto read_frags = [&](int buf, int ks, bf16x8(&f)[TM + TN]) {
-    const uint8_t* A = lds + buf * (A_BYTES + B_BYTES);
-    const uint8_t* B = A + A_BYTES;
-    const int piece = ks * 2 + kg;
-#pragma unroll
-    for (int x = 0; x < TM; ++x) f[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, piece) * 16);
-#pragma unroll
-    for (int y = 0; y < TN; ++y)
-      f[TM + y] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, piece) * 16);
-  };
-  auto mfmas = [&](const bf16x8(&f)[TM + TN]) {
-#pragma unroll
-    for (int x = 0; x < TM; ++x)
-#pragma unroll
-      for (int y = 0; y < TN; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[x], f[TM + y], acc[x][y], 0, 0, 0);
-  };
-
-  const int nk = int(a.K / kTileK);
-  load(0);
-  store(0);
-  __syncthreads();
-  read_frags(0, 0, F[0]);
-  // Each k-step is a scheduling region of its own: the next k-step's LDS
-  // fragment reads (into the other register set) interleave with this
-  // k-step's MFMAs, and their wait lands at the start of the next region.
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    const int buf = kt & 1;
-    if (more) load(kt + 1);  // global loads, in flight during the MFMAs below
-#pragma unroll
-    for (int ks = 0; ks < kTileK / 16; ++ks) {
-      if (ks + 1 < kTileK / 16) read_frags(buf, ks + 1, F[(ks + 1) & 1]);
-      mfmas(F[ks & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) store(buf ^ 1);  // the other buffer was last read before the previous barrier
-    __syncthreads();
-    if (more) read_frags(buf ^ 1, 0, F[0]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg);
 }
 
 // ---------------------------------------------------------------------------
@@ -416,6 +302,139 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
   tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
 }
 
+// ---------------------------------------------------------------------------
+// BF16 weights: both operands by buffer-to-LDS loads as above, in 32-K steps
+// (a 256-row stage of BF16 weights at 64 K would take 32 KB, too much for a
+// three-stage ring beside X) through a four-stage ring, three steps ahead.
+//   * X stage: 256 rows x 64 B, W stage: BN rows x 64 B, both with piece q of
+//     row r at r * 4 + (q ^ ((r >> 2) & 3)); a load instruction fills 16 rows;
+//   * a step is two 16-K slices; lane group g of an MFMA reads piece 2s + g of
+//     its row for slice s, K in natural order;
+//   * per step: wait until this wave's loads of step t have landed, barrier,
+//     issue the loads of step t + 3 into the stage that step t - 1 read,
+//     multiply step t.
+constexpr int kStepK16 = 32;
+
+template <int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArgs a) {
+  constexpr int WGN = WAVES / 2;
+  constexpr int WN = BN / WGN;
+  constexpr int TM = 4;
+  constexpr int TN = WN / 32;
+  constexpr int BK = kStepK16;
+  constexpr int A_BYTES = kTileM * BK * 2;  // 16 KB
+  constexpr int B_BYTES = BN * BK * 2;
+  constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per step
+  constexpr int NB = B_BYTES / 1024 / WAVES;  // 1 KB loads of W per wave per step
+  static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
+                "stage must split into whole 1 KB loads per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[A_BYTES], a3[A_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[B_BYTES], b3[B_BYTES];
+  // first in LDS, for the same reason as in the FP8 kernel
+  __shared__ __attribute__((aligned(4096))) float row_scale[BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const TileCoord tc = tile_coord<BN>(a);
+  const int64_t m0 = tc.m0;
+  for (int c = tid; c < BN; c += 64 * WAVES) {
+    const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
+    row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
+  }
+
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * 2);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * 2);
+  // Source offsets of this lane's pieces (step 0): a load fills rows
+  // 16 * i .. 16 * i + 15 of the stage, lane l position l % 4 of row l / 4;
+  // rows past the end are read from the last row and never stored.
+  int aoff[NA], boff[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = (wave * NA + i) * 16 + lane / 4;
+    const int q = (lane % 4) ^ ((row >> 2) & 3);
+    const int64_t m = min(m0 + row, a.M - 1);
+    aoff[i] = int((m * a.ldx + q * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = (wave * NB + i) * 16 + lane / 4;
+    const int q = (lane % 4) ^ ((row >> 2) & 3);
+    const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
+    boff[i] = int((r * a.K + q * 8) * 2);
+  }
+  auto issue = [&](uint8_t* A, uint8_t* B, int kt) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kt * BK * 2);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_load16<true>(wres, B + (wave * NB + i) * 1024, boff[i], kt * BK * 2);
+  };
+
+  const int r32 = lane & 31, kg = lane >> 5;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int x = 0; x < TM; ++x)
+#pragma unroll
+    for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
+
+  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+        fa[x] = *reinterpret_cast<const bf16x8*>(A + wswz(wm * 128 + x * 32 + r32, 2 * s + kg) * 16);
+#pragma unroll
+      for (int y = 0; y < TN; ++y)
+        fb[y] = *reinterpret_cast<const bf16x8*>(B + wswz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+    }
+  };
+
+  constexpr int kLoads = NA + NB;  // loads per wave per step
+  const int nk = int(a.K / BK);
+  // prologue: steps 0, 1 and 2 in flight
+  issue(a0, b0, 0);
+  if (nk > 1) issue(a1, b1, 1);
+  if (nk > 2) issue(a2, b2, 2);
+
+  // Step t uses stage t % 4; the loop is unrolled by the ring so every stage
+  // is a fixed array.  A step opens with the wait for its own loads (those of
+  // the next two steps may stay in flight) and a barrier, which also frees
+  // the stage that step t - 1 read for the loads of step t + 3.
+  auto step = [&](const uint8_t* A, const uint8_t* B, uint8_t* An, uint8_t* Bn, int kt) {
+    if (kt + 2 < nk)
+      wait_vm<2 * kLoads>();
+    else if (kt + 1 < nk)
+      wait_vm<kLoads>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 3 < nk) issue(An, Bn, kt + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(A, B);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // whole ring cycles without branches around the MFMAs, then the tail
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    step(a0, b0, a3, b3, kt);
+    step(a1, b1, a0, b0, kt + 1);
+    step(a2, b2, a1, b1, kt + 2);
+    step(a3, b3, a2, b2, kt + 3);
+  }
+  if (kt < nk) step(a0, b0, a3, b3, kt);
+  if (kt + 1 < nk) step(a1, b1, a0, b0, kt + 1);
+  if (kt + 2 < nk) step(a2, b2, a1, b1, kt + 2);
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
+}
+
 template <int BN>
 dim3 tile_grid(const StreamArgs& a) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
@@ -427,8 +446,8 @@ dim3 tile_grid(const StreamArgs& a) {
 }
 
 template <int BN, int WAVES>
-hipError_t launch_bf16(const StreamArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tile_gemm_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+hipError_t launch_bf16_lds(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((tile_gemm_bf16_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -443,8 +462,8 @@ hipError_t launch_fp8(const StreamArgs& a, hipStream_t stream) {
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
   // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
   // waits on LDS and barriers are covered by the other's MFMAs
-  if (bn == 256) return fp8 ? launch_fp8<256, 8>(a, stream) : launch_bf16<256, 8>(a, stream);
-  return fp8 ? launch_fp8<128, 4>(a, stream) : launch_bf16<128, 4>(a, stream);
+  if (bn == 256) return fp8 ? launch_fp8<256, 8>(a, stream) : launch_bf16_lds<256, 8>(a, stream);
+  return fp8 ? launch_fp8<128, 4>(a, stream) : launch_bf16_lds<128, 4>(a, stream);
 }
 
 }  // namespace swr

@@ -196,6 +196,9 @@ def test_full_size_projection_layer_sampled_rows():
     (2048, 1024, synth.BF16, 513),
     (384, 192, synth.FP8, 257),      # 3 K tiles, 128-row weight tiles
     (4096, 256, synth.BF16, 1024),   # 256-row weight tiles
+    (300, 64, synth.BF16, 260),      # a single K tile: two BF16 steps, no full ring cycle
+    (640, 192, synth.BF16, 300),     # six BF16 steps: one ring cycle and a tail of two
+    (200, 64, synth.FP8, 270),       # a single FP8 step
 ])
 def test_tiled_prefill_parity(o, k, dt, m):
     note(f"tiled proj o={o} k={k} {dt} m={m}")
