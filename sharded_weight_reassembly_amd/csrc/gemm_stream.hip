@@ -869,7 +869,8 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   if (plan.kind == 1) return true;
   if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
   if (plan.kind == 3)
-    return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1;
+    return p.K % kTileK == 0 && (plan.rt == 256 || plan.rt == 128) && plan.ksplit == 1 &&
+           p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31) && p.ldx < (INT64_C(1) << 22);
   // row blocks: whole tiles (the streaming kind), or a multiple of 4 rows
   // up to the tiles' rows (staged kinds)
   const int64_t full = full_rows(p, plan.rt);
@@ -906,9 +907,11 @@ GemmPlan plan_gemm(const GemmProblem& p) {
   plan.mt = p.M <= 16 ? 1 : (p.M <= 32 ? 2 : 4);
   const int64_t tok_blocks = (p.M + 16 * plan.mt - 1) / (16 * plan.mt);
   const int64_t w_bytes = p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2);
-  if (aligned_ok && p.M > 64 && p.K % kTileK == 0) {
+  if (aligned_ok && p.M > 64 && p.K % kTileK == 0 && w_bytes < (INT64_C(1) << 31) && p.ldx < (INT64_C(1) << 22)) {
     // Prefill-sized M: the tiled MFMA kernel.  256-row weight tiles when they
-    // still give at least two waves of workgroups over the 256 CUs.
+    // still give at least two waves of workgroups over the 256 CUs.  Its
+    // buffer offsets are 32-bit: weights under 2 GiB (larger ones stream),
+    // and the launch splits the tokens so that each part's X is under 2 GiB.
     plan.kind = 3;
     const int64_t tiles_m = (p.M + 255) / 256;
     const int64_t cols = silu_mode ? inter : p.rows;

@@ -460,10 +460,27 @@ hipError_t launch_fp8(const StreamArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
-  // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
-  // waits on LDS and barriers are covered by the other's MFMAs
-  if (bn == 256) return fp8 ? launch_fp8<256, 8>(a, stream) : launch_bf16_lds<256, 8>(a, stream);
-  return fp8 ? launch_fp8<128, 4>(a, stream) : launch_bf16_lds<128, 4>(a, stream);
+  // The kernels address X through 32-bit buffer offsets: tokens go in parts
+  // whose X spans less than 2 GiB (whole 256-token tiles).
+  const int64_t x_row = a.ldx * 2;
+  int64_t part = ((INT64_C(1) << 31) - 1) / x_row / kTileM * kTileM;
+  if (part < kTileM) return hipErrorInvalidValue;  // a 256-token tile alone would exceed 2 GiB
+  const int64_t y_elem = a.mode == OUT_F32 ? 4 : 2;
+  for (int64_t m0 = 0; m0 < a.M; m0 += part) {
+    StreamArgs p = a;
+    p.M = a.M - m0 < part ? a.M - m0 : part;
+    p.X = a.X + m0 * a.ldx;
+    p.Y = static_cast<uint8_t*>(a.Y) + m0 * a.ldy * y_elem;
+    // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
+    // waits on LDS and barriers are covered by the other's MFMAs
+    hipError_t e;
+    if (bn == 256)
+      e = fp8 ? launch_fp8<256, 8>(p, stream) : launch_bf16_lds<256, 8>(p, stream);
+    else
+      e = fp8 ? launch_fp8<128, 4>(p, stream) : launch_bf16_lds<128, 4>(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace swr

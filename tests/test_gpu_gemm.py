@@ -210,6 +210,30 @@ def test_tiled_prefill_parity(o, k, dt, m):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+def test_tiled_prefill_x_beyond_4gib(dt):
+    """X of 131372 tokens x 16384 (4.01 GiB of bf16) runs in three launches,
+    each spanning less than 2 GiB (the tiled kernels address X with 32-bit
+    buffer offsets); tokens on both sides of each split and at the ends are
+    checked."""
+    o, k, m, base_rows = 384, 16384, 131372, 512
+    assert m * k * 2 >= 1 << 32
+    note(f"tiled proj beyond 4 GiB of X: o={o} k={k} {dt} m={m}")
+    w = synth.weight(synth.seed_for(14, 1, 0), o, k, dt)
+    xb = synth.activations(synth.seed_for(14, 1, 50), base_rows, k)  # token t is row t % 512
+    x = bf16(xb).repeat((m + base_rows - 1) // base_rows, 1)[:m].contiguous()
+    y = torch.full((m, o), float("nan"), dtype=torch.bfloat16, device=DEV)
+    swr.proj_forward(u8(w.raw()), dt, f32(w.scale) if w.scale is not None else None, o, k, x, y)
+    torch.cuda.synchronize()
+    del x
+    part = ((1 << 31) - 1) // (k * 2) // 256 * 256
+    toks = sorted({0, 1, 255, 256, part - 1, part, part + 1, part + 256, 2 * part - 1, 2 * part, 2 * part + 1,
+                   m - 2, m - 1, 40000, 100000})
+    got = values(y[toks])
+    ref = gemm.proj_f64(xb[[t % base_rows for t in toks]], w.raw(), dt, o, k, w.scale)
+    assert_close_rows(got, ref, what=f"tokens {toks}")
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
 @pytest.mark.parametrize("hidden,inter,m", [(256, 320, 300), (512, 1024, 600), (128, 256, 4096)])
 def test_tiled_prefill_mlp(dt, hidden, inter, m):
     note(f"tiled mlp h={hidden} i={inter} {dt} m={m}")
