@@ -882,7 +882,8 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
     if (!(plan.rt == 4 || (plan.rt == 8 && p.dtype == SWR_FP8_E4M3FN))) return false;
     if (silu_mode && inter % (8 * plan.rt) != 0) return false;
     return plan.sk == kStageK && p.K % kStageK == 0 && plan.kper % kStageK == 0 &&
-           p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31);
+           p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31) &&
+           p.M * p.ldx * 2 < (INT64_C(1) << 31);
   }
   if (plan.mt != 1 && plan.mt != 2 && plan.mt != 4) return false;
   if (plan.rt != 1 && plan.rt != 2 && plan.rt != 4 && !(plan.kind == 2 && plan.rt == 8)) return false;
@@ -894,7 +895,8 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
         !(plan.sk == 2 * kStageK && plan.mt == 1 && p.dtype == SWR_FP8_E4M3FN && plan.rt <= 4))
       return false;
     return p.K % plan.sk == 0 && plan.kper % plan.sk == 0 &&
-           p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31);
+           p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) < (INT64_C(1) << 31) &&
+           p.M * p.ldx * 2 < (INT64_C(1) << 31);
   }
   return false;
 }
@@ -923,7 +925,8 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     plan.partial_bytes = 0;
     return plan;
   }
-  if (aligned_ok && p.K % kStageK == 0 && (!silu_mode || inter % 16 == 0) && w_bytes < (INT64_C(1) << 31)) {
+  if (aligned_ok && p.K % kStageK == 0 && (!silu_mode || inter % 16 == 0) && w_bytes < (INT64_C(1) << 31) &&
+      p.M * p.ldx * 2 < (INT64_C(1) << 31)) {
     // Staged kernel.  Row block and K split from a sweep of the shared-expert
     // shapes on MI355X: 32-row blocks when one 16-token block suffices, 64-row
     // blocks otherwise (fewer activation re-reads per weight byte); K is split
@@ -1117,7 +1120,9 @@ bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt) {
     const GemmProblem& p = ps[i];
     if (p.dtype != ps[0].dtype || p.M != M || p.mode == OUT_SILU_BF16) return false;
     if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0)) return false;
-    if (p.K % kStageK != 0 || p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) >= (INT64_C(1) << 31)) return false;
+    if (p.K % kStageK != 0 || p.rows * p.K * (p.dtype == SWR_FP8_E4M3FN ? 1 : 2) >= (INT64_C(1) << 31) ||
+        p.M * p.ldx * 2 >= (INT64_C(1) << 31))
+      return false;
     blocks += (p.rows + 16 * *rt - 1) / (16 * *rt);
   }
   return blocks < (INT64_C(1) << 30);
