@@ -293,12 +293,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
     compute(A, B);
     __builtin_amdgcn_sched_barrier(0);
   };
-  step(a0, b0, a2, b2, 0);
-  for (int kt = 1; kt < nk; kt += kStages) {
-    step(a1, b1, a0, b0, kt);
-    if (kt + 1 < nk) step(a2, b2, a1, b1, kt + 1);
-    if (kt + 2 < nk) step(a0, b0, a2, b2, kt + 2);
+  // whole ring cycles without branches around the MFMAs, then the tail
+  int kt = 0;
+  for (; kt + kStages <= nk; kt += kStages) {
+    step(a0, b0, a2, b2, kt);
+    step(a1, b1, a0, b0, kt + 1);
+    step(a2, b2, a1, b1, kt + 2);
   }
+  if (kt < nk) step(a0, b0, a2, b2, kt);
+  if (kt + 1 < nk) step(a1, b1, a0, b0, kt + 1);
   tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
 }
 
