@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+YIELD_LDS = 56 * 1024  # gather LDS reservation reported beside the headline
 
 
 def log(msg: str) -> None:
@@ -53,6 +54,9 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--gate", choices=["done", "begin"], default="done",
                     help="decode: what the gather of layer l+1 waits for -- layer l-1 being done (the pages' gate) "
                          "or the compute stream beginning layer l")
+    ap.add_argument("--gather-lds", type=int, default=0,
+                    help="decode: LDS bytes each copy workgroup of the planner's gathers reserves, to leave CUs "
+                         "to the GEMMs (0: none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--minimal", action="store_true",
                     help="only the pipelined steps and isolated kernels (no serial, DMA, tensor-parallel or graph "
@@ -134,6 +138,7 @@ def main() -> int:
         planner.set_cyclic(True)
     gate_of = {"begin": swr.GATE_BEGIN, "done": swr.GATE_DONE}
     planner.set_gate(gate_of[args.gate])
+    planner.set_gather_lds(args.gather_lds)
     o_gu, o_d = views[0]["offset"], views[1]["offset"]
 
     def forward(m: int, gemm_events=None, pl=None) -> None:
@@ -247,7 +252,7 @@ def main() -> int:
     # The sections below (serial reference, DMA-engine gather, tensor-parallel
     # share, graph replay) are reports beside the headline; --minimal skips
     # them, e.g. for hardware-counter runs that average over every MLP call.
-    serial_ms, dma, graph, tpres, gate_begin, R, rank_bytes = {}, {}, {}, {}, {}, 4, 0
+    serial_ms, dma, graph, tpres, gate_begin, yielding, R, rank_bytes = {}, {}, {}, {}, {}, {}, 4, 0
     if not args.minimal:
         # ---------------------------------------------------------------- serial reference
         # the same gathers and MLPs back to back on one stream (no side stream, no overlap):
@@ -310,6 +315,29 @@ def main() -> int:
                 e1.record(compute)
             torch.cuda.synchronize()
             gate_begin[str(m)] = {"pipelined_ms_per_forward": round(e0.elapsed_time(e1) / (dma_steps * 2), 4)}
+        planner.set_gate(gate_of[args.gate])
+
+        # ---------------------------------------------------------------- a gather that yields CUs
+        # The same pipelined forwards, without timing events, with and without
+        # the gather's LDS reservation (swr_planner_set_gather_lds), both gates.
+        yielding = {"gather_lds": YIELD_LDS}
+        for lds in (0, YIELD_LDS):
+            planner.set_gather_lds(lds)
+            for gname in ("done", "begin"):
+                planner.set_gate(gate_of[gname])
+                row = {}
+                for m in tokens:
+                    with torch.cuda.stream(compute):
+                        forward(m)
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(compute)
+                        for _ in range(dma_steps * 2):
+                            forward(m)
+                        e1.record(compute)
+                    torch.cuda.synchronize()
+                    row[str(m)] = round(e0.elapsed_time(e1) / (dma_steps * 2), 4)
+                yielding[f"lds_{lds}_gate_{gname}_ms_per_forward"] = row
+        planner.set_gather_lds(args.gather_lds)
         planner.set_gate(gate_of[args.gate])
 
         # ---------------------------------------------------------------- tensor-parallel share
@@ -487,12 +515,14 @@ def main() -> int:
         "config": {
             "workload": wl.name, "hidden": H, "intermediate": I, "layers": L, "n_chunks": N,
             "tokens": tokens, "layer_bytes": T, "chunk_bytes": C, "slots": 2, "gate": args.gate,
+            "gather_lds": args.gather_lds,
             "step": "pipelined forward (side-stream reassembly + MLP) over all layers for every M",
         },
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "per_tokens": per_m,
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1) if iso_gather_ms else None,
         "dma_engine_gather": dma,
+        "yielding_gather": yielding,
         "other_gate": gate_begin,
         "graph_replay_no_prefetch": graph,
         "tensor_parallel_share": {"ranks": R, "rank_weight_bytes_per_layer": rank_bytes, "per_tokens": tpres},

@@ -424,6 +424,26 @@ int swr_planner_set_gate(swr_planner* p, int32_t gate);
  */
 int swr_planner_set_copy_engine(swr_planner* p, int32_t engine);
 
+#define SWR_MAX_GATHER_LDS 65536
+
+/*
+ * swr_planner_set_gather_lds -- LDS, in bytes, that each workgroup of the
+ * planner's copy-kernel gathers reserves and never touches (0, the default:
+ * none).  It only limits how many copy workgroups share a CU.  On one GPU the
+ * gather of layer l+1 and the GEMMs of layer l share the CUs and HBM, and the
+ * copy's many short workgroups otherwise crowd out the GEMMs' long-lived ones;
+ * the weight_sharding page's copy-engine gather exists so that the copy does
+ * not take compute units from the GEMMs (NCCL policy / copy engine section),
+ * and this is the compute-unit copy's way to yield them.  A reservation R
+ * leaves floor(160 KB / R) copy workgroups per idle CU and
+ * floor((160 KB - G) / R) beside compute workgroups holding G bytes of LDS.
+ * The copy alone keeps its bandwidth with two workgroups per CU (R up to
+ * 64 KB).  The DMA engine (SWR_ENGINE_DMA) ignores it.  Host only; applies to
+ * gathers enqueued from now on.
+ * Errors: SWR_E_INVALID (null planner, bytes outside [0, SWR_MAX_GATHER_LDS]).
+ */
+int swr_planner_set_gather_lds(swr_planner* p, int32_t bytes);
+
 /* Cyclic mode, for a model that runs the same layers forward after forward.
  * The pages move the draft model's first-layer gather out of the loop so it
  * overlaps other work (weight_sharding, "CUDA graph and the draft model");

@@ -36,7 +36,7 @@ TRACE_STREAMS = {0: "compute", 1: "side"}
 EXPORTS = (
     "swr_plan_layer", "swr_pack_layer", "swr_redistribute_row_shards", "swr_reassemble_into_slot",
     "swr_reassemble_into_slot_dma",
-    "swr_planner_set_copy_engine", "swr_planner_set_gate", "swr_proj_forward",
+    "swr_planner_set_copy_engine", "swr_planner_set_gate", "swr_planner_set_gather_lds", "swr_proj_forward",
     "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward",
     "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
@@ -109,6 +109,7 @@ def lib() -> ctypes.CDLL:
                                                 ctypes.POINTER(_i64)]),
         "swr_planner_set_copy_engine": (_i32, [_vp, _i32]),
         "swr_planner_set_gate": (_i32, [_vp, _i32]),
+        "swr_planner_set_gather_lds": (_i32, [_vp, _i32]),
         "swr_proj_forward": (_i32, [_vp, _i32, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i32, _i64, _vp, _i64, _vp]),
         "swr_proj_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
         "swr_proj_forward_grouped": (_i32, [ctypes.POINTER(ProjDesc), _i32, _i64, _vp, _i64, _vp]),
@@ -425,6 +426,10 @@ class Planner:
     def set_copy_engine(self, engine: int) -> None:
         """ENGINE_KERNEL (the copy kernel, default) or ENGINE_DMA (the DMA engines)."""
         _check("swr_planner_set_copy_engine", lib().swr_planner_set_copy_engine(self._h, int(engine)))
+
+    def set_gather_lds(self, nbytes: int) -> None:
+        """LDS each copy workgroup of the planner's gathers reserves, to leave CUs to the GEMMs (0: none)."""
+        _check("swr_planner_set_gather_lds", lib().swr_planner_set_gather_lds(self._h, int(nbytes)))
 
     def set_timing(self, capacity: int) -> None:
         """Time the copies of the next dispatches in a ring of `capacity` event pairs (0: off)."""

@@ -190,8 +190,10 @@ int grid_for(int64_t work_items, int per_block_items) {
 
 }  // namespace
 
+// lds_bytes: LDS each workgroup reserves and never touches (see
+// swr_planner_set_gather_lds); it only limits how many share a CU.
 hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chunk_bytes, void* slot,
-                             hipStream_t stream) {
+                             unsigned lds_bytes, hipStream_t stream) {
   const int64_t chunk_vecs = chunk_bytes / 16;
   int64_t span = kCopySpanVecs;
 #ifdef SWR_TUNING
@@ -213,7 +215,7 @@ hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chun
   }
 #endif
   const dim3 grid = dim3(unsigned(blocks), unsigned(n_chunks));
-  hipLaunchKernelGGL(reassemble_kernel, grid, dim3(kThreads), 0, stream, chunks, static_cast<u32x4*>(slot),
+  hipLaunchKernelGGL(reassemble_kernel, grid, dim3(kThreads), lds_bytes, stream, chunks, static_cast<u32x4*>(slot),
                      chunk_vecs, span);
   return hipGetLastError();
 }
@@ -371,7 +373,7 @@ namespace {
 // gate wait, the copy and the ready record are enqueued on `side`.
 int reassemble(const char* fn, const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes, void* slot,
                int64_t slot_bytes, int32_t self_rank, hipStream_t side, hipEvent_t gate, hipEvent_t ready,
-               int64_t* remote_bytes, bool dma) {
+               int64_t* remote_bytes, bool dma, unsigned lds_bytes) {
   if (!chunk_dev || !slot) return fail(SWR_E_INVALID, "%s: null pointer", fn);
   if (n_chunks < 1 || n_chunks > SWR_MAX_CHUNKS)
     return fail(SWR_E_INVALID, "%s: n_chunks=%d outside [1, %d]", fn, n_chunks, SWR_MAX_CHUNKS);
@@ -402,7 +404,7 @@ int reassemble(const char* fn, const void* const* chunk_dev, int32_t n_chunks, i
       if (e != hipSuccess) return swr::hip_fail(e, "reassembly: DMA copy");
     }
   } else {
-    e = swr::launch_reassemble(ptrs, n_chunks, chunk_bytes, slot, side);
+    e = swr::launch_reassemble(ptrs, n_chunks, chunk_bytes, slot, lds_bytes, side);
     if (e != hipSuccess) return swr::hip_fail(e, "reassembly: launch");
   }
   if (ready) {
@@ -420,14 +422,23 @@ extern "C" int swr_reassemble_into_slot(const void* const* chunk_dev, int32_t n_
                                         void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
                                         hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes) {
   return reassemble("swr_reassemble_into_slot", chunk_dev, n_chunks, chunk_bytes, slot, slot_bytes, self_rank, side,
-                    gate, ready, remote_bytes, false);
+                    gate, ready, remote_bytes, false, 0);
 }
+
+namespace swr {
+int reassemble_reserving(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes, void* slot,
+                         int64_t slot_bytes, int32_t self_rank, hipStream_t side, hipEvent_t gate, hipEvent_t ready,
+                         int64_t* remote_bytes, unsigned lds_bytes) {
+  return reassemble("swr_reassemble_into_slot", chunk_dev, n_chunks, chunk_bytes, slot, slot_bytes, self_rank, side,
+                    gate, ready, remote_bytes, false, lds_bytes);
+}
+}  // namespace swr
 
 extern "C" int swr_reassemble_into_slot_dma(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes,
                                             void* slot, int64_t slot_bytes, int32_t self_rank, hipStream_t side,
                                             hipEvent_t gate, hipEvent_t ready, int64_t* remote_bytes) {
   return reassemble("swr_reassemble_into_slot_dma", chunk_dev, n_chunks, chunk_bytes, slot, slot_bytes, self_rank,
-                    side, gate, ready, remote_bytes, true);
+                    side, gate, ready, remote_bytes, true, 0);
 }
 
 extern "C" int swr_sum_partials(const float* const* parts, int32_t n, int64_t count, void* out, int32_t out_bf16,

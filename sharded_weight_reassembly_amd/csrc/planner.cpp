@@ -47,6 +47,8 @@ struct swr_planner {
 
   // gather engine: 0 the copy kernel, 1 the DMA engines
   int32_t engine = 0;
+  // LDS each copy workgroup of the planner's gathers reserves (0: none)
+  int32_t gather_lds = 0;
 
   // gate mode: each gather of layer l+1 waits for the compute stream to begin
   // layer l (after its ready(l) wait) instead of done(l-1); the gather is
@@ -121,7 +123,13 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false, hipEvent_t be
   const int s = p->slot_of(layer);
   int64_t remote = 0;
   int rc;
-  auto gather = p->engine == SWR_ENGINE_DMA ? swr_reassemble_into_slot_dma : swr_reassemble_into_slot;
+  const unsigned lds = unsigned(p->gather_lds);
+  auto gather = [p, lds](const void* const* chunks, int32_t n, int64_t c, void* slot, int64_t slot_bytes, int32_t rank,
+                         hipStream_t side, hipEvent_t g, hipEvent_t ready, int64_t* remote_bytes) {
+    if (p->engine == SWR_ENGINE_DMA)
+      return swr_reassemble_into_slot_dma(chunks, n, c, slot, slot_bytes, rank, side, g, ready, remote_bytes);
+    return swr::reassemble_reserving(chunks, n, c, slot, slot_bytes, rank, side, g, ready, remote_bytes, lds);
+  };
   if (p->t0.empty()) {
     rc = gather(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s], p->slot_bytes, 0, p->side, gate,
                 p->ready[i], &remote);
@@ -392,6 +400,15 @@ extern "C" int swr_planner_set_copy_engine(swr_planner* p, int32_t engine) {
   if (engine != SWR_ENGINE_KERNEL && engine != SWR_ENGINE_DMA)
     return fail(SWR_E_INVALID, "swr_planner_set_copy_engine: unknown engine %d", engine);
   p->engine = engine;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_gather_lds(swr_planner* p, int32_t bytes) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_set_gather_lds: null pointer");
+  if (bytes < 0 || bytes > SWR_MAX_GATHER_LDS)
+    return fail(SWR_E_INVALID, "swr_planner_set_gather_lds: %d bytes outside [0, %d]", bytes, SWR_MAX_GATHER_LDS);
+  p->gather_lds = bytes;
   swr::clear_error();
   return SWR_OK;
 }

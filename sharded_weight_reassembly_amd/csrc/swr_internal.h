@@ -38,7 +38,12 @@ struct RedistArgs {
 hipError_t launch_redistribute(const RedistArgs& a, hipStream_t stream);
 
 hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chunk_bytes, void* slot,
-                             hipStream_t stream);
+                             unsigned lds_bytes, hipStream_t stream);
+// swr_reassemble_into_slot whose copy workgroups each reserve lds_bytes of
+// LDS (the planner's gather, swr_planner_set_gather_lds).
+int reassemble_reserving(const void* const* chunk_dev, int32_t n_chunks, int64_t chunk_bytes, void* slot,
+                         int64_t slot_bytes, int32_t self_rank, hipStream_t side, hipEvent_t gate, hipEvent_t ready,
+                         int64_t* remote_bytes, unsigned lds_bytes);
 
 struct PackPlan {
   const void* src[SWR_MAX_WEIGHTS];

@@ -240,3 +240,4 @@ def test_planner_errors_without_gpu_work():
     assert L.swr_planner_create(0, 4, 1, 2, None, a, 4096, ctypes.byref(h)) == swr.E_INVALID
     assert L.swr_planner_reset(None) == swr.E_INVALID
     assert L.swr_planner_set_copy_engine(None, 0) == swr.E_INVALID
+    assert L.swr_planner_set_gather_lds(None, 0) == swr.E_INVALID

@@ -16,6 +16,7 @@ import torch
 import sharded_weight_reassembly_amd as swr
 import synth
 from oracle import accounting, gemm
+from oracle import layout as olayout
 from oracle import scheduler as osch
 
 from gpu_util import DEV, assert_close_rows, bf16, note, u8, values
@@ -242,15 +243,62 @@ def test_dma_engine_planner(start, n_layers, cyclic):
     p.close()
 
 
-@pytest.mark.parametrize("engine,gate", [(swr.ENGINE_KERNEL, swr.GATE_DONE), (swr.ENGINE_DMA, swr.GATE_DONE),
-                                         (swr.ENGINE_KERNEL, swr.GATE_BEGIN)])
-def test_forward_captured_in_a_graph(engine, gate):
+@pytest.mark.parametrize("gather_lds,gate", [(57344, swr.GATE_DONE), (32768, swr.GATE_BEGIN), (65536, swr.GATE_DONE)])
+def test_gather_lds_reservation(gather_lds, gate):
+    """Copy workgroups that reserve LDS (fewer per CU): the same launch/wait
+    sequence, slots bit-exact to the flat buffer, outputs equal to the oracle;
+    reservations outside [0, 64 KiB] are refused."""
+    note(f"planner gather_lds={gather_lds} gate={gate}")
+    wl = synth.TINY
+    n_layers = 4
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    p = swr.Planner(0, n_layers, torch.cuda.current_stream(), torch.cuda.Stream(), slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
+    for bad in (-1, 65537):
+        with pytest.raises(swr.SwrError) as e:
+            p.set_gather_lds(bad)
+        assert e.value.code == swr.E_INVALID
+    p.set_gather_lds(gather_lds)
+    p.set_gate(gate)
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    traces = []
+    for _ in range(2):
+        outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+        _forward(p, layers, 0, xd, outs, wsb)
+        traces.append(p.trace())
+        torch.cuda.synchronize()
+        for i, L in enumerate(layers):
+            ws = L["ws"]
+            _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)
+            assert_close_rows(values(outs[i]), ref, what=f"gather_lds={gather_lds} layer {i}")
+    g = "begin" if gate == swr.GATE_BEGIN else "done"
+    assert all(t == osch.expected_trace(0, n_layers, gate=g) for t in traces)
+    assert osch.check_trace(traces) == []
+    # the last layer's slot holds the oracle's flat buffer bit for bit
+    last = slot_b if (n_layers - 1) % 2 else slot_a
+    plan = olayout.plan_layer([(o, i, d) for _, o, i, d in wl.weights], wl.n_chunks)
+    t_ref, _ = olayout.pack_layer(plan, [w.raw() for w in layers[-1]["ws"]])
+    assert np.array_equal(last.cpu().numpy(), t_ref)
+    p.close()
+
+
+@pytest.mark.parametrize("engine,gate,gather_lds", [(swr.ENGINE_KERNEL, swr.GATE_DONE, 0),
+                                                    (swr.ENGINE_DMA, swr.GATE_DONE, 0),
+                                                    (swr.ENGINE_KERNEL, swr.GATE_BEGIN, 0),
+                                                    (swr.ENGINE_KERNEL, swr.GATE_DONE, 57344)])
+def test_forward_captured_in_a_graph(engine, gate, gather_lds):
     """weight_sharding, CUDA graph section: the launch/wait sequence is fixed,
     so one forward (gathers on the side stream, MLPs on the compute stream)
     can be captured once and replayed.  Between replays both slots and every
     output are overwritten with garbage by eager work; each replay must
     gather again and reproduce the oracle's outputs."""
-    note(f"graph capture engine={engine}")
+    note(f"graph capture engine={engine} gate={gate} gather_lds={gather_lds}")
     wl = synth.TINY
     n_layers = 4
     layers = _layers(wl, n_layers, wl.n_chunks)
@@ -263,6 +311,7 @@ def test_forward_captured_in_a_graph(engine, gate):
         p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
     p.set_copy_engine(engine)
     p.set_gate(gate)
+    p.set_gather_lds(gather_lds)
     x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
     xd = bf16(x)
     outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
