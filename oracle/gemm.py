@@ -13,6 +13,11 @@ split, names the same gate_up -> SiLU x up -> down chain):
   h = bf16( silu(G[:, :I]) * G[:, I:] )
   Y = bf16( (h @ dec(W_down)^T) * s_d )
 
+FP8-activation MLP (an option beyond the pages; numerics.quantize_rows_e4m3):
+  X is quantised per token, G = (dec(q_X) @ dec(W_gate_up)^T) * s_X[:, None] * s_gu,
+  h = bf16( silu(G[:, :I]) * G[:, I:] ) is quantised per token in turn, and
+  Y = bf16( (dec(q_h) @ dec(W_down)^T) * s_h[:, None] * s_d ).
+
 Sharded matmul (copecc.github.io sharded-matrices notes, "local matmul"
 cases): X[B, D] @ W[D, F].  Splitting F (the output columns) leaves the
 contraction whole, so every shard is a finished slice of Y (case 1);
@@ -22,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_to_f64, decode_weight, f64_to_bf16_bits, silu
+from .numerics import bf16_to_f64, decode_weight, f64_to_bf16_bits, fp8_to_f64, quantize_rows_e4m3, silu
 
 
 def proj_f64(x_bits: np.ndarray, w_raw: np.ndarray, dtype: str, out_f: int, in_f: int,
@@ -84,6 +89,27 @@ def mlp_intermediate_slice_f64(x_bits, w_gu_raw, s_gu, w_d_raw, s_d, dtype, hidd
     sub_d = np.ascontiguousarray(w_d[:, lo * elem:hi * elem])
     _, _, y = mlp_f64(x_bits, sub_gu, sub_s_gu, sub_d, s_d, dtype, hidden, hi - lo)
     return y
+
+
+def proj_fp8act_f64(x: np.ndarray, w_raw, out_f: int, in_f: int, scale) -> tuple:
+    """FP8 weights, FP8 activations: X (float values of bf16 tokens) is
+    quantised per token; returns (q_x, s_x, unrounded Y float64 [M, out])."""
+    q_x, s_x = quantize_rows_e4m3(np.asarray(x, dtype=np.float64).reshape(-1, in_f))
+    w = decode_weight(w_raw, "fp8_e4m3fn", out_f, in_f)
+    y = (fp8_to_f64(q_x) @ w.T) * s_x.astype(np.float64)[:, None]
+    if scale is not None:
+        y = y * np.asarray(scale, dtype=np.float32).astype(np.float64)[None, :]
+    return q_x, s_x, y
+
+
+def mlp_fp8act_f64(x_bits, w_gu_raw, s_gu, w_d_raw, s_d, hidden, inter):
+    """FP8 weights and FP8 activations.  Returns (q_x, s_x, G float64 [M, 2I],
+    h bf16 bits [M, I], q_h, s_h, Y float64 unrounded [M, H])."""
+    q_x, s_x, g = proj_fp8act_f64(bf16_to_f64(x_bits), w_gu_raw, 2 * inter, hidden, s_gu)
+    with np.errstate(over="ignore"):
+        h_bits = f64_to_bf16_bits(silu(g[:, :inter]) * g[:, inter:])
+    q_h, s_h, y = proj_fp8act_f64(bf16_to_f64(h_bits), w_d_raw, hidden, inter, s_d)
+    return q_x, s_x, g, h_bits, q_h, s_h, y
 
 
 # ---------------------------------------------------------------- sharded matmul

@@ -11,6 +11,12 @@
   outside it; the weight value is decode(code) * scale[row].
 * SiLU(z) = z / (1 + exp(-z)) (the gate activation of the shared-expert MLP,
   vLLM PR #50656 report, test code section).
+* FP8 activations (an option beyond the pages, which keep activations in
+  BF16): a token row x is quantised to E4M3FN codes with one fp32 scale,
+  s = amax(|x|) / 448 in binary32 (s = 1 for an all-zero row); each code is
+  the E4M3FN value nearest to the binary32 quotient x / s, ties to the even
+  code, magnitudes above 448 saturating to 448 -- the definition written out
+  as an argmin over the format's value table, not as bit arithmetic.
 """
 from __future__ import annotations
 
@@ -71,3 +77,31 @@ def decode_weight(raw: np.ndarray, dtype: str, out_f: int, in_f: int) -> np.ndar
 def silu(z: np.ndarray) -> np.ndarray:
     z = np.asarray(z, dtype=np.float64)
     return z / (1.0 + np.exp(-z))
+
+
+# the non-negative finite E4M3FN values, increasing with the code 0x00..0x7E
+_E4M3_POS = FP8_E4M3FN_TABLE[:0x7F]
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """E4M3FN codes of binary32 values: nearest finite value, ties to the even
+    code, magnitudes above 448 saturate; the sign bit is the input's."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.minimum(np.abs(y).astype(np.float64), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return code | (np.signbit(y).astype(np.uint8) << np.uint8(7))
+
+
+def quantize_rows_e4m3(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row E4M3FN quantisation of float values (bf16 values as float64 or
+    float32): returns (codes uint8 [rows, cols], scales float32 [rows])."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (x32 / s[:, None]).astype(np.float32)
+    return e4m3_encode(q), s
