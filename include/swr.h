@@ -313,6 +313,43 @@ int swr_mlp_forward_partial(const void* W_gate_up, const float* s_gu, const void
 int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int32_t dtype);
 
 /*
+ * FP8 activations (an option beyond the pages, which keep activations in
+ * BF16; the weight_sharding page's FP8 variant quantises the weights only).
+ *
+ * swr_quantize_rows_e4m3 -- per-token quantisation of BF16 rows:
+ *   S[m] = max_k |X[m, k]| / 448 in binary32 (1 for an all-zero row),
+ *   Q[m, k] = the E4M3FN value nearest to the binary32 quotient X[m, k] / S[m],
+ *   ties to the even code, magnitudes above 448 saturating to 448.
+ * X: M x K BF16, row stride ldx elements (X 16-byte aligned, ldx % 8 == 0);
+ * Q: M x K E4M3FN codes, row stride ldq bytes (Q 8-byte aligned, ldq % 8 ==
+ * 0); S: M floats.  Finite inputs.  Enqueued on `stream`; caller-owned memory.
+ * Errors: SWR_E_INVALID (null pointer), SWR_E_SHAPE (M < 0, K < 1, ld < K),
+ * SWR_E_ALIGN, SWR_E_HIP.
+ */
+int swr_quantize_rows_e4m3(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q, int64_t ldq, float* S,
+                           hipStream_t stream);
+
+/*
+ * swr_mlp_forward_fp8act -- the shared-expert MLP with FP8 weights and FP8
+ * activations on the FP8 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4):
+ *   (q_x, s_x) = quantize(X);  G = (q_x @ W_gate_up^T) * s_x[m] * s_gu[o];
+ *   h = bf16(silu(G[:, :I]) * G[:, I:]);  (q_h, s_h) = quantize(h);
+ *   Y = bf16((q_h @ W_down^T) * s_h[m] * s_d[o]),
+ * fp32 accumulation, quantize as in swr_quantize_rows_e4m3.  Weights and
+ * layouts as swr_mlp_forward with dtype SWR_FP8_E4M3FN; H and I multiples of
+ * 64; s_gu and s_d required.  The workspace (swr_mlp_fp8act_workspace_bytes,
+ * 256-byte aligned) holds the codes and scales of X and h, and h.  Every M is
+ * accepted; the tiled kernels suit prefill-sized M.
+ * Errors: SWR_E_INVALID (null pointer), SWR_E_SHAPE (sizes, weights of 2 GiB
+ * or more), SWR_E_ALIGN, SWR_E_CAPACITY (workspace), SWR_E_HIP.
+ */
+int swr_mlp_forward_fp8act(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d, int64_t H,
+                           int64_t I, const void* X, int64_t M, void* Y, void* workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
+int64_t swr_mlp_fp8act_workspace_bytes(int64_t M, int64_t H, int64_t I);
+
+
+/*
  * swr_sum_partials -- enqueue on `stream`.
  * Sharded-matrices notes (copecc.github.io), local matmul case 3: when the
  * contraction dimension is split, each shard yields a partial result and

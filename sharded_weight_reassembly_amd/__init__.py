@@ -38,7 +38,8 @@ EXPORTS = (
     "swr_reassemble_into_slot_dma",
     "swr_planner_set_copy_engine", "swr_planner_set_gate", "swr_planner_set_gather_lds", "swr_proj_forward",
     "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward",
-    "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials",
+    "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials", "swr_quantize_rows_e4m3",
+    "swr_mlp_forward_fp8act", "swr_mlp_fp8act_workspace_bytes",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
@@ -118,6 +119,9 @@ def lib() -> ctypes.CDLL:
         "swr_mlp_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
         "swr_mlp_forward_partial": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
         "swr_sum_partials": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i32, _vp]),
+        "swr_quantize_rows_e4m3": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
+        "swr_mlp_forward_fp8act": (_i32, [_vp, _vp, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
+        "swr_mlp_fp8act_workspace_bytes": (_i64, [_i64, _i64, _i64]),
         "swr_planner_create": (_i32, [_i32, _i32, _vp, _vp, _vp, _vp, _i64, ctypes.POINTER(_vp)]),
         "swr_planner_set_layer": (_i32, [_vp, _i32, ctypes.POINTER(_vp), _i32, _i64]),
         "swr_planner_reset": (_i32, [_vp]),
@@ -367,6 +371,31 @@ def mlp_forward_partial(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter:
            lib().swr_mlp_forward_partial(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), _dtype(dtype),
                                          int(hidden), int(inter), _ptr(x), int(m), _ptr(y), _ptr(workspace),
                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def quantize_rows_e4m3(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, m: int | None = None,
+                       stream=None) -> None:
+    """Per-token E4M3FN codes q [M, K] (uint8) and scales s [M] (fp32) of bf16 rows x [M, K]."""
+    if m is None:
+        m = x.shape[0]
+    k = x.shape[1]
+    _check("swr_quantize_rows_e4m3", lib().swr_quantize_rows_e4m3(_ptr(x), x.stride(0), int(m), int(k), _ptr(q),
+                                                                  q.stride(0), _ptr(s), _stream(stream)))
+
+
+def mlp_fp8act_workspace_bytes(m: int, hidden: int, inter: int) -> int:
+    return _check("swr_mlp_fp8act_workspace_bytes", lib().swr_mlp_fp8act_workspace_bytes(m, hidden, inter))
+
+
+def mlp_forward_fp8act(w_gate_up, s_gu, w_down, s_d, hidden: int, inter: int, x: torch.Tensor, y: torch.Tensor,
+                       workspace: torch.Tensor, m: int | None = None, stream=None) -> None:
+    """The MLP with FP8 weights and per-token FP8 activations (X and h quantised)."""
+    if m is None:
+        m = x.shape[0]
+    _check("swr_mlp_forward_fp8act",
+           lib().swr_mlp_forward_fp8act(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), int(hidden), int(inter),
+                                        _ptr(x), int(m), _ptr(y), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def sum_partials(parts, out: torch.Tensor, count: int | None = None, stream=None) -> None:

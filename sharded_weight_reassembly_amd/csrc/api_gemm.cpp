@@ -300,3 +300,75 @@ extern "C" int swr_mlp_forward_partial(const void* W_gate_up, const float* s_gu,
   return mlp_impl("swr_mlp_forward_partial", W_gate_up, s_gu, W_down, s_d, dtype, H, I, X, M, Y, true, workspace,
                   workspace_bytes, stream);
 }
+
+// ---------------------------------------------------------------- FP8 activations
+
+namespace {
+
+// Workspace of swr_mlp_forward_fp8act: [q_x: M*H][s_x: M][h: M*I bf16][q_h: M*I][s_h: M], 256-byte sections.
+struct Fp8ActSections {
+  int64_t qx, sx, h, qh, sh, total;
+};
+
+Fp8ActSections fp8act_sections(int64_t M, int64_t H, int64_t I) {
+  Fp8ActSections w{};
+  w.qx = 0;
+  w.sx = w.qx + round_up(M * H, kWorkspaceAlign);
+  w.h = w.sx + round_up(M * 4, kWorkspaceAlign);
+  w.qh = w.h + round_up(M * I * 2, kWorkspaceAlign);
+  w.sh = w.qh + round_up(M * I, kWorkspaceAlign);
+  w.total = w.sh + round_up(M * 4, kWorkspaceAlign);
+  return w;
+}
+
+}  // namespace
+
+extern "C" int64_t swr_mlp_fp8act_workspace_bytes(int64_t M, int64_t H, int64_t I) {
+  if (int rc = check_sizes("swr_mlp_fp8act_workspace_bytes", M, H, 2 * I)) return rc;
+  swr::clear_error();
+  return fp8act_sections(M, H, I).total;
+}
+
+extern "C" int swr_mlp_forward_fp8act(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
+                                      int64_t H, int64_t I, const void* X, int64_t M, void* Y, void* workspace,
+                                      int64_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "swr_mlp_forward_fp8act";
+  if (!W_gate_up || !W_down || !X || !Y || !workspace || !s_gu || !s_d)
+    return fail(SWR_E_INVALID, "%s: null pointer (FP8 weights need row scales)", fn);
+  if (int rc = check_sizes(fn, M, H, 2 * I)) return rc;
+  if (H % 64 != 0 || I % 64 != 0)
+    return fail(SWR_E_SHAPE, "%s: H=%lld and I=%lld must be multiples of 64", fn, (long long)H, (long long)I);
+  if (2 * I * H >= (INT64_C(1) << 31) || H * I >= (INT64_C(1) << 31) || H >= (INT64_C(1) << 22) ||
+      I >= (INT64_C(1) << 22))
+    return fail(SWR_E_SHAPE, "%s: weights of 2 GiB or more", fn);
+  if (!aligned(W_gate_up, 16) || !aligned(W_down, 16) || !aligned(X, 16) || !aligned(Y, 16) || !aligned(s_gu, 16) ||
+      !aligned(s_d, 16))
+    return fail(SWR_E_ALIGN, "%s: weights, scales, X and Y must be 16-byte aligned", fn);
+  if (!aligned(workspace, kWorkspaceAlign)) return fail(SWR_E_ALIGN, "%s: workspace must be 256-byte aligned", fn);
+  const Fp8ActSections w = fp8act_sections(M, H, I);
+  if (workspace_bytes < w.total)
+    return fail(SWR_E_CAPACITY, "%s: workspace holds %lld bytes, needs %lld", fn, (long long)workspace_bytes,
+                (long long)w.total);
+  if (M == 0) {
+    swr::clear_error();
+    return SWR_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  void* qx = ws + w.qx;
+  float* sx = reinterpret_cast<float*>(ws + w.sx);
+  void* h = ws + w.h;
+  void* qh = ws + w.qh;
+  float* sh = reinterpret_cast<float*>(ws + w.sh);
+  hipError_t e = swr::launch_quantize_rows(X, H, M, H, qx, H, sx, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "mlp fp8act: quantize X");
+  const swr::GemmProblem gu = mlp_gate_up(W_gate_up, s_gu, SWR_FP8_E4M3FN, H, I, qx, M, h);
+  e = swr::launch_tile_fp8act(gu, sx, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "mlp fp8act: gate_up launch");
+  e = swr::launch_quantize_rows(h, I, M, I, qh, I, sh, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "mlp fp8act: quantize h");
+  const swr::GemmProblem dn = mlp_down(W_down, s_d, SWR_FP8_E4M3FN, H, I, qh, M, Y);
+  e = swr::launch_tile_fp8act(dn, sh, stream);
+  if (e != hipSuccess) return swr::hip_fail(e, "mlp fp8act: down launch");
+  swr::clear_error();
+  return SWR_OK;
+}

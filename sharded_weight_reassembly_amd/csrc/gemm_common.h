@@ -20,6 +20,7 @@ struct StreamArgs {
   void* Y;
   int64_t ldy;
   float* partial;  // [ksplit][M][rows] when ksplit > 1
+  const float* xscale;  // tiled kernels, FP8 activations: one scale per token (X holds E4M3FN codes)
   int mode;
   int ksplit;
 };

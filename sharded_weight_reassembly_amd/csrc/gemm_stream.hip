@@ -1158,6 +1158,18 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
   return fp8 ? launch_grouped_mt<4, 4, true>(ga, grid, stream) : launch_grouped_mt<4, 4, false>(ga, grid, stream);
 }
 
+hipError_t launch_tile_fp8act(const GemmProblem& p, const float* xscale, hipStream_t stream) {
+  if (p.M == 0) return hipSuccess;
+  const bool silu_mode = p.mode == OUT_SILU_BF16;
+  const int64_t cols = silu_mode ? p.rows / 2 : p.rows;
+  const int64_t tiles_m = (p.M + 255) / 256;
+  // 256-row weight tiles when they still give two waves of workgroups (as plan_gemm)
+  const int64_t t256 = tiles_m * ((cols + (silu_mode ? 127 : 255)) / (silu_mode ? 128 : 256));
+  StreamArgs a = make_args(p, p.K, 1, nullptr, 0);
+  a.xscale = xscale;
+  return launch_tile_gemm(a, t256 >= 512 ? 256 : 128, true, stream);
+}
+
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream) {
   StreamArgs a = make_args(p, plan.kper, plan.ksplit, partial, plan.rb);
   const bool fp8 = p.dtype == SWR_FP8_E4M3FN;

@@ -31,6 +31,7 @@ namespace swr {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kTileM = 256;
@@ -81,7 +82,8 @@ __device__ inline int64_t w_row(const StreamArgs& a, int64_t tile_n, int c) {
 // 8*(v/4) + 4*(l/32) + v%4; scale, SiLU*up, rounding.
 template <int BN, int WN, int TM, int TN>
 __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t tile_n,
-                                     int wm, int wn, int r32, int kg, const float* lds_scale = nullptr) {
+                                     int wm, int wn, int r32, int kg, const float* lds_scale = nullptr,
+                                     const float* lds_tscale = nullptr) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int tn_out = silu_mode ? TN / 2 : TN;
 #pragma unroll
@@ -102,11 +104,13 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
     for (int x = 0; x < TM; ++x) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * 128 + x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
+        const int ml = wm * 128 + x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
+        const int64_t m = m0 + ml;
         if (m >= a.M) continue;
-        float out = acc[x][y][v] * sc;
+        const float ts = lds_tscale ? lds_tscale[ml] : 1.f;  // token scale (FP8 activations)
+        float out = acc[x][y][v] * ts * sc;
         if (silu_mode) {
-          const float u = acc[x][y + TN / 2][v] * su;
+          const float u = acc[x][y + TN / 2][v] * ts * su;
           out = silu(out) * u;
           static_cast<uint16_t*>(a.Y)[m * a.ldy + ocol] = bf16_bits(out);
         } else if (a.mode == OUT_F32) {
@@ -316,17 +320,23 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
 //   * per step: wait until this wave's loads of step t have landed, barrier,
 //     issue the loads of step t + 3 into the stage that step t - 1 read,
 //     multiply step t.
+// F8 = true: FP8 weights and FP8 activations (codes of both operands, one
+// fp32 scale per token in StreamArgs::xscale).  A 64-byte row then holds 64 K,
+// so a step is 64 K with the same stage bytes and LDS layout, multiplied by
+// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, no block scale): lane group
+// g reads pieces 2g and 2g + 1 (K = 32g .. 32g + 31).
 constexpr int kStepK16 = 32;
 
-template <int BN, int WAVES>
+template <int BN, int WAVES, bool F8 = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArgs a) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = 4;
   constexpr int TN = WN / 32;
-  constexpr int BK = kStepK16;
-  constexpr int A_BYTES = kTileM * BK * 2;  // 16 KB
-  constexpr int B_BYTES = BN * BK * 2;
+  constexpr int EB = F8 ? 1 : 2;            // bytes per element of both operands
+  constexpr int BK = F8 ? 64 : kStepK16;    // K per step: 64 bytes of every row
+  constexpr int A_BYTES = kTileM * BK * EB;  // 16 KB
+  constexpr int B_BYTES = BN * BK * EB;
   constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per step
   constexpr int NB = B_BYTES / 1024 / WAVES;  // 1 KB loads of W per wave per step
   static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
@@ -335,6 +345,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
   __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[B_BYTES], b3[B_BYTES];
   // first in LDS, for the same reason as in the FP8 kernel
   __shared__ __attribute__((aligned(4096))) float row_scale[BN];
+  __shared__ float tok_scale[F8 ? kTileM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -346,9 +357,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
     row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
   }
+  if constexpr (F8)
+    for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
 
-  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * 2);
-  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * 2);
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * EB);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * EB);
   // Source offsets of this lane's pieces (step 0): a load fills rows
   // 16 * i .. 16 * i + 15 of the stage, lane l position l % 4 of row l / 4;
   // rows past the end are read from the last row and never stored.
@@ -358,20 +371,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
     const int row = (wave * NA + i) * 16 + lane / 4;
     const int q = (lane % 4) ^ ((row >> 2) & 3);
     const int64_t m = min(m0 + row, a.M - 1);
-    aoff[i] = int((m * a.ldx + q * 8) * 2);
+    aoff[i] = int(m * a.ldx * EB + q * 16);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int row = (wave * NB + i) * 16 + lane / 4;
     const int q = (lane % 4) ^ ((row >> 2) & 3);
     const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
-    boff[i] = int((r * a.K + q * 8) * 2);
+    boff[i] = int(r * a.K * EB + q * 16);
   }
   auto issue = [&](uint8_t* A, uint8_t* B, int kt) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kt * BK * 2);
+    for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kt * 64);
 #pragma unroll
-    for (int i = 0; i < NB; ++i) lds_load16<true>(wres, B + (wave * NB + i) * 1024, boff[i], kt * BK * 2);
+    for (int i = 0; i < NB; ++i) lds_load16<true>(wres, B + (wave * NB + i) * 1024, boff[i], kt * 64);
   };
 
   const int r32 = lane & 31, kg = lane >> 5;
@@ -382,6 +395,25 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
     for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
 
   auto compute = [&](const uint8_t* A, const uint8_t* B) {
+    if constexpr (F8) {
+      // 32 codes per lane: pieces 2g and 2g + 1 of its row
+      i32x8 fa[TM], fb[TN];
+      auto frag = [&](const uint8_t* base, int row) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + wswz(row, 2 * kg) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + wswz(row, 2 * kg + 1) * 16);
+        return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+      };
+#pragma unroll
+      for (int x = 0; x < TM; ++x) fa[x] = frag(A, wm * 128 + x * 32 + r32);
+#pragma unroll
+      for (int y = 0; y < TN; ++y) fb[y] = frag(B, wn * WN + y * 32 + r32);
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[x], fb[y], acc[x][y], 0, 0, 0, 0, 0, 0);
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       bf16x8 fa[TM], fb[TN];
@@ -435,7 +467,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
   if (kt < nk) step(a0, b0, a3, b3, kt);
   if (kt + 1 < nk) step(a1, b1, a0, b0, kt + 1);
   if (kt + 2 < nk) step(a2, b2, a1, b1, kt + 2);
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
 }
 
 template <int BN>
@@ -448,9 +480,9 @@ dim3 tile_grid(const StreamArgs& a) {
   return dim3(unsigned(tiles_m * tiles_n));
 }
 
-template <int BN, int WAVES>
+template <int BN, int WAVES, bool F8 = false>
 hipError_t launch_bf16_lds(const StreamArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tile_gemm_bf16_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  hipLaunchKernelGGL((tile_gemm_bf16_kernel<BN, WAVES, F8>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -465,15 +497,22 @@ hipError_t launch_fp8(const StreamArgs& a, hipStream_t stream) {
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
   // The kernels address X through 32-bit buffer offsets: tokens go in parts
   // whose X spans less than 2 GiB (whole 256-token tiles).
-  const int64_t x_row = a.ldx * 2;
+  const bool f8x = a.xscale != nullptr;  // FP8 activations (FP8 weights too)
+  const int64_t x_row = a.ldx * (f8x ? 1 : 2);
   int64_t part = ((INT64_C(1) << 31) - 1) / x_row / kTileM * kTileM;
   if (part < kTileM) return hipErrorInvalidValue;  // a 256-token tile alone would exceed 2 GiB
   const int64_t y_elem = a.mode == OUT_F32 ? 4 : 2;
   for (int64_t m0 = 0; m0 < a.M; m0 += part) {
     StreamArgs p = a;
     p.M = a.M - m0 < part ? a.M - m0 : part;
-    p.X = a.X + m0 * a.ldx;
+    p.X = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.X) + m0 * x_row);
     p.Y = static_cast<uint8_t*>(a.Y) + m0 * a.ldy * y_elem;
+    if (f8x) {
+      p.xscale = a.xscale + m0;
+      hipError_t e = bn == 256 ? launch_bf16_lds<256, 8, true>(p, stream) : launch_bf16_lds<128, 4, true>(p, stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
     // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
     // waits on LDS and barriers are covered by the other's MFMAs
     hipError_t e;

@@ -73,7 +73,7 @@ struct GemmProblem {
   const void* W;
   int dtype;
   const float* scale;  // may be null
-  const void* X;       // bf16
+  const void* X;       // bf16 (E4M3FN codes for launch_tile_fp8act)
   int64_t ldx;
   int64_t M;
   int64_t rows;  // output rows of W (2I in SILU mode)
@@ -108,5 +108,13 @@ hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partia
 constexpr int kMaxGroup = SWR_MAX_GROUP;
 bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt);
 hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStream_t stream);
+
+// ---------------------------------------------------------------- FP8 activations
+// Per-token E4M3FN codes and scales of BF16 rows (quant.hip).
+hipError_t launch_quantize_rows(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q, int64_t ldq, float* S,
+                                hipStream_t stream);
+// The tiled GEMM with FP8 weights and FP8 activations: p.X holds E4M3FN codes
+// (p.ldx bytes per token), xscale one fp32 scale per token; p.K % 64 == 0.
+hipError_t launch_tile_fp8act(const GemmProblem& p, const float* xscale, hipStream_t stream);
 
 }  // namespace swr

@@ -23,7 +23,7 @@ HEADER = os.path.join(ROOT, "include", "swr.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(swr_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(swr_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
@@ -241,3 +241,20 @@ def test_planner_errors_without_gpu_work():
     assert L.swr_planner_reset(None) == swr.E_INVALID
     assert L.swr_planner_set_copy_engine(None, 0) == swr.E_INVALID
     assert L.swr_planner_set_gather_lds(None, 0) == swr.E_INVALID
+
+
+def test_fp8act_entry_points_validate_without_gpu_work():
+    L = swr.lib()
+    a = 1 << 20
+    # null pointers and shapes are refused before anything is enqueued
+    assert L.swr_quantize_rows_e4m3(None, 16, 4, 16, a, 16, a, None) == swr.E_INVALID
+    assert L.swr_quantize_rows_e4m3(a, 16, -1, 16, a, 16, a, None) == swr.E_SHAPE
+    assert L.swr_quantize_rows_e4m3(a, 8, 4, 16, a, 16, a, None) == swr.E_SHAPE
+    assert L.swr_mlp_forward_fp8act(a, None, a, a, 256, 320, a, 4, a, a, 1 << 20, None) == swr.E_INVALID
+    assert L.swr_mlp_forward_fp8act(a, a, a, a, 250, 320, a, 4, a, a, 1 << 20, None) == swr.E_SHAPE
+    # workspace: codes and scales of X and h, and h, in 256-byte sections
+    m, h, i = 300, 256, 320
+    def up(n):
+        return (n + 255) // 256 * 256
+    assert swr.mlp_fp8act_workspace_bytes(m, h, i) == up(m * h) + up(4 * m) + up(2 * m * i) + up(m * i) + up(4 * m)
+    assert swr.mlp_fp8act_workspace_bytes(0, h, i) == 0
