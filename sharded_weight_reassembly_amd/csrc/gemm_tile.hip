@@ -327,8 +327,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
 // g reads pieces 2g and 2g + 1 (K = 32g .. 32g + 31).
 constexpr int kStepK16 = 32;
 
-template <int BN, int WAVES, bool F8 = false>
-__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArgs a) {
+template <int BN, int WAVES, bool F8>
+__device__ inline void ring_tile_body(const StreamArgs& a) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = 4;
@@ -470,6 +470,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
   tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
 }
 
+template <int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArgs a) {
+  ring_tile_body<BN, WAVES, false>(a);
+}
+
+// FP8 weights and FP8 activations (the same ring, 64-K steps)
+template <int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8_kernel(StreamArgs a) {
+  ring_tile_body<BN, WAVES, true>(a);
+}
+
 template <int BN>
 dim3 tile_grid(const StreamArgs& a) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
@@ -482,7 +493,10 @@ dim3 tile_grid(const StreamArgs& a) {
 
 template <int BN, int WAVES, bool F8 = false>
 hipError_t launch_bf16_lds(const StreamArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tile_gemm_bf16_kernel<BN, WAVES, F8>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  if constexpr (F8)
+    hipLaunchKernelGGL((tile_gemm_f8f8_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tile_gemm_bf16_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
