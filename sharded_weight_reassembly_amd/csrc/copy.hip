@@ -247,6 +247,17 @@ hipError_t launch_sum_partials(const PartPtrs& parts, int n, int64_t count, void
 using swr::aligned;
 using swr::fail;
 
+namespace {
+
+// A view lies inside the payload, 16-byte aligned, after the previous one
+// (prev_end >= 0, 0 <= payload); no sum here can overflow.
+bool view_fits(const swr_view_desc& v, int64_t prev_end, int64_t payload) {
+  return v.offset % 16 == 0 && v.offset >= prev_end && v.offset <= payload && v.nbytes > 0 &&
+         v.nbytes <= payload - v.offset;
+}
+
+}  // namespace
+
 extern "C" int swr_pack_layer(const swr_layout* layout, const swr_view_desc* views,
                               const void* const* src_dev, void* const* chunk_dev, hipStream_t stream) {
   if (!layout || !views || !src_dev || !chunk_dev) return fail(SWR_E_INVALID, "swr_pack_layer: null pointer");
@@ -254,14 +265,16 @@ extern "C" int swr_pack_layer(const swr_layout* layout, const swr_view_desc* vie
   if (nw < 1 || nw > SWR_MAX_WEIGHTS || nc < 1 || nc > SWR_MAX_CHUNKS)
     return fail(SWR_E_INVALID, "swr_pack_layer: n_weights=%d n_chunks=%d out of range", nw, nc);
   if (layout->total_bytes <= 0 || layout->total_bytes % (16 * int64_t(nc)) != 0 ||
-      layout->chunk_bytes * nc != layout->total_bytes)
+      layout->chunk_bytes != layout->total_bytes / nc)
     return fail(SWR_E_INVALID, "swr_pack_layer: inconsistent layout (|T|=%lld, C=%lld, N=%d)",
                 (long long)layout->total_bytes, (long long)layout->chunk_bytes, nc);
+  if (layout->payload_bytes < 0 || layout->payload_bytes > layout->total_bytes)
+    return fail(SWR_E_INVALID, "swr_pack_layer: payload outside [0, |T|]");
   swr::PackPlan plan{};
   int64_t prev_end = 0;
   for (int j = 0; j < nw; ++j) {
     const swr_view_desc& v = views[j];
-    if (v.offset % 16 != 0 || v.offset < prev_end || v.nbytes <= 0 || v.offset + v.nbytes > layout->payload_bytes)
+    if (!view_fits(v, prev_end, layout->payload_bytes))
       return fail(SWR_E_INVALID, "swr_pack_layer: view %d (offset %lld, %lld bytes) does not fit the layout", j,
                   (long long)v.offset, (long long)v.nbytes);
     if (!src_dev[j]) return fail(SWR_E_INVALID, "swr_pack_layer: src_dev[%d] is null", j);
@@ -271,8 +284,6 @@ extern "C" int swr_pack_layer(const swr_layout* layout, const swr_view_desc* vie
     plan.size[j] = v.nbytes;
     prev_end = v.offset + v.nbytes;
   }
-  if (layout->payload_bytes > layout->total_bytes)
-    return fail(SWR_E_INVALID, "swr_pack_layer: payload larger than |T|");
   for (int i = 0; i < nc; ++i) {
     if (!chunk_dev[i]) return fail(SWR_E_INVALID, "swr_pack_layer: chunk_dev[%d] is null", i);
     if (!aligned(chunk_dev[i], 16)) return fail(SWR_E_ALIGN, "swr_pack_layer: chunk_dev[%d] not 16-byte aligned", i);
@@ -297,7 +308,8 @@ extern "C" int swr_redistribute_row_shards(const swr_layout* layout, const swr_v
   if (nw < 1 || nw > SWR_MAX_WEIGHTS || nc < 1 || nc > SWR_MAX_CHUNKS)
     return fail(SWR_E_INVALID, "%s: n_weights=%d n_chunks=%d out of range", fn, nw, nc);
   if (layout->total_bytes <= 0 || layout->total_bytes % (16 * int64_t(nc)) != 0 ||
-      layout->chunk_bytes * nc != layout->total_bytes || layout->payload_bytes > layout->total_bytes)
+      layout->chunk_bytes != layout->total_bytes / nc || layout->payload_bytes < 0 ||
+      layout->payload_bytes > layout->total_bytes)
     return fail(SWR_E_INVALID, "%s: inconsistent layout", fn);
   for (int i = 0; i < nc; ++i) {
     if (!chunk_dev[i]) return fail(SWR_E_INVALID, "%s: chunk_dev[%d] is null", fn, i);
@@ -309,8 +321,10 @@ extern "C" int swr_redistribute_row_shards(const swr_layout* layout, const swr_v
     const swr_view_desc& v = views[j];
     const swr_row_shards& sh = shards[j];
     const int64_t elem = v.dtype == SWR_FP8_E4M3FN ? 1 : 2;
-    if (v.offset % 16 != 0 || v.offset < prev_end || v.nbytes <= 0 || v.offset + v.nbytes > layout->payload_bytes ||
-        v.out_features * v.in_features * elem != v.nbytes)
+    int64_t item = 0;
+    if (!view_fits(v, prev_end, layout->payload_bytes) || v.out_features < 1 || v.in_features < 1 ||
+        __builtin_mul_overflow(v.out_features, v.in_features, &item) || __builtin_mul_overflow(item, elem, &item) ||
+        item != v.nbytes)
       return fail(SWR_E_INVALID, "%s: view %d does not fit the layout", fn, j);
     prev_end = v.offset + v.nbytes;
     if (sh.replicated) {
@@ -381,9 +395,10 @@ int reassemble(const char* fn, const void* const* chunk_dev, int32_t n_chunks, i
     return fail(SWR_E_ALIGN, "%s: chunk_bytes=%lld is not a positive multiple of 16", fn, (long long)chunk_bytes);
   if (self_rank < 0 || self_rank >= n_chunks)
     return fail(SWR_E_INVALID, "%s: self_rank=%d outside [0, %d)", fn, self_rank, n_chunks);
-  if (slot_bytes < chunk_bytes * n_chunks)
-    return fail(SWR_E_CAPACITY, "%s: slot holds %lld bytes, layer needs %lld", fn, (long long)slot_bytes,
-                (long long)(chunk_bytes * n_chunks));
+  // (divided, not multiplied: no overflow for any chunk_bytes)
+  if (chunk_bytes > slot_bytes / n_chunks)
+    return fail(SWR_E_CAPACITY, "%s: slot holds %lld bytes, layer needs %d chunks of %lld", fn,
+                (long long)slot_bytes, n_chunks, (long long)chunk_bytes);
   if (!aligned(slot, 16)) return fail(SWR_E_ALIGN, "%s: slot not 16-byte aligned", fn);
   swr::ChunkPtrs ptrs{};
   for (int i = 0; i < n_chunks; ++i) {

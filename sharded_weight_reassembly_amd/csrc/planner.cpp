@@ -221,9 +221,9 @@ extern "C" int swr_planner_set_layer(swr_planner* p, int32_t layer, const void* 
     return fail(SWR_E_INVALID, "swr_planner_set_layer: n_chunks=%d outside [1, 64]", n_chunks);
   if (chunk_bytes <= 0 || chunk_bytes % 16)
     return fail(SWR_E_ALIGN, "swr_planner_set_layer: chunk_bytes must be a positive multiple of 16");
-  if (chunk_bytes * n_chunks > p->slot_bytes)
-    return fail(SWR_E_CAPACITY, "swr_planner_set_layer: layer %d needs %lld bytes, slots hold %lld", layer,
-                (long long)(chunk_bytes * n_chunks), (long long)p->slot_bytes);
+  if (chunk_bytes > p->slot_bytes / n_chunks)
+    return fail(SWR_E_CAPACITY, "swr_planner_set_layer: layer %d needs %d chunks of %lld bytes, slots hold %lld",
+                layer, n_chunks, (long long)chunk_bytes, (long long)p->slot_bytes);
   for (int i = 0; i < n_chunks; ++i) {
     if (!chunk_dev[i]) return fail(SWR_E_INVALID, "swr_planner_set_layer: chunk %d is null", i);
     if (!swr::aligned(chunk_dev[i], 16)) return fail(SWR_E_ALIGN, "swr_planner_set_layer: chunk %d misaligned", i);

@@ -132,6 +132,36 @@ def test_redistribute_errors_before_enqueue():
     assert call([good[0], dict(replicated=True, src=[None])]) == swr.E_INVALID
 
 
+def test_size_checks_do_not_overflow():
+    """Sizes whose products or sums would wrap in int64 are refused before
+    anything is enqueued (a wrapped size would pass a capacity check)."""
+    L = swr.lib()
+    a = 1 << 20
+    huge = 1 << 62  # 4 * huge wraps to 0
+    chunks4 = _vp_array([a] * 4)
+    for fn in (L.swr_reassemble_into_slot, L.swr_reassemble_into_slot_dma):
+        assert fn(chunks4, 4, huge, a, 8192, 0, None, None, None, None) == swr.E_CAPACITY
+    shp = [(512, 128, "bf16"), (100, 128, "bf16")]
+    views, lay = swr.plan_layer(shp, 4)
+    chunks = _vp_array([a + i * lay["chunk_bytes"] for i in range(4)])
+    srcs = _vp_array([a, a])
+    # N * (C + 2^62) wraps to N * C = |T|
+    wrapped = dict(lay, chunk_bytes=lay["chunk_bytes"] + huge)
+    assert L.swr_pack_layer(ctypes.byref(swr._layout_struct(wrapped)), swr._views_struct(views), srcs, chunks,
+                            None) == swr.E_INVALID
+    # a view whose offset + nbytes wraps below the payload end
+    long_view = [views[0], dict(views[1], nbytes=(1 << 63) - views[1]["offset"])]
+    assert L.swr_pack_layer(ctypes.byref(swr._layout_struct(lay)), swr._views_struct(long_view), srcs, chunks,
+                            None) == swr.E_INVALID
+    # negative shapes whose product matches the view's bytes
+    neg = [views[0], dict(views[1], out_features=-100, in_features=-128)]
+    rs = swr.row_shards_struct([dict(sub_rows=[256, 256], src=[a] * 4), dict(replicated=True, src=[a])])
+    assert L.swr_redistribute_row_shards(ctypes.byref(swr._layout_struct(lay)), swr._views_struct(neg), rs, chunks,
+                                         None) == swr.E_INVALID
+    assert L.swr_redistribute_row_shards(ctypes.byref(swr._layout_struct(wrapped)), swr._views_struct(views), rs,
+                                         chunks, None) == swr.E_INVALID
+
+
 def test_dma_reassemble_checks_like_the_kernel_path():
     L = swr.lib()
     good = 1 << 20

@@ -123,6 +123,10 @@ def test_sequence_errors():
     with pytest.raises(swr.SwrError) as e:
         p.set_layer(0, layers[0]["chunks"], 1 << 40)
     assert e.value.code == swr.E_CAPACITY
+    with pytest.raises(swr.SwrError) as e:
+        # N * C wraps to 0 in int64: still refused
+        p.set_layer(0, layers[0]["chunks"][:4], 1 << 62)
+    assert e.value.code == swr.E_CAPACITY
     torch.cuda.synchronize()
     p.close()
 
