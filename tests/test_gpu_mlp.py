@@ -56,6 +56,36 @@ def test_short_row_blocks_silu(hidden, inter, m):
     assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} m={m}")
 
 
+@pytest.mark.parametrize("hidden,inter,m", [(512, 4096, 64), (448, 4096, 40), (512, 2048, 17)])
+def test_down_split_k_matches_projection(hidden, inter, m):
+    """17-64 tokens: the MLP's down GEMM splits K over workgroups (512 x 4096
+    at 64 tokens: 4 row blocks x 4 splits) and a finalize kernel adds the
+    splits.  Its output must be the bits of swr_proj_forward on the MLP's own
+    h (which sits at the start of the workspace) and within the bar of the
+    oracle; a second, smaller call on the same workspace must be right too."""
+    note(f"down split-K h={hidden} i={inter} m={m}")
+    gu = synth.weight(synth.seed_for(13, 3, 0), 2 * inter, hidden, synth.FP8)
+    d = synth.weight(synth.seed_for(13, 3, 1), hidden, inter, synth.FP8)
+    x = synth.activations(synth.seed_for(13, 3, 50), m, hidden)
+    nb = swr.mlp_workspace_bytes(m, hidden, inter, synth.FP8)
+    assert nb > (m * inter * 2 + 255) // 256 * 256  # the down GEMM splits K
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    wgu, sgu, wd, sd = u8(gu.raw()), f32(gu.scale), u8(d.raw()), f32(d.scale)
+    for mm in (m, m - 7):
+        y = torch.full((mm, hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+        swr.mlp_forward(wgu, sgu, wd, sd, synth.FP8, hidden, inter, bf16(x[:mm]), y, ws, m=mm)
+        torch.cuda.synchronize()
+        h = ws[: mm * inter * 2].view(torch.bfloat16).view(mm, inter).clone()
+        y2 = torch.full((mm, hidden), float("nan"), dtype=torch.bfloat16, device=DEV)
+        pb = swr.proj_workspace_bytes(mm, hidden, inter, synth.FP8)  # 0: this token count does not split K
+        pw = torch.empty(pb, dtype=torch.uint8, device=DEV) if pb > 0 else None
+        swr.proj_forward(wd, synth.FP8, sd, hidden, inter, h, y2, workspace=pw)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "MLP down differs from the projection"
+        _, _, ref = gemm.mlp_f64(x[:mm], gu.raw(), gu.scale, d.raw(), d.scale, synth.FP8, hidden, inter)
+        assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} m={mm}")
+
+
 def test_tiny_config_mlp_and_projection():
     """The tiny workload: hidden 128, intermediate 256, BF16, 4 tokens, N=4 chunks,
     run through views of the reassembled slot."""
