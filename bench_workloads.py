@@ -402,14 +402,21 @@ def run_sharded(args, swr, torch, np, synth, dev):
     def full():
         swr.proj_forward(w_t, "bf16", None, F, D, x, y_full, stream=stream)
 
+    # the S shard GEMMs of a variant go in one grouped call (one launch over all
+    # their tiles: a single shard fills less than one wave of the CUs)
+    col_projs = [dict(w=w_t.data_ptr() + j * fs * D * esz, dtype="bf16", row_scale=None, out_f=fs, in_f=D, x=x,
+                      y=y_cols.data_ptr() + j * fs * esz, ldy=F, y_fp32=False) for j in range(S)]
+    k_projs = [dict(w=wk[j], dtype="bf16", row_scale=None, out_f=F, in_f=ds, x=xk[j], y=parts[j], y_fp32=True)
+               for j in range(S)]
+
     def columns():
-        for j in range(S):
-            swr.proj_forward(w_t.data_ptr() + j * fs * D * esz, "bf16", None, fs, D, x,
-                             y_cols.data_ptr() + j * fs * esz, m=B, ldy=F, y_fp32=False, stream=stream)
+        swr.proj_forward_grouped(col_projs, B, stream=stream)
+
+    def kshard_gemms():
+        swr.proj_forward_grouped(k_projs, B, stream=stream)
 
     def kshards():
-        for j in range(S):
-            swr.proj_forward(wk[j], "bf16", None, F, ds, xk[j], parts[j], y_fp32=True, stream=stream)
+        kshard_gemms()
         swr.sum_partials(parts, y_k, stream=stream)
 
     variants = {"full": full, "column_shards": columns, "k_shards_plus_sum": kshards}
@@ -428,8 +435,7 @@ def run_sharded(args, swr, torch, np, synth, dev):
             for k, fn in variants.items():
                 ev[k][s][0].record(stream)
                 if k == "k_shards_plus_sum":
-                    for j in range(S):
-                        swr.proj_forward(wk[j], "bf16", None, F, ds, xk[j], parts[j], y_fp32=True, stream=stream)
+                    kshard_gemms()
                     sum_ev[s][0].record(stream)
                     swr.sum_partials(parts, y_k, stream=stream)
                     sum_ev[s][1].record(stream)

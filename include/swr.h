@@ -242,10 +242,12 @@ typedef struct {
  * reassembled slot (weight_sharding, section "flat layout" step 4, and the
  * section on targets: one gather per layer serves every projection in it).
  * Each descriptor computes exactly what swr_proj_forward computes for it.
- * When every projection can use the staged matrix-core kernel with the same
- * dtype (K a multiple of 256, M <= 64, weights under 2 GiB, aligned) they
- * run as ONE launch, which removes the per-launch ramp and tail that
- * dominate small views; otherwise they are enqueued one after another.
+ * When every projection has the same dtype and can use the staged
+ * matrix-core kernel (M <= 64, K a multiple of 256, weights under 2 GiB,
+ * aligned) or the tiled one (M > 64, K a multiple of 64, weights and X under
+ * 2 GiB, aligned) they run as ONE launch over all their tiles, which removes
+ * the per-launch ramp and tail that dominate small views and small shards;
+ * otherwise they are enqueued one after another.
  *   descs      host array of n descriptors, 1 <= n <= SWR_MAX_GROUP; read
  *              before the call returns
  *   M          tokens, shared by all projections (M == 0 enqueues nothing)

@@ -65,4 +65,13 @@ __device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16
 // Tiled MFMA GEMM for prefill-sized M (gemm_tile.hip).  bn is 256 or 128.
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream);
 
+// n tiled GEMMs of one weight dtype (BF16 activations, no SiLU mode, each
+// X under 2 GiB) in one launch of the bn-row tile kernel.
+struct TileGroup {
+  StreamArgs g[kMaxGroup];
+  int64_t first[kMaxGroup + 1];  // first tile of each problem; first[n] tiles in all
+  int n;
+};
+hipError_t launch_tile_group(const StreamArgs* as, int n, int bn, bool fp8, hipStream_t stream);
+
 }  // namespace swr

@@ -1112,7 +1112,25 @@ hipError_t launch_grouped_mt(const GroupArgs& ga, dim3 grid, hipStream_t stream)
 bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt) {
   if (n < 1 || n > kMaxGroup) return false;
   const int64_t M = ps[0].M;
-  if (M < 1 || M > 64) return false;
+  if (M < 1) return false;
+  if (M > 64) {
+    // prefill-sized: every projection takes the tiled kernel, X in one token
+    // part; 256-row tiles when the group gives two waves of them (as plan_gemm)
+    int64_t t256 = 0;
+    for (int i = 0; i < n; ++i) {
+      const GemmProblem& p = ps[i];
+      const int64_t eb = p.dtype == SWR_FP8_E4M3FN ? 1 : 2;
+      if (p.dtype != ps[0].dtype || p.M != M || p.mode == OUT_SILU_BF16) return false;
+      if (!(aligned(p.W, 16) && aligned(p.X, 16) && p.ldx % 8 == 0) || p.K % kTileK != 0) return false;
+      if (p.rows * p.K * eb >= (INT64_C(1) << 31) || p.ldx >= (INT64_C(1) << 22) ||
+          M * p.ldx * 2 >= (INT64_C(1) << 31))
+        return false;
+      t256 += ((M + 255) / 256) * ((p.rows + 255) / 256);
+    }
+    *mt = 16;
+    *rt = t256 >= 512 ? 256 : 128;
+    return true;
+  }
   int64_t blocks = 0;
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   *rt = *mt == 1 ? 2 : 4;
@@ -1138,6 +1156,11 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
       order[j] = order[j - 1];
       order[j - 1] = t;
     }
+  if (ps[0].M > 64) {
+    StreamArgs as[kMaxGroup];
+    for (int i = 0; i < n; ++i) as[i] = make_args(ps[order[i]], ps[order[i]].K, 1, nullptr, 0);
+    return launch_tile_group(as, n, rt, ps[0].dtype == SWR_FP8_E4M3FN, stream);
+  }
   GroupArgs ga{};
   ga.n = n;
   int first = 0;

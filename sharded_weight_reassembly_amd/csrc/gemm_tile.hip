@@ -46,14 +46,12 @@ struct TileCoord {
 };
 
 template <int BN>
-__device__ inline TileCoord tile_coord(const StreamArgs& a) {
+__device__ inline TileCoord tile_coord(const StreamArgs& a, int64_t i, int64_t ntiles) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
   const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
   const int64_t cols = silu_mode ? a.inter : a.rows;  // output columns
   const int64_t col_tile = silu_mode ? BN / 2 : BN;
   const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
-  const int64_t ntiles = int64_t(gridDim.x);
-  const int64_t i = blockIdx.x;
   const int64_t t = (ntiles % 8 == 0) ? (i % 8) * (ntiles / 8) + i / 8 : i;
   const int64_t group = t / (kGroupM * tiles_n);
   const int64_t first_m = group * kGroupM;
@@ -146,10 +144,11 @@ __device__ inline int wswz(int row, int q) { return row * 4 + (q ^ ((row >> 2) &
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 __device__ inline u32x4s raw_rsrc(const void* base, int64_t bytes) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
+  // the same in every lane: kept in scalar registers (the loads take it there)
   u32x4s r;
-  r[0] = uint32_t(p);
-  r[1] = uint32_t(p >> 32) & 0xFFFFu;  // stride 0
-  r[2] = uint32_t(bytes);
+  r[0] = __builtin_amdgcn_readfirstlane(uint32_t(p));
+  r[1] = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32) & 0xFFFFu);  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(uint32_t(bytes));
   r[3] = 0x00020000u;
   return r;
 }
@@ -184,7 +183,7 @@ __device__ inline void wait_vm() {
 }
 
 template <int BN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs a) {
+__device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = 4;
@@ -208,7 +207,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const TileCoord tc = tile_coord<BN>(a);
+  const TileCoord tc = tile_coord<BN>(a, tile, ntiles);
   const int64_t m0 = tc.m0;
   for (int c = tid; c < BN; c += 64 * WAVES) {
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
@@ -328,7 +327,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
 constexpr int kStepK16 = 32;
 
 template <int BN, int WAVES, bool F8>
-__device__ inline void ring_tile_body(const StreamArgs& a) {
+__device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = 4;
@@ -351,7 +350,7 @@ __device__ inline void ring_tile_body(const StreamArgs& a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const TileCoord tc = tile_coord<BN>(a);
+  const TileCoord tc = tile_coord<BN>(a, tile, ntiles);
   const int64_t m0 = tc.m0;
   for (int c = tid; c < BN; c += 64 * WAVES) {
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
@@ -471,24 +470,48 @@ __device__ inline void ring_tile_body(const StreamArgs& a) {
 }
 
 template <int BN, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs a) {
+  fp8_tile_body<BN, WAVES>(a, blockIdx.x, gridDim.x);
+}
+
+template <int BN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArgs a) {
-  ring_tile_body<BN, WAVES, false>(a);
+  ring_tile_body<BN, WAVES, false>(a, blockIdx.x, gridDim.x);
 }
 
 // FP8 weights and FP8 activations (the same ring, 64-K steps)
 template <int BN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8_kernel(StreamArgs a) {
-  ring_tile_body<BN, WAVES, true>(a);
+  ring_tile_body<BN, WAVES, true>(a, blockIdx.x, gridDim.x);
+}
+
+// Several GEMMs of one weight dtype in one launch (a layer's projections, the
+// shards of a sharded product): workgroup x computes tile x - first[g] of
+// problem g, the g with first[g] <= x < first[g + 1].
+template <int BN, int WAVES, bool FP8>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_group_kernel(TileGroup tg) {
+  const int64_t x = blockIdx.x;
+  int g = 0;
+  while (g + 1 < tg.n && x >= tg.first[g + 1]) ++g;
+  g = __builtin_amdgcn_readfirstlane(g);  // one problem per workgroup
+  if constexpr (FP8)
+    fp8_tile_body<BN, WAVES>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
+  else
+    ring_tile_body<BN, WAVES, false>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
+}
+
+int64_t tile_count(const StreamArgs& a, int bn) {
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
+  const int64_t cols = silu_mode ? a.inter : a.rows;
+  const int64_t col_tile = silu_mode ? bn / 2 : bn;
+  const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
+  return tiles_m * tiles_n;
 }
 
 template <int BN>
 dim3 tile_grid(const StreamArgs& a) {
-  const bool silu_mode = a.mode == OUT_SILU_BF16;
-  const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
-  const int64_t cols = silu_mode ? a.inter : a.rows;
-  const int64_t col_tile = silu_mode ? BN / 2 : BN;
-  const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
-  return dim3(unsigned(tiles_m * tiles_n));
+  return dim3(unsigned(tile_count(a, BN)));
 }
 
 template <int BN, int WAVES, bool F8 = false>
@@ -506,7 +529,29 @@ hipError_t launch_fp8(const StreamArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BN, int WAVES, bool FP8>
+hipError_t launch_group(const TileGroup& tg, hipStream_t stream) {
+  hipLaunchKernelGGL((tile_group_kernel<BN, WAVES, FP8>), dim3(unsigned(tg.first[tg.n])), dim3(64 * WAVES), 0,
+                     stream, tg);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_tile_group(const StreamArgs* as, int n, int bn, bool fp8, hipStream_t stream) {
+  if (n < 1 || n > kMaxGroup) return hipErrorInvalidValue;
+  TileGroup tg{};
+  tg.n = n;
+  tg.first[0] = 0;
+  for (int i = 0; i < n; ++i) {
+    tg.g[i] = as[i];
+    tg.first[i + 1] = tg.first[i] + tile_count(as[i], bn);
+  }
+  if (tg.first[n] == 0) return hipSuccess;
+  if (tg.first[n] >= (INT64_C(1) << 31)) return hipErrorInvalidValue;
+  if (bn == 256) return fp8 ? launch_group<256, 8, true>(tg, stream) : launch_group<256, 8, false>(tg, stream);
+  return fp8 ? launch_group<128, 4, true>(tg, stream) : launch_group<128, 4, false>(tg, stream);
+}
 
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
   // The kernels address X through 32-bit buffer offsets: tokens go in parts

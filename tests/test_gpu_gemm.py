@@ -286,6 +286,32 @@ def test_grouped_projection_parity(gi, m):
         assert_close_rows(values(y), ref, what=f"grouped {w.out_features}x{w.in_features} {w.dtype} m={m}")
 
 
+@pytest.mark.parametrize("gi,y_fp32", [(0, False), (1, False), (0, True)])
+@pytest.mark.parametrize("m", [65, 300, 600])
+def test_grouped_prefill_one_launch_equals_separate(gi, y_fp32, m):
+    """Prefill-sized groups (M > 64, K a multiple of 64) run as one launch of
+    the tiled kernels over all the group's tiles.  Each projection must give
+    the bits of its own swr_proj_forward call (the same K order per output,
+    whichever tile width either launch picks) and meet the bar against the
+    oracle on sampled token rows."""
+    shapes, dt = GROUPS[gi]
+    note(f"grouped prefill group={gi} fp32={y_fp32} m={m}")
+    ws = [synth.weight(synth.seed_for(17, gi, j), o, k, dt) for j, (o, k) in enumerate(shapes)]
+    xs = {k: synth.activations(synth.seed_for(17, gi, 50 + k % 97), m, k) for _, k in shapes}
+    nb, ys = _grouped(ws, xs, m, y_fp32=y_fp32)
+    assert nb == 0  # one launch, no scratch
+    rows = np.random.default_rng(m).choice(m, size=min(m, 24), replace=False)
+    for w, y in zip(ws, ys):
+        y1 = torch.full_like(y, float("nan"))
+        swr.proj_forward(u8(w.raw()), w.dtype, f32(w.scale) if w.scale is not None else None, w.out_features,
+                         w.in_features, bf16(xs[w.in_features]), y1)
+        torch.cuda.synchronize()
+        bits = torch.int32 if y_fp32 else torch.int16
+        assert torch.equal(y.view(bits), y1.view(bits)), f"{w.out_features}x{w.in_features} differs from one launch"
+        ref = gemm.proj_f64(xs[w.in_features][rows], w.raw(), w.dtype, w.out_features, w.in_features, w.scale)
+        assert_close_rows(values(y[rows]), ref, what=f"grouped prefill {w.out_features}x{w.in_features} m={m}")
+
+
 def test_grouped_fp32_output_and_zero_tokens():
     note("grouped fp32 output, M=0")
     ws = [synth.weight(31, 320, 512, synth.FP8), synth.weight(32, 96, 256, synth.FP8)]
