@@ -232,9 +232,13 @@ def test_grouped_workspace_bytes():
     need = L.swr_proj_grouped_workspace_bytes(_descs(mixed), 3, 16)
     singles = [swr.proj_workspace_bytes(16, o, k, "fp8_e4m3fn") for (_, _, _, _, o, k, _, _, _) in mixed]
     assert need == max(singles)
-    # tokens past the decode range: separate launches as well
-    assert L.swr_proj_grouped_workspace_bytes(_descs(stageable), 2, 65) == max(
-        swr.proj_workspace_bytes(65, o, k, "fp8_e4m3fn") for (_, _, _, _, o, k, _, _, _) in stageable)
+    # tokens past the decode range: one launch of the tiled kernel, no scratch
+    assert L.swr_proj_grouped_workspace_bytes(_descs(stageable), 2, 65) == 0
+    assert L.swr_proj_grouped_workspace_bytes(_descs(mixed), 3, 300) == 0  # K = 320 is a multiple of 64
+    # K = 100 fits no tiled kernel: separate launches, scratch of the largest single projection
+    odd = stageable + [(a, a, a, a, 640, 100, 104, 640, swr.FP8_E4M3FN)]
+    assert L.swr_proj_grouped_workspace_bytes(_descs(odd), 3, 300) == max(
+        swr.proj_workspace_bytes(300, o, k, "fp8_e4m3fn") for (_, _, _, _, o, k, _, _, _) in odd)
 
 
 def test_planner_handles_every_token_count():
