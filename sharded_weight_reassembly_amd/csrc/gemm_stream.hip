@@ -940,6 +940,11 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       plan.rt = (plan.mt > 1 && fp8 && inter % 64 == 0) ? 8 : (inter % 32 == 0 ? 4 : 2);
     else
       plan.rt = plan.mt == 1 ? 2 : 4;
+    // One FP8 token block over more than two waves of 32-row blocks: the deep
+    // 32-row variant holds a CU alone, so every later wave of workgroups waits
+    // for its first loads; 64-row blocks run two per CU and cover them
+    // (24576 x 7168 at 16 tokens: 35.6 against 43.2 us; no change up to 8192 rows)
+    if (!silu_mode && plan.mt == 1 && fp8 && row_blocks_of(p, full_rows(p, 2)) * tok_blocks > 512) plan.rt = 4;
     // 17-64 tokens of FP8 weights: eight K-split waves in two row halves
     // with X through LDS (each weight byte widened once, X read in whole
     // cache lines, two waves per SIMD to cover each other's waits); 128-row

@@ -191,6 +191,22 @@ def test_full_size_projection_layer_sampled_rows():
         assert_close_rows(values(y)[:, cols], ref, what=f"projection {j} [{o}x{k}]")
 
 
+@pytest.mark.parametrize("o,k,m", [(16452, 512, 5), (20000, 256, 16), (16400, 768, 1)])
+def test_many_row_blocks_at_few_tokens(o, k, m):
+    """FP8 weights with more than two waves of 32-row blocks at <= 16 tokens:
+    the planner takes 64-row blocks at two workgroups per CU; ragged rows."""
+    note(f"many row blocks {o}x{k} m={m}")
+    w = synth.weight(synth.seed_for(18, o % 97, 0), o, k, synth.FP8)
+    x = synth.activations(synth.seed_for(18, o % 97, 50), m, k)
+    y = torch.full((m, o), float("nan"), dtype=torch.bfloat16, device=DEV)
+    nb = swr.proj_workspace_bytes(m, o, k, synth.FP8)
+    wsp = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV)
+    swr.proj_forward(u8(w.raw()), synth.FP8, f32(w.scale), o, k, bf16(x), y, workspace=wsp)
+    torch.cuda.synchronize()
+    ref = gemm.proj_f64(x, w.raw(), synth.FP8, o, k, w.scale)
+    assert_close_rows(values(y), ref, what=f"{o}x{k} m={m}")
+
+
 @pytest.mark.parametrize("o,k,dt,m", [
     (1000, 512, synth.FP8, 300),     # row tail and token tail in the tiled kernel
     (2048, 1024, synth.BF16, 513),
