@@ -1152,7 +1152,7 @@ bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt) {
       return false;
     blocks += (p.rows + 16 * *rt - 1) / (16 * *rt);
   }
-  return blocks < (INT64_C(1) << 30);
+  return blocks < (INT64_C(1) << 29);  // (launch_grouped may double it)
 }
 
 hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStream_t stream) {
@@ -1170,19 +1170,33 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
     for (int i = 0; i < n; ++i) as[i] = make_args(ps[order[i]], ps[order[i]].K, 1, nullptr, 0);
     return launch_tile_group(as, n, rt, ps[0].dtype == SWR_FP8_E4M3FN, stream);
   }
+  // Row blocks of one length rb for the whole group, as in fill_slots: the
+  // shortest multiple of 4 (at least half the tiles' rows) whose block count
+  // still fits the waves of workgroups that full blocks need, so that the
+  // last wave is as full as the others.
+  const int64_t tok_blocks = (ps[0].M + 16 * mt - 1) / (16 * mt);
+  const bool fp8 = ps[0].dtype == SWR_FP8_E4M3FN;
+  const int64_t slots = 256 * int64_t(staged_occupancy(mt, rt, fp8, false, false, kStageK, kWaves));
+  auto blocks_for = [&](int64_t rb) {
+    int64_t b = 0;
+    for (int i = 0; i < n; ++i) b += (ps[i].rows + rb - 1) / rb;
+    return b * tok_blocks;
+  };
+  const int64_t full = 16 * int64_t(rt);
+  const int64_t target = (blocks_for(full) + slots - 1) / slots * slots;
+  int64_t rb = full;
+  for (int64_t r = full - 4; r >= full / 2 && blocks_for(r) <= target; r -= 4) rb = r;
   GroupArgs ga{};
   ga.n = n;
   int first = 0;
   for (int i = 0; i < n; ++i) {
     const GemmProblem& p = ps[order[i]];
-    ga.g[i] = make_args(p, p.K, 1, nullptr, full_rows(p, rt));
+    ga.g[i] = make_args(p, p.K, 1, nullptr, rb);
     ga.first[i] = first;
-    first += int((p.rows + 16 * rt - 1) / (16 * rt));
+    first += int((p.rows + rb - 1) / rb);
   }
   ga.first[n] = first;
-  const int64_t tok_blocks = (ps[0].M + 16 * mt - 1) / (16 * mt);
   const dim3 grid = dim3(unsigned(first), 1, unsigned(tok_blocks));
-  const bool fp8 = ps[0].dtype == SWR_FP8_E4M3FN;
   if (mt == 1 && rt == 4)
     return fp8 ? launch_grouped_mt<1, 4, true>(ga, grid, stream) : launch_grouped_mt<1, 4, false>(ga, grid, stream);
   if (mt == 1)
