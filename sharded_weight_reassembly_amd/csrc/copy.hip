@@ -2,8 +2,6 @@
 // per-layer reassembly of the chunks into a workspace slot, and the fixed-order
 // sum of split-contraction partials.  All three are HBM-bound streams of
 // 16-byte vectors; none of them does arithmetic on weight values.
-#include <stdlib.h>
-
 #include <algorithm>
 
 #include "swr_internal.h"
@@ -113,7 +111,8 @@ __global__ __launch_bounds__(kThreads) void redistribute_kernel(RedistArgs a) {
        p += int64_t(gridDim.x) * kThreads * 16) {
     const int64_t rel = p - a.off;
     uint4 out = make_uint4(0, 0, 0, 0);
-    if (rel < a.size) {
+    // bytes before the item (the first launch starts at 0) and after it are padding
+    if (rel >= 0 && rel < a.size) {
       const uint8_t* s0 = shard_byte(a, rel);
       const bool one_row = (rel / a.row_bytes) == ((rel + 15) / a.row_bytes);
       if (rel + 16 <= a.size && (a.replicated || one_row) && (reinterpret_cast<uintptr_t>(s0) & 15) == 0) {
@@ -195,25 +194,9 @@ int grid_for(int64_t work_items, int per_block_items) {
 hipError_t launch_reassemble(const ChunkPtrs& chunks, int n_chunks, int64_t chunk_bytes, void* slot,
                              unsigned lds_bytes, hipStream_t stream) {
   const int64_t chunk_vecs = chunk_bytes / 16;
-  int64_t span = kCopySpanVecs;
-#ifdef SWR_TUNING
-  if (const char* env = getenv("SWR_COPY_SPAN")) span = atol(env);  // tuning builds only
-#endif
+  const int64_t span = kCopySpanVecs;
   int64_t blocks = (chunk_vecs + span - 1) / span;
   if (blocks < 1) blocks = 1;
-#ifdef SWR_TUNING
-  if (const char* env = getenv("SWR_COPY_GRID")) blocks = std::min<int64_t>(blocks, atol(env));  // workgroups per chunk
-  if (const char* env = getenv("SWR_COPY_ENGINE")) {
-    if (atoi(env) == 1) {  // the runtime's device-to-device copy (a blit kernel), one per chunk
-      for (int i = 0; i < n_chunks; ++i) {
-        const hipError_t e = hipMemcpyAsync(static_cast<uint8_t*>(slot) + int64_t(i) * chunk_bytes, chunks.p[i],
-                                            size_t(chunk_bytes), hipMemcpyDeviceToDevice, stream);
-        if (e != hipSuccess) return e;
-      }
-      return hipSuccess;
-    }
-  }
-#endif
   const dim3 grid = dim3(unsigned(blocks), unsigned(n_chunks));
   hipLaunchKernelGGL(reassemble_kernel, grid, dim3(kThreads), lds_bytes, stream, chunks, static_cast<u32x4*>(slot),
                      chunk_vecs, span);
@@ -349,7 +332,9 @@ extern "C" int swr_redistribute_row_shards(const swr_layout* layout, const swr_v
       if (!aligned(sh.src[r], 16)) return fail(SWR_E_ALIGN, "%s: weight %d: src[%d] not 16-byte aligned", fn, j, r);
     }
   }
-  // leading zero padding cannot occur: the first item starts at 0
+  // launch j writes T[begin, end): from the item's offset (0 for the first
+  // item, so that any bytes before it are written as zero padding, as
+  // swr_pack_layer does) to the next item's offset or |T|
   for (int j = 0; j < nw; ++j) {
     const swr_view_desc& v = views[j];
     const swr_row_shards& sh = shards[j];

@@ -23,9 +23,6 @@
 // rows j..j+8RT and the matching up rows I+j..I+j+8RT, and writes
 // h = bf16(silu(G_gate) * G_up) directly (vLLM PR #50656 report, test code:
 // gate rows first, SiLU of the gate half times the up half).
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "gemm_common.h"
 
 namespace swr {
@@ -984,29 +981,6 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     plan.kper = p.K;
     return plan;
   }
-#ifdef SWR_TUNING
-  // tuning builds only: SWR_PLAN / SWR_PLAN_SILU = "kind,rt,ks" override the heuristic
-  if (const char* env = getenv(silu_mode ? "SWR_PLAN_SILU" : "SWR_PLAN")) {
-    int kind, rt, ks;
-    if (sscanf(env, "%d,%d,%d", &kind, &rt, &ks) == 3) {
-      GemmPlan t = plan;
-      t.kind = kind;
-      t.rt = rt;
-      t.rb = full_rows(p, rt);
-      if (const char* rb_env = getenv("SWR_RB")) t.rb = atoi(rb_env);
-      if (kind != 2) t.sk = kStageK;
-      if (const char* sk_env = getenv("SWR_SK")) t.sk = atoi(sk_env);
-      set_split(t, p, ks, (kind == 2 || kind == 6) ? t.sk : 256);
-      if (getenv("SWR_FILL") && (kind == 2 || kind == 6)) {
-        const bool f8 = p.dtype == SWR_FP8_E4M3FN;
-        const int occ = kind == 6 ? staged_occupancy(t.mt, t.rt, f8, true, true, t.sk, 8)
-                                  : staged_occupancy(t.mt, t.rt, f8, false, false, t.sk, kWaves);
-        fill_slots(t, p, tok_blocks, 256 * int64_t(occ));
-      }
-      if (plan_is_valid(p, t)) plan = t;
-    }
-  }
-#endif
   return plan;
 }
 

@@ -156,22 +156,22 @@ __device__ inline u32x4s raw_rsrc(const void* base, int64_t bytes) {
 // One 16-byte buffer-to-LDS load per lane: lane l's bytes land at lds + 16*l
 // (the wave-uniform base goes in M0).  Written as assembly so that the
 // compiler adds no waits of its own for it: this kernel orders these loads
-// itself (wait_vm before each barrier).  NT selects the streaming hint.  M0
-// is set here and holds nothing else in this kernel (no other instruction in
-// it reads M0; checked in its ISA).
+// itself (wait_vm before each barrier).  NT selects the streaming hint.  The
+// LDS base is an M0 operand of the statement ("{m0}"), so the compiler itself
+// writes M0 before it and knows what M0 holds.
 template <bool NT>
 __device__ inline void lds_load16(const u32x4s& res, uint8_t* lds, int voffset, int soffset) {
   // the base is the same in every lane of the wave
   const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds)));
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
                  :
-                 : "s"(base), "v"(voffset), "s"(res), "s"(soffset)
+                 : "v"(voffset), "s"(res), "s"(soffset), "{m0}"(base)
                  : "memory");
   else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(base), "v"(voffset), "s"(res), "s"(soffset)
+                 : "v"(voffset), "s"(res), "s"(soffset), "{m0}"(base)
                  : "memory");
 }
 

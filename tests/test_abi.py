@@ -292,3 +292,29 @@ def test_fp8act_entry_points_validate_without_gpu_work():
         return (n + 255) // 256 * 256
     assert swr.mlp_fp8act_workspace_bytes(m, h, i) == up(m * h) + up(4 * m) + up(2 * m * i) + up(m * i) + up(4 * m)
     assert swr.mlp_fp8act_workspace_bytes(0, h, i) == 0
+
+
+def test_memory_and_transfer_account_from_library_layouts():
+    """weight_sharding, cost section: per rank R/N + 2 max_l |T_l| bytes of
+    weights (its chunks plus two slots) and (N-1)/N * S bytes received per
+    layer.  The library's own layouts for the two decode workloads against
+    numbers worked out by hand:
+      shared expert, 8 layers, N = 16: |T| = 28672*6144 + 6144*14336 =
+        264,241,152 (no padding: both items are multiples of 16 and the sum
+        of 256); C = 16,515,072; R/N = 8 C = 132,120,576; two slots
+        528,482,304; total 660,602,880; received per layer 15 C = 247,726,080;
+      attention projections, 16 layers, N = 16: |T| = 385,179,648,
+        C = 24,073,728; R/N = 16 C = 385,179,648; two slots 770,359,296;
+        total 1,155,538,944; received per layer 15 C = 361,105,920."""
+    se = [(28672, 6144, "fp8_e4m3fn"), (6144, 14336, "fp8_e4m3fn")]
+    attn = [(24576, 7168), (8192, 7168), (7168, 8192), (4096, 7168), (1000, 7168), (7168, 3072), (3072, 7168),
+            (1536, 7168)]
+    attn = [(o, i, "fp8_e4m3fn") for o, i in attn]
+    for ws, layers, want in ((se, 8, (264_241_152, 16_515_072, 660_602_880, 247_726_080)),
+                             (attn, 16, (385_179_648, 24_073_728, 1_155_538_944, 361_105_920))):
+        lays = [swr.plan_layer(ws, 16)[1] for _ in range(layers)]
+        totals = [lay["total_bytes"] for lay in lays]
+        resident = sum(lay["chunk_bytes"] for lay in lays)  # one rank's chunks: R / N
+        memory = resident + 2 * max(totals)
+        received = (16 - 1) * lays[0]["chunk_bytes"]
+        assert (totals[0], lays[0]["chunk_bytes"], memory, received) == want

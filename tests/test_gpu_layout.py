@@ -199,18 +199,55 @@ def test_redistribute_row_shards_bit_exact(shapes, n, merged):
 def test_redistribute_full_size_layer(wl, merged):
     """A full-size layer at N=16: the projection layer ([1000 x 7168] stays
     whole: 1000 rows do not split over 16 ranks) and the shared expert with
-    gate_up split per sub-block.  Chunks equal swr_pack_layer's."""
+    gate_up split per sub-block.  Both the chunks written from the row shards
+    and the chunks swr_pack_layer writes from the whole weights equal the
+    oracle's chunks of T, byte for byte."""
     note(f"redistribute full-size {wl.name}")
     n = wl.n_chunks
     ws = wl.layer_weights(0)
     shp = [(o, i, d) for _, o, i, d in wl.weights]
     views, lay = swr.plan_layer(shp, n)
-    specs, _ = _shard_specs(wl.weights, ws, n, merged)
-    chunks = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(n)]
+    specs, oracle_ws = _shard_specs(wl.weights, ws, n, merged)
+    chunks = [torch.full((lay["chunk_bytes"],), 0xA5, dtype=torch.uint8, device=DEV) for _ in range(n)]
     swr.redistribute_row_shards(lay, views, specs, chunks)
     del specs
-    ref = [torch.empty(lay["chunk_bytes"], dtype=torch.uint8, device=DEV) for _ in range(n)]
-    swr.pack_layer(lay, views, [u8(w.raw()) for w in ws], ref)
+    packed = [torch.full((lay["chunk_bytes"],), 0x5A, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    swr.pack_layer(lay, views, [u8(w.raw()) for w in ws], packed)
     torch.cuda.synchronize()
+    plan = olayout.plan_layer(shp, n)
+    ref = olayout.redistribute(plan, oracle_ws)
+    del oracle_ws
     for i in range(n):
-        assert torch.equal(chunks[i], ref[i]), f"chunk {i}"
+        assert np.array_equal(chunks[i].cpu().numpy(), ref[i]), f"redistributed chunk {i}"
+        assert np.array_equal(packed[i].cpu().numpy(), ref[i]), f"packed chunk {i}"
+
+
+def test_redistribute_leading_padding_is_zero():
+    """Views whose first item starts after byte 0 (a caller-built table): the
+    bytes before it are padding and are written as zero, as swr_pack_layer
+    writes them; the shards are never read before their start."""
+    note("redistribute with a leading gap")
+    shapes = [("a", 8, 16, synth.BF16), ("b", 12, 32, synth.FP8)]
+    n = 4
+    ws = [synth.weight(synth.seed_for(19, 0, t), o, i, d) for t, (_, o, i, d) in enumerate(shapes)]
+    shp = [(o, i, d) for _, o, i, d in shapes]
+    views, lay = swr.plan_layer(shp, n)
+    gap = 64  # move both items 64 bytes up; |T| still covers them
+    for v in views:
+        v["offset"] += gap
+    lay = dict(lay, payload_bytes=lay["payload_bytes"] + gap)
+    total = -(-lay["payload_bytes"] // (16 * n)) * 16 * n
+    lay = dict(lay, total_bytes=total, chunk_bytes=total // n)
+    specs, _ = _shard_specs(shapes, ws, n)
+    chunks = [torch.full((lay["chunk_bytes"],), 0xA5, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    swr.redistribute_row_shards(lay, views, specs, chunks)
+    packed = [torch.full((lay["chunk_bytes"],), 0x5A, dtype=torch.uint8, device=DEV) for _ in range(n)]
+    swr.pack_layer(lay, views, [u8(w.raw()) for w in ws], packed)
+    torch.cuda.synchronize()
+    # the oracle's T for this table: zeros, with each weight's bytes at its offset
+    t_ref = np.zeros(total, np.uint8)
+    for v, w in zip(views, ws):
+        t_ref[v["offset"]:v["offset"] + v["nbytes"]] = w.raw().view(np.uint8).reshape(-1)
+    got = np.concatenate([c.cpu().numpy() for c in chunks])
+    assert np.array_equal(got, t_ref)
+    assert np.array_equal(np.concatenate([c.cpu().numpy() for c in packed]), t_ref)

@@ -116,8 +116,11 @@ def test_tiny_config_mlp_and_projection():
 def test_intermediate_slices_add_up_on_gpu():
     """The PR report's equivalence: the MLP over intermediate slices [r*s, (r+1)*s)
     (gate rows, matching up rows, down columns) summed over r equals the full
-    MLP; here the slices run through mlp_forward with fp32-exact slicing of the
-    inputs and the sum is checked against the oracle's full MLP."""
+    MLP.  Here each slice runs through mlp_forward, whose output is rounded to
+    bf16: each slice is held to the bar against the oracle's slice, and the sum
+    of the four bf16 slices against the sum of the oracle's bf16-rounded slices
+    (the same composition).  The unrounded fp32 form of the same equivalence is
+    test_tensor_parallel_partials."""
     note("intermediate-slice partials")
     hidden, inter, ranks = 256, 512, 4
     dt = synth.FP8
@@ -126,13 +129,21 @@ def test_intermediate_slices_add_up_on_gpu():
     x = synth.activations(23, 12, hidden)
     sh = inter // ranks
     total = np.zeros((12, hidden))
+    total_ref = np.zeros((12, hidden))
     for r in range(ranks):
         rows = np.r_[r * sh:(r + 1) * sh, inter + r * sh:inter + (r + 1) * sh]
         gu_r = synth.Weight(2 * sh, hidden, dt, np.ascontiguousarray(gu.data[rows]), gu.scale[rows])
         d_r = synth.Weight(hidden, sh, dt, np.ascontiguousarray(d.data[:, r * sh:(r + 1) * sh]), d.scale)
-        total += values(_mlp(gu_r, d_r, hidden, sh, x))
+        y_r = values(_mlp(gu_r, d_r, hidden, sh, x))
+        ref_r = gemm.mlp_intermediate_slice_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter,
+                                                r * sh, (r + 1) * sh)
+        assert_close_rows(y_r, ref_r, what=f"slice {r}")
+        total += y_r
+        total_ref += numerics.bf16_round(ref_r)
+    assert_close_rows(total, total_ref, what="sum of bf16 slices")
     _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, dt, hidden, inter)
-    assert_close_rows(total, ref, rel=2e-2, what="sum of slices")
+    # and the oracle's own rounded slices add up to its full MLP within the bar
+    assert_close_rows(total_ref, ref, what="oracle: sum of bf16 slices vs full MLP")
 
 
 @pytest.fixture(scope="module")

@@ -131,13 +131,6 @@ def test_sequence_errors():
     p.close()
 
 
-def test_slot_memory_account():
-    """Two slots sized by the largest layer: R/N + 2 max|T_l| per rank."""
-    wl = synth.TINY
-    sizes = [swr.plan_layer([(o, i, d) for _, o, i, d in wl.weights], n)[1]["total_bytes"] for n in (4, 4, 4)]
-    assert accounting.weight_shard_memory(sizes, 4) == sum(sizes) // 4 + 2 * max(sizes)
-
-
 @pytest.mark.parametrize("start,n_layers", [(0, 2), (1, 4)])
 def test_cyclic_prefetch_on_gpu(start, n_layers):
     """Cyclic mode: each forward gathers the next forward's first layer during its

@@ -144,3 +144,87 @@ def test_sharded_matmul_layouts_agree():
 def test_row_tolerance():
     y = np.array([[0.5, -0.2], [30.0, -100.0]])
     assert gemm.row_tolerance(y).ravel().tolist() == [1e-2, 1.0]
+
+
+def test_mlp_fp8act_hand_case():
+    """The FP8-activation MLP composition (quantise X -> gate_up -> SiLU*up ->
+    bf16 h -> quantise h -> down) on two hand-built tokens whose every
+    rounding is worked out below, so that quantising G instead of h, skipping
+    h's or X's quantisation, putting s_x on the down GEMM, dropping s_h or
+    swapping gate and up each changes an output.
+
+    Weights (E4M3FN codes: 0x38 = 1, 0x30 = 0.5, 0x28 = 0.25, 0 = 0):
+      gate rows 0, 1 = [0.25, 0, 0, 0]      scale 1   -> g = x0 / 4
+      up row 0       = [0, 1, 0, 0]         scale 8   -> u0 = 8 x1
+      up row 1       = [0, 0, 1, 0.5]       scale 0.5 -> u1 = (x2 + x3/2) / 2
+      down rows      = [1, 0], [0, 0.5], [0.25, 0.25], [0, 0]; scales 1, 1, 2, 1
+    g is 112 or 56, where z / (1 + exp(-z)) == z exactly in float64.
+
+    Token 0: x = [448, 1, -28, 8]; amax 448 -> s_x = 1, every x is an E4M3
+      value.  g = 112, u = [8, -12], h = [896, -1344] (both exact in bf16).
+      s_h = 1344 / 448 = 3; h / s_h = [298.67, -448] -> codes 288, -448
+      (E4M3 spacing is 32 in [256, 448]), so dequantised h = [864, -1344].
+      y = [864, -672, 2 * (216 - 336), 0] = [864, -672, -240, 0].
+    Token 1: x = [224, 0.30078125, 3, -1]; s_x = 0.5; x / s_x =
+      [448, 0.6015625, 6, -2] -> 0.6015625 lies between 0.5625 and 0.625
+      (spacing 1/16) and is nearer 0.625, so dequantised x1 = 0.3125.
+      g = 56, u = [2.5, 1.25], h = [140, 70]; s_h = 140 / 448 = 0.3125,
+      h / s_h = [448, 224] exact.  y = [140, 35, 2 * (35 + 17.5), 0].
+    The BF16-activation MLP of the same inputs gives token 0 y0 = 896 and
+    token 1 y0 = bf16(56 * 8 * 0.30078125 = 134.75) = 135: both differ."""
+    hidden, inter = 4, 2
+    wgu = np.array([[0x28, 0, 0, 0], [0x28, 0, 0, 0], [0, 0x38, 0, 0], [0, 0, 0x38, 0x30]], np.uint8)
+    s_gu = np.array([1.0, 1.0, 8.0, 0.5], np.float32)
+    wd = np.array([[0x38, 0], [0, 0x30], [0x28, 0x28], [0, 0]], np.uint8)
+    s_d = np.array([1.0, 1.0, 2.0, 1.0], np.float32)
+    x = numerics.f64_to_bf16_bits(np.array([[448.0, 1.0, -28.0, 8.0], [224.0, 0.30078125, 3.0, -1.0]]))
+    assert numerics.bf16_to_f64(x)[1, 1] == 0.30078125  # representable in bf16
+    q_x, s_x, g, h, q_h, s_h, y = gemm.mlp_fp8act_f64(x, wgu, s_gu, wd, s_d, hidden, inter)
+    assert s_x.tolist() == [1.0, 0.5]
+    assert (numerics.fp8_to_f64(q_x) * s_x[:, None]).tolist() == [[448, 1, -28, 8], [224, 0.3125, 3, -1]]
+    assert g.tolist() == [[112, 112, 8, -12], [56, 56, 2.5, 1.25]]
+    assert numerics.bf16_to_f64(h).tolist() == [[896, -1344], [140, 70]]
+    assert s_h.tolist() == [3.0, 0.3125]
+    assert (numerics.fp8_to_f64(q_h) * s_h[:, None]).tolist() == [[864, -1344], [140, 70]]
+    assert y.tolist() == [[864, -672, -240, 0], [140, 35, 105, 0]]
+    # the BF16-activation MLP of the same inputs differs where the pages' path
+    # keeps activations unquantised
+    _, _, y16 = gemm.mlp_f64(x, wgu, s_gu, wd, s_d, "fp8_e4m3fn", hidden, inter)
+    assert y16[0, 0] == 896 and numerics.bf16_round(y16[1, 0]) == 135
+
+
+def test_mlp_fp8act_equals_w8a16_on_representable_activations():
+    """When both quantisations are exact, the FP8-activation MLP equals the
+    pages' W8A16 MLP bit for bit.  Token row: x0 = 256 * 2**e, x1 = +-448 *
+    2**e (the row maximum, so s_x = 2**e) and E4M3 values times 2**e
+    elsewhere.  gate rows: 0.25 * x0 = 64 * 2**e (>= 64, where silu(z) == z
+    in float64); up row j: x_{j+1}.  So h_j = 64 * 2**e * x_{j+1}, its row
+    maximum is |h_0| = 448 * 64 * 4**e, s_h = 64 * 4**e and h / s_h are the
+    E4M3 codes of x_{j+1} / 2**e: exact.  Power-of-two scales commute with
+    float64 rounding, so the two compositions give identical bits; a wrong
+    scale (s_x on the down GEMM, a missing s_x or s_h) would not."""
+    rng = np.random.default_rng(5)
+    hidden, inter, m = 8, 5, 12
+    e = rng.integers(0, 3, size=(m, 1)).astype(np.float64)
+    mags = numerics.fp8_to_f64(rng.integers(0x08, 0x7F, size=(m, hidden)).astype(np.uint8))
+    signs = np.where(rng.integers(0, 2, size=(m, hidden)) == 1, -1.0, 1.0)
+    xv = mags * signs
+    xv[:, 0] = 256.0
+    xv[:, 1] = 448.0 * signs[:, 1]
+    xv = xv * 2.0 ** e
+    x = numerics.f64_to_bf16_bits(xv)
+    assert np.array_equal(numerics.bf16_to_f64(x), xv)
+    wgu = np.zeros((2 * inter, hidden), np.uint8)
+    wgu[:inter, 0] = 0x28  # 0.25
+    for j in range(inter):
+        wgu[inter + j, j + 1] = 0x38  # 1.0
+    s_gu = np.ones(2 * inter, np.float32)
+    wd = rng.integers(0, 0x7F, size=(hidden, inter)).astype(np.uint8)
+    s_d = (2.0 ** rng.integers(-3, 3, size=hidden)).astype(np.float32)
+    q_x, s_x, g, h, q_h, s_h, y = gemm.mlp_fp8act_f64(x, wgu, s_gu, wd, s_d, hidden, inter)
+    _, h16, y16 = gemm.mlp_f64(x, wgu, s_gu, wd, s_d, "fp8_e4m3fn", hidden, inter)
+    assert s_x.tolist() == (2.0 ** e[:, 0]).tolist()
+    assert s_h.tolist() == (64.0 * 4.0 ** e[:, 0]).tolist()
+    assert np.array_equal(numerics.fp8_to_f64(q_h) * s_h[:, None].astype(np.float64), numerics.bf16_to_f64(h))
+    assert np.array_equal(h, h16)
+    assert np.array_equal(y, y16)
