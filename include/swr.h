@@ -314,6 +314,34 @@ int swr_mlp_forward_partial(const void* W_gate_up, const float* s_gu, const void
  * status for invalid sizes.  Host only. */
 int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int32_t dtype);
 
+/* Bytes of the fixed device scratch of swr_mlp_forward_noalloc (16 MiB). */
+#define SWR_NOALLOC_SCRATCH_BYTES (INT64_C(16) << 20)
+
+/*
+ * swr_mlp_forward_noalloc -- enqueue on `stream`.
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): computes exactly
+ * what swr_mlp_forward computes, with the same kernels and the same bits,
+ * but takes no workspace.  Its scratch (h and any split-K partial sums) is a
+ * fixed array of SWR_NOALLOC_SCRATCH_BYTES in the library's device memory,
+ * one per GPU, held until the process ends; the call itself allocates
+ * nothing.  The first call on a device (with that device current) looks up
+ * the array's address there.
+ *   Arguments as swr_mlp_forward without workspace / workspace_bytes.
+ *   Limit: swr_mlp_workspace_bytes(M, H, I, dtype) must not exceed
+ *   SWR_NOALLOC_SCRATCH_BYTES (the shared-expert MLP, H = 6144, I = 14336,
+ *   needs about 8 MB at 64 tokens); larger calls fail with SWR_E_CAPACITY
+ *   before any HIP call.
+ *   Concurrency: every call on one GPU uses that GPU's single array, which
+ *   keeps the last call's contents; calls whose work overlaps on one GPU (two
+ *   streams, two threads) race on it and must be ordered by the caller.
+ * Errors: as swr_mlp_forward, plus SWR_E_CAPACITY for sizes beyond the
+ * scratch.
+ */
+int swr_mlp_forward_noalloc(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
+                            int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y,
+                            hipStream_t stream);
+
 /*
  * FP8 activations (an option beyond the pages, which keep activations in
  * BF16; the weight_sharding page's FP8 variant quantises the weights only).

@@ -38,7 +38,8 @@ EXPORTS = (
     "swr_reassemble_into_slot_dma",
     "swr_planner_set_copy_engine", "swr_planner_set_gate", "swr_planner_set_gather_lds", "swr_proj_forward",
     "swr_proj_workspace_bytes", "swr_proj_forward_grouped", "swr_proj_grouped_workspace_bytes", "swr_mlp_forward",
-    "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_sum_partials", "swr_quantize_rows_e4m3",
+    "swr_mlp_forward_partial", "swr_mlp_workspace_bytes", "swr_mlp_forward_noalloc", "swr_sum_partials",
+    "swr_quantize_rows_e4m3",
     "swr_mlp_forward_fp8act", "swr_mlp_fp8act_workspace_bytes",
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
@@ -117,6 +118,7 @@ def lib() -> ctypes.CDLL:
         "swr_proj_grouped_workspace_bytes": (_i64, [ctypes.POINTER(ProjDesc), _i32, _i64]),
         "swr_mlp_forward": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
         "swr_mlp_workspace_bytes": (_i64, [_i64, _i64, _i64, _i32]),
+        "swr_mlp_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp]),
         "swr_mlp_forward_partial": (_i32, [_vp, _vp, _vp, _vp, _i32, _i64, _i64, _vp, _i64, _vp, _vp, _i64, _vp]),
         "swr_sum_partials": (_i32, [ctypes.POINTER(_vp), _i32, _i64, _vp, _i32, _vp]),
         "swr_quantize_rows_e4m3": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp]),
@@ -360,6 +362,20 @@ def mlp_forward(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter: int, x:
            lib().swr_mlp_forward(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), _dtype(dtype), int(hidden),
                                  int(inter), _ptr(x), int(m), _ptr(y), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def mlp_forward_noalloc(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter: int, x, y, m: int | None = None,
+                        stream=None) -> None:
+    """mlp_forward without a workspace: the library's fixed per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) holds h and the split-K partials."""
+    if m is None:
+        m = x.shape[0]
+    _check("swr_mlp_forward_noalloc",
+           lib().swr_mlp_forward_noalloc(_ptr(w_gate_up), _ptr(s_gu), _ptr(w_down), _ptr(s_d), _dtype(dtype),
+                                         int(hidden), int(inter), _ptr(x), int(m), _ptr(y), _stream(stream)))
 
 
 def mlp_forward_partial(w_gate_up, s_gu, w_down, s_d, dtype, hidden: int, inter: int, x: torch.Tensor,

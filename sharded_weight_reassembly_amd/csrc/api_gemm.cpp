@@ -246,7 +246,7 @@ extern "C" int64_t swr_mlp_workspace_bytes(int64_t M, int64_t H, int64_t I, int3
   return h_bytes(M, I) + round_up(pg > pd ? pg : pd, kWorkspaceAlign);
 }
 
-namespace {
+namespace swr {
 
 // The MLP of swr_mlp_forward; with y_fp32 the down GEMM writes fp32 (no rounding).
 int mlp_impl(const char* fn, const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
@@ -284,7 +284,9 @@ int mlp_impl(const char* fn, const void* W_gate_up, const float* s_gu, const voi
   return SWR_OK;
 }
 
-}  // namespace
+}  // namespace swr
+
+using swr::mlp_impl;
 
 extern "C" int swr_mlp_forward(const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
                                int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y,

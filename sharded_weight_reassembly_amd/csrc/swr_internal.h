@@ -109,6 +109,12 @@ constexpr int kMaxGroup = SWR_MAX_GROUP;
 bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt);
 hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStream_t stream);
 
+// The MLP behind swr_mlp_forward (y_fp32: swr_mlp_forward_partial): checks
+// every argument, then enqueues the GEMMs with `workspace` as scratch.
+int mlp_impl(const char* fn, const void* W_gate_up, const float* s_gu, const void* W_down, const float* s_d,
+             int32_t dtype, int64_t H, int64_t I, const void* X, int64_t M, void* Y, bool y_fp32, void* workspace,
+             int64_t workspace_bytes, hipStream_t stream);
+
 // ---------------------------------------------------------------- FP8 activations
 // Per-token E4M3FN codes and scales of BF16 rows (quant.hip).
 hipError_t launch_quantize_rows(const void* X, int64_t ldx, int64_t M, int64_t K, void* Q, int64_t ldq, float* S,

@@ -318,3 +318,15 @@ def test_memory_and_transfer_account_from_library_layouts():
         memory = resident + 2 * max(totals)
         received = (16 - 1) * lays[0]["chunk_bytes"]
         assert (totals[0], lays[0]["chunk_bytes"], memory, received) == want
+
+
+def test_noalloc_mlp_refuses_before_any_hip_call():
+    """swr_mlp_forward_noalloc checks pointers and its scratch limit on the host
+    first: 4096 shared-expert tokens need about 117 MB of scratch, more than
+    its fixed 16 MiB, and come back as SWR_E_CAPACITY (no GPU is touched)."""
+    L = swr.lib()
+    p = 1 << 20
+    assert L.swr_mlp_forward_noalloc(p, p, p, p, 1, 6144, 14336, p, 4096, p, None) == swr.E_CAPACITY
+    assert "scratch" in L.swr_last_error().decode()
+    assert L.swr_mlp_forward_noalloc(None, p, p, p, 1, 6144, 14336, p, 64, p, None) == swr.E_INVALID
+    assert swr.mlp_workspace_bytes(64, 6144, 14336, "fp8_e4m3fn") <= swr.NOALLOC_SCRATCH_BYTES
