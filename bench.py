@@ -51,9 +51,12 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=str, default="1,8,32,64")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: its own count)")
-    ap.add_argument("--gate", choices=["done", "begin"], default="done",
-                    help="decode: what the gather of layer l+1 waits for -- layer l-1 being done (the pages' gate) "
-                         "or the compute stream beginning layer l")
+    ap.add_argument("--gate", choices=["done", "begin", "after"], default="after",
+                    help="decode: what the gather of layer l+1 waits for -- layer l-1 being done (the pages' gate), "
+                         "the compute stream beginning layer l, or layer l being done (no overlap; the default: "
+                         "on one GPU the gather and the GEMMs share one HBM)")
+    ap.add_argument("--queues", type=int, choices=[1, 2], default=1,
+                    help="decode: 2 puts the gathers on a side stream, 1 on the compute stream itself (one queue)")
     ap.add_argument("--gather-lds", type=int, default=0,
                     help="decode: LDS bytes each copy workgroup of the planner's gathers reserves, to leave CUs "
                          "to the GEMMs (0: none)")
@@ -129,16 +132,22 @@ def main() -> int:
            for m in tokens}
 
     compute = torch.cuda.Stream()
-    side = torch.cuda.Stream()
-    planner = swr.Planner(0, L, compute, side, slot_a, slot_b)
-    for layer in range(L):
-        planner.set_layer(layer, chunks[layer], C)
-    if L % 2 == 0:
-        # forwards run back to back: each gathers the next one's first layer during its last layer
-        planner.set_cyclic(True)
-    gate_of = {"begin": swr.GATE_BEGIN, "done": swr.GATE_DONE}
-    planner.set_gate(gate_of[args.gate])
-    planner.set_gather_lds(args.gather_lds)
+    side_stream = torch.cuda.Stream()
+    side = compute if args.queues == 1 else side_stream
+    gate_of = {"begin": swr.GATE_BEGIN, "done": swr.GATE_DONE, "after": swr.GATE_AFTER}
+
+    def make_planner(gate: str, queues: int, gather_lds: int = 0, cyclic: bool = True):
+        pl = swr.Planner(0, L, compute, compute if queues == 1 else side_stream, slot_a, slot_b)
+        for layer in range(L):
+            pl.set_layer(layer, chunks[layer], C)
+        if cyclic and L % 2 == 0:
+            # forwards run back to back: each gathers the next one's first layer during its last layer
+            pl.set_cyclic(True)
+        pl.set_gate(gate_of[gate])
+        pl.set_gather_lds(gather_lds)
+        return pl
+
+    planner = make_planner(args.gate, args.queues, args.gather_lds)
     o_gu, o_d = views[0]["offset"], views[1]["offset"]
 
     def forward(m: int, gemm_events=None, pl=None) -> None:
@@ -171,6 +180,7 @@ def main() -> int:
     # packet before the layer's kernels -- to a record after done): no event
     # of the bench sits between a gate and the work it orders.
     planner.set_timing(args.steps * len(tokens) * L)
+    remote_before, gathers_before = planner.counters()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     with torch.cuda.stream(compute):
@@ -181,6 +191,7 @@ def main() -> int:
                 fwd_ev[m][s][1].record(compute)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    remote_after, gathers_after = planner.counters()
     gathers = planner.gather_times()
     layer_spans = planner.layer_times()
     planner.set_timing(0)
@@ -243,6 +254,7 @@ def main() -> int:
         torch.cuda.synchronize()
         return gemm, e0.elapsed_time(e1) / (args.isolated_reps * L)
 
+    default_schedule = f"gate_{args.gate}_queues_{args.queues}_lds_{args.gather_lds}"
     iso_gemm, iso_gather_ms = {}, None
     if args.timed_only:
         args.minimal = True  # nothing else after the timed steps
@@ -252,38 +264,80 @@ def main() -> int:
     # The sections below (serial reference, DMA-engine gather, tensor-parallel
     # share, graph replay) are reports beside the headline; --minimal skips
     # them, e.g. for hardware-counter runs that average over every MLP call.
-    serial_ms, dma, graph, tpres, gate_begin, yielding, R, rank_bytes = {}, {}, {}, {}, {}, {}, 4, 0
+    serial_ms, serial_bare_ms, dma, graph, tpres, schedules, R, rank_bytes = {}, {}, {}, {}, {}, {}, 4, 0
     if not args.minimal:
         # ---------------------------------------------------------------- serial reference
-        # the same gathers and MLPs back to back on one stream (no side stream, no overlap):
-        # on one GPU both share the HBM, so this shows what the overlap costs or gains
+        # the same gathers and MLPs back to back on one stream, without the
+        # planner: once bare, and once with timing events at the four places the
+        # planner's timing puts them in the timed steps (around each gather and
+        # each MLP; the same fence-free events), so that the timed steps compare
+        # with a reference that carries the same instrumentation
+        from bench_workloads import FenceFreeEvents
+
+        ev_pool = FenceFreeEvents(4 * L)
         with torch.cuda.stream(compute):
             for m in tokens:
-                def serial_forward():
+                def serial_forward(instrumented):
                     for layer in range(L):
                         s_ = slot_a if layer % 2 == 0 else slot_b
+                        if instrumented:
+                            ev_pool.record(4 * layer, compute)
                         swr.reassemble_into_slot(chunks[layer], C, s_, stream=compute)
+                        if instrumented:
+                            ev_pool.record(4 * layer + 1, compute)
+                            ev_pool.record(4 * layer + 2, compute)
                         b = s_.data_ptr()
                         swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
                                         xs[m], ys[m], wsp[m], stream=compute)
-                serial_forward()
+                        if instrumented:
+                            ev_pool.record(4 * layer + 3, compute)
+                for instrumented in (False, True):
+                    serial_forward(instrumented)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(compute)
+                    for _ in range(args.isolated_reps):
+                        serial_forward(instrumented)
+                    e1.record(compute)
+                    torch.cuda.synchronize()
+                    (serial_ms if instrumented else serial_bare_ms)[m] = e0.elapsed_time(e1) / args.isolated_reps
+        ev_pool.close()
+
+        # ---------------------------------------------------------------- schedules
+        # The same forwards under every gate, on two streams and on one queue,
+        # without timing events (ms per 8-layer forward).  On one GPU the
+        # gather (2|T| bytes) and the MLP (|T| bytes) draw on one HBM.
+        fwd_reps = max(4, args.steps // 2)
+
+        def time_forwards(pl, m, reps=fwd_reps):
+            with torch.cuda.stream(compute):
+                forward(m, pl=pl)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(compute)
-                for _ in range(args.isolated_reps):
-                    serial_forward()
+                for _ in range(reps):
+                    forward(m, pl=pl)
                 e1.record(compute)
-                torch.cuda.synchronize()
-                serial_ms[m] = e0.elapsed_time(e1) / args.isolated_reps
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        combos = [("done", 2, 0), ("begin", 2, 0), ("after", 2, 0), ("done", 2, YIELD_LDS), ("begin", 2, YIELD_LDS),
+                  ("done", 1, 0), ("after", 1, 0)]
+        if (args.gate, args.queues, args.gather_lds) not in combos:
+            combos.append((args.gate, args.queues, args.gather_lds))
+        for gname, q, lds in combos:
+            pl = make_planner(gname, q, lds)
+            schedules[f"gate_{gname}_queues_{q}_lds_{lds}"] = {str(m): round(time_forwards(pl, m), 4) for m in tokens}
+            pl.close()
 
         # ---------------------------------------------------------------- DMA-engine gather
-        # the same pipelined forwards with the gathers on the DMA engines (no compute
-        # units): the copy-engine path of the pages, at the smallest and largest M
+        # the pages' gate with the gathers on the DMA engines (no compute
+        # units): the copy-engine path, at the smallest and largest M
         dma = {}
-        planner.set_copy_engine(swr.ENGINE_DMA)
+        dpl = make_planner("done", 2)
+        dpl.set_copy_engine(swr.ENGINE_DMA)
         dma_steps = max(2, args.steps // 4)
         for m in sorted({tokens[0], tokens[-1]}):
             with torch.cuda.stream(compute):
-                forward(m)
+                forward(m, pl=dpl)
             torch.cuda.synchronize()
             evd = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
                    for _ in range(dma_steps)]
@@ -291,54 +345,14 @@ def main() -> int:
             with torch.cuda.stream(compute):
                 for s in range(dma_steps):
                     fwd_d[s][0].record(compute)
-                    forward(m, evd[s])
+                    forward(m, evd[s], pl=dpl)
                     fwd_d[s][1].record(compute)
             torch.cuda.synchronize()
             f = float(np.median([a.elapsed_time(b) for a, b in fwd_d]))
             g = float(np.mean([a.elapsed_time(b) for row in evd for a, b in row]))
             dma[str(m)] = {"pipelined_ms_per_forward": round(f, 4), "gemm_ms_per_layer_in_pipeline": round(g, 4),
                            "gemm_slowdown_vs_isolated": round(g / iso_gemm[m], 3)}
-        planner.set_copy_engine(swr.ENGINE_KERNEL)
-
-        # ---------------------------------------------------------------- the other gate
-        # the same pipelined forwards with the other gate, without timing events
-        other = "done" if args.gate == "begin" else "begin"
-        gate_begin = {"gate": other}
-        planner.set_gate(gate_of[other])
-        for m in tokens:
-            with torch.cuda.stream(compute):
-                forward(m)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(compute)
-                for _ in range(dma_steps * 2):
-                    forward(m)
-                e1.record(compute)
-            torch.cuda.synchronize()
-            gate_begin[str(m)] = {"pipelined_ms_per_forward": round(e0.elapsed_time(e1) / (dma_steps * 2), 4)}
-        planner.set_gate(gate_of[args.gate])
-
-        # ---------------------------------------------------------------- a gather that yields CUs
-        # The same pipelined forwards, without timing events, with and without
-        # the gather's LDS reservation (swr_planner_set_gather_lds), both gates.
-        yielding = {"gather_lds": YIELD_LDS}
-        for lds in (0, YIELD_LDS):
-            planner.set_gather_lds(lds)
-            for gname in ("done", "begin"):
-                planner.set_gate(gate_of[gname])
-                row = {}
-                for m in tokens:
-                    with torch.cuda.stream(compute):
-                        forward(m)
-                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                        e0.record(compute)
-                        for _ in range(dma_steps * 2):
-                            forward(m)
-                        e1.record(compute)
-                    torch.cuda.synchronize()
-                    row[str(m)] = round(e0.elapsed_time(e1) / (dma_steps * 2), 4)
-                yielding[f"lds_{lds}_gate_{gname}_ms_per_forward"] = row
-        planner.set_gather_lds(args.gather_lds)
-        planner.set_gate(gate_of[args.gate])
+        dpl.close()
 
         # ---------------------------------------------------------------- tensor-parallel share
         # The PR report's alternative to weight sharding: each of R ranks (its
@@ -439,36 +453,42 @@ def main() -> int:
     gemm_avg = {m: float(np.mean(gemm_ms[m])) for m in tokens}
     gather_avg = float(np.mean([v for m in tokens for v in gather_ms[m]]))
     per_kernel = {
-        "reassemble_into_slot": {
-            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS, "bytes_per_launch": 2 * T,
-            "avg_ms": gather_avg, "achieved": 2 * T / (gather_avg * 1e-3) / 1e9,
-        },
         "mlp_forward": {
+            "kernels": "staged_gemm_kernel (gate_up with SiLU*up) + staged_gemm_kernel (down) "
+                       "[+ splitk_finalize_kernel]",
             "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
             "bytes_per_launch": {str(m): mlp_alg_bytes(m) for m in tokens},
             "avg_ms": {str(m): gemm_avg[m] for m in tokens},
             "achieved": sum(mlp_alg_bytes(m) for m in tokens) / (sum(gemm_avg[m] for m in tokens) * 1e-3) / 1e9,
+            "frac_by_tokens": {str(m): round(mlp_alg_bytes(m) / (gemm_avg[m] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                               for m in tokens},
+        },
+        "reassemble_into_slot": {
+            "kernels": "reassemble_kernel",
+            "bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS, "bytes_per_launch": 2 * T,
+            "avg_ms": gather_avg, "achieved": 2 * T / (gather_avg * 1e-3) / 1e9,
         },
     }
     for k in per_kernel.values():
         k["frac"] = k["achieved"] / k["peak"]
-    # The roofline names one HIP kernel: the reassembly kernel (one launch per
-    # gather, timed by the planner's events on the side stream) takes the most
-    # GPU time of any single kernel in the timed steps (the kernel trace of
-    # `bench.py --timed-only` in profiles/: about 40% of the kernel time; the
-    # MLP's largest kernel, gate_up at one token block, about 23%).  The
-    # MLP call (two or three kernels, timed per layer on the compute stream)
-    # is reported beside it.
-    dominant = "reassemble_into_slot"
-    dk = per_kernel[dominant]
+        k["traffic"] = None
     for name, k in per_kernel.items():
         k["traffic"] = measured_traffic(name)
+    # The roofline names the decode MLP, the metric's own kernels: each call's
+    # duration is the span the planner records on the compute stream from the
+    # layer's begin (after its ready wait) to just after its done record, which
+    # holds the MLP's launches and nothing else; bytes are the algorithmic
+    # bytes of one call.  The gather's kernel is reported beside it.
+    dk = per_kernel["mlp_forward"]
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 1), "peak": dk["peak"], "unit": dk["unit"],
-                "frac": round(dk["frac"], 4), "traffic": dk["traffic"], "kernel": "reassemble_kernel"}
+                "frac": round(dk["frac"], 4), "traffic": dk["traffic"], "kernel": "mlp_forward",
+                "kernels": dk["kernels"], "target_frac": 0.80,
+                "target_met": bool(min(dk["frac_by_tokens"].values()) >= 0.80)}
 
     per_m = {}
     for m in tokens:
         fwd = float(np.median(fwd_ms[m]))
+        g_layer = float(np.mean(gather_ms[m]))
         per_m[str(m)] = {
             "pipelined_ms_per_forward": round(fwd, 4),
             "pipelined_tokens_per_s": round(m / (fwd * 1e-3), 1),
@@ -476,13 +496,41 @@ def main() -> int:
             "pipelined_hbm_frac": round(L * (3 * T + mlp_alg_bytes(m) - w_bytes) / (fwd * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "compute_stall_ms": round(fwd - L * gemm_avg[m], 4),
             "gemm_ms_per_layer_in_pipeline": round(gemm_avg[m], 4),
+            "gather_ms_per_layer_in_pipeline": round(g_layer, 4),
+            # the pages' evaluation: per layer, gather time over compute time,
+            # and the part of a layer's wall time that is not its GEMMs
+            "gather_to_compute_ratio": round(g_layer / gemm_avg[m], 3),
+            "exposed_ms_per_layer": round(fwd / L - gemm_avg[m], 4),
             **({} if m not in iso_gemm else {
                 "isolated_gemm_ms_per_layer": round(iso_gemm[m], 4),
                 "isolated_weight_GBps": round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9, 1),
                 "isolated_weight_frac": round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "isolated_tokens_per_s": round(m / (L * iso_gemm[m] * 1e-3), 1)}),
+                "isolated_tokens_per_s": round(m / (L * iso_gemm[m] * 1e-3), 1),
+                "isolated_gather_to_compute_ratio": round(iso_gather_ms / iso_gemm[m], 3)}),
             "serial_reference_ms_per_forward": round(serial_ms[m], 4) if m in serial_ms else None,
+            "serial_reference_bare_ms_per_forward": round(serial_bare_ms[m], 4) if m in serial_bare_ms else None,
+            "pipelined_bare_ms_per_forward": schedules.get(default_schedule, {}).get(str(m)),
         }
+
+    # ---------------------------------------------------------------- accounts
+    # weight_sharding, cost section: received bytes per layer (N-1)/N * |T| and
+    # per-rank weight memory R/N + 2 max|T_l|, from the library's own layouts
+    # and the planner's transfer counter over the timed steps
+    lays = [swr.plan_layer(shp, N)[1] for _ in range(L)]
+    r_total = sum(l_["total_bytes"] for l_ in lays)
+    per_rank = sum(l_["chunk_bytes"] for l_ in lays)
+    timed_gathers = gathers_after - gathers_before
+    accounts = {
+        "transfer_bytes_counted": remote_after - remote_before,
+        "gathers_counted": timed_gathers,
+        "transfer_bytes_per_gather": (remote_after - remote_before) // max(1, timed_gathers),
+        "transfer_bytes_per_gather_expected": (N - 1) * C,
+        "replicated_weight_bytes_R": r_total,
+        "resident_chunk_bytes_per_rank_R_over_N": per_rank,
+        "slot_bytes_2_max_T": 2 * max(l_["total_bytes"] for l_ in lays),
+        "weight_memory_per_rank": per_rank + 2 * max(l_["total_bytes"] for l_ in lays),
+        "all_chunks_on_this_gpu": N * per_rank,
+    }
 
     # a plain device-to-device copy of known size (read + write of the same
     # byte count), the reference that hardware byte counters are scaled by
@@ -515,17 +563,17 @@ def main() -> int:
         "config": {
             "workload": wl.name, "hidden": H, "intermediate": I, "layers": L, "n_chunks": N,
             "tokens": tokens, "layer_bytes": T, "chunk_bytes": C, "slots": 2, "gate": args.gate,
-            "gather_lds": args.gather_lds,
-            "step": "pipelined forward (side-stream reassembly + MLP) over all layers for every M",
+            "queues": args.queues, "gather_lds": args.gather_lds,
+            "step": "pipelined forward (reassembly + MLP per layer through the planner) over all layers for every M",
         },
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "per_tokens": per_m,
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1) if iso_gather_ms else None,
+        "schedules_ms_per_forward": schedules,
         "dma_engine_gather": dma,
-        "yielding_gather": yielding,
-        "other_gate": gate_begin,
-        "graph_replay_no_prefetch": graph,
+        "graph_replay": graph,
         "tensor_parallel_share": {"ranks": R, "rank_weight_bytes_per_layer": rank_bytes, "per_tokens": tpres},
+        "accounts": accounts,
         "roofline": roofline,
         "roofline_by_kernel": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                                for k, v in per_kernel.items()},
@@ -556,6 +604,17 @@ def measured_traffic(kernel: str):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, H, I, x_all, tokens) -> dict:
     """The oracle (float64 NumPy, untuned) on one layer at the largest M."""
     import numpy as np
@@ -583,6 +642,7 @@ def cpu_baseline(wl, H, I, x_all, tokens) -> dict:
         "unit": "GB/s",
         "tokens_per_s": round(m / (best * wl.layers), 3),
         "cores": int(threads),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"one shared-expert layer (of {wl.layers}) at M={m}, float64 NumPy oracle, best of 2 runs; "
                   f"tokens/s scaled to the {wl.layers}-layer stack",

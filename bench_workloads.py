@@ -45,6 +45,34 @@ def _threads() -> int:
         return os.cpu_count() or 1
 
 
+class FenceFreeEvents:
+    """HIP timing events without the system-scope fence on record (the kind the
+    planner's timing uses), made through the HIP runtime torch has loaded."""
+
+    def __init__(self, n: int):
+        import ctypes
+
+        self._ct = ctypes
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self._hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(0x20000000))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+            self.ev.append(e)
+
+    def record(self, i: int, stream) -> None:
+        rc = self._hip.hipEventRecord(self.ev[i], self._ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def close(self) -> None:
+        for e in self.ev:
+            self._hip.hipEventDestroy(e)
+        self.ev = []
+
+
 def _pack_layers(swr, torch, dev, wl, n_layers):
     shp = [(o, i, d) for _, o, i, d in wl.weights]
     views, lay = swr.plan_layer(shp, wl.n_chunks)
@@ -62,53 +90,70 @@ def _pack_layers(swr, torch, dev, wl, n_layers):
     return views, lay, chunks, scales
 
 
-class _Pipeline:
-    """A planner over ping-pong slots plus the timing the report needs."""
+GATES = ("done", "begin", "after")
 
-    def __init__(self, swr, torch, dev, lay, chunks):
+
+class _Pipeline:
+    """A planner over ping-pong slots plus the timing the report needs.
+    gate: "done" (the pages' gate), "begin" or "after"; queues: 2 puts the
+    gathers on a side stream, 1 on the compute stream itself."""
+
+    def __init__(self, swr, torch, dev, lay, chunks, gate="done", queues=2):
         self.swr, self.torch = swr, torch
         T, C = lay["total_bytes"], lay["chunk_bytes"]
         self.L = len(chunks)
         self.slot_a = torch.empty(T, dtype=torch.uint8, device=dev)
         self.slot_b = torch.empty(T, dtype=torch.uint8, device=dev)
         self.compute = torch.cuda.Stream()
-        self.side = torch.cuda.Stream()
-        self.planner = swr.Planner(0, self.L, self.compute, self.side, self.slot_a, self.slot_b)
-        for layer in range(self.L):
-            self.planner.set_layer(layer, chunks[layer], C)
-        if self.L % 2 == 0:
-            self.planner.set_cyclic(True)
+        self.side_stream = torch.cuda.Stream()
         self.chunks, self.C = chunks, C
+        self.gate, self.queues = gate, queues
+        self.planner = self.make_planner(gate, queues)
 
-    def forward(self, layer_fn, events=None):
-        p = self.planner
+    def make_planner(self, gate, queues):
+        swr = self.swr
+        p = swr.Planner(0, self.L, self.compute, self.compute if queues == 1 else self.side_stream, self.slot_a,
+                        self.slot_b)
+        for layer in range(self.L):
+            p.set_layer(layer, self.chunks[layer], self.C)
+        if self.L % 2 == 0:
+            p.set_cyclic(True)
+        p.set_gate({"done": swr.GATE_DONE, "begin": swr.GATE_BEGIN, "after": swr.GATE_AFTER}[gate])
+        return p
+
+    def forward(self, layer_fn, planner=None):
+        p = self.planner if planner is None else planner
         p.reset()
         p.pre_dispatch(0)
         for layer in range(self.L):
             p.maybe_dispatch(layer + 1)
             base = p.wait_ready_once(layer)
-            if events is not None:
-                events[layer][0].record(self.compute)
             layer_fn(layer, base)
-            if events is not None:
-                events[layer][1].record(self.compute)
             p.update_done_event(layer)
 
-    def serial_forward(self, layer_fn):
+    def serial_forward(self, layer_fn, events=None):
         for layer in range(self.L):
             s = self.slot_a if layer % 2 == 0 else self.slot_b
+            if events is not None:
+                events.record(4 * layer, self.compute)
             self.swr.reassemble_into_slot(self.chunks[layer], self.C, s, stream=self.compute)
+            if events is not None:
+                events.record(4 * layer + 1, self.compute)
+                events.record(4 * layer + 2, self.compute)
             layer_fn(layer, s.data_ptr())
+            if events is not None:
+                events.record(4 * layer + 3, self.compute)
 
     def timed(self, layer_fn, steps, warmup):
-        """Pipelined forwards: (wall s, per-forward ms, per-layer compute ms, gather ms)."""
+        """Pipelined forwards: (wall s, per-forward ms, per-layer compute ms, gather ms).
+        The planner's own fence-free timing events time each gather on the
+        stream it runs on and each layer's compute from its begin (after the
+        ready wait) to its done record."""
         torch = self.torch
         with torch.cuda.stream(self.compute):
             for _ in range(warmup):
                 self.forward(layer_fn)
         torch.cuda.synchronize()
-        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.L)]
-              for _ in range(steps)]
         fwd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         self.planner.set_timing(steps * self.L)
         torch.cuda.synchronize()
@@ -116,26 +161,55 @@ class _Pipeline:
         with torch.cuda.stream(self.compute):
             for s in range(steps):
                 fwd[s][0].record(self.compute)
-                self.forward(layer_fn, ev[s])
+                self.forward(layer_fn)
                 fwd[s][1].record(self.compute)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         gathers = self.planner.gather_times()
+        layer_ms = self.planner.layer_times()
         self.planner.set_timing(0)
         fwd_ms = [a.elapsed_time(b) for a, b in fwd]
-        layer_ms = [a.elapsed_time(b) for row in ev for a, b in row]
         return wall, fwd_ms, layer_ms, gathers
 
-    def timed_serial(self, layer_fn, reps):
+    def timed_bare(self, layer_fn, reps, planner=None):
+        """ms per pipelined forward with no timing events between kernels."""
         torch = self.torch
         with torch.cuda.stream(self.compute):
-            self.serial_forward(layer_fn)
+            self.forward(layer_fn, planner)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(self.compute)
             for _ in range(reps):
-                self.serial_forward(layer_fn)
+                self.forward(layer_fn, planner)
             e1.record(self.compute)
         torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def schedules(self, layer_fn, reps):
+        """ms per forward without timing events for each gate on two queues
+        and the done/after gates on one queue."""
+        out = {}
+        for gate, q in [(g, 2) for g in GATES] + [("done", 1), ("after", 1)]:
+            p = self.make_planner(gate, q)
+            out[f"gate_{gate}_queues_{q}"] = round(self.timed_bare(layer_fn, reps, p), 4)
+            p.close()
+        return out
+
+    def timed_serial(self, layer_fn, reps, instrumented=False):
+        """The same gathers and layers back to back on the compute stream; with
+        `instrumented`, fence-free timing events at the four places the
+        planner's timing puts them (around each gather and each layer)."""
+        torch = self.torch
+        ev = FenceFreeEvents(4 * self.L) if instrumented else None
+        with torch.cuda.stream(self.compute):
+            self.serial_forward(layer_fn, ev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.compute)
+            for _ in range(reps):
+                self.serial_forward(layer_fn, ev)
+            e1.record(self.compute)
+        torch.cuda.synchronize()
+        if ev is not None:
+            ev.close()
         return e0.elapsed_time(e1) / reps
 
     def isolated_gather_ms(self, reps):
@@ -196,7 +270,9 @@ def run_projections(args, swr, torch, np, synth, dev):
     xs = {i: torch.from_numpy(synth.activations(synth.seed_for(3, 0, 50 + j), m, i).view(np.int16).copy())
           .view(torch.bfloat16).to(dev) for j, i in enumerate(in_dims)}
     ys = [torch.empty((m, o), dtype=torch.bfloat16, device=dev) for _, o, _, _ in wl.weights]
-    pipe = _Pipeline(swr, torch, dev, lay, chunks)
+    # decode-shaped (16 tokens): the gather and the projections both stream
+    # HBM, so the default is the one-GPU schedule (gate after, one queue)
+    pipe = _Pipeline(swr, torch, dev, lay, chunks, gate=args.gate, queues=args.queues)
 
     def projs(layer, base):
         return [dict(w=base + views[j]["offset"], dtype=d, row_scale=scales[layer][j], out_f=o, in_f=i, x=xs[i],
@@ -218,7 +294,9 @@ def run_projections(args, swr, torch, np, synth, dev):
                     args.isolated_reps)
     del full
     iso_gather = pipe.isolated_gather_ms(args.isolated_reps)
-    serial = pipe.timed_serial(layer_fn, args.isolated_reps)
+    serial = pipe.timed_serial(layer_fn, args.isolated_reps, instrumented=True)
+    serial_bare = pipe.timed_serial(layer_fn, args.isolated_reps)
+    schedules = pipe.schedules(layer_fn, max(4, args.steps // 2))
     pipe.close()
 
     alg = w_bytes + s_bytes + sum(m * i * 2 for _, _, i, _ in wl.weights) + sum(m * o * 2 for _, o, _, _ in wl.weights)
@@ -256,8 +334,9 @@ def run_projections(args, swr, torch, np, synth, dev):
                        "synthetic: seeded N(0,0.02) weights quantised per row to E4M3FN, N(0,1) bf16 tokens",
                        {"workload": wl.name, "layers": L, "n_chunks": wl.n_chunks, "tokens": m, "layer_bytes": T,
                         "projections": [[o, i] for _, o, i, _ in wl.weights],
-                        "step": "pipelined forward (side-stream reassembly + the 8 projections as one grouped "
-                                "launch) over all layers"})
+                        "gate": args.gate, "queues": args.queues,
+                        "step": "pipelined forward (reassembly + the 8 projections as one grouped launch, per "
+                                "layer through the planner) over all layers"})
     rec.update({
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "pipelined_ms_per_forward": round(fwd, 4),
@@ -266,7 +345,12 @@ def run_projections(args, swr, torch, np, synth, dev):
         "isolated_weight_frac": round((w_bytes + s_bytes) / (iso * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "isolated_reassembly_GBps": round(2 * T / (iso_gather * 1e-3) / 1e9, 1),
         "serial_reference_ms_per_forward": round(serial, 4),
+        "serial_reference_bare_ms_per_forward": round(serial_bare, 4),
+        "pipelined_bare_ms_per_forward": schedules.get(f"gate_{args.gate}_queues_{args.queues}"),
+        "schedules_ms_per_forward": schedules,
         "compute_stall_ms": round(fwd - L * layer_avg, 4),
+        "gather_to_compute_ratio": round(gather_avg / layer_avg, 3),
+        "exposed_ms_per_layer": round(fwd / L - layer_avg, 4),
         "roofline": {"bound": dk["bound"], "achieved": round(dk["achieved"], 1), "peak": dk["peak"],
                      "unit": dk["unit"], "frac": round(dk["frac"], 4), "traffic": None, "kernel": dom},
         "roofline_by_kernel": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

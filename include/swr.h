@@ -429,8 +429,11 @@ enum swr_trace_op {
 enum swr_trace_stream { SWR_STREAM_COMPUTE = 0, SWR_STREAM_SIDE = 1 };
 
 /* start < end; slot_a, slot_b device pointers (16-byte aligned, slot_bytes
- * each); compute and side must be different streams.  Errors:
- * SWR_E_INVALID, SWR_E_ALIGN, SWR_E_HIP (event creation). */
+ * each).  compute and side are normally two streams; they may be the same
+ * stream ("one queue"): the gathers then run between the layers' GEMMs in
+ * queue order, the waits between the two roles are implied by that order and
+ * are not enqueued, and the trace is unchanged.  Errors: SWR_E_INVALID,
+ * SWR_E_ALIGN, SWR_E_HIP (event creation). */
 int swr_planner_create(int32_t start, int32_t end, hipStream_t compute, hipStream_t side,
                        void* slot_a, void* slot_b, int64_t slot_bytes, swr_planner** out);
 
@@ -456,6 +459,7 @@ int swr_planner_update_done_event(swr_planner* p, int32_t layer);
 /* Gate of the planner's gathers (swr_planner_set_gate). */
 #define SWR_GATE_DONE 0  /* gather(l+1) waits for done(l-1), as the pages (default)     */
 #define SWR_GATE_BEGIN 1 /* gather(l+1) waits for the compute stream to begin layer l */
+#define SWR_GATE_AFTER 2 /* gather(l+1) waits for done(l): no overlap                  */
 
 /*
  * swr_planner_set_gate -- which compute-stream event gates each gather.
@@ -472,7 +476,16 @@ int swr_planner_update_done_event(swr_planner* p, int32_t layer);
  *                   pending), and on one GPU the layer's GEMM workgroups are
  *                   resident before the copy's many short workgroups arrive.
  * The trace then shows SWR_OP_RECORD_BEGIN / SWR_OP_WAIT_BEGIN in place of
- * SWR_OP_WAIT_DONE.  Host only.
+ * SWR_OP_WAIT_DONE.
+ *   SWR_GATE_AFTER  the gather of l+1 waits for done(l) and is enqueued by
+ *                   swr_planner_update_done_event(l) (swr_planner_maybe_dispatch
+ *                   only marks it pending): the same gathers, slots and events
+ *                   with no overlap.  On one GPU the gather (2|T| bytes) and the
+ *                   GEMMs (|T| bytes) draw on the same HBM, and a slot that the
+ *                   GEMMs read right after it was written is partly still in the
+ *                   last-level cache; this is the one-GPU schedule.  The trace
+ *                   shows SWR_OP_WAIT_DONE of layer l before each gather.
+ * Host only.
  * Errors: SWR_E_INVALID (null planner, unknown gate), SWR_E_SEQUENCE (a
  * gather is pending).
  */

@@ -32,6 +32,14 @@ l+1 on the side stream, so the gather may start exactly when the page's gate
 allows; it is enqueued after the compute stream's ready wait instead of
 before it.
 
+Gate "after" (a one-GPU schedule, same slots and ready/done events): the
+gather of layer l+1 waits for done(l), the layer that runs just before it,
+and is enqueued when that done event is recorded.  On one GPU the gather
+and the GEMMs draw on the same HBM, so running them one after the other (and
+reading each slot right after it was written) can beat running them side by
+side; the gate is the page's done gate moved one layer later, which orders
+the gather after both earlier readers of its slot.
+
 An op is a tuple (name, stream, layer, slot) with names
   record_start  wait_start  wait_done  copy  copy_next  record_ready
   wait_ready  record_done  record_begin  wait_begin
@@ -54,14 +62,27 @@ def expected_trace(start: int, end: int, prefetched: bool = False, prefetch_next
 
     prefetched: the previous forward already gathered layer `start` (cyclic mode);
     prefetch_next: this forward gathers the next forward's layer `start`;
-    gate: "done" (the page's gate) or "begin"."""
+    gate: "done" (the page's gate), "begin" or "after"."""
     ops: list[tuple] = [("record_start", COMPUTE, -1, -1)]
     if end <= start:
         return ops
     if prefetch_next and ((end - start) % 2 or end - start < 2):
         raise ValueError("cyclic prefetch needs an even number of layers")
-    if gate not in ("done", "begin"):
-        raise ValueError("gate is 'done' or 'begin'")
+    if gate not in ("done", "begin", "after"):
+        raise ValueError("gate is 'done', 'begin' or 'after'")
+    if gate == "after":
+        if not prefetched:
+            ops += [("wait_start", SIDE, -1, -1), ("copy", SIDE, start, 0), ("record_ready", SIDE, start, -1)]
+        for layer in range(start, end):
+            ops.append(("wait_ready", COMPUTE, layer, slot_of(layer, start)))
+            ops.append(("record_done", COMPUTE, layer, -1))
+            if layer + 1 < end:
+                ops += [("wait_done", SIDE, layer, -1), ("copy", SIDE, layer + 1, slot_of(layer + 1, start)),
+                        ("record_ready", SIDE, layer + 1, -1)]
+            elif prefetch_next:
+                ops += [("wait_done", SIDE, layer, -1), ("copy_next", SIDE, start, 0),
+                        ("record_ready", SIDE, start, -1)]
+        return ops
     if gate == "begin":
         if not prefetched:
             ops += [("wait_start", SIDE, -1, -1), ("copy", SIDE, start, 0), ("record_ready", SIDE, start, -1)]

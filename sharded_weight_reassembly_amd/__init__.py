@@ -280,7 +280,7 @@ def reassemble_into_slot_dma(chunks, chunk_bytes: int, slot, slot_bytes: int | N
 
 
 ENGINE_KERNEL, ENGINE_DMA = 0, 1
-GATE_DONE, GATE_BEGIN = 0, 1
+GATE_DONE, GATE_BEGIN, GATE_AFTER = 0, 1, 2
 
 
 def view(slot: torch.Tensor, v: dict) -> torch.Tensor:

@@ -15,6 +15,13 @@
 // section, maybe_dispatch(end) gathers the next forward's first layer into
 // slot 0 -- free once done(end - 2) is recorded, since the last layer reads
 // slot 1 -- so the next forward starts without an exposed gather.
+//
+// Gates: the gather of l+1 waits for done(l-1) (the pages' gate), for the
+// compute stream to begin layer l, or for done(l) ("after": no overlap; on
+// one GPU the gather and the GEMMs share one HBM, and a slot read right after
+// it was written is partly still in the last-level cache).  With one queue
+// (compute == side) the waits between the two roles are implied by queue
+// order and are not enqueued; the trace still lists them.
 #include <vector>
 
 #include "swr_internal.h"
@@ -50,12 +57,14 @@ struct swr_planner {
   // LDS each copy workgroup of the planner's gathers reserves (0: none)
   int32_t gather_lds = 0;
 
-  // gate mode: each gather of layer l+1 waits for the compute stream to begin
-  // layer l (after its ready(l) wait) instead of done(l-1); the gather is
-  // enqueued by wait_ready_once(l)
+  // gate mode SWR_GATE_BEGIN: each gather of layer l+1 waits for the compute
+  // stream to begin layer l (after its ready(l) wait) instead of done(l-1);
+  // the gather is enqueued by wait_ready_once(l).  SWR_GATE_AFTER: it waits
+  // for done(l) and is enqueued by update_done_event(l).
   bool gate_begin = false;
+  bool gate_after = false;
   std::vector<hipEvent_t> begin;
-  int32_t pending = -1;       // layer whose gather waits for the next begin record
+  int32_t pending = -1;       // layer whose gather waits for the next begin (or done) record
   bool pending_next = false;  // the next forward's first layer waits likewise
 
   // cyclic first-layer prefetch
@@ -70,6 +79,7 @@ struct swr_planner {
   int64_t gathers = 0;
   std::vector<int32_t> trace;
 
+  bool one_queue() const { return compute == side; }
   int idx(int32_t layer) const { return layer - start; }
   bool in_range(int32_t layer) const { return layer >= start && layer < end; }
   int slot_of(int32_t layer) const { return (layer - start) & 1; }
@@ -103,16 +113,20 @@ void destroy_events(swr_planner* p) {
 
 // Side stream: gate, gather of `layer` into its slot, ready record.  With
 // `for_next`, the gather is the next forward's first layer (cyclic mode): its
-// slot's last reader in this forward is layer end - 2.
-int dispatch(swr_planner* p, int32_t layer, bool for_next = false, hipEvent_t begin_gate = nullptr,
-             int32_t begin_layer = -1) {
+// slot's last reader in this forward is layer end - 2.  `begin_layer` >= 0
+// (gate SWR_GATE_BEGIN) gates it on the begin record of that layer;
+// `after_layer` >= 0 (gate SWR_GATE_AFTER) on done(after_layer).
+int dispatch(swr_planner* p, int32_t layer, bool for_next = false, int32_t begin_layer = -1,
+             int32_t after_layer = -1) {
   const int i = p->idx(layer);
   const swr_planner::Layer& L = p->layers[i];
   if (L.chunks.empty()) return fail(SWR_E_SEQUENCE, "planner: layer %d has no chunks (swr_planner_set_layer)", layer);
   hipEvent_t gate;
-  const int32_t prev = for_next ? p->end - 2 : layer - 2;  // last reader of the slot this gather overwrites
-  if (begin_gate) {
-    gate = begin_gate;  // recorded on the compute stream after done(prev)
+  const bool by_begin = begin_layer >= 0;
+  const int32_t prev = after_layer >= 0 ? after_layer
+                       : (for_next ? p->end - 2 : layer - 2);  // last reader of the slot this gather overwrites
+  if (by_begin) {
+    gate = p->begin[p->idx(begin_layer)];  // recorded on the compute stream after done(prev)
   } else if (prev >= p->start) {
     if (!p->finished[p->idx(prev)])
       return fail(SWR_E_SEQUENCE, "planner: gather of layer %d needs done(%d), which was not recorded", layer, prev);
@@ -130,13 +144,18 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false, hipEvent_t be
       return swr_reassemble_into_slot_dma(chunks, n, c, slot, slot_bytes, rank, side, g, ready, remote_bytes);
     return swr::reassemble_reserving(chunks, n, c, slot, slot_bytes, rank, side, g, ready, remote_bytes, lds);
   };
+  // one queue: the gate precedes the gather and the gather precedes its
+  // reader in queue order already, so neither the gate wait nor the ready
+  // record is enqueued
+  hipEvent_t wait_on = p->one_queue() ? nullptr : gate;
+  hipEvent_t ready = p->one_queue() ? nullptr : p->ready[i];
   if (p->t0.empty()) {
-    rc = gather(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s], p->slot_bytes, 0, p->side, gate,
-                p->ready[i], &remote);
+    rc = gather(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s], p->slot_bytes, 0, p->side,
+                wait_on, ready, &remote);
   } else {
     // same sequence with timing records between the gate wait and the ready record
     const size_t r = size_t(p->timed_dispatches % int64_t(p->t0.size()));
-    hipError_t e = hipStreamWaitEvent(p->side, gate, 0);
+    hipError_t e = wait_on ? hipStreamWaitEvent(p->side, wait_on, 0) : hipSuccess;
     if (e != hipSuccess) return swr::hip_fail(e, "planner: wait gate");
     e = hipEventRecord(p->t0[r], p->side);
     if (e != hipSuccess) return swr::hip_fail(e, "planner: record timing start");
@@ -144,13 +163,13 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false, hipEvent_t be
                 nullptr, nullptr, &remote);
     if (rc == SWR_OK) {
       e = hipEventRecord(p->t1[r], p->side);
-      if (e == hipSuccess) e = hipEventRecord(p->ready[i], p->side);
+      if (e == hipSuccess && ready) e = hipEventRecord(ready, p->side);
       if (e != hipSuccess) return swr::hip_fail(e, "planner: record timing end / ready");
       p->timed_dispatches += 1;
     }
   }
   if (rc != SWR_OK) return rc;
-  if (begin_gate)
+  if (by_begin)
     p->log(SWR_OP_WAIT_BEGIN, SWR_STREAM_SIDE, begin_layer, -1);
   else if (prev >= p->start)
     p->log(SWR_OP_WAIT_DONE, SWR_STREAM_SIDE, prev, -1);
@@ -175,7 +194,6 @@ extern "C" int swr_planner_create(int32_t start, int32_t end, hipStream_t comput
   *out = nullptr;
   if (end <= start || start < 0) return fail(SWR_E_INVALID, "swr_planner_create: empty range [%d, %d)", start, end);
   if (end - start > (1 << 20)) return fail(SWR_E_INVALID, "swr_planner_create: too many layers");
-  if (compute == side) return fail(SWR_E_INVALID, "swr_planner_create: compute and side must be different streams");
   if (slot_bytes <= 0) return fail(SWR_E_INVALID, "swr_planner_create: slot_bytes must be positive");
   if (!swr::aligned(slot_a, 16) || !swr::aligned(slot_b, 16))
     return fail(SWR_E_ALIGN, "swr_planner_create: slots must be 16-byte aligned");
@@ -237,7 +255,8 @@ extern "C" int swr_planner_set_layer(swr_planner* p, int32_t layer, const void* 
 
 extern "C" int swr_planner_reset(swr_planner* p) {
   if (!p) return fail(SWR_E_INVALID, "swr_planner_reset: null pointer");
-  const hipError_t e = hipEventRecord(p->start_evt, p->compute);
+  // (one queue: the forward-start point is implied by queue order)
+  const hipError_t e = p->one_queue() ? hipSuccess : hipEventRecord(p->start_evt, p->compute);
   if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_reset: record start");
   std::fill(p->dispatched.begin(), p->dispatched.end(), 0);
   std::fill(p->waited.begin(), p->waited.end(), 0);
@@ -277,7 +296,7 @@ extern "C" int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer) {
   if (layer == p->end && p->cyclic && p->reset_called && !p->next_prefetched) {
     if (!p->dispatched[p->idx(p->end - 1)])
       return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: next forward before layer %d", p->end - 1);
-    if (p->gate_begin) {  // enqueued by wait_ready_once(end - 1)
+    if (p->gate_begin || p->gate_after) {  // enqueued by wait_ready_once / update_done_event(end - 1)
       p->pending_next = true;
       swr::clear_error();
       return SWR_OK;
@@ -295,7 +314,8 @@ extern "C" int swr_planner_maybe_dispatch(swr_planner* p, int32_t layer) {
     return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d already dispatched in this forward", layer);
   if (layer > p->start && !p->dispatched[p->idx(layer - 1)])
     return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d before layer %d", layer, layer - 1);
-  if (p->gate_begin && layer > p->start) {  // enqueued by wait_ready_once(layer - 1)
+  if ((p->gate_begin || p->gate_after) && layer > p->start) {
+    // enqueued by wait_ready_once(layer - 1) (begin) or update_done_event(layer - 1) (after)
     if (p->pending >= 0)
       return fail(SWR_E_SEQUENCE, "swr_planner_maybe_dispatch: layer %d is still pending", p->pending);
     p->pending = layer;
@@ -314,36 +334,36 @@ extern "C" int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void**
   const int i = p->idx(layer);
   if (!p->dispatched[i]) return fail(SWR_E_SEQUENCE, "swr_planner_wait_ready_once: layer %d not dispatched", layer);
   if (!p->waited[i]) {
-    const hipError_t e = hipStreamWaitEvent(p->compute, p->ready[i], 0);
+    // one queue: the gather precedes this point in queue order already
+    const hipError_t e = p->one_queue() ? hipSuccess : hipStreamWaitEvent(p->compute, p->ready[i], 0);
     if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_wait_ready_once: wait");
     p->waited[i] = 1;
     p->log(SWR_OP_WAIT_READY, SWR_STREAM_COMPUTE, layer, p->slot_of(layer));
     const bool next_due = p->pending == layer + 1;
     const bool first_due = p->pending_next && layer == p->end - 1;
     const bool gate_due = p->gate_begin && (next_due || first_due);
-    // the begin record: a timing event when layers are timed, the gate of the
-    // pending gather in SWR_GATE_BEGIN mode, or both
-    hipEvent_t begin_ev = nullptr;
+    // the begin records: the gate of the pending gather in SWR_GATE_BEGIN
+    // mode (two queues only), and the layer's timing start when layers are
+    // timed
+    if (gate_due && !p->one_queue()) {
+      const hipError_t eb = hipEventRecord(p->begin[i], p->compute);
+      if (eb != hipSuccess) return swr::hip_fail(eb, "swr_planner_wait_ready_once: record begin");
+    }
     if (!p->c0.empty()) {
       const int64_t r = p->timed_layers % int64_t(p->c0.size());
       p->layer_slot[i] = r;
-      begin_ev = p->c0[size_t(r)];
-    } else if (gate_due) {
-      begin_ev = p->begin[i];
-    }
-    if (begin_ev) {
-      const hipError_t eb = hipEventRecord(begin_ev, p->compute);
-      if (eb != hipSuccess) return swr::hip_fail(eb, "swr_planner_wait_ready_once: record begin");
+      const hipError_t eb = hipEventRecord(p->c0[size_t(r)], p->compute);
+      if (eb != hipSuccess) return swr::hip_fail(eb, "swr_planner_wait_ready_once: record timing start");
     }
     if (gate_due) {
       p->log(SWR_OP_RECORD_BEGIN, SWR_STREAM_COMPUTE, layer, -1);
       int rc;
       if (next_due) {
         p->pending = -1;
-        rc = dispatch(p, layer + 1, false, begin_ev, layer);
+        rc = dispatch(p, layer + 1, false, layer);
       } else {
         p->pending_next = false;
-        rc = dispatch(p, p->start, true, begin_ev, layer);
+        rc = dispatch(p, p->start, true, layer);
       }
       if (rc != SWR_OK) return rc;
     }
@@ -360,7 +380,7 @@ extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
   const int i = p->idx(layer);
   if (!p->waited[i])
     return fail(SWR_E_SEQUENCE, "swr_planner_update_done_event: layer %d did not wait for its weights", layer);
-  hipError_t e = hipEventRecord(p->done[i], p->compute);
+  hipError_t e = p->one_queue() ? hipSuccess : hipEventRecord(p->done[i], p->compute);
   if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record");
   if (!p->c1.empty() && p->layer_slot[i] >= 0) {
     e = hipEventRecord(p->c1[size_t(p->layer_slot[i])], p->compute);
@@ -370,6 +390,19 @@ extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
   }
   p->finished[i] = 1;
   p->log(SWR_OP_RECORD_DONE, SWR_STREAM_COMPUTE, layer, -1);
+  if (p->gate_after) {
+    // the pending gather of layer + 1 (or of the next forward's first layer)
+    // waits for done(layer), just recorded
+    int rc = SWR_OK;
+    if (p->pending == layer + 1) {
+      p->pending = -1;
+      rc = dispatch(p, layer + 1, false, -1, layer);
+    } else if (p->pending_next && layer == p->end - 1) {
+      p->pending_next = false;
+      rc = dispatch(p, p->start, true, -1, layer);
+    }
+    if (rc != SWR_OK) return rc;
+  }
   swr::clear_error();
   return SWR_OK;
 }
@@ -386,11 +419,12 @@ extern "C" int swr_planner_set_cyclic(swr_planner* p, int32_t enabled) {
 
 extern "C" int swr_planner_set_gate(swr_planner* p, int32_t gate) {
   if (!p) return fail(SWR_E_INVALID, "swr_planner_set_gate: null pointer");
-  if (gate != SWR_GATE_DONE && gate != SWR_GATE_BEGIN)
+  if (gate != SWR_GATE_DONE && gate != SWR_GATE_BEGIN && gate != SWR_GATE_AFTER)
     return fail(SWR_E_INVALID, "swr_planner_set_gate: unknown gate %d", gate);
   if (p->pending >= 0 || p->pending_next)
     return fail(SWR_E_SEQUENCE, "swr_planner_set_gate: a gather is still pending");
   p->gate_begin = gate == SWR_GATE_BEGIN;
+  p->gate_after = gate == SWR_GATE_AFTER;
   swr::clear_error();
   return SWR_OK;
 }
@@ -433,11 +467,15 @@ extern "C" int swr_planner_set_timing(swr_planner* p, int32_t capacity) {
   p->timed_dispatches = 0;
   p->timed_layers = 0;
   hipError_t e = hipSuccess;
+  // Timing events carry no system-scope fence: they only mark time, and on
+  // MI355X a fenced record costs about 2.5 us between two kernels (its cache
+  // writeback) against under 1 us without it.
+  const unsigned tf = hipEventDisableSystemFence;
   for (int i = 0; e == hipSuccess && i < capacity; ++i) {
-    e = hipEventCreate(&p->t0[i]);
-    if (e == hipSuccess) e = hipEventCreate(&p->t1[i]);
-    if (e == hipSuccess) e = hipEventCreate(&p->c0[i]);
-    if (e == hipSuccess) e = hipEventCreate(&p->c1[i]);
+    e = hipEventCreateWithFlags(&p->t0[i], tf);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->t1[i], tf);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->c0[i], tf);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->c1[i], tf);
   }
   if (e != hipSuccess) {
     for (auto* v : {&p->t0, &p->t1, &p->c0, &p->c1}) {

@@ -269,7 +269,8 @@ def test_planner_errors_without_gpu_work():
     h = ctypes.c_void_p()
     a = 1 << 20
     assert L.swr_planner_create(3, 3, 1, 2, a, a, 4096, ctypes.byref(h)) == swr.E_INVALID
-    assert L.swr_planner_create(0, 4, 1, 1, a, a, 4096, ctypes.byref(h)) == swr.E_INVALID
+    assert L.swr_planner_create(0, 4, 1, 2, a, a, 0, ctypes.byref(h)) == swr.E_INVALID
+    assert L.swr_planner_set_gate(None, swr.GATE_AFTER) == swr.E_INVALID
     assert L.swr_planner_create(0, 4, 1, 2, a + 8, a, 4096, ctypes.byref(h)) == swr.E_ALIGN
     assert L.swr_planner_create(0, 4, 1, 2, None, a, 4096, ctypes.byref(h)) == swr.E_INVALID
     assert L.swr_planner_reset(None) == swr.E_INVALID

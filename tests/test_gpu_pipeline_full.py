@@ -62,12 +62,15 @@ def stack():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("m", [1, 64])
-@pytest.mark.parametrize("gate,gather_lds", [(swr.GATE_DONE, 0), (swr.GATE_BEGIN, 57344), (swr.GATE_DONE, 57344)])
-def test_full_size_pipeline_matches_oracle(stack, m, gate, gather_lds):
+@pytest.mark.parametrize("gate,gather_lds,one_queue", [(swr.GATE_DONE, 0, False), (swr.GATE_BEGIN, 57344, False),
+                                                       (swr.GATE_DONE, 57344, False), (swr.GATE_AFTER, 0, False),
+                                                       (swr.GATE_AFTER, 0, True)])
+def test_full_size_pipeline_matches_oracle(stack, m, gate, gather_lds, one_queue):
     wl, lay, views = stack["wl"], stack["lay"], stack["views"]
     H, I, C = wl.hidden, wl.intermediate, lay["chunk_bytes"]
-    note(f"full-size pipeline m={m} gate={gate} gather_lds={gather_lds}")
-    compute, side = torch.cuda.Stream(), torch.cuda.Stream()
+    note(f"full-size pipeline m={m} gate={gate} gather_lds={gather_lds} one_queue={one_queue}")
+    compute = torch.cuda.Stream()
+    side = compute if one_queue else torch.cuda.Stream()
     slot_a, slot_b = stack["slots"]
     # garbage in both slots: a layer that computed before its gather landed would show it
     slot_a.fill_(0x7F)
@@ -100,7 +103,7 @@ def test_full_size_pipeline_matches_oracle(stack, m, gate, gather_lds):
                 p.update_done_event(layer)
             traces.append(p.trace())
     torch.cuda.synchronize()
-    g = "begin" if gate == swr.GATE_BEGIN else "done"
+    g = {swr.GATE_DONE: "done", swr.GATE_BEGIN: "begin", swr.GATE_AFTER: "after"}[gate]
     assert traces[0] == osch.expected_trace(0, N_LAYERS, prefetched=False, prefetch_next=True, gate=g)
     assert traces[1] == osch.expected_trace(0, N_LAYERS, prefetched=True, prefetch_next=True, gate=g)
     assert osch.check_trace(traces) == []

@@ -23,6 +23,8 @@ from gpu_util import DEV, assert_close_rows, bf16, note, u8, values
 
 pytestmark = pytest.mark.gpu
 
+GATE_NAMES = {swr.GATE_DONE: "done", swr.GATE_BEGIN: "begin", swr.GATE_AFTER: "after"}
+
 
 def _layers(wl, n_layers, n_chunks):
     layers = []
@@ -285,24 +287,27 @@ def test_gather_lds_reservation(gather_lds, gate):
     p.close()
 
 
-@pytest.mark.parametrize("engine,gate,gather_lds", [(swr.ENGINE_KERNEL, swr.GATE_DONE, 0),
-                                                    (swr.ENGINE_DMA, swr.GATE_DONE, 0),
-                                                    (swr.ENGINE_KERNEL, swr.GATE_BEGIN, 0),
-                                                    (swr.ENGINE_KERNEL, swr.GATE_DONE, 57344)])
-def test_forward_captured_in_a_graph(engine, gate, gather_lds):
+@pytest.mark.parametrize("engine,gate,gather_lds,one_queue", [(swr.ENGINE_KERNEL, swr.GATE_DONE, 0, False),
+                                                              (swr.ENGINE_DMA, swr.GATE_DONE, 0, False),
+                                                              (swr.ENGINE_KERNEL, swr.GATE_BEGIN, 0, False),
+                                                              (swr.ENGINE_KERNEL, swr.GATE_DONE, 57344, False),
+                                                              (swr.ENGINE_KERNEL, swr.GATE_AFTER, 0, False),
+                                                              (swr.ENGINE_KERNEL, swr.GATE_AFTER, 0, True)])
+def test_forward_captured_in_a_graph(engine, gate, gather_lds, one_queue):
     """weight_sharding, CUDA graph section: the launch/wait sequence is fixed,
     so one forward (gathers on the side stream, MLPs on the compute stream)
     can be captured once and replayed.  Between replays both slots and every
     output are overwritten with garbage by eager work; each replay must
     gather again and reproduce the oracle's outputs."""
-    note(f"graph capture engine={engine} gate={gate} gather_lds={gather_lds}")
+    note(f"graph capture engine={engine} gate={gate} gather_lds={gather_lds} one_queue={one_queue}")
     wl = synth.TINY
     n_layers = 4
     layers = _layers(wl, n_layers, wl.n_chunks)
     total = layers[0]["lay"]["total_bytes"]
     slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
     slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
-    compute, side = torch.cuda.Stream(), torch.cuda.Stream()
+    compute = torch.cuda.Stream()
+    side = compute if one_queue else torch.cuda.Stream()
     p = swr.Planner(0, n_layers, compute, side, slot_a, slot_b)
     for i, L in enumerate(layers):
         p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
@@ -324,7 +329,7 @@ def test_forward_captured_in_a_graph(engine, gate, gather_lds):
     with torch.cuda.graph(g, stream=compute):
         _forward(p, layers, 0, xd, outs, wsb)
     # the captured sequence is the model's
-    assert p.trace() == osch.expected_trace(0, n_layers, gate="begin" if gate == swr.GATE_BEGIN else "done")
+    assert p.trace() == osch.expected_trace(0, n_layers, gate=GATE_NAMES[gate])
     torch.cuda.synchronize()
     for rep in range(4):
         slot_a.fill_(0xFF)  # 0xFFFF as bf16 is NaN: a replay that skipped a gather would show it
@@ -419,4 +424,70 @@ def test_set_gate_refused_while_a_gather_is_pending():
     p.update_done_event(1)
     p.set_gate(swr.GATE_DONE)
     torch.cuda.synchronize()
+    p.close()
+
+
+@pytest.mark.parametrize("start,n_layers,cyclic,one_queue", [(0, 3, False, False), (1, 4, True, False),
+                                                             (0, 2, True, True), (1, 5, False, True)])
+def test_after_gate_on_gpu(start, n_layers, cyclic, one_queue):
+    """SWR_GATE_AFTER: the gather of layer l+1 waits for done(l) and is enqueued
+    by update_done_event(l); with one queue (compute == side) the waits are
+    implied by queue order.  The trace equals the oracle's model of that gate,
+    passes the happens-before checker, and every layer's outputs equal the
+    oracle's with the compute stream delayed; the slots hold the oracle's T."""
+    note(f"planner after gate start={start} layers={n_layers} cyclic={cyclic} one_queue={one_queue}")
+    wl = synth.TINY
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    compute = torch.cuda.current_stream()
+    side = compute if one_queue else torch.cuda.Stream()
+    p = swr.Planner(start, start + n_layers, compute, side, slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(start + i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_gate(swr.GATE_AFTER)
+    if cyclic:
+        p.set_cyclic(True)
+    p.set_timing(64)
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    a = torch.randn(2048, 2048, device=DEV)
+
+    def delay():
+        for _ in range(4):
+            torch.mm(a, a)
+
+    traces, outs_all = [], []
+    for _ in range(3):
+        outs = [torch.empty((4, wl.hidden), dtype=torch.bfloat16, device=DEV) for _ in layers]
+        _forward(p, layers, start, xd, outs, wsb, delay)
+        traces.append(p.trace())
+        outs_all.append(outs)
+    torch.cuda.synchronize()
+    end = start + n_layers
+    if cyclic:
+        assert traces[0] == osch.expected_trace(start, end, prefetch_next=True, gate="after")
+        assert all(t == osch.expected_trace(start, end, prefetched=True, prefetch_next=True, gate="after")
+                   for t in traces[1:])
+    else:
+        assert all(t == osch.expected_trace(start, end, gate="after") for t in traces)
+    assert osch.check_trace(traces) == []
+    for outs in outs_all:
+        for i, L in enumerate(layers):
+            ws = L["ws"]
+            _, _, ref = gemm.mlp_f64(x, ws[0].raw(), None, ws[1].raw(), None, "bf16", wl.hidden, wl.intermediate)
+            assert_close_rows(values(outs[i]), ref, what=f"after gate layer {start + i}")
+    times = p.layer_times()
+    assert len(times) == 3 * n_layers and all(t > 0 for t in times)
+    assert len(p.gather_times()) == (3 * n_layers + 1 if cyclic else 3 * n_layers)
+    # the last layer's slot holds the oracle's flat buffer bit for bit
+    last = slot_b if (n_layers - 1) % 2 else slot_a
+    plan = olayout.plan_layer([(o, i, d) for _, o, i, d in wl.weights], wl.n_chunks)
+    if not cyclic:
+        t_ref, _ = olayout.pack_layer(plan, [w.raw() for w in layers[-1]["ws"]])
+        assert np.array_equal(last.cpu().numpy(), t_ref)
+    p.set_timing(0)
+    p.set_cyclic(False)
     p.close()

@@ -117,3 +117,37 @@ def test_begin_gate_mistakes_are_caught():
     assert any("race" in p for p in sch.check_trace([early]))
     with pytest.raises(ValueError):
         sch.expected_trace(0, 4, gate="ready")
+
+
+@pytest.mark.parametrize("start,end", [(0, 1), (0, 2), (1, 5), (3, 11)])
+def test_after_gate_is_race_free(start, end):
+    t = sch.expected_trace(start, end, gate="after")
+    assert sch.check_trace([t, t, t]) == []
+    # the same gathers into the same slots as the page's gate, in the same order
+    copies = lambda tr: [op for op in tr if op[0] in ("copy", "copy_next")]
+    assert copies(t) == copies(sch.expected_trace(start, end))
+    # each gather after the first follows the done record of the layer before it
+    for i, op in enumerate(t):
+        if op[0] == "copy" and op[2] > start:
+            assert t[i - 1] == ("wait_done", "side", op[2] - 1, -1)
+            assert t[i - 2] == ("record_done", "compute", op[2] - 1, -1)
+
+
+@pytest.mark.parametrize("start,end", [(0, 2), (1, 9)])
+def test_after_gate_cyclic_is_race_free(start, end):
+    first = sch.expected_trace(start, end, prefetch_next=True, gate="after")
+    mid = sch.expected_trace(start, end, prefetched=True, prefetch_next=True, gate="after")
+    last = sch.expected_trace(start, end, prefetched=True, gate="after")
+    assert sch.check_trace([first, mid, mid, last]) == []
+    assert first[-3:] == [("wait_done", "side", end - 1, -1), ("copy_next", "side", start, 0),
+                          ("record_ready", "side", start, -1)]
+
+
+def test_after_gate_mistakes_are_caught():
+    t = sch.expected_trace(0, 6, gate="after")
+    no_wait = [op for op in t if op[0] != "wait_done"]
+    assert any("race" in p for p in sch.check_trace([no_wait]))
+    # a layer that does not wait for its gather reads whatever the slot holds
+    no_ready = [op for op in t if op != ("wait_ready", "compute", 3, 1)]
+    assert sch.check_trace([no_ready])
+
