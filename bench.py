@@ -407,43 +407,64 @@ def main() -> int:
         del shards
 
         # ---------------------------------------------------------------- graph replay
-        # one forward captured as a graph (weight_sharding, CUDA graph section) and
-        # replayed: a planner without the cross-forward prefetch, so every replay
-        # is self-contained, against the same planner run eagerly
+        # one forward captured as a graph (weight_sharding, CUDA graph section)
+        # and replayed, against the same planner run eagerly:
+        #   * without a prefetch: the captured forward gathers its first layer
+        #     itself, so every replay stands alone;
+        #   * with the first layer gathered on a dedicated stream outside the
+        #     graph (swr_planner_set_first_prefetch): each replay's prefetch for
+        #     the next replay is enqueued right behind it and overlaps its last
+        #     layer; the graph waits for it.
         graph = {}
-        gp = swr.Planner(0, L, compute, side, slot_a, slot_b)
-        gp.set_gate(gate_of[args.gate])
-        for layer in range(L):
-            gp.set_layer(layer, chunks[layer], C)
         reps = max(4, args.steps // 2)
-        for m in sorted({tokens[0], tokens[-1]}):
-            with torch.cuda.stream(compute):
-                forward(m, pl=gp)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(compute):
-                e0.record(compute)
-                for _ in range(reps):
+        pf_stream = torch.cuda.Stream()
+        for mode in ("no_prefetch", "first_layer_prefetch_stream"):
+            gp = swr.Planner(0, L, compute, side, slot_a, slot_b)
+            gp.set_gate(gate_of[args.gate])
+            for layer in range(L):
+                gp.set_layer(layer, chunks[layer], C)
+            pre = mode != "no_prefetch"
+            if pre:
+                gp.set_first_prefetch(pf_stream)
+                gp.prefetch_first()
+            row = {}
+            for m in sorted({tokens[0], tokens[-1]}):
+                def eager_fwd():
                     forward(m, pl=gp)
-                e1.record(compute)
-            torch.cuda.synchronize()
-            eager = e0.elapsed_time(e1) / reps
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=compute):
-                forward(m, pl=gp)
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with torch.cuda.stream(compute):
-                e0.record(compute)
-                for _ in range(reps):
-                    g.replay()
-                e1.record(compute)
-            torch.cuda.synchronize()
-            graph[str(m)] = {"eager_ms_per_forward": round(eager, 4),
-                             "graph_replay_ms_per_forward": round(e0.elapsed_time(e1) / reps, 4)}
-            del g
-        gp.close()
+                    if pre:
+                        gp.prefetch_first()
+                with torch.cuda.stream(compute):
+                    eager_fwd()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(compute):
+                    e0.record(compute)
+                    for _ in range(reps):
+                        eager_fwd()
+                    e1.record(compute)
+                torch.cuda.synchronize()
+                eager = e0.elapsed_time(e1) / reps
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=compute):
+                    forward(m, pl=gp)
+                g.replay()
+                if pre:
+                    gp.prefetch_first()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(compute):
+                    e0.record(compute)
+                    for _ in range(reps):
+                        g.replay()
+                        if pre:
+                            gp.prefetch_first()
+                    e1.record(compute)
+                torch.cuda.synchronize()
+                row[str(m)] = {"eager_ms_per_forward": round(eager, 4),
+                               "graph_replay_ms_per_forward": round(e0.elapsed_time(e1) / reps, 4)}
+                del g
+            graph[mode] = row
+            gp.close()
 
     # ---------------------------------------------------------------- roofline
     def mlp_alg_bytes(m: int) -> int:

@@ -424,9 +424,11 @@ enum swr_trace_op {
   SWR_OP_RECORD_READY = 5, SWR_OP_WAIT_READY = 6, SWR_OP_RECORD_DONE = 7,
   SWR_OP_COPY_NEXT = 8, /* cyclic mode: the next forward's first layer */
   SWR_OP_RECORD_BEGIN = 9, /* gate SWR_GATE_BEGIN: compute stream begins layer l (after its ready wait) */
-  SWR_OP_WAIT_BEGIN = 10   /* side stream waits for that record before a gather */
+  SWR_OP_WAIT_BEGIN = 10,  /* side stream waits for that record before a gather */
+  SWR_OP_RECORD_FREE = 11, /* dedicated first-layer prefetch: slot 0's last reader (layer l) is done */
+  SWR_OP_WAIT_FREE = 12    /* the prefetch stream waits for that record before gathering the first layer */
 };
-enum swr_trace_stream { SWR_STREAM_COMPUTE = 0, SWR_STREAM_SIDE = 1 };
+enum swr_trace_stream { SWR_STREAM_COMPUTE = 0, SWR_STREAM_SIDE = 1, SWR_STREAM_PREFETCH = 2 };
 
 /* start < end; slot_a, slot_b device pointers (16-byte aligned, slot_bytes
  * each).  compute and side are normally two streams; they may be the same
@@ -533,6 +535,43 @@ int swr_planner_set_gather_lds(swr_planner* p, int32_t bytes);
  * wait_ready_once(start) waits for that gather.  The trace shows the early
  * gather as SWR_OP_COPY_NEXT.  SWR_E_INVALID for an odd number of layers. */
 int swr_planner_set_cyclic(swr_planner* p, int32_t enabled);
+
+/*
+ * swr_planner_set_first_prefetch -- gather the first layer on a dedicated
+ * stream, outside the forward (weight_sharding, "CUDA graph and the draft
+ * model": the draft model's layer-0 gather runs outside the captured graph on
+ * its own stream, overlapping the main model's last layers, and the graph
+ * waits for it).  With a non-null `stream`:
+ *   - swr_planner_pre_dispatch(start) enqueues nothing; the forward's first
+ *     layer is the one swr_planner_prefetch_first gathered into slot 0;
+ *   - swr_planner_wait_ready_once(start) makes the compute stream wait for
+ *     that gather's ready event (while the compute stream is capturing, with
+ *     hipEventWaitExternal, so the graph holds the wait as a node and every
+ *     replay waits again);
+ *   - swr_planner_update_done_event(l0), l0 the last layer of the forward
+ *     that reads slot 0 (the last l with l - start even), records a "free"
+ *     event (while capturing, as an event-record node added to the graph,
+ *     which every replay records).
+ * Call swr_planner_prefetch_first once before the first forward and once
+ * after each forward (or each replay of a captured forward), outside any
+ * capture.  Refused while a forward is in progress, with the compute stream,
+ * and in cyclic mode (which gathers the first layer in the previous forward
+ * instead).  NULL turns the mode off.  Host only.
+ * Errors: SWR_E_INVALID, SWR_E_SEQUENCE.
+ */
+int swr_planner_set_first_prefetch(swr_planner* p, hipStream_t stream);
+
+/*
+ * swr_planner_prefetch_first -- enqueue on the dedicated stream: wait for the
+ * latest "free" event (none before the first forward), gather layer start
+ * into slot 0 (copy kernel or DMA engines, as swr_planner_set_copy_engine),
+ * record ready(start).  The trace lists SWR_OP_WAIT_FREE, SWR_OP_COPY_NEXT and
+ * SWR_OP_RECORD_READY on SWR_STREAM_PREFETCH.  Counts as a gather in
+ * swr_planner_counters.
+ * Errors: SWR_E_INVALID, SWR_E_SEQUENCE (no prefetch stream, no chunks for
+ * the first layer), SWR_E_HIP.
+ */
+int swr_planner_prefetch_first(swr_planner* p);
 
 /* Timing of the gathers and of the layers.  swr_planner_set_timing(p, capacity)
  * with capacity > 0 makes every later dispatch record two timing events on the

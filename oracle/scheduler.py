@@ -40,32 +40,67 @@ reading each slot right after it was written) can beat running them side by
 side; the gate is the page's done gate moved one layer later, which orders
 the gather after both earlier readers of its slot.
 
+First-layer prefetch on a dedicated stream (the page's CUDA-graph section:
+the draft model's layer-0 gather runs outside the captured graph, on its own
+stream, overlapping the main model's last layers, and the graph waits for
+it).  Here the forward (which may be captured) does not gather its first
+layer: its compute stream waits for ready(start) recorded by a prefetch made
+outside it, and it records a "free" event once slot 0's last reader in the
+forward, layer l0 = the last layer with (l - start) even, is done.  The
+prefetch, on stream "prefetch", waits for that event, gathers layer start
+into slot 0 for the next forward and records ready(start).
+
 An op is a tuple (name, stream, layer, slot) with names
   record_start  wait_start  wait_done  copy  copy_next  record_ready
-  wait_ready  record_done  record_begin  wait_begin
+  wait_ready  record_done  record_begin  wait_begin  record_free  wait_free
 and layer/slot -1 where they do not apply; ``copy_next`` is a gather made in
 one forward for the next one.  ``check_trace`` is an independent
 happens-before checker: it does not reuse ``expected_trace``.
 """
 from __future__ import annotations
 
-COMPUTE, SIDE = "compute", "side"
+COMPUTE, SIDE, PREFETCH = "compute", "side", "prefetch"
 
 
 def slot_of(layer: int, start: int) -> int:
     return (layer - start) % 2
 
 
+def last_slot0_reader(start: int, end: int) -> int:
+    """The last layer of [start, end) that reads slot 0."""
+    return start + ((end - 1 - start) & ~1)
+
+
+def prefetch_first_ops(start: int, end: int) -> list[tuple]:
+    """The dedicated-stream gather of the next forward's first layer."""
+    return [("wait_free", PREFETCH, last_slot0_reader(start, end), -1), ("copy_next", PREFETCH, start, 0),
+            ("record_ready", PREFETCH, start, -1)]
+
+
 def expected_trace(start: int, end: int, prefetched: bool = False, prefetch_next: bool = False,
-                   gate: str = "done") -> list[tuple]:
+                   gate: str = "done", first_external: bool = False) -> list[tuple]:
     """Launch/wait sequence of one forward over layers [start, end).
 
     prefetched: the previous forward already gathered layer `start` (cyclic mode);
     prefetch_next: this forward gathers the next forward's layer `start`;
-    gate: "done" (the page's gate), "begin" or "after"."""
+    gate: "done" (the page's gate), "begin" or "after";
+    first_external: layer `start` comes from a dedicated-stream prefetch made
+    outside the forward (prefetch_first_ops), and the forward records the
+    "free" event after its last reader of slot 0."""
     ops: list[tuple] = [("record_start", COMPUTE, -1, -1)]
     if end <= start:
         return ops
+    if first_external:
+        if prefetched or prefetch_next:
+            raise ValueError("the dedicated first-layer prefetch replaces the cyclic one")
+        inner = expected_trace(start, end, prefetched=True, gate=gate)
+        l0 = last_slot0_reader(start, end)
+        out = []
+        for op in inner:
+            out.append(op)
+            if op == ("record_done", COMPUTE, l0, -1):
+                out.append(("record_free", COMPUTE, l0, 0))
+        return out
     if prefetch_next and ((end - start) % 2 or end - start < 2):
         raise ValueError("cyclic prefetch needs an even number of layers")
     if gate not in ("done", "begin", "after"):
@@ -136,6 +171,8 @@ def _event(op: tuple):
         return ("done", layer)
     if name in ("record_begin", "wait_begin"):
         return ("begin", layer)
+    if name in ("record_free", "wait_free"):
+        return ("free",)
     return None
 
 

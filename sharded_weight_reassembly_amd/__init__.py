@@ -29,8 +29,9 @@ STATUS_NAMES = {0: "SWR_OK", -1: "SWR_E_INVALID", -2: "SWR_E_ALIGN", -3: "SWR_E_
                 -5: "SWR_E_HIP", -6: "SWR_E_SEQUENCE"}
 
 TRACE_OPS = {1: "record_start", 2: "wait_start", 3: "wait_done", 4: "copy", 5: "record_ready", 6: "wait_ready",
-             7: "record_done", 8: "copy_next", 9: "record_begin", 10: "wait_begin"}
-TRACE_STREAMS = {0: "compute", 1: "side"}
+             7: "record_done", 8: "copy_next", 9: "record_begin", 10: "wait_begin", 11: "record_free",
+             12: "wait_free"}
+TRACE_STREAMS = {0: "compute", 1: "side", 2: "prefetch"}
 
 # Every function include/swr.h declares.
 EXPORTS = (
@@ -44,7 +45,8 @@ EXPORTS = (
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
-    "swr_planner_gather_times", "swr_planner_layer_times", "swr_planner_set_cyclic", "swr_last_error", "swr_version",
+    "swr_planner_gather_times", "swr_planner_layer_times", "swr_planner_set_cyclic", "swr_planner_set_first_prefetch",
+    "swr_planner_prefetch_first", "swr_last_error", "swr_version",
 )
 
 
@@ -136,6 +138,8 @@ def lib() -> ctypes.CDLL:
         "swr_planner_destroy": (None, [_vp]),
         "swr_planner_set_timing": (_i32, [_vp, _i32]),
         "swr_planner_set_cyclic": (_i32, [_vp, _i32]),
+        "swr_planner_set_first_prefetch": (_i32, [_vp, _vp]),
+        "swr_planner_prefetch_first": (_i32, [_vp]),
         "swr_planner_gather_times": (_i32, [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]),
         "swr_planner_layer_times": (_i32, [_vp, ctypes.POINTER(ctypes.c_float), _i32, ctypes.POINTER(_i32)]),
         "swr_last_error": (ctypes.c_char_p, []),
@@ -463,6 +467,15 @@ class Planner:
     def set_cyclic(self, enabled: bool) -> None:
         """Gather the next forward's first layer during the last layer (even layer counts)."""
         _check("swr_planner_set_cyclic", lib().swr_planner_set_cyclic(self._h, int(bool(enabled))))
+
+    def set_first_prefetch(self, stream) -> None:
+        """Gather the first layer on a dedicated stream (None: off); see prefetch_first."""
+        _check("swr_planner_set_first_prefetch",
+               lib().swr_planner_set_first_prefetch(self._h, None if stream is None else _stream(stream)))
+
+    def prefetch_first(self) -> None:
+        """On the dedicated stream: wait for slot 0 to be free, gather the first layer, record its ready event."""
+        _check("swr_planner_prefetch_first", lib().swr_planner_prefetch_first(self._h))
 
     def set_gate(self, gate: int) -> None:
         """GATE_DONE (gather(l+1) waits for done(l-1), default) or GATE_BEGIN (waits for layer l to begin)."""

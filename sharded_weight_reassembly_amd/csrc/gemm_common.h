@@ -56,6 +56,51 @@ __device__ inline bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Raw buffer resource (base, no stride, num_records bytes) in scalar registers.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+__device__ inline u32x4s raw_rsrc(const void* base, int64_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  // the same in every lane: kept in scalar registers (the loads take it there)
+  u32x4s r;
+  r[0] = __builtin_amdgcn_readfirstlane(uint32_t(p));
+  r[1] = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32) & 0xFFFFu);  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(uint32_t(bytes));
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// One 16-byte buffer-to-LDS load per lane: lane l's bytes land at lds + 16*l
+// (the wave-uniform base goes in M0).  Written as assembly so that the
+// compiler adds no waits of its own for it: this kernel orders these loads
+// itself (wait_vm before each barrier).  NT selects the streaming hint.  The
+// LDS base is an M0 operand of the statement ("{m0}"), so the compiler itself
+// writes M0 before it and knows what M0 holds.
+template <bool NT>
+__device__ inline void lds_load16(const u32x4s& res, uint8_t* lds, int voffset, int soffset) {
+  // the base is the same in every lane of the wave
+  const uint32_t base = __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)lds)));
+  if constexpr (NT)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds"
+                 :
+                 : "v"(voffset), "s"(res), "s"(soffset), "{m0}"(base)
+                 : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voffset), "s"(res), "s"(soffset), "{m0}"(base)
+                 : "memory");
+}
+
+template <int N>
+__device__ inline void wait_vm() {
+  // s_waitcnt with vmcnt = N and the other counters at their maximum
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+
 __device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 __device__ inline uint16_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x)); }

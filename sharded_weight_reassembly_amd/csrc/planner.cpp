@@ -16,6 +16,14 @@
 // slot 0 -- free once done(end - 2) is recorded, since the last layer reads
 // slot 1 -- so the next forward starts without an exposed gather.
 //
+// First layer on a dedicated stream (the CUDA-graph section's draft-model
+// prefetch, outside the captured graph): the forward does not gather its
+// first layer; its compute stream waits (an external wait, a node of a
+// captured graph) for ready(start), which swr_planner_prefetch_first records
+// on the dedicated stream after gathering layer start into slot 0; that
+// gather waits for the "free" event the forward records (external record)
+// once slot 0's last reader is done.
+//
 // Gates: the gather of l+1 waits for done(l-1) (the pages' gate), for the
 // compute stream to begin layer l, or for done(l) ("after": no overlap; on
 // one GPU the gather and the GEMMs share one HBM, and a slot read right after
@@ -71,6 +79,12 @@ struct swr_planner {
   bool cyclic = false;
   bool next_prefetched = false;  // the next forward's first layer is already gathered
 
+  // first layer gathered on a dedicated stream outside the forward
+  hipStream_t pf = nullptr;
+  hipEvent_t first_ready = nullptr;  // recorded on pf after the first-layer gather
+  hipEvent_t slot0_free = nullptr;   // recorded (external) after slot 0's last reader
+  int64_t pf_issued = 0;             // first-layer gathers enqueued on pf
+
   // per-forward state
   bool reset_called = false;
   std::vector<uint8_t> dispatched, waited, finished;
@@ -80,6 +94,8 @@ struct swr_planner {
   std::vector<int32_t> trace;
 
   bool one_queue() const { return compute == side; }
+  bool first_external() const { return pf != nullptr; }
+  int32_t last_slot0_reader() const { return start + ((end - 1 - start) & ~1); }
   int idx(int32_t layer) const { return layer - start; }
   bool in_range(int32_t layer) const { return layer >= start && layer < end; }
   int slot_of(int32_t layer) const { return (layer - start) & 1; }
@@ -93,8 +109,39 @@ struct swr_planner {
 
 namespace {
 
+// True while `s` is capturing a graph.  The external record/wait flags make
+// graph nodes during a capture and are not used outside one.
+hipError_t capturing(hipStream_t s, bool* out) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(s, &st);
+  *out = st == hipStreamCaptureStatusActive;
+  return e;
+}
+
+// Records `ev` on `s`; while `s` captures a graph, as an event-record node of
+// that graph after the stream's current capture dependencies, so that every
+// replay records it (HIP refuses hipEventRecordExternal under capture).
+hipError_t record_visible(hipEvent_t ev, hipStream_t s) {
+  bool cap = false;
+  hipError_t e = capturing(s, &cap);
+  if (e != hipSuccess || !cap) return e == hipSuccess ? hipEventRecord(ev, s) : e;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  unsigned long long id = 0;
+  hipGraph_t graph = nullptr;
+  const hipGraphNode_t* deps = nullptr;
+  size_t ndeps = 0;
+  e = hipStreamGetCaptureInfo_v2(s, &st, &id, &graph, &deps, &ndeps);
+  if (e != hipSuccess) return e;
+  hipGraphNode_t node = nullptr;
+  e = hipGraphAddEventRecordNode(&node, graph, deps, ndeps, ev);
+  if (e != hipSuccess) return e;
+  return hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
+}
+
 void destroy_events(swr_planner* p) {
   if (p->start_evt) (void)hipEventDestroy(p->start_evt);
+  if (p->first_ready) (void)hipEventDestroy(p->first_ready);
+  if (p->slot0_free) (void)hipEventDestroy(p->slot0_free);
   for (hipEvent_t e : p->ready)
     if (e) (void)hipEventDestroy(e);
   for (hipEvent_t e : p->done)
@@ -215,6 +262,8 @@ extern "C" int swr_planner_create(int32_t start, int32_t end, hipStream_t comput
   p->waited.assign(n, 0);
   p->finished.assign(n, 0);
   hipError_t e = hipEventCreateWithFlags(&p->start_evt, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->first_ready, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&p->slot0_free, hipEventDisableTiming);
   for (int i = 0; e == hipSuccess && i < n; ++i) {
     e = hipEventCreateWithFlags(&p->ready[i], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->done[i], hipEventDisableTiming);
@@ -286,6 +335,14 @@ extern "C" int swr_planner_pre_dispatch(swr_planner* p, int32_t layer) {
     }
     return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: already dispatched");
   }
+  if (p->first_external()) {
+    // gathered on the dedicated stream (swr_planner_prefetch_first)
+    if (p->pf_issued == 0)
+      return fail(SWR_E_SEQUENCE, "swr_planner_pre_dispatch: call swr_planner_prefetch_first before the first forward");
+    p->dispatched[0] = 1;
+    swr::clear_error();
+    return SWR_OK;
+  }
   const int rc = dispatch(p, layer);
   if (rc == SWR_OK) swr::clear_error();
   return rc;
@@ -334,8 +391,17 @@ extern "C" int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void**
   const int i = p->idx(layer);
   if (!p->dispatched[i]) return fail(SWR_E_SEQUENCE, "swr_planner_wait_ready_once: layer %d not dispatched", layer);
   if (!p->waited[i]) {
-    // one queue: the gather precedes this point in queue order already
-    const hipError_t e = p->one_queue() ? hipSuccess : hipStreamWaitEvent(p->compute, p->ready[i], 0);
+    hipError_t e;
+    if (p->first_external() && layer == p->start) {
+      // the dedicated stream's gather; while capturing, an external wait (a
+      // node of the graph, so every replay waits again)
+      bool cap = false;
+      e = capturing(p->compute, &cap);
+      if (e == hipSuccess) e = hipStreamWaitEvent(p->compute, p->first_ready, cap ? hipEventWaitExternal : 0);
+    } else {
+      // one queue: the gather precedes this point in queue order already
+      e = p->one_queue() ? hipSuccess : hipStreamWaitEvent(p->compute, p->ready[i], 0);
+    }
     if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_wait_ready_once: wait");
     p->waited[i] = 1;
     p->log(SWR_OP_WAIT_READY, SWR_STREAM_COMPUTE, layer, p->slot_of(layer));
@@ -390,6 +456,13 @@ extern "C" int swr_planner_update_done_event(swr_planner* p, int32_t layer) {
   }
   p->finished[i] = 1;
   p->log(SWR_OP_RECORD_DONE, SWR_STREAM_COMPUTE, layer, -1);
+  if (p->first_external() && layer == p->last_slot0_reader()) {
+    // slot 0 is free for the next forward's first layer (while capturing, a
+    // record node of the graph, so that every replay records it)
+    e = record_visible(p->slot0_free, p->compute);
+    if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_update_done_event: record free");
+    p->log(SWR_OP_RECORD_FREE, SWR_STREAM_COMPUTE, layer, 0);
+  }
   if (p->gate_after) {
     // the pending gather of layer + 1 (or of the next forward's first layer)
     // waits for done(layer), just recorded
@@ -411,8 +484,55 @@ extern "C" int swr_planner_set_cyclic(swr_planner* p, int32_t enabled) {
   if (!p) return fail(SWR_E_INVALID, "swr_planner_set_cyclic: null pointer");
   if (enabled && ((p->end - p->start) % 2 != 0 || p->end - p->start < 2))
     return fail(SWR_E_INVALID, "swr_planner_set_cyclic: needs an even number of layers (have %d)", p->end - p->start);
+  if (enabled && p->first_external())
+    return fail(SWR_E_INVALID, "swr_planner_set_cyclic: the first layer is gathered on a dedicated stream");
   p->cyclic = enabled != 0;
   if (!p->cyclic) p->next_prefetched = false;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_set_first_prefetch(swr_planner* p, hipStream_t stream) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_set_first_prefetch: null pointer");
+  if (stream && stream == p->compute)
+    return fail(SWR_E_INVALID, "swr_planner_set_first_prefetch: the prefetch stream must not be the compute stream");
+  if (stream && p->cyclic)
+    return fail(SWR_E_INVALID, "swr_planner_set_first_prefetch: cyclic mode gathers the first layer already");
+  if (p->reset_called && p->dispatched[0] && !p->finished[p->idx(p->end - 1)])
+    return fail(SWR_E_SEQUENCE, "swr_planner_set_first_prefetch: a forward is in progress");
+  p->pf = stream;
+  p->pf_issued = 0;
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_prefetch_first(swr_planner* p) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_prefetch_first: null pointer");
+  if (!p->first_external())
+    return fail(SWR_E_SEQUENCE, "swr_planner_prefetch_first: no prefetch stream (swr_planner_set_first_prefetch)");
+  const swr_planner::Layer& L = p->layers[0];
+  if (L.chunks.empty())
+    return fail(SWR_E_SEQUENCE, "swr_planner_prefetch_first: layer %d has no chunks (swr_planner_set_layer)", p->start);
+  // slot 0's last reader in the latest forward; before any forward the event
+  // was never recorded and the wait orders nothing
+  hipError_t e = hipStreamWaitEvent(p->pf, p->slot0_free, 0);
+  if (e != hipSuccess) return swr::hip_fail(e, "swr_planner_prefetch_first: wait free");
+  int64_t remote = 0;
+  int rc;
+  if (p->engine == SWR_ENGINE_DMA)
+    rc = swr_reassemble_into_slot_dma(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[0],
+                                      p->slot_bytes, 0, p->pf, nullptr, p->first_ready, &remote);
+  else
+    rc = swr::reassemble_reserving(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[0],
+                                   p->slot_bytes, 0, p->pf, nullptr, p->first_ready, &remote,
+                                   unsigned(p->gather_lds));
+  if (rc != SWR_OK) return rc;
+  p->log(SWR_OP_WAIT_FREE, SWR_STREAM_PREFETCH, p->last_slot0_reader(), -1);
+  p->log(SWR_OP_COPY_NEXT, SWR_STREAM_PREFETCH, p->start, 0);
+  p->log(SWR_OP_RECORD_READY, SWR_STREAM_PREFETCH, p->start, -1);
+  p->remote_bytes += remote;
+  p->gathers += 1;
+  p->pf_issued += 1;
   swr::clear_error();
   return SWR_OK;
 }

@@ -491,3 +491,96 @@ def test_after_gate_on_gpu(start, n_layers, cyclic, one_queue):
     p.set_timing(0)
     p.set_cyclic(False)
     p.close()
+
+
+@pytest.mark.parametrize("gate,one_queue,engine", [(swr.GATE_DONE, False, swr.ENGINE_KERNEL),
+                                                   (swr.GATE_AFTER, True, swr.ENGINE_KERNEL),
+                                                   (swr.GATE_BEGIN, False, swr.ENGINE_KERNEL),
+                                                   (swr.GATE_DONE, False, swr.ENGINE_DMA)])
+def test_first_layer_prefetch_outside_a_graph(gate, one_queue, engine):
+    """weight_sharding, CUDA graph section: the first layer is gathered on a
+    dedicated stream outside the captured forward, overlapping the previous
+    replay's last layers, and the graph waits for it.  The eager sequence
+    equals the oracle's model (prologue prefetch, then forward + prefetch) and
+    passes its race checker; then one forward is captured and replayed, each
+    replay's prefetch for the next enqueued right behind it while the replay
+    (with its layers delayed) still runs.  Every replay's outputs equal the
+    oracle's; slot 1 and the outputs are clobbered between replays."""
+    note(f"first-layer prefetch stream gate={gate} one_queue={one_queue} engine={engine}")
+    wl = synth.TINY
+    n_layers = 4
+    layers = _layers(wl, n_layers, wl.n_chunks)
+    total = layers[0]["lay"]["total_bytes"]
+    slot_a = torch.empty(total, dtype=torch.uint8, device=DEV)
+    slot_b = torch.empty(total, dtype=torch.uint8, device=DEV)
+    compute = torch.cuda.Stream()
+    side = compute if one_queue else torch.cuda.Stream()
+    pf = torch.cuda.Stream()
+    p = swr.Planner(0, n_layers, compute, side, slot_a, slot_b)
+    for i, L in enumerate(layers):
+        p.set_layer(i, L["chunks"], L["lay"]["chunk_bytes"])
+    p.set_gate(gate)
+    p.set_copy_engine(engine)
+    with pytest.raises(swr.SwrError) as e:
+        p.set_first_prefetch(compute)
+    assert e.value.code == swr.E_INVALID
+    p.set_first_prefetch(pf)
+    with pytest.raises(swr.SwrError) as e:
+        p.set_cyclic(True)
+    assert e.value.code == swr.E_INVALID
+    p.reset()
+    with pytest.raises(swr.SwrError) as e:
+        p.pre_dispatch(0)  # no prefetch yet
+    assert e.value.code == swr.E_SEQUENCE
+    x = synth.activations(synth.seed_for(1, 0, 50), 4, wl.hidden)
+    xd = bf16(x)
+    outs = [torch.full((4, wl.hidden), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in layers]
+    wsb = torch.empty(swr.mlp_workspace_bytes(4, wl.hidden, wl.intermediate, "bf16"), dtype=torch.uint8, device=DEV)
+    refs = [gemm.mlp_f64(x, L["ws"][0].raw(), None, L["ws"][1].raw(), None, "bf16", wl.hidden, wl.intermediate)[2]
+            for L in layers]
+    a = torch.randn(2048, 2048, device=DEV)
+
+    def delay():
+        for _ in range(2):
+            torch.mm(a, a)
+
+    g = GATE_NAMES[gate]
+    # eager: prologue prefetch, then forward + the next forward's prefetch
+    traces = []
+    p.prefetch_first()
+    traces.append(p.trace())
+    with torch.cuda.stream(compute):
+        for _ in range(2):
+            _forward(p, layers, 0, xd, outs, wsb, delay)
+            p.prefetch_first()
+            traces.append(p.trace())
+    torch.cuda.synchronize()
+    want = osch.expected_trace(0, n_layers, gate=g, first_external=True) + osch.prefetch_first_ops(0, n_layers)
+    # (the refused pre_dispatch above came after a reset, which the prologue trace begins with)
+    assert traces[0] == [("record_start", "compute", -1, -1)] + osch.prefetch_first_ops(0, n_layers)
+    assert all(t == want for t in traces[1:])
+    assert osch.check_trace(traces) == []
+    for i in range(n_layers):
+        assert_close_rows(values(outs[i]), refs[i], what=f"eager prefetch layer {i}")
+    # captured: the forward (without its first gather) as a graph; the prefetch outside it
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=compute):
+        _forward(p, layers, 0, xd, outs, wsb, delay)
+    assert p.trace() == osch.expected_trace(0, n_layers, gate=g, first_external=True)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        graph.replay()
+        p.prefetch_first()  # for the next replay, while this one still runs
+        torch.cuda.synchronize()
+        for i in range(n_layers):
+            assert_close_rows(values(outs[i]), refs[i], what=f"replay {rep} layer {i}")
+        slot_b.fill_(0xFF)  # slot 0 now holds the next replay's first layer
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+    _, gathers = p.counters()
+    # prologue prefetch; two eager forwards (n - 1 gathers + a prefetch each); the
+    # gathers enqueued while capturing; one prefetch per replay
+    assert gathers == 1 + 2 * n_layers + (n_layers - 1) + 4
+    p.set_first_prefetch(None)
+    p.close()

@@ -151,3 +151,40 @@ def test_after_gate_mistakes_are_caught():
     no_ready = [op for op in t if op != ("wait_ready", "compute", 3, 1)]
     assert sch.check_trace([no_ready])
 
+
+
+@pytest.mark.parametrize("gate", ["done", "begin", "after"])
+@pytest.mark.parametrize("start,end", [(0, 1), (0, 2), (1, 4), (0, 5), (3, 11)])
+def test_dedicated_first_prefetch_is_race_free(gate, start, end):
+    """The first layer gathered on its own stream outside the forward: a
+    prologue prefetch, then forwards each followed by the prefetch for the next."""
+    fwd = sch.expected_trace(start, end, gate=gate, first_external=True)
+    pf = sch.prefetch_first_ops(start, end)
+    assert sch.check_trace([pf, fwd + pf, fwd + pf, fwd]) == []
+    # the forward itself gathers every layer but its first, into the same slots
+    copies = [op for op in fwd if op[0] == "copy"]
+    assert [(op[2], op[3]) for op in copies] == [(layer, (layer - start) % 2) for layer in range(start + 1, end)]
+    l0 = sch.last_slot0_reader(start, end)
+    assert (l0 - start) % 2 == 0 and l0 + 2 >= end
+    assert fwd[fwd.index(("record_done", "compute", l0, -1)) + 1] == ("record_free", "compute", l0, 0)
+
+
+def test_dedicated_first_prefetch_mistakes_are_caught():
+    fwd = sch.expected_trace(0, 4, first_external=True)
+    pf = sch.prefetch_first_ops(0, 4)
+    # the prefetch without its gate overwrites slot 0 while layer 2 reads it
+    no_wait = [op for op in pf if op[0] != "wait_free"]
+    assert any("race" in p for p in sch.check_trace([pf, fwd + no_wait, fwd]))
+    # a forward that never records the free event gives the prefetch nothing to wait for
+    no_free = [op for op in fwd if op[0] != "record_free"]
+    assert any("race" in p for p in sch.check_trace([pf, no_free + pf, fwd]))
+    # freeing slot 0 after layer 0 instead of its last reader, layer 2
+    early = [("record_free", "compute", 0, 0) if op[0] == "record_free" else op for op in fwd]
+    early.remove(("record_free", "compute", 0, 0))
+    early.insert(early.index(("record_done", "compute", 0, -1)) + 1, ("record_free", "compute", 0, 0))
+    assert any("race" in p for p in sch.check_trace([pf, early + pf, fwd]))
+    # a forward that does not wait for the prefetch reads whatever slot 0 holds
+    no_ready = [op for op in fwd if op != ("wait_ready", "compute", 0, 0)]
+    assert sch.check_trace([pf, no_ready])
+    with pytest.raises(ValueError):
+        sch.expected_trace(0, 4, first_external=True, prefetch_next=True)
