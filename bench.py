@@ -65,6 +65,9 @@ def parse() -> argparse.Namespace:
                     help="only the pipelined steps and isolated kernels (no serial, DMA, tensor-parallel or graph "
                          "sections)")
     ap.add_argument("--isolated-reps", type=int, default=10)
+    ap.add_argument("--isolated-only", action="store_true",
+                    help="decode: only the isolated MLPs at every M and the isolated gathers, then the calibration "
+                         "copy (for hardware-counter runs)")
     ap.add_argument("--timed-only", action="store_true",
                     help="decode: only the warmup and the timed steps (for a kernel trace of the timed region)")
     ap.add_argument("--calibration-copy-mib", type=int, default=256,
@@ -165,6 +168,68 @@ def main() -> int:
                 gemm_events[layer][1].record(compute)
             pl.update_done_event(layer)
 
+    # ---------------------------------------------------------------- isolated kernels
+    # every layer reassembled into its own buffer, then the MLPs alone and the gathers alone
+    def isolated_kernels():
+        full = [torch.empty(T, dtype=torch.uint8, device=dev) for _ in range(L)]
+        for layer in range(L):
+            swr.reassemble_into_slot(chunks[layer], C, full[layer], stream=compute)
+        torch.cuda.synchronize()
+        gemm = {}
+        with torch.cuda.stream(compute):
+            for m in tokens:
+                for _ in range(2):
+                    for layer in range(L):
+                        b = full[layer].data_ptr()
+                        swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
+                                        xs[m], ys[m], wsp[m], stream=compute)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(compute)
+                for _ in range(args.isolated_reps):
+                    for layer in range(L):
+                        b = full[layer].data_ptr()
+                        swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
+                                        xs[m], ys[m], wsp[m], stream=compute)
+                e1.record(compute)
+                torch.cuda.synchronize()
+                gemm[m] = e0.elapsed_time(e1) / (args.isolated_reps * L)  # ms per layer
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(compute):
+            for layer in range(L):
+                swr.reassemble_into_slot(chunks[layer], C, full[(layer + 1) % L], stream=compute)
+            e0.record(compute)
+            for _ in range(args.isolated_reps):
+                for layer in range(L):
+                    swr.reassemble_into_slot(chunks[layer], C, full[(layer + 1) % L], stream=compute)
+            e1.record(compute)
+        torch.cuda.synchronize()
+        return gemm, e0.elapsed_time(e1) / (args.isolated_reps * L)
+
+    def calibration_copy():
+        # a plain device-to-device copy of known size (read + write of the same
+        # byte count), the reference that hardware byte counters are scaled by
+        if args.calibration_copy_mib > 0:
+            src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(2):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+
+    if args.isolated_only:
+        # only the isolated MLPs (every M) and gathers, then the calibration
+        # copy: hardware-counter runs then attribute every GEMM launch to one
+        # isolated call at a known token count
+        iso_gemm, iso_gather_ms = isolated_kernels()
+        calibration_copy()
+        print(json.dumps({"isolated_gemm_ms_per_layer": {str(m): round(iso_gemm[m], 4) for m in tokens},
+                          "isolated_weight_GBps": {str(m): round((w_bytes + s_bytes) / (iso_gemm[m] * 1e-3) / 1e9, 1)
+                                                   for m in tokens},
+                          "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1),
+                          "isolated_reps": args.isolated_reps}), flush=True)
+        planner.close()
+        return 0
+
     # ---------------------------------------------------------------- warmup
     with torch.cuda.stream(compute):
         for _ in range(args.warmup):
@@ -216,43 +281,6 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     mlp_bytes_per_step = len(tokens) * L * (w_bytes + s_bytes)
     value = mlp_bytes_per_step * args.steps / wall / 1e9
-
-    # ---------------------------------------------------------------- isolated kernels
-    # every layer reassembled into its own buffer, then the MLPs alone and the gathers alone
-    def isolated_kernels():
-        full = [torch.empty(T, dtype=torch.uint8, device=dev) for _ in range(L)]
-        for layer in range(L):
-            swr.reassemble_into_slot(chunks[layer], C, full[layer], stream=compute)
-        torch.cuda.synchronize()
-        gemm = {}
-        with torch.cuda.stream(compute):
-            for m in tokens:
-                for _ in range(2):
-                    for layer in range(L):
-                        b = full[layer].data_ptr()
-                        swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
-                                        xs[m], ys[m], wsp[m], stream=compute)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(compute)
-                for _ in range(args.isolated_reps):
-                    for layer in range(L):
-                        b = full[layer].data_ptr()
-                        swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
-                                        xs[m], ys[m], wsp[m], stream=compute)
-                e1.record(compute)
-                torch.cuda.synchronize()
-                gemm[m] = e0.elapsed_time(e1) / (args.isolated_reps * L)  # ms per layer
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(compute):
-            for layer in range(L):
-                swr.reassemble_into_slot(chunks[layer], C, full[(layer + 1) % L], stream=compute)
-            e0.record(compute)
-            for _ in range(args.isolated_reps):
-                for layer in range(L):
-                    swr.reassemble_into_slot(chunks[layer], C, full[(layer + 1) % L], stream=compute)
-            e1.record(compute)
-        torch.cuda.synchronize()
-        return gemm, e0.elapsed_time(e1) / (args.isolated_reps * L)
 
     default_schedule = f"gate_{args.gate}_queues_{args.queues}_lds_{args.gather_lds}"
     iso_gemm, iso_gather_ms = {}, None
@@ -501,8 +529,11 @@ def main() -> int:
     # holds the MLP's launches and nothing else; bytes are the algorithmic
     # bytes of one call.  The gather's kernel is reported beside it.
     dk = per_kernel["mlp_forward"]
+    tr = dk["traffic"]
+    if isinstance(tr, dict):  # per token count -> per launch, averaged over the token counts
+        tr = int(sum(tr[str(m)] for m in tokens) / len(tokens)) if all(str(m) in tr for m in tokens) else None
     roofline = {"bound": dk["bound"], "achieved": round(dk["achieved"], 1), "peak": dk["peak"], "unit": dk["unit"],
-                "frac": round(dk["frac"], 4), "traffic": dk["traffic"], "kernel": "mlp_forward",
+                "frac": round(dk["frac"], 4), "traffic": tr, "kernel": "mlp_forward",
                 "kernels": dk["kernels"], "target_frac": 0.80,
                 "target_met": bool(min(dk["frac_by_tokens"].values()) >= 0.80)}
 
@@ -553,15 +584,7 @@ def main() -> int:
         "all_chunks_on_this_gpu": N * per_rank,
     }
 
-    # a plain device-to-device copy of known size (read + write of the same
-    # byte count), the reference that hardware byte counters are scaled by
-    if args.calibration_copy_mib > 0:
-        src = torch.empty(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy()
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -609,7 +632,7 @@ def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by the counter's reading for a plain
     copy of known size), or None if there is none or the kernel's sources changed
-    since the counters were taken."""
+    since the counters were taken.  For mlp_forward, a dict by token count."""
     import hashlib
 
     path = os.path.join(ROOT, "profiles", "hbm_traffic_shared_expert_decode.json")
@@ -620,7 +643,8 @@ def measured_traffic(kernel: str):
             h.update(open(os.path.join(ROOT, f), "rb").read())
         if h.hexdigest()[:16] != rec["source_sha"]:
             return None
-        return int(rec["bytes_per_launch"])
+        b = rec["bytes_per_launch"]
+        return {k: int(v) for k, v in b.items()} if isinstance(b, dict) else int(b)
     except (OSError, KeyError, ValueError):
         return None
 
