@@ -65,6 +65,9 @@ def parse() -> argparse.Namespace:
                     help="only the pipelined steps and isolated kernels (no serial, DMA, tensor-parallel or graph "
                          "sections)")
     ap.add_argument("--isolated-reps", type=int, default=10)
+    ap.add_argument("--timing-every", type=int, default=4,
+                    help="the planner times the gathers and layers of every k-th timed step (a timing record "
+                         "costs about 2 us between two kernels)")
     ap.add_argument("--isolated-only", action="store_true",
                     help="decode: only the isolated MLPs at every M and the isolated gathers, then the calibration "
                          "copy (for hardware-counter runs)")
@@ -238,45 +241,57 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # ---------------------------------------------------------------- timed
-    fwd_ev = {m: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.steps)] for m in tokens}
+    # each forward bracketed by fence-free events, the kind the planner's own
+    # timing uses (a default event's system-scope release costs a few us)
+    from bench_workloads import FenceFreeEvents
+
+    fwd_ev = FenceFreeEvents(2 * args.steps * len(tokens))
     # The planner times every copy (events on the side stream around it) and
     # every layer's compute (its begin record after the ready wait -- the last
     # packet before the layer's kernels -- to a record after done): no event
     # of the bench sits between a gate and the work it orders.
-    planner.set_timing(args.steps * len(tokens) * L)
+    sampled = [s for s in range(args.steps) if s % max(1, args.timing_every) == 0]
+    planner.set_timing(len(sampled) * len(tokens) * L)
     remote_before, gathers_before = planner.counters()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     with torch.cuda.stream(compute):
         for s in range(args.steps):
-            for m in tokens:
-                fwd_ev[m][s][0].record(compute)
+            # in cyclic mode the gather of the next forward's first layer is
+            # dispatched during this forward: the sample is the gathers issued
+            # in the sampled steps, L per forward as well
+            planner.pause_timing(s not in sampled)
+            for j, m in enumerate(tokens):
+                k = 2 * (s * len(tokens) + j)
+                fwd_ev.record(k, compute)
                 forward(m)
-                fwd_ev[m][s][1].record(compute)
+                fwd_ev.record(k + 1, compute)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     remote_after, gathers_after = planner.counters()
     gathers = planner.gather_times()
     layer_spans = planner.layer_times()
     planner.set_timing(0)
-    assert len(gathers) == args.steps * len(tokens) * L and len(layer_spans) == len(gathers)
+    planner.pause_timing(False)
+    assert len(gathers) == len(sampled) * len(tokens) * L and len(layer_spans) == len(gathers)
     # (in cyclic mode the first timed forward's first layer was gathered during warmup, and
     # the last timed forward gathers one layer for a forward that does not run; the count is
     # the same)
     gather_ms = {m: [] for m in tokens}
     k = 0
-    for s in range(args.steps):
+    for s in sampled:
         for m in tokens:
             gather_ms[m].extend(gathers[k:k + L])
             k += L
     gemm_ms = {m: [] for m in tokens}
     k = 0
-    for s in range(args.steps):
+    for s in sampled:
         for m in tokens:
             gemm_ms[m].extend(layer_spans[k:k + L])
             k += L
-    fwd_ms = {m: [fwd_ev[m][s][0].elapsed_time(fwd_ev[m][s][1]) for s in range(args.steps)] for m in tokens}
+    fwd_ms = {m: [fwd_ev.elapsed_ms(2 * (s * len(tokens) + j), 2 * (s * len(tokens) + j) + 1)
+                  for s in range(args.steps)] for j, m in enumerate(tokens)}
+    fwd_ev.close()
 
     ms_per_step = wall * 1e3 / args.steps
     mlp_bytes_per_step = len(tokens) * L * (w_bytes + s_bytes)
@@ -293,47 +308,18 @@ def main() -> int:
     # share, graph replay) are reports beside the headline; --minimal skips
     # them, e.g. for hardware-counter runs that average over every MLP call.
     serial_ms, serial_bare_ms, dma, graph, tpres, schedules, R, rank_bytes = {}, {}, {}, {}, {}, {}, 4, 0
+    pipelined_bare_ms, bare_trials, serial_timed_ms = {}, {}, {}
     if not args.minimal:
         # ---------------------------------------------------------------- serial reference
         # the same gathers and MLPs back to back on one stream, without the
-        # planner: once bare, and once with timing events at the four places the
-        # planner's timing puts them in the timed steps (around each gather and
-        # each MLP; the same fence-free events), so that the timed steps compare
-        # with a reference that carries the same instrumentation
+        # planner, at three levels of instrumentation: "timed" (fence-free
+        # events around each gather, each MLP and the forward, as in the timed
+        # steps the planner times), "bracketed" (the forward's two events only,
+        # as in the other timed steps) and bare (no events, timed in trials
+        # that alternate with the default schedule's bare forwards, median of
+        # each, so that both see the same clocks and temperature).
         from bench_workloads import FenceFreeEvents
 
-        ev_pool = FenceFreeEvents(4 * L)
-        with torch.cuda.stream(compute):
-            for m in tokens:
-                def serial_forward(instrumented):
-                    for layer in range(L):
-                        s_ = slot_a if layer % 2 == 0 else slot_b
-                        if instrumented:
-                            ev_pool.record(4 * layer, compute)
-                        swr.reassemble_into_slot(chunks[layer], C, s_, stream=compute)
-                        if instrumented:
-                            ev_pool.record(4 * layer + 1, compute)
-                            ev_pool.record(4 * layer + 2, compute)
-                        b = s_.data_ptr()
-                        swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
-                                        xs[m], ys[m], wsp[m], stream=compute)
-                        if instrumented:
-                            ev_pool.record(4 * layer + 3, compute)
-                for instrumented in (False, True):
-                    serial_forward(instrumented)
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(compute)
-                    for _ in range(args.isolated_reps):
-                        serial_forward(instrumented)
-                    e1.record(compute)
-                    torch.cuda.synchronize()
-                    (serial_ms if instrumented else serial_bare_ms)[m] = e0.elapsed_time(e1) / args.isolated_reps
-        ev_pool.close()
-
-        # ---------------------------------------------------------------- schedules
-        # The same forwards under every gate, on two streams and on one queue,
-        # without timing events (ms per 8-layer forward).  On one GPU the
-        # gather (2|T| bytes) and the MLP (|T| bytes) draw on one HBM.
         fwd_reps = max(4, args.steps // 2)
 
         def time_forwards(pl, m, reps=fwd_reps):
@@ -347,6 +333,54 @@ def main() -> int:
             torch.cuda.synchronize()
             return e0.elapsed_time(e1) / reps
 
+        ev_pool = FenceFreeEvents(4 * L + 2)
+
+        def serial_forward(m, level):
+            # level 0: bare, 1: the forward bracketed, 2: every gather and MLP timed too
+            if level:
+                ev_pool.record(4 * L, compute)
+            for layer in range(L):
+                s_ = slot_a if layer % 2 == 0 else slot_b
+                if level > 1:
+                    ev_pool.record(4 * layer, compute)
+                swr.reassemble_into_slot(chunks[layer], C, s_, stream=compute)
+                if level > 1:
+                    ev_pool.record(4 * layer + 1, compute)
+                    ev_pool.record(4 * layer + 2, compute)
+                b = s_.data_ptr()
+                swr.mlp_forward(b + o_gu, scales[layer][0], b + o_d, scales[layer][1], "fp8_e4m3fn", H, I,
+                                xs[m], ys[m], wsp[m], stream=compute)
+                if level > 1:
+                    ev_pool.record(4 * layer + 3, compute)
+            if level:
+                ev_pool.record(4 * L + 1, compute)
+
+        def time_serial(m, level, reps=fwd_reps):
+            with torch.cuda.stream(compute):
+                serial_forward(m, level)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(compute)
+                for _ in range(reps):
+                    serial_forward(m, level)
+                e1.record(compute)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        for m in tokens:
+            serial_timed_ms[m] = time_serial(m, 2)
+            serial_ms[m] = time_serial(m, 1)
+            ts, tp = [], []
+            for _ in range(3):
+                ts.append(time_serial(m, 0))
+                tp.append(time_forwards(planner, m))
+            serial_bare_ms[m], pipelined_bare_ms[m] = float(np.median(ts)), float(np.median(tp))
+            bare_trials[m] = {"serial": [round(t, 4) for t in ts], "pipelined": [round(t, 4) for t in tp]}
+        ev_pool.close()
+
+        # ---------------------------------------------------------------- schedules
+        # The same forwards under every gate, on two streams and on one queue,
+        # without timing events (ms per 8-layer forward).  On one GPU the
+        # gather (2|T| bytes) and the MLP (|T| bytes) draw on one HBM.
         combos = [("done", 2, 0), ("begin", 2, 0), ("after", 2, 0), ("done", 2, YIELD_LDS), ("begin", 2, YIELD_LDS),
                   ("done", 1, 0), ("after", 1, 0)]
         if (args.gate, args.queues, args.gather_lds) not in combos:
@@ -539,7 +573,12 @@ def main() -> int:
 
     per_m = {}
     for m in tokens:
-        fwd = float(np.median(fwd_ms[m]))
+        # forwards without the planner's timing records (the forward's own two
+        # events only), and the sampled ones that carry them; means, like the
+        # serial references'
+        plain = [t for s, t in enumerate(fwd_ms[m]) if s not in sampled]
+        fwd = float(np.mean(plain if plain else fwd_ms[m]))
+        fwd_timed = float(np.mean([fwd_ms[m][s] for s in sampled]))
         g_layer = float(np.mean(gather_ms[m]))
         per_m[str(m)] = {
             "pipelined_ms_per_forward": round(fwd, 4),
@@ -560,8 +599,11 @@ def main() -> int:
                 "isolated_tokens_per_s": round(m / (L * iso_gemm[m] * 1e-3), 1),
                 "isolated_gather_to_compute_ratio": round(iso_gather_ms / iso_gemm[m], 3)}),
             "serial_reference_ms_per_forward": round(serial_ms[m], 4) if m in serial_ms else None,
+            "pipelined_timed_ms_per_forward": round(fwd_timed, 4),
+            "serial_reference_timed_ms_per_forward": round(serial_timed_ms[m], 4) if m in serial_timed_ms else None,
             "serial_reference_bare_ms_per_forward": round(serial_bare_ms[m], 4) if m in serial_bare_ms else None,
-            "pipelined_bare_ms_per_forward": schedules.get(default_schedule, {}).get(str(m)),
+            "pipelined_bare_ms_per_forward": round(pipelined_bare_ms[m], 4) if m in pipelined_bare_ms else None,
+            "bare_trials_ms_per_forward": bare_trials.get(m),
         }
 
     # ---------------------------------------------------------------- accounts

@@ -67,6 +67,13 @@ class FenceFreeEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
 
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = self._ct.c_float()
+        rc = self._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
     def close(self) -> None:
         for e in self.ev:
             self._hip.hipEventDestroy(e)
@@ -131,44 +138,54 @@ class _Pipeline:
             layer_fn(layer, base)
             p.update_done_event(layer)
 
-    def serial_forward(self, layer_fn, events=None):
+    def serial_forward(self, layer_fn, events=None, inner=True):
+        inner = events is not None and inner
+        if events is not None:
+            events.record(4 * self.L, self.compute)
         for layer in range(self.L):
             s = self.slot_a if layer % 2 == 0 else self.slot_b
-            if events is not None:
+            if inner:
                 events.record(4 * layer, self.compute)
             self.swr.reassemble_into_slot(self.chunks[layer], self.C, s, stream=self.compute)
-            if events is not None:
+            if inner:
                 events.record(4 * layer + 1, self.compute)
                 events.record(4 * layer + 2, self.compute)
             layer_fn(layer, s.data_ptr())
-            if events is not None:
+            if inner:
                 events.record(4 * layer + 3, self.compute)
+        if events is not None:
+            events.record(4 * self.L + 1, self.compute)
 
-    def timed(self, layer_fn, steps, warmup):
+    def timed(self, layer_fn, steps, warmup, every=1):
         """Pipelined forwards: (wall s, per-forward ms, per-layer compute ms, gather ms).
         The planner's own fence-free timing events time each gather on the
         stream it runs on and each layer's compute from its begin (after the
-        ready wait) to its done record."""
+        ready wait) to its done record, in every `every`-th step (the
+        forwards of the other steps carry only their own two events)."""
         torch = self.torch
         with torch.cuda.stream(self.compute):
             for _ in range(warmup):
                 self.forward(layer_fn)
         torch.cuda.synchronize()
-        fwd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        self.planner.set_timing(steps * self.L)
+        fwd = FenceFreeEvents(2 * steps)
+        self.sampled = [s for s in range(steps) if s % max(1, every) == 0]
+        self.planner.set_timing(len(self.sampled) * self.L)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(self.compute):
             for s in range(steps):
-                fwd[s][0].record(self.compute)
+                self.planner.pause_timing(s not in self.sampled)
+                fwd.record(2 * s, self.compute)
                 self.forward(layer_fn)
-                fwd[s][1].record(self.compute)
+                fwd.record(2 * s + 1, self.compute)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         gathers = self.planner.gather_times()
         layer_ms = self.planner.layer_times()
+        self.planner.pause_timing(False)
         self.planner.set_timing(0)
-        fwd_ms = [a.elapsed_time(b) for a, b in fwd]
+        fwd_ms = [fwd.elapsed_ms(2 * s, 2 * s + 1) for s in range(steps)]
+        fwd.close()
         return wall, fwd_ms, layer_ms, gathers
 
     def timed_bare(self, layer_fn, reps, planner=None):
@@ -194,23 +211,36 @@ class _Pipeline:
             p.close()
         return out
 
-    def timed_serial(self, layer_fn, reps, instrumented=False):
-        """The same gathers and layers back to back on the compute stream; with
-        `instrumented`, fence-free timing events at the four places the
-        planner's timing puts them (around each gather and each layer)."""
+    def timed_serial(self, layer_fn, reps, level=0):
+        """The same gathers and layers back to back on the compute stream;
+        level 1: the forward bracketed by two fence-free events, as the timed
+        steps' forwards are; level 2: also around each gather and each layer,
+        as in the steps the planner times."""
         torch = self.torch
-        ev = FenceFreeEvents(4 * self.L) if instrumented else None
+        ev = FenceFreeEvents(4 * self.L + 2) if level else None
         with torch.cuda.stream(self.compute):
-            self.serial_forward(layer_fn, ev)
+            self.serial_forward(layer_fn, ev, level > 1)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(self.compute)
             for _ in range(reps):
-                self.serial_forward(layer_fn, ev)
+                self.serial_forward(layer_fn, ev, level > 1)
             e1.record(self.compute)
         torch.cuda.synchronize()
         if ev is not None:
             ev.close()
         return e0.elapsed_time(e1) / reps
+
+    def bare_trials(self, layer_fn, reps, trials=3):
+        """Serial and default-schedule forwards without timing events, timed in
+        alternating trials: (median serial ms, median pipelined ms, trials)."""
+        import numpy as np
+
+        ts, tp = [], []
+        for _ in range(trials):
+            ts.append(self.timed_serial(layer_fn, reps))
+            tp.append(self.timed_bare(layer_fn, reps))
+        return float(np.median(ts)), float(np.median(tp)), {"serial": [round(t, 4) for t in ts],
+                                                           "pipelined": [round(t, 4) for t in tp]}
 
     def isolated_gather_ms(self, reps):
         torch = self.torch
@@ -285,7 +315,8 @@ def run_projections(args, swr, torch, np, synth, dev):
     def layer_fn(layer, base):
         swr.proj_forward_grouped(projs(layer, base), m, workspace=wsp, stream=pipe.compute)
 
-    wall, fwd_ms, layer_ms, gathers = pipe.timed(layer_fn, args.steps, args.warmup)
+    wall, fwd_ms, layer_ms, gathers = pipe.timed(layer_fn, args.steps, args.warmup, every=args.timing_every)
+    sampled = pipe.sampled
     full = [torch.empty(T, dtype=torch.uint8, device=dev) for _ in range(L)]
     for layer in range(L):
         swr.reassemble_into_slot(chunks[layer], lay["chunk_bytes"], full[layer], stream=pipe.compute)
@@ -294,8 +325,9 @@ def run_projections(args, swr, torch, np, synth, dev):
                     args.isolated_reps)
     del full
     iso_gather = pipe.isolated_gather_ms(args.isolated_reps)
-    serial = pipe.timed_serial(layer_fn, args.isolated_reps, instrumented=True)
-    serial_bare = pipe.timed_serial(layer_fn, args.isolated_reps)
+    serial_timed = pipe.timed_serial(layer_fn, args.isolated_reps, level=2)
+    serial = pipe.timed_serial(layer_fn, args.isolated_reps, level=1)
+    serial_bare, pipelined_bare, trials = pipe.bare_trials(layer_fn, max(4, args.steps // 2))
     schedules = pipe.schedules(layer_fn, max(4, args.steps // 2))
     pipe.close()
 
@@ -303,7 +335,11 @@ def run_projections(args, swr, torch, np, synth, dev):
     layer_avg = float(np.mean(layer_ms))
     gather_avg = float(np.mean(gathers))
     value = L * args.steps * (w_bytes + s_bytes) / wall / 1e9
-    fwd = float(np.median(fwd_ms))
+    # forwards without the planner's timing records, and the sampled ones
+    # that carry them; means, like the serial references'
+    plain = [t for s, t in enumerate(fwd_ms) if s not in sampled]
+    fwd = float(np.mean(plain if plain else fwd_ms))
+    fwd_timed = float(np.mean([fwd_ms[s] for s in sampled]))
     kernels = {
         "projection_layer": {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS, "bytes_per_launch": alg,
                              "avg_ms": layer_avg, "achieved": alg / (layer_avg * 1e-3) / 1e9},
@@ -345,8 +381,11 @@ def run_projections(args, swr, torch, np, synth, dev):
         "isolated_weight_frac": round((w_bytes + s_bytes) / (iso * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "isolated_reassembly_GBps": round(2 * T / (iso_gather * 1e-3) / 1e9, 1),
         "serial_reference_ms_per_forward": round(serial, 4),
+        "pipelined_timed_ms_per_forward": round(fwd_timed, 4),
+        "serial_reference_timed_ms_per_forward": round(serial_timed, 4),
         "serial_reference_bare_ms_per_forward": round(serial_bare, 4),
-        "pipelined_bare_ms_per_forward": schedules.get(f"gate_{args.gate}_queues_{args.queues}"),
+        "pipelined_bare_ms_per_forward": round(pipelined_bare, 4),
+        "bare_trials_ms_per_forward": trials,
         "schedules_ms_per_forward": schedules,
         "compute_stall_ms": round(fwd - L * layer_avg, 4),
         "gather_to_compute_ratio": round(gather_avg / layer_avg, 3),

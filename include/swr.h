@@ -584,6 +584,11 @@ int swr_planner_prefetch_first(swr_planner* p);
  * first, at most `cap` of them, and sets *n to the number written; every one
  * of those copies must have finished (else SWR_E_HIP). */
 int swr_planner_set_timing(swr_planner* p, int32_t capacity);
+/* With paused != 0, later dispatches and layers record no timing events (a
+ * layer that already recorded its begin still records its end), so that a
+ * caller can time a sample of its forwards; the rings keep their contents.
+ * 0 resumes.  Has no effect while timing is off.  Errors: SWR_E_INVALID. */
+int swr_planner_pause_timing(swr_planner* p, int32_t paused);
 int swr_planner_gather_times(const swr_planner* p, float* ms, int32_t cap, int32_t* n);
 
 /* The compute span of each timed layer, oldest first: from the begin record

@@ -45,6 +45,7 @@ EXPORTS = (
     "swr_planner_create", "swr_planner_set_layer", "swr_planner_reset", "swr_planner_pre_dispatch",
     "swr_planner_maybe_dispatch", "swr_planner_wait_ready_once", "swr_planner_update_done_event",
     "swr_planner_counters", "swr_planner_trace", "swr_planner_destroy", "swr_planner_set_timing",
+    "swr_planner_pause_timing",
     "swr_planner_gather_times", "swr_planner_layer_times", "swr_planner_set_cyclic", "swr_planner_set_first_prefetch",
     "swr_planner_prefetch_first", "swr_last_error", "swr_version",
 )
@@ -137,6 +138,7 @@ def lib() -> ctypes.CDLL:
         "swr_planner_trace": (_i32, [_vp, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
         "swr_planner_destroy": (None, [_vp]),
         "swr_planner_set_timing": (_i32, [_vp, _i32]),
+        "swr_planner_pause_timing": (_i32, [_vp, _i32]),
         "swr_planner_set_cyclic": (_i32, [_vp, _i32]),
         "swr_planner_set_first_prefetch": (_i32, [_vp, _vp]),
         "swr_planner_prefetch_first": (_i32, [_vp]),
@@ -492,6 +494,10 @@ class Planner:
     def set_timing(self, capacity: int) -> None:
         """Time the copies of the next dispatches in a ring of `capacity` event pairs (0: off)."""
         _check("swr_planner_set_timing", lib().swr_planner_set_timing(self._h, int(capacity)))
+
+    def pause_timing(self, paused: bool) -> None:
+        """Records no timing events while paused (the rings keep their contents)."""
+        _check("swr_planner_pause_timing", lib().swr_planner_pause_timing(self._h, int(bool(paused))))
 
     def gather_times(self, cap: int = 1 << 16) -> list[float]:
         """Copy durations (ms) of the timed dispatches still in the ring, oldest first."""

@@ -58,6 +58,9 @@ struct swr_planner {
   // kernels), c1 after its done record
   std::vector<hipEvent_t> c0, c1;
   int64_t timed_layers = 0;
+  // while set, dispatches and layers record no timing events (the rings keep
+  // what they hold)
+  bool timing_paused = false;
   std::vector<int64_t> layer_slot;  // ring slot of each layer's c0 in this forward
 
   // gather engine: 0 the copy kernel, 1 the DMA engines
@@ -196,7 +199,7 @@ int dispatch(swr_planner* p, int32_t layer, bool for_next = false, int32_t begin
   // record is enqueued
   hipEvent_t wait_on = p->one_queue() ? nullptr : gate;
   hipEvent_t ready = p->one_queue() ? nullptr : p->ready[i];
-  if (p->t0.empty()) {
+  if (p->t0.empty() || p->timing_paused) {
     rc = gather(L.chunks.data(), int32_t(L.chunks.size()), L.chunk_bytes, p->slot[s], p->slot_bytes, 0, p->side,
                 wait_on, ready, &remote);
   } else {
@@ -415,7 +418,7 @@ extern "C" int swr_planner_wait_ready_once(swr_planner* p, int32_t layer, void**
       const hipError_t eb = hipEventRecord(p->begin[i], p->compute);
       if (eb != hipSuccess) return swr::hip_fail(eb, "swr_planner_wait_ready_once: record begin");
     }
-    if (!p->c0.empty()) {
+    if (!p->c0.empty() && !p->timing_paused) {
       const int64_t r = p->timed_layers % int64_t(p->c0.size());
       p->layer_slot[i] = r;
       const hipError_t eb = hipEventRecord(p->c0[size_t(r)], p->compute);
@@ -605,6 +608,13 @@ extern "C" int swr_planner_set_timing(swr_planner* p, int32_t capacity) {
     }
     return swr::hip_fail(e, "swr_planner_set_timing: hipEventCreate");
   }
+  swr::clear_error();
+  return SWR_OK;
+}
+
+extern "C" int swr_planner_pause_timing(swr_planner* p, int32_t paused) {
+  if (!p) return fail(SWR_E_INVALID, "swr_planner_pause_timing: null pointer");
+  p->timing_paused = paused != 0;
   swr::clear_error();
   return SWR_OK;
 }

@@ -276,6 +276,7 @@ def test_planner_errors_without_gpu_work():
     assert L.swr_planner_reset(None) == swr.E_INVALID
     assert L.swr_planner_set_copy_engine(None, 0) == swr.E_INVALID
     assert L.swr_planner_set_gather_lds(None, 0) == swr.E_INVALID
+    assert L.swr_planner_pause_timing(None, 1) == swr.E_INVALID
 
 
 def test_fp8act_entry_points_validate_without_gpu_work():
