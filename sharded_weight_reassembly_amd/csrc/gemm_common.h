@@ -100,6 +100,13 @@ __device__ inline void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+template <int N>
+__device__ inline void wait_vm_lds() {
+  // s_waitcnt with vmcnt = N, lgkmcnt = 0 (every LDS access of the wave done)
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
+}
+
 
 __device__ inline float silu(float z) { return z / (1.0f + __expf(-z)); }
 

@@ -132,9 +132,14 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
 //     K = 32*s + 16*g + 8*h .. +7 in the MFMA pair h = 0, 1, for both
 //     operands: one 16-byte fragment read of 16 FP8 codes feeds both MFMAs
 //     of the pair (the sum over K does not depend on the order);
-//   * per step: wait until this wave's loads of step t have landed (loads
-//     complete in issue order), barrier, issue the loads of step t + 2 into
-//     the stage that step t - 1 read, multiply step t.
+//   * per step t, software-pipelined by 32-K slice: read slice 1 of step t
+//     while the MFMAs of slice 0 run; wait until this wave's reads of stage t
+//     and its loads of step t + 1 are done (loads complete in issue order);
+//     barrier; issue the loads of step t + 3 into stage t; read slice 0 of
+//     step t + 1 while the MFMAs of slice 1 run.  The MFMAs after the barrier
+//     use fragments already in registers, so no wave waits on LDS there
+//     (measured on MI355X: 1-6% faster per GEMM than reading a step's
+//     fragments after its barrier).
 constexpr int kStages = 3;
 
 __device__ inline int wswz(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
@@ -204,64 +209,87 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
 #pragma unroll
     for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
 
-  // one step of stage (A, B): two 32-K halves, each an MFMA pair
-  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+  // The fragments of one 32-K slice s of a stage: the raw FP8 codes of the
+  // wave's TN weight tiles and its TM activation tiles for both MFMA halves.
+  struct Slice {
+    u32x4 w[TN];
+    bf16x8 a[2][TM];
+  };
+  auto read_slice = [&](const uint8_t* A, const uint8_t* B, int s, Slice& f) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 wraw[TN];
+    for (int y = 0; y < TN; ++y)
+      f.w[y] = *reinterpret_cast<const u32x4*>(B + wswz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
 #pragma unroll
-      for (int y = 0; y < TN; ++y) {
-        const int row = wn * WN + y * 32 + r32;
-        wraw[y] = *reinterpret_cast<const u32x4*>(B + wswz(row, 2 * s + kg) * 16);
-      }
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        bf16x8 fa[TM], fb[TN];
+      for (int x = 0; x < TM; ++x)
+        f.a[h][x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
+  };
+  auto mfma_slice = [&](const Slice& f) {
 #pragma unroll
-        for (int x = 0; x < TM; ++x)
-          fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
+    for (int h = 0; h < 2; ++h) {
+      bf16x8 fb[TN];
 #pragma unroll
-        for (int y = 0; y < TN; ++y) fb[y] = fp8x8_to_bf16(wraw[y][2 * h], wraw[y][2 * h + 1]);
+      for (int y = 0; y < TN; ++y) fb[y] = fp8x8_to_bf16(f.w[y][2 * h], f.w[y][2 * h + 1]);
 #pragma unroll
-        for (int x = 0; x < TM; ++x)
+      for (int x = 0; x < TM; ++x)
 #pragma unroll
-          for (int y = 0; y < TN; ++y)
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-      }
+        for (int y = 0; y < TN; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[h][x], fb[y], acc[x][y], 0, 0, 0);
     }
   };
 
   constexpr int kLoads = NA + NB;  // loads per wave per step
   const int nk = int(a.K / kTileK);
-  // prologue: steps 0 and 1 in flight
+  // Prologue: steps 0 and 1 in flight, step 0 landed in every wave, step 2
+  // issued, and slice 0 of step 0 read into registers.
   issue(a0, b0, 0);
   if (nk > 1) issue(a1, b1, 1);
+  if (nk > 1)
+    wait_vm<kLoads>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  if (nk > 2) issue(a2, b2, 2);
+  Slice f0, f1;
+  read_slice(a0, b0, 0, f0);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Step t uses stage t % 3; the loop is unrolled by the ring so every stage
-  // is a fixed array.  A step opens with the wait for its own loads (those
-  // of step t + 1 may stay in flight) and a barrier, which also frees the
-  // stage that step t - 1 read for the loads of step t + 2.
-  auto step = [&](const uint8_t* A, const uint8_t* B, uint8_t* An, uint8_t* Bn, int kt) {
-    if (kt + 1 < nk)
-      wait_vm<kLoads>();
+  // Iteration t (stage t % 3 in A, B; the next stage in An, Bn): slice 1's
+  // fragments are read while slice 0's MFMAs run; then, once this wave's
+  // reads of stage t and its loads of step t + 1 are done, one barrier: every
+  // wave is past stage t (the loads of step t + 3 may overwrite it) and step
+  // t + 1 has landed everywhere, so slice 0 of step t + 1 is read while slice
+  // 1's MFMAs run.  No wave waits on LDS right after the barrier.  Steps past
+  // the end are read (into registers never used) but not loaded.
+  auto iter = [&](uint8_t* A, uint8_t* B, const uint8_t* An, const uint8_t* Bn, int kt) {
+    read_slice(A, B, 1, f1);
+    mfma_slice(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of step t + 1 (those of t + 2 may stay in flight) and its reads of stage t
+    if (kt + 2 < nk)
+      wait_vm_lds<kLoads>();
     else
-      wait_vm<0>();
+      wait_vm_lds<0>();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 2 < nk) issue(An, Bn, kt + 2);
+    if (kt + 3 < nk) issue(A, B, kt + 3);
     __builtin_amdgcn_sched_barrier(0);
-    compute(A, B);
+    read_slice(An, Bn, 0, f0);
+    mfma_slice(f1);
     __builtin_amdgcn_sched_barrier(0);
   };
   // whole ring cycles without branches around the MFMAs, then the tail
   int kt = 0;
   for (; kt + kStages <= nk; kt += kStages) {
-    step(a0, b0, a2, b2, kt);
-    step(a1, b1, a0, b0, kt + 1);
-    step(a2, b2, a1, b1, kt + 2);
+    iter(a0, b0, a1, b1, kt);
+    iter(a1, b1, a2, b2, kt + 1);
+    iter(a2, b2, a0, b0, kt + 2);
   }
-  if (kt < nk) step(a0, b0, a2, b2, kt);
-  if (kt + 1 < nk) step(a1, b1, a0, b0, kt + 1);
+  if (kt < nk) iter(a0, b0, a1, b1, kt);
+  if (kt + 1 < nk) iter(a1, b1, a2, b2, kt + 1);
+  wait_vm<0>();
   tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
 }
 

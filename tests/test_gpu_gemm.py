@@ -215,6 +215,9 @@ def test_many_row_blocks_at_few_tokens(o, k, m):
     (300, 64, synth.BF16, 260),      # a single K tile: two BF16 steps, no full ring cycle
     (640, 192, synth.BF16, 300),     # six BF16 steps: one ring cycle and a tail of two
     (200, 64, synth.FP8, 270),       # a single FP8 step
+    (320, 128, synth.FP8, 270),      # two FP8 steps: no full ring cycle
+    (4096, 256, synth.FP8, 600),     # four FP8 steps with 256-row tiles: one ring cycle and a tail of one
+    (2000, 320, synth.FP8, 513),     # five FP8 steps: one ring cycle and a tail of two
 ])
 def test_tiled_prefill_parity(o, k, dt, m):
     note(f"tiled proj o={o} k={k} {dt} m={m}")
