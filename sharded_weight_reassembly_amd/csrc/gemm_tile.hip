@@ -18,6 +18,9 @@
 //     (exact) after the fragment read;
 //   * BF16 weights (tile_gemm_bf16_kernel): steps of 32 K, a four-stage ring
 //     three steps ahead, rows of 64 B for both operands;
+//   * FP8 weights and FP8 activations (tile_gemm_f8f8d_kernel): double steps
+//     of 128 K, rows of 128 B for both operands (whole cache lines per load),
+//     two or three double stages;
 //   * tiles are numbered so that each XCD (workgroups are dealt round-robin
 //     to the 8 XCDs) works through a compact group of 4 token blocks x all
 //     weight blocks, which keeps the X and W tiles of concurrently running
@@ -454,6 +457,149 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
   tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
 }
 
+// ---------------------------------------------------------------------------
+// FP8 weights and FP8 activations in 128-K double steps.  Rows of both
+// operands are 128 bytes per double step, so each buffer-to-LDS load fills 8
+// whole 128-byte lines (1 KB) instead of 16 half lines: half the requests of
+// 64-K steps per byte.  (Measured on MI355X: the 64-K kernel is bound by
+// these loads -- with them removed it runs twice as fast, while removing its
+// MFMAs or its fragment reads changes nothing -- and the double steps take
+// the FP8-activation MLP from 1.39 to 1.08 ms at 4096 tokens and from 5.50
+// to 4.08 ms at 16384.)  NST double stages in LDS (2 for 256-row tiles, 3 for
+// 128-row ones), loads NST - 1 double steps ahead; the layout is the 128-byte
+// row swizzle swz() of the FP8-weight kernel's X.  Within a double step, MFMA
+// slice s (0, 1) takes K = 64s .. 64s + 63: lane group g reads pieces
+// 4s + 2g and 4s + 2g + 1 of its row in both operands.
+template <int BN, int WAVES, int NST>
+__device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
+  constexpr int WGN = WAVES / 2;
+  constexpr int WN = BN / WGN;
+  constexpr int TM = 4;
+  constexpr int TN = WN / 32;
+  constexpr int DK = 128;                     // K per double step (one byte per element)
+  constexpr int A_BYTES = kTileM * DK;         // 32 KB
+  constexpr int B_BYTES = BN * DK;
+  constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per double step
+  constexpr int NB = B_BYTES / 1024 / WAVES;
+  static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
+                "stage must split into whole 1 KB loads per wave");
+  static_assert(NST == 2 || NST == 3, "two or three double stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[NST > 2 ? A_BYTES : 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[NST > 2 ? B_BYTES : 1024];
+  __shared__ __attribute__((aligned(4096))) float row_scale[BN];
+  __shared__ float tok_scale[kTileM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const TileCoord tc = tile_coord<BN>(a, tile, ntiles);
+  const int64_t m0 = tc.m0;
+  for (int c = tid; c < BN; c += 64 * WAVES) {
+    const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
+    row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
+  }
+  for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
+
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K);
+  // a load fills rows 8i .. 8i + 7 of the stage: lane l writes slot l % 8 of
+  // row l / 8, which holds piece (l % 8) ^ ((row >> 1) & 7) of that row
+  int aoff[NA], boff[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = (wave * NA + i) * 8 + lane / 8;
+    const int q = (lane % 8) ^ ((row >> 1) & 7);
+    const int64_t m = min(m0 + row, a.M - 1);
+    aoff[i] = int(m * a.ldx + q * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = (wave * NB + i) * 8 + lane / 8;
+    const int q = (lane % 8) ^ ((row >> 1) & 7);
+    const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
+    boff[i] = int(r * a.K + q * 16);
+  }
+  auto issue = [&](uint8_t* A, uint8_t* B, int kd) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kd * DK);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_load16<true>(wres, B + (wave * NB + i) * 1024, boff[i], kd * DK);
+  };
+
+  const int r32 = lane & 31, kg = lane >> 5;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int x = 0; x < TM; ++x)
+#pragma unroll
+    for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
+
+  auto frag = [&](const uint8_t* base, int row, int s) {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, 4 * s + 2 * kg) * 16);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, 4 * s + 2 * kg + 1) * 16);
+    return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+  };
+  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      i32x8 fa[TM], fb[TN];
+#pragma unroll
+      for (int x = 0; x < TM; ++x) fa[x] = frag(A, wm * 128 + x * 32 + r32, s);
+#pragma unroll
+      for (int y = 0; y < TN; ++y) fb[y] = frag(B, wn * WN + y * 32 + r32, s);
+#pragma unroll
+      for (int x = 0; x < TM; ++x)
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+          acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[x], fb[y], acc[x][y], 0, 0, 0, 0, 0, 0);
+    }
+  };
+
+  constexpr int kLoads = NA + NB;  // loads per wave per double step
+  const int nd = int(a.K / DK);
+  // prologue: double steps 0 .. NST - 2 in flight
+  issue(a0, b0, 0);
+  if (NST > 2 && nd > 1) issue(a1, b1, 1);
+  // Double step d uses stage d % NST.  It opens with the wait for this
+  // wave's loads of step d (those of d + 1 may stay in flight with three
+  // stages) and a barrier, which also frees the stage that step d - 1 read
+  // for the loads of step d + NST - 1.
+  auto step = [&](const uint8_t* A, const uint8_t* B, uint8_t* An, uint8_t* Bn, int kd) {
+    if (NST > 2 && kd + 1 < nd)
+      wait_vm<kLoads>();
+    else
+      wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kd + NST - 1 < nd) issue(An, Bn, kd + NST - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(A, B);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kd = 0;
+  if constexpr (NST == 2) {
+    for (; kd + 2 <= nd; kd += 2) {
+      step(a0, b0, a1, b1, kd);
+      step(a1, b1, a0, b0, kd + 1);
+    }
+    if (kd < nd) step(a0, b0, a1, b1, kd);
+  } else {
+    for (; kd + 3 <= nd; kd += 3) {
+      step(a0, b0, a2, b2, kd);
+      step(a1, b1, a0, b0, kd + 1);
+      step(a2, b2, a1, b1, kd + 2);
+    }
+    if (kd < nd) step(a0, b0, a2, b2, kd);
+    if (kd + 1 < nd) step(a1, b1, a0, b0, kd + 1);
+  }
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, tok_scale);
+}
+
+template <int BN, int WAVES, int NST>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8d_kernel(StreamArgs a) {
+  f8f8_tile_body<BN, WAVES, NST>(a, blockIdx.x, gridDim.x);
+}
+
 template <int BN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs a) {
   fp8_tile_body<BN, WAVES>(a, blockIdx.x, gridDim.x);
@@ -464,7 +610,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArg
   ring_tile_body<BN, WAVES, false>(a, blockIdx.x, gridDim.x);
 }
 
-// FP8 weights and FP8 activations (the same ring, 64-K steps)
+// FP8 weights and FP8 activations (the same ring, 64-K steps), for K a
+// multiple of 64 but not of 128; otherwise tile_gemm_f8f8d_kernel
 template <int BN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8_kernel(StreamArgs a) {
   ring_tile_body<BN, WAVES, true>(a, blockIdx.x, gridDim.x);
@@ -553,7 +700,17 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
     p.Y = static_cast<uint8_t*>(a.Y) + m0 * a.ldy * y_elem;
     if (f8x) {
       p.xscale = a.xscale + m0;
-      hipError_t e = bn == 256 ? launch_bf16_lds<256, 8, true>(p, stream) : launch_bf16_lds<128, 4, true>(p, stream);
+      hipError_t e;
+      if (p.K % 128 == 0) {
+        // 128-K double steps: whole 128-byte lines per load
+        if (bn == 256)
+          hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 2>), tile_grid<256>(p), dim3(512), 0, stream, p);
+        else
+          hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<128, 4, 3>), tile_grid<128>(p), dim3(256), 0, stream, p);
+        e = hipGetLastError();
+      } else {
+        e = bn == 256 ? launch_bf16_lds<256, 8, true>(p, stream) : launch_bf16_lds<128, 4, true>(p, stream);
+      }
       if (e != hipSuccess) return e;
       continue;
     }

@@ -98,7 +98,9 @@ def _mlp(hidden, inter, m, seed):
 
 
 @pytest.mark.parametrize("hidden,inter,m", [(256, 320, 300), (512, 1024, 600), (128, 256, 4096), (256, 192, 1),
-                                            (192, 128, 70)])
+                                            (192, 128, 70),
+                                            # 256-row tiles in 128-K double steps: odd count, then a single one
+                                            (384, 4096, 4096), (128, 8192, 4096)])
 def test_mlp_fp8act_parity(hidden, inter, m):
     note(f"mlp fp8act h={hidden} i={inter} m={m}")
     gu, d, x, y = _mlp(hidden, inter, m, seed=hidden + inter)
