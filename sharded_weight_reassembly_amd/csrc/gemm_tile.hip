@@ -16,11 +16,10 @@
 //     two steps ahead; X rows of 128 B with piece p of row r at
 //     r * 8 + (p ^ ((r >> 1) & 7)), and the raw FP8 codes, widened to BF16
 //     (exact) after the fragment read;
-//   * BF16 weights (tile_gemm_bf16_kernel): steps of 32 K, a four-stage ring
-//     three steps ahead, rows of 64 B for both operands;
-//   * FP8 weights and FP8 activations (tile_gemm_f8f8d_kernel): double steps
-//     of 128 K, rows of 128 B for both operands (whole cache lines per load),
-//     two or three double stages;
+//   * BF16 weights (tile_gemm_bf16d_kernel) and FP8 weights with FP8
+//     activations (tile_gemm_f8f8d_kernel): double steps of 128 bytes per row
+//     for both operands (64 K of BF16, 128 K of FP8: whole cache lines per
+//     load), two or three double stages;
 //   * tiles are numbered so that each XCD (workgroups are dealt round-robin
 //     to the 8 XCDs) works through a compact group of 4 token blocks x all
 //     weight blocks, which keeps the X and W tiles of concurrently running
@@ -297,33 +296,27 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// BF16 weights: both operands by buffer-to-LDS loads as above, in 32-K steps
-// (a 256-row stage of BF16 weights at 64 K would take 32 KB, too much for a
-// three-stage ring beside X) through a four-stage ring, three steps ahead.
+// FP8 weights and FP8 activations (codes of both operands, one fp32 scale per
+// token in StreamArgs::xscale) in 64-K steps, for K a multiple of 64 but not
+// of 128 (otherwise the double-step kernel below): both operands by
+// buffer-to-LDS loads through a four-stage ring, three steps ahead.
 //   * X stage: 256 rows x 64 B, W stage: BN rows x 64 B, both with piece q of
 //     row r at r * 4 + (q ^ ((r >> 2) & 3)); a load instruction fills 16 rows;
-//   * a step is two 16-K slices; lane group g of an MFMA reads piece 2s + g of
-//     its row for slice s, K in natural order;
+//   * a step is one v_mfma_scale_f32_32x32x64_f8f6f4 per tile pair (E4M3 x
+//     E4M3, no block scale): lane group g reads pieces 2g and 2g + 1
+//     (K = 32g .. 32g + 31);
 //   * per step: wait until this wave's loads of step t have landed, barrier,
 //     issue the loads of step t + 3 into the stage that step t - 1 read,
 //     multiply step t.
-// F8 = true: FP8 weights and FP8 activations (codes of both operands, one
-// fp32 scale per token in StreamArgs::xscale).  A 64-byte row then holds 64 K,
-// so a step is 64 K with the same stage bytes and LDS layout, multiplied by
-// v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 x E4M3, no block scale): lane group
-// g reads pieces 2g and 2g + 1 (K = 32g .. 32g + 31).
-constexpr int kStepK16 = 32;
-
-template <int BN, int WAVES, bool F8>
+template <int BN, int WAVES>
 __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = 4;
   constexpr int TN = WN / 32;
-  constexpr int EB = F8 ? 1 : 2;            // bytes per element of both operands
-  constexpr int BK = F8 ? 64 : kStepK16;    // K per step: 64 bytes of every row
-  constexpr int A_BYTES = kTileM * BK * EB;  // 16 KB
-  constexpr int B_BYTES = BN * BK * EB;
+  constexpr int BK = 64;                     // K per step: 64 bytes of every row
+  constexpr int A_BYTES = kTileM * BK;       // 16 KB
+  constexpr int B_BYTES = BN * BK;
   constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per step
   constexpr int NB = B_BYTES / 1024 / WAVES;  // 1 KB loads of W per wave per step
   static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
@@ -332,7 +325,7 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
   __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[B_BYTES], b3[B_BYTES];
   // first in LDS, for the same reason as in the FP8 kernel
   __shared__ __attribute__((aligned(4096))) float row_scale[BN];
-  __shared__ float tok_scale[F8 ? kTileM : 1];
+  __shared__ float tok_scale[kTileM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -344,11 +337,10 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
     row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
   }
-  if constexpr (F8)
-    for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
+  for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
 
-  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * EB);
-  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * EB);
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K);
   // Source offsets of this lane's pieces (step 0): a load fills rows
   // 16 * i .. 16 * i + 15 of the stage, lane l position l % 4 of row l / 4;
   // rows past the end are read from the last row and never stored.
@@ -358,14 +350,14 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
     const int row = (wave * NA + i) * 16 + lane / 4;
     const int q = (lane % 4) ^ ((row >> 2) & 3);
     const int64_t m = min(m0 + row, a.M - 1);
-    aoff[i] = int(m * a.ldx * EB + q * 16);
+    aoff[i] = int(m * a.ldx + q * 16);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int row = (wave * NB + i) * 16 + lane / 4;
     const int q = (lane % 4) ^ ((row >> 2) & 3);
     const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
-    boff[i] = int(r * a.K * EB + q * 16);
+    boff[i] = int(r * a.K + q * 16);
   }
   auto issue = [&](uint8_t* A, uint8_t* B, int kt) {
 #pragma unroll
@@ -382,40 +374,22 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
     for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
 
   auto compute = [&](const uint8_t* A, const uint8_t* B) {
-    if constexpr (F8) {
-      // 32 codes per lane: pieces 2g and 2g + 1 of its row
-      i32x8 fa[TM], fb[TN];
-      auto frag = [&](const uint8_t* base, int row) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + wswz(row, 2 * kg) * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + wswz(row, 2 * kg + 1) * 16);
-        return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-      };
+    // 32 codes per lane: pieces 2g and 2g + 1 of its row
+    i32x8 fa[TM], fb[TN];
+    auto frag = [&](const uint8_t* base, int row) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(base + wswz(row, 2 * kg) * 16);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(base + wswz(row, 2 * kg + 1) * 16);
+      return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+    };
 #pragma unroll
-      for (int x = 0; x < TM; ++x) fa[x] = frag(A, wm * 128 + x * 32 + r32);
+    for (int x = 0; x < TM; ++x) fa[x] = frag(A, wm * 128 + x * 32 + r32);
 #pragma unroll
-      for (int y = 0; y < TN; ++y) fb[y] = frag(B, wn * WN + y * 32 + r32);
+    for (int y = 0; y < TN; ++y) fb[y] = frag(B, wn * WN + y * 32 + r32);
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
-#pragma unroll
-        for (int y = 0; y < TN; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[x], fb[y], acc[x][y], 0, 0, 0, 0, 0, 0);
-      return;
-    }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 fa[TM], fb[TN];
-#pragma unroll
-      for (int x = 0; x < TM; ++x)
-        fa[x] = *reinterpret_cast<const bf16x8*>(A + wswz(wm * 128 + x * 32 + r32, 2 * s + kg) * 16);
+    for (int x = 0; x < TM; ++x)
 #pragma unroll
       for (int y = 0; y < TN; ++y)
-        fb[y] = *reinterpret_cast<const bf16x8*>(B + wswz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
-#pragma unroll
-      for (int x = 0; x < TM; ++x)
-#pragma unroll
-        for (int y = 0; y < TN; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-    }
+        acc[x][y] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[x], fb[y], acc[x][y], 0, 0, 0, 0, 0, 0);
   };
 
   constexpr int kLoads = NA + NB;  // loads per wave per step
@@ -454,29 +428,32 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
   if (kt < nk) step(a0, b0, a3, b3, kt);
   if (kt + 1 < nk) step(a1, b1, a0, b0, kt + 1);
   if (kt + 2 < nk) step(a2, b2, a1, b1, kt + 2);
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, tok_scale);
 }
 
 // ---------------------------------------------------------------------------
-// FP8 weights and FP8 activations in 128-K double steps.  Rows of both
-// operands are 128 bytes per double step, so each buffer-to-LDS load fills 8
-// whole 128-byte lines (1 KB) instead of 16 half lines: half the requests of
-// 64-K steps per byte.  (Measured on MI355X: the 64-K kernel is bound by
+// Both operands in double steps of 128 bytes per row (128 K of FP8 codes for
+// FP8 weights with FP8 activations, 64 K of BF16 for BF16 weights and
+// activations), so each buffer-to-LDS load fills 8 whole 128-byte lines
+// (1 KB) instead of 16 half lines: half the requests per byte of the 64-byte
+// rows of the ring kernel below.  (Measured on MI355X: the 64-K kernel is bound by
 // these loads -- with them removed it runs twice as fast, while removing its
 // MFMAs or its fragment reads changes nothing -- and the double steps take
 // the FP8-activation MLP from 1.39 to 1.08 ms at 4096 tokens and from 5.50
-// to 4.08 ms at 16384.)  NST double stages in LDS (2 for 256-row tiles, 3 for
-// 128-row ones), loads NST - 1 double steps ahead; the layout is the 128-byte
-// row swizzle swz() of the FP8-weight kernel's X.  Within a double step, MFMA
-// slice s (0, 1) takes K = 64s .. 64s + 63: lane group g reads pieces
-// 4s + 2g and 4s + 2g + 1 of its row in both operands.
-template <int BN, int WAVES, int NST>
-__device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
+// to 4.08 ms at 16384; for BF16 the sharded-matmul GEMMs gain 8-11%.)  NST
+// double stages in LDS (2 for 256-row tiles, 3 for 128-row ones), loads
+// NST - 1 double steps ahead; the layout is the 128-byte row swizzle swz() of
+// the FP8-weight kernel's X.  Within a double step of FP8, MFMA slice s
+// (0, 1) takes K = 64s .. 64s + 63: lane group g reads pieces 4s + 2g and
+// 4s + 2g + 1 of its row in both operands; of BF16, slice s (0 .. 3) takes
+// K = 16s .. 16s + 15 and lane group g reads piece 2s + g.
+template <int BN, int WAVES, int NST, bool F8 = true>
+__device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = 4;
   constexpr int TN = WN / 32;
-  constexpr int DK = 128;                     // K per double step (one byte per element)
+  constexpr int DK = 128;                     // bytes of a row per double step (128 / EB elements)
   constexpr int A_BYTES = kTileM * DK;         // 32 KB
   constexpr int B_BYTES = BN * DK;
   constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per double step
@@ -487,7 +464,8 @@ __device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t
   __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[NST > 2 ? A_BYTES : 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[NST > 2 ? B_BYTES : 1024];
   __shared__ __attribute__((aligned(4096))) float row_scale[BN];
-  __shared__ float tok_scale[kTileM];
+  __shared__ float tok_scale[F8 ? kTileM : 1];
+  constexpr int EB = F8 ? 1 : 2;  // bytes per element of both operands
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -499,10 +477,11 @@ __device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
     row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
   }
-  for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
+  if constexpr (F8)
+    for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
 
-  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx);
-  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K);
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * EB);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * EB);
   // a load fills rows 8i .. 8i + 7 of the stage: lane l writes slot l % 8 of
   // row l / 8, which holds piece (l % 8) ^ ((row >> 1) & 7) of that row
   int aoff[NA], boff[NB];
@@ -511,14 +490,14 @@ __device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t
     const int row = (wave * NA + i) * 8 + lane / 8;
     const int q = (lane % 8) ^ ((row >> 1) & 7);
     const int64_t m = min(m0 + row, a.M - 1);
-    aoff[i] = int(m * a.ldx + q * 16);
+    aoff[i] = int(m * a.ldx * EB + q * 16);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int row = (wave * NB + i) * 8 + lane / 8;
     const int q = (lane % 8) ^ ((row >> 1) & 7);
     const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
-    boff[i] = int(r * a.K + q * 16);
+    boff[i] = int(r * a.K * EB + q * 16);
   }
   auto issue = [&](uint8_t* A, uint8_t* B, int kd) {
 #pragma unroll
@@ -540,6 +519,25 @@ __device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t
     return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
   };
   auto compute = [&](const uint8_t* A, const uint8_t* B) {
+    if constexpr (!F8) {
+      // BF16: four 16-K slices; lane group g reads piece 2s + g of its row
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 fa[TM], fb[TN];
+#pragma unroll
+        for (int x = 0; x < TM; ++x)
+          fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, 2 * s + kg) * 16);
+#pragma unroll
+        for (int y = 0; y < TN; ++y)
+          fb[y] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
+#pragma unroll
+        for (int x = 0; x < TM; ++x)
+#pragma unroll
+          for (int y = 0; y < TN; ++y)
+            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       i32x8 fa[TM], fb[TN];
@@ -556,7 +554,7 @@ __device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t
   };
 
   constexpr int kLoads = NA + NB;  // loads per wave per double step
-  const int nd = int(a.K / DK);
+  const int nd = int(a.K * EB / DK);
   // prologue: double steps 0 .. NST - 2 in flight
   issue(a0, b0, 0);
   if (NST > 2 && nd > 1) issue(a1, b1, 1);
@@ -592,12 +590,17 @@ __device__ inline void f8f8_tile_body(const StreamArgs& a, int64_t tile, int64_t
     if (kd < nd) step(a0, b0, a2, b2, kd);
     if (kd + 1 < nd) step(a1, b1, a0, b0, kd + 1);
   }
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, tok_scale);
+  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
 }
 
 template <int BN, int WAVES, int NST>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8d_kernel(StreamArgs a) {
-  f8f8_tile_body<BN, WAVES, NST>(a, blockIdx.x, gridDim.x);
+  dstep_tile_body<BN, WAVES, NST>(a, blockIdx.x, gridDim.x);
+}
+
+template <int BN, int WAVES, int NST>
+__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16d_kernel(StreamArgs a) {
+  dstep_tile_body<BN, WAVES, NST, false>(a, blockIdx.x, gridDim.x);
 }
 
 template <int BN, int WAVES>
@@ -605,16 +608,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs
   fp8_tile_body<BN, WAVES>(a, blockIdx.x, gridDim.x);
 }
 
-template <int BN, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16_kernel(StreamArgs a) {
-  ring_tile_body<BN, WAVES, false>(a, blockIdx.x, gridDim.x);
-}
-
-// FP8 weights and FP8 activations (the same ring, 64-K steps), for K a
-// multiple of 64 but not of 128; otherwise tile_gemm_f8f8d_kernel
+// FP8 weights and FP8 activations in 64-K steps, for K a multiple of 64 but
+// not of 128; otherwise tile_gemm_f8f8d_kernel
 template <int BN, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8_kernel(StreamArgs a) {
-  ring_tile_body<BN, WAVES, true>(a, blockIdx.x, gridDim.x);
+  ring_tile_body<BN, WAVES>(a, blockIdx.x, gridDim.x);
 }
 
 // Several GEMMs of one weight dtype in one launch (a layer's projections, the
@@ -629,7 +627,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_group_kernel(TileGroup tg)
   if constexpr (FP8)
     fp8_tile_body<BN, WAVES>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
   else
-    ring_tile_body<BN, WAVES, false>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
+    dstep_tile_body<BN, WAVES, BN == 256 ? 2 : 3, false>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
 }
 
 int64_t tile_count(const StreamArgs& a, int bn) {
@@ -646,12 +644,15 @@ dim3 tile_grid(const StreamArgs& a) {
   return dim3(unsigned(tile_count(a, BN)));
 }
 
-template <int BN, int WAVES, bool F8 = false>
-hipError_t launch_bf16_lds(const StreamArgs& a, hipStream_t stream) {
-  if constexpr (F8)
-    hipLaunchKernelGGL((tile_gemm_f8f8_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
-  else
-    hipLaunchKernelGGL((tile_gemm_bf16_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+template <int BN, int WAVES>
+hipError_t launch_f8f8_ring(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((tile_gemm_f8f8_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int BN, int WAVES, int NST>
+hipError_t launch_bf16d(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((tile_gemm_bf16d_kernel<BN, WAVES, NST>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -709,7 +710,7 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
           hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<128, 4, 3>), tile_grid<128>(p), dim3(256), 0, stream, p);
         e = hipGetLastError();
       } else {
-        e = bn == 256 ? launch_bf16_lds<256, 8, true>(p, stream) : launch_bf16_lds<128, 4, true>(p, stream);
+        e = bn == 256 ? launch_f8f8_ring<256, 8>(p, stream) : launch_f8f8_ring<128, 4>(p, stream);
       }
       if (e != hipSuccess) return e;
       continue;
@@ -718,9 +719,9 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
     // waits on LDS and barriers are covered by the other's MFMAs
     hipError_t e;
     if (bn == 256)
-      e = fp8 ? launch_fp8<256, 8>(p, stream) : launch_bf16_lds<256, 8>(p, stream);
+      e = fp8 ? launch_fp8<256, 8>(p, stream) : launch_bf16d<256, 8, 2>(p, stream);
     else
-      e = fp8 ? launch_fp8<128, 4>(p, stream) : launch_bf16_lds<128, 4>(p, stream);
+      e = fp8 ? launch_fp8<128, 4>(p, stream) : launch_bf16d<128, 4, 3>(p, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

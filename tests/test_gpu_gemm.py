@@ -218,6 +218,8 @@ def test_many_row_blocks_at_few_tokens(o, k, m):
     (320, 128, synth.FP8, 270),      # two FP8 steps: no full ring cycle
     (4096, 256, synth.FP8, 600),     # four FP8 steps with 256-row tiles: one ring cycle and a tail of one
     (2000, 320, synth.FP8, 513),     # five FP8 steps: one ring cycle and a tail of two
+    (8192, 192, synth.BF16, 4096),   # BF16, 256-row tiles: three double steps (one cycle of two and a tail)
+    (8192, 128, synth.BF16, 4096),   # BF16, 256-row tiles: two double steps
 ])
 def test_tiled_prefill_parity(o, k, dt, m):
     note(f"tiled proj o={o} k={k} {dt} m={m}")
