@@ -2,10 +2,13 @@
 //
 //   Y[m, o] = s[o] * sum_k X[m, k] * W[o, k]      (or the fused SiLU*up mode)
 //
-// At thousands of tokens the weights are reused by every token block and the
-// product is bound by the matrix cores, so this is a classic LDS-tiled GEMM:
-//   * a workgroup computes a 256-token x BN-row tile of Y with 2 x WAVES/2
-//     waves; each wave a 128 x (2*BN/WAVES) sub-tile with
+// At thousands of tokens the weights are reused by every token block, so this
+// is a classic LDS-tiled GEMM (measured on MI355X, it is bound by its loads
+// into LDS more than by the matrix cores):
+//   * a workgroup computes a BM-token x BN-row tile of Y (BM = 256, or 128
+//     for FP8 weights where 256 x 256 tiles would not fill two waves of
+//     workgroups) with 2 x WAVES/2 waves; each wave a BM/2 x (2*BN/WAVES)
+//     sub-tile with
 //     v_mfma_f32_32x32x16_bf16 (tokens are the MFMA rows, weight rows the
 //     MFMA columns, so a lane's outputs run along a row of Y);
 //   * both operands go from memory straight into an LDS ring with
@@ -46,10 +49,10 @@ struct TileCoord {
   int64_t tile_n;  // weight-row block
 };
 
-template <int BN>
+template <int BN, int BM = kTileM>
 __device__ inline TileCoord tile_coord(const StreamArgs& a, int64_t i, int64_t ntiles) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
-  const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t cols = silu_mode ? a.inter : a.rows;  // output columns
   const int64_t col_tile = silu_mode ? BN / 2 : BN;
   const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
@@ -58,7 +61,7 @@ __device__ inline TileCoord tile_coord(const StreamArgs& a, int64_t i, int64_t n
   const int64_t first_m = group * kGroupM;
   const int64_t gsize = min<int64_t>(tiles_m - first_m, kGroupM);
   TileCoord c;
-  c.m0 = (first_m + (t % (kGroupM * tiles_n)) % gsize) * kTileM;
+  c.m0 = (first_m + (t % (kGroupM * tiles_n)) % gsize) * BM;
   c.tile_n = (t % (kGroupM * tiles_n)) / gsize;
   return c;
 }
@@ -103,7 +106,7 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
     for (int x = 0; x < TM; ++x) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int ml = wm * 128 + x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
+        const int ml = wm * (TM * 32) + x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
         const int64_t m = m0 + ml;
         if (m >= a.M) continue;
         const float ts = lds_tscale ? lds_tscale[ml] : 1.f;  // token scale (FP8 activations)
@@ -146,13 +149,13 @@ constexpr int kStages = 3;
 
 __device__ inline int wswz(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
 
-template <int BN, int WAVES>
+template <int BN, int WAVES, int BM = kTileM>
 __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
-  constexpr int TM = 4;
+  constexpr int TM = BM / 64;  // two rows of waves along the tokens
   constexpr int TN = WN / 32;
-  constexpr int A_BYTES = kTileM * kTileK * 2;  // 32 KB
+  constexpr int A_BYTES = BM * kTileK * 2;  // 32 KB for 256 tokens
   constexpr int B_BYTES = BN * kTileK;          // FP8 codes
   constexpr int NA = A_BYTES / 1024 / WAVES;    // 1 KB loads of X per wave per stage
   constexpr int NB = B_BYTES / 1024 / WAVES;    // 1 KB loads of W per wave per stage
@@ -171,7 +174,7 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const TileCoord tc = tile_coord<BN>(a, tile, ntiles);
+  const TileCoord tc = tile_coord<BN, BM>(a, tile, ntiles);
   const int64_t m0 = tc.m0;
   for (int c = tid; c < BN; c += 64 * WAVES) {
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
@@ -225,7 +228,7 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int x = 0; x < TM; ++x)
-        f.a[h][x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
+        f.a[h][x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * (BM / 2) + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
   };
   auto mfma_slice = [&](const Slice& f) {
 #pragma unroll
@@ -603,9 +606,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16d_kernel(StreamAr
   dstep_tile_body<BN, WAVES, NST, false>(a, blockIdx.x, gridDim.x);
 }
 
-template <int BN, int WAVES>
+template <int BN, int WAVES, int BM = kTileM>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs a) {
-  fp8_tile_body<BN, WAVES>(a, blockIdx.x, gridDim.x);
+  fp8_tile_body<BN, WAVES, BM>(a, blockIdx.x, gridDim.x);
 }
 
 // FP8 weights and FP8 activations in 64-K steps, for K a multiple of 64 but
@@ -630,18 +633,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_group_kernel(TileGroup tg)
     dstep_tile_body<BN, WAVES, BN == 256 ? 2 : 3, false>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
 }
 
-int64_t tile_count(const StreamArgs& a, int bn) {
+int64_t tile_count(const StreamArgs& a, int bn, int bm = kTileM) {
   const bool silu_mode = a.mode == OUT_SILU_BF16;
-  const int64_t tiles_m = (a.M + kTileM - 1) / kTileM;
+  const int64_t tiles_m = (a.M + bm - 1) / bm;
   const int64_t cols = silu_mode ? a.inter : a.rows;
   const int64_t col_tile = silu_mode ? bn / 2 : bn;
   const int64_t tiles_n = (cols + col_tile - 1) / col_tile;
   return tiles_m * tiles_n;
 }
 
-template <int BN>
+template <int BN, int BM = kTileM>
 dim3 tile_grid(const StreamArgs& a) {
-  return dim3(unsigned(tile_count(a, BN)));
+  return dim3(unsigned(tile_count(a, BN, BM)));
 }
 
 template <int BN, int WAVES>
@@ -720,7 +723,14 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
     hipError_t e;
     if (bn == 256)
       e = fp8 ? launch_fp8<256, 8>(p, stream) : launch_bf16d<256, 8, 2>(p, stream);
-    else
+    else if (fp8 && tile_count(p, 256, 128) >= 512) {
+      // 128 tokens x 256 weight rows, eight waves of 64 x 64: per FLOP 20%
+      // fewer bytes loaded into LDS than 256 x 128 (the BF16 X, twice the
+      // bytes of the FP8 W, is the shorter side), and two waves per SIMD
+      // (measured on the 4096-token down GEMM: 1065 against 1000 TFLOP/s)
+      hipLaunchKernelGGL((tile_gemm_fp8_kernel<256, 8, 128>), (tile_grid<256, 128>(p)), dim3(512), 0, stream, p);
+      e = hipGetLastError();
+    } else
       e = fp8 ? launch_fp8<128, 4>(p, stream) : launch_bf16d<128, 4, 3>(p, stream);
     if (e != hipSuccess) return e;
   }

@@ -218,6 +218,8 @@ def test_many_row_blocks_at_few_tokens(o, k, m):
     (320, 128, synth.FP8, 270),      # two FP8 steps: no full ring cycle
     (4096, 256, synth.FP8, 600),     # four FP8 steps with 256-row tiles: one ring cycle and a tail of one
     (2000, 320, synth.FP8, 513),     # five FP8 steps: one ring cycle and a tail of two
+    (6144, 512, synth.FP8, 4096),    # FP8 weights in 128-token x 256-row tiles (the 4096-token down GEMM's shape class)
+    (6144, 320, synth.FP8, 4000),    # the same tiles with a token tail and five steps
     (8192, 192, synth.BF16, 4096),   # BF16, 256-row tiles: three double steps (one cycle of two and a tail)
     (8192, 128, synth.BF16, 4096),   # BF16, 256-row tiles: two double steps
 ])
@@ -255,7 +257,8 @@ def test_tiled_prefill_x_beyond_4gib(dt):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
-@pytest.mark.parametrize("hidden,inter,m", [(256, 320, 300), (512, 1024, 600), (128, 256, 4096)])
+@pytest.mark.parametrize("hidden,inter,m", [(256, 320, 300), (512, 1024, 600), (128, 256, 4096),
+                                            (256, 2048, 4096)])  # FP8 gate_up in 128-token x 256-row tiles
 def test_tiled_prefill_mlp(dt, hidden, inter, m):
     note(f"tiled mlp h={hidden} i={inter} {dt} m={m}")
     gu = synth.weight(synth.seed_for(15, 0, 0), 2 * inter, hidden, dt)
