@@ -450,14 +450,14 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
 // (0, 1) takes K = 64s .. 64s + 63: lane group g reads pieces 4s + 2g and
 // 4s + 2g + 1 of its row in both operands; of BF16, slice s (0 .. 3) takes
 // K = 16s .. 16s + 15 and lane group g reads piece 2s + g.
-template <int BN, int WAVES, int NST, bool F8 = true>
+template <int BN, int WAVES, int NST, bool F8 = true, int BM = kTileM>
 __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
-  constexpr int TM = 4;
+  constexpr int TM = BM / 64;  // two rows of waves along the tokens
   constexpr int TN = WN / 32;
   constexpr int DK = 128;                     // bytes of a row per double step (128 / EB elements)
-  constexpr int A_BYTES = kTileM * DK;         // 32 KB
+  constexpr int A_BYTES = BM * DK;             // 32 KB for 256 tokens
   constexpr int B_BYTES = BN * DK;
   constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per double step
   constexpr int NB = B_BYTES / 1024 / WAVES;
@@ -467,21 +467,21 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
   __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[NST > 2 ? A_BYTES : 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[NST > 2 ? B_BYTES : 1024];
   __shared__ __attribute__((aligned(4096))) float row_scale[BN];
-  __shared__ float tok_scale[F8 ? kTileM : 1];
+  __shared__ float tok_scale[F8 ? BM : 1];
   constexpr int EB = F8 ? 1 : 2;  // bytes per element of both operands
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
-  const TileCoord tc = tile_coord<BN>(a, tile, ntiles);
+  const TileCoord tc = tile_coord<BN, BM>(a, tile, ntiles);
   const int64_t m0 = tc.m0;
   for (int c = tid; c < BN; c += 64 * WAVES) {
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
     row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
   }
   if constexpr (F8)
-    for (int c = tid; c < kTileM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
+    for (int c = tid; c < BM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
 
   const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * EB);
   const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * EB);
@@ -529,7 +529,7 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
         bf16x8 fa[TM], fb[TN];
 #pragma unroll
         for (int x = 0; x < TM; ++x)
-          fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * 128 + x * 32 + r32, 2 * s + kg) * 16);
+          fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * (BM / 2) + x * 32 + r32, 2 * s + kg) * 16);
 #pragma unroll
         for (int y = 0; y < TN; ++y)
           fb[y] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
@@ -545,7 +545,7 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
     for (int s = 0; s < 2; ++s) {
       i32x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int x = 0; x < TM; ++x) fa[x] = frag(A, wm * 128 + x * 32 + r32, s);
+      for (int x = 0; x < TM; ++x) fa[x] = frag(A, wm * (BM / 2) + x * 32 + r32, s);
 #pragma unroll
       for (int y = 0; y < TN; ++y) fb[y] = frag(B, wn * WN + y * 32 + r32, s);
 #pragma unroll
@@ -596,9 +596,9 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
   tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
 }
 
-template <int BN, int WAVES, int NST>
+template <int BN, int WAVES, int NST, int BM = kTileM>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8d_kernel(StreamArgs a) {
-  dstep_tile_body<BN, WAVES, NST>(a, blockIdx.x, gridDim.x);
+  dstep_tile_body<BN, WAVES, NST, true, BM>(a, blockIdx.x, gridDim.x);
 }
 
 template <int BN, int WAVES, int NST>
@@ -709,6 +709,10 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
         // 128-K double steps: whole 128-byte lines per load
         if (bn == 256)
           hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 2>), tile_grid<256>(p), dim3(512), 0, stream, p);
+        else if (tile_count(p, 256, 128) >= 512)
+          // 128 tokens x 256 weight rows, eight waves (as for FP8 weights)
+          hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 3, 128>), (tile_grid<256, 128>(p)), dim3(512), 0, stream,
+                             p);
         else
           hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<128, 4, 3>), tile_grid<128>(p), dim3(256), 0, stream, p);
         e = hipGetLastError();
