@@ -50,6 +50,8 @@ def parse() -> argparse.Namespace:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=str, default="1,8,32,64")
+    ap.add_argument("--curve-tokens", type=str, default="2,4,16",
+                    help="further token counts timed isolated only, to draw the decode MLP's curve")
     ap.add_argument("--layers", type=int, default=0, help="layers of the workload (0: its own count)")
     ap.add_argument("--gate", choices=["done", "begin", "after"], default="after",
                     help="decode: what the gather of layer l+1 waits for -- layer l-1 being done (the pages' gate), "
@@ -131,11 +133,15 @@ def main() -> int:
     log(f"setup {time.time() - t0:.1f}s")
     slot_a = torch.empty(T, dtype=torch.uint8, device=dev)
     slot_b = torch.empty(T, dtype=torch.uint8, device=dev)
-    x_all = synth.activations(synth.seed_for(2, 0, 50), max(tokens), H)
-    xs = {m: torch.from_numpy(x_all[:m].view(np.int16).copy()).view(torch.bfloat16).to(dev) for m in tokens}
-    ys = {m: torch.empty((m, H), dtype=torch.bfloat16, device=dev) for m in tokens}
+    # the isolated MLPs also run at the curve's token counts (not in
+    # --isolated-only, whose counter runs attribute launches by token count)
+    curve = [] if args.isolated_only or not args.curve_tokens else [int(t) for t in args.curve_tokens.split(",")]
+    iso_tokens = sorted(set(tokens) | set(curve))
+    x_all = synth.activations(synth.seed_for(2, 0, 50), max(iso_tokens), H)
+    xs = {m: torch.from_numpy(x_all[:m].view(np.int16).copy()).view(torch.bfloat16).to(dev) for m in iso_tokens}
+    ys = {m: torch.empty((m, H), dtype=torch.bfloat16, device=dev) for m in iso_tokens}
     wsp = {m: torch.empty(swr.mlp_workspace_bytes(m, H, I, "fp8_e4m3fn"), dtype=torch.uint8, device=dev)
-           for m in tokens}
+           for m in iso_tokens}
 
     compute = torch.cuda.Stream()
     side_stream = torch.cuda.Stream()
@@ -180,7 +186,7 @@ def main() -> int:
         torch.cuda.synchronize()
         gemm = {}
         with torch.cuda.stream(compute):
-            for m in tokens:
+            for m in tokens + [t for t in iso_tokens if t not in tokens]:
                 for _ in range(2):
                     for layer in range(L):
                         b = full[layer].data_ptr()
@@ -654,6 +660,11 @@ def main() -> int:
         },
         "value_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "per_tokens": per_m,
+        # the isolated MLP at every token count timed, headline and curve alike
+        "isolated_curve": {str(m): {"ms_per_layer": round(g, 4),
+                                    "weight_GBps": round((w_bytes + s_bytes) / (g * 1e-3) / 1e9, 1),
+                                    "weight_frac": round((w_bytes + s_bytes) / (g * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                           for m, g in sorted(iso_gemm.items())},
         "isolated_reassembly_GBps": round(2 * T / (iso_gather_ms * 1e-3) / 1e9, 1) if iso_gather_ms else None,
         "schedules_ms_per_forward": schedules,
         "dma_engine_gather": dma,

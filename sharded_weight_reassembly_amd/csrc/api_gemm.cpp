@@ -107,13 +107,8 @@ extern "C" int swr_proj_forward(const void* W, int32_t dtype, const float* row_s
   p.Y = Y;
   p.ldy = ldy;
   p.mode = y_fp32 ? swr::OUT_F32 : swr::OUT_BF16;
-  swr::GemmPlan plan = swr::plan_gemm(p);
-  if (plan.partial_bytes > 0 && !workspace) {
-    // no scratch given: one K split per row tile (same kernel, no partials)
-    plan.ksplit = 1;
-    plan.kper = in_f;
-    plan.partial_bytes = 0;
-  }
+  // no scratch given: a plan without K splits (no partial sums)
+  const swr::GemmPlan plan = swr::plan_gemm(p, workspace != nullptr);
   if (plan.partial_bytes > workspace_bytes)
     return fail(SWR_E_CAPACITY, "%s: workspace holds %lld bytes, needs %lld", fn, (long long)workspace_bytes,
                 (long long)plan.partial_bytes);
@@ -207,12 +202,7 @@ extern "C" int swr_proj_forward_grouped(const swr_proj_desc* descs, int32_t n, i
   swr::GemmPlan plans[SWR_MAX_GROUP];
   if (!one) {
     for (int i = 0; i < n; ++i) {
-      plans[i] = swr::plan_gemm(ps[i]);
-      if (plans[i].partial_bytes > 0 && !workspace) {
-        plans[i].ksplit = 1;
-        plans[i].kper = ps[i].K;
-        plans[i].partial_bytes = 0;
-      }
+      plans[i] = swr::plan_gemm(ps[i], workspace != nullptr);
       if (plans[i].partial_bytes > workspace_bytes)
         return fail(SWR_E_CAPACITY, "%s: workspace holds %lld bytes, descriptor %d needs %lld", fn,
                     (long long)workspace_bytes, i, (long long)plans[i].partial_bytes);

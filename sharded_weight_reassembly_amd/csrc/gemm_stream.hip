@@ -343,8 +343,8 @@ __global__ __launch_bounds__(kThreads, 2) void stream_gemm_kernel(StreamArgs a) 
 //       wave reads and widens the W pieces of its K groups, so with MT token
 //       blocks every W piece is widened MT times -- the mode for one token
 //       block, where it is a pure K split;
-//     - K split with X in LDS (WK and XL; 8 waves in two row halves for 2 or
-//       4 token blocks): wave w works on K group w % 4 of row half w / 4 for
+//     - K split with X in LDS (WK and XL; 8 waves in two row halves for 1, 2
+//       or 4 token blocks): wave w works on K group w % 4 of row half w / 4 for
 //       every token block, so each W piece is read from LDS and widened once;
 //       the stage's X tile (16*MT token rows x 512 B) is loaded with
 //       row-contiguous 16-byte pieces, which keeps the L2 -> CU traffic of X
@@ -406,13 +406,16 @@ struct StagedShape {
   static constexpr int WCAP = OCC == 2 || NW == 8 ? 112 : 128;
   // One 16-token block: X is cheap, so W and X of a stage share a slot (D
   // deep).  More tokens: X runs DX = 4 or 2 stages ahead in a ring of its own
-  // and W gets the rest, at most WCAP VGPRs.
-  static constexpr int DX0 = MT == 1 ? 0 : (MT == 2 && NV < 8 ? 4 : 2);
+  // and W gets the rest, at most WCAP VGPRs.  Eight waves keep two stages of
+  // each in flight: with twice the waves per CU that is as many bytes in
+  // flight as four stages of four waves, and deeper rings measured slower
+  // (17-32 tokens: 54.3 against 57.6 us per shared-expert MLP at 24 tokens).
+  static constexpr int DX0 = MT == 1 ? 0 : (NW == 8 ? 2 : (MT == 2 && NV < 8 ? 4 : 2));
   static constexpr int MT1CAP = DEEP ? 208 : 140;
   static constexpr int RING = MT == 1 ? (FREE < MT1CAP ? FREE : MT1CAP) / (WS + XS)
                                       : ((FREE - DX0 * XS) < WCAP ? (FREE - DX0 * XS) : WCAP) / WS;
   static constexpr int STEP = MT == 1 ? 2 : DX0;  // D must be a multiple of this (and even)
-  static constexpr int DMAX = DEEP ? 20 : 12;
+  static constexpr int DMAX = DEEP ? 20 : (NW == 8 ? 2 : 12);
   static constexpr int D1 = RING < STEP ? STEP : (RING > DMAX ? DMAX : RING);
   static constexpr int D = D1 - (D1 % STEP);
   static constexpr int DX = MT == 1 ? D : DX0;
@@ -847,6 +850,17 @@ void fill_slots(GemmPlan& plan, const GemmProblem& p, int64_t tok_blocks, int64_
   plan.rb = rb;
 }
 
+// K splits of a staged plan with `wgs` workgroups over `stages` stages: the
+// split doubles while fewer than 160 workgroups would run and each split
+// keeps at least 4 stages (the split-K finalize costs about as much as a 1/8
+// split); none past 64 tokens or without scratch for the partial sums.
+int64_t staged_split(int64_t wgs, int64_t stages, int64_t M, bool may_split) {
+  int64_t ks = 1;
+  if (M <= 64 && may_split)
+    while (wgs * ks < 160 && stages / (2 * ks) >= 4) ks *= 2;
+  return ks;
+}
+
 // Fills ksplit/kper/partial_bytes for `ks` K splits of `granule`-element pieces.
 void set_split(GemmPlan& plan, const GemmProblem& p, int64_t ks, int64_t granule) {
   const int64_t units = (p.K + granule - 1) / granule;
@@ -874,8 +888,8 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   if (plan.kind == 0 ? plan.rb != full : (plan.rb < 4 || plan.rb % 4 != 0 || plan.rb > full)) return false;
   if (plan.kind == 6) {
     // staged with eight K-split waves in two row halves and X through LDS:
-    // 2 or 4 token blocks; 64-row blocks, 128 for FP8
-    if (plan.mt != 2 && plan.mt != 4) return false;
+    // 1, 2 or 4 token blocks; 64-row blocks, 128 for FP8
+    if (plan.mt != 1 && plan.mt != 2 && plan.mt != 4) return false;
     if (!(plan.rt == 4 || (plan.rt == 8 && p.dtype == SWR_FP8_E4M3FN))) return false;
     if (silu_mode && inter % (8 * plan.rt) != 0) return false;
     return plan.sk == kStageK && p.K % kStageK == 0 && plan.kper % kStageK == 0 &&
@@ -898,7 +912,7 @@ bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan) {
   return false;
 }
 
-GemmPlan plan_gemm(const GemmProblem& p) {
+GemmPlan plan_gemm(const GemmProblem& p, bool may_split) {
   GemmPlan plan{};
   const bool silu_mode = p.mode == OUT_SILU_BF16;
   const int64_t inter = silu_mode ? p.rows / 2 : 0;
@@ -951,6 +965,19 @@ GemmPlan plan_gemm(const GemmProblem& p) {
       plan.kind = 6;
       plan.rt = (!silu_mode || inter % 64 == 0) ? 8 : 4;
     }
+    // One FP8 token block of 13-16 tokens: the activations of a stage are
+    // then about as many bytes as the weights of a 32-row block, and the
+    // eight-wave kernel reads them once per stage in whole cache lines for
+    // 128 (gate_up) or 64 rows.  Shared-expert MLP: 50.2 against 57.0 us at
+    // 16 tokens, 51.4 against 56.6 at 13, no gain at 12 or fewer.  Only where
+    // those larger blocks, K split as below, still give 160 workgroups.
+    if (plan.mt == 1 && fp8 && p.M >= 13 && (!silu_mode || inter % 64 == 0)) {
+      const int64_t blocks = row_blocks_of(p, 64);
+      if (blocks * staged_split(blocks, p.K / kStageK, p.M, may_split) >= 160) {
+        plan.kind = 6;
+        plan.rt = silu_mode ? 8 : 4;
+      }
+    }
     // One FP8 token block outside the SiLU mode (the down GEMM, projections):
     // 512-K stages halve the per-stage fixed cost (LDS round trip, barrier,
     // widening latency); measured 7% faster on the 14336-long down rows, 3%
@@ -960,10 +987,7 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     plan.rb = full_rows(p, plan.rt);
     const int64_t wgs = row_blocks_of(p, plan.rb) * tok_blocks;
     const int64_t stages = p.K / plan.sk;
-    int64_t ks = 1;
-    if (p.M <= 64)
-      while (wgs * ks < 160 && stages / (2 * ks) >= 4) ks *= 2;
-    set_split(plan, p, ks, plan.sk);
+    set_split(plan, p, staged_split(wgs, stages, p.M, may_split), plan.sk);
     // every CU busy to the end: 256 CUs times the kernel's workgroups per CU
     const int occ = plan.kind == 6 ? staged_occupancy(plan.mt, plan.rt, fp8, true, true, plan.sk, 8)
                                    : staged_occupancy(plan.mt, plan.rt, fp8, false, false, plan.sk, kWaves);
@@ -973,7 +997,7 @@ GemmPlan plan_gemm(const GemmProblem& p) {
     plan.rt = 4;
     plan.rb = full_rows(p, 4);
     int64_t ks = 1;
-    if (p.M <= 64) ks = (512 + row_blocks_of(p, plan.rb) - 1) / row_blocks_of(p, plan.rb);
+    if (p.M <= 64 && may_split) ks = (512 + row_blocks_of(p, plan.rb) - 1) / row_blocks_of(p, plan.rb);
     set_split(plan, p, ks, 256);
   } else {
     plan.kind = 1;
@@ -992,11 +1016,15 @@ hipError_t launch_staged(const StreamArgs& a, dim3 grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Eight-wave K-split kernels with X through LDS: 2 or 4 token blocks, 64
+// Eight-wave K-split kernels with X through LDS: 1, 2 or 4 token blocks, 64
 // rows, or 128 rows of FP8 weights.
 template <bool FP8>
 hipError_t dispatch_staged8(int mt, int rt, const StreamArgs& a, dim3 grid, hipStream_t stream) {
-  if (mt == 2) {
+  if (mt == 1) {
+    if (rt == 4) return launch_staged<1, 4, FP8, true, true, kStageK, 8>(a, grid, stream);
+    if constexpr (FP8)
+      if (rt == 8) return launch_staged<1, 8, FP8, true, true, kStageK, 8>(a, grid, stream);
+  } else if (mt == 2) {
     if (rt == 4) return launch_staged<2, 4, FP8, true, true, kStageK, 8>(a, grid, stream);
     if constexpr (FP8)
       if (rt == 8) return launch_staged<2, 8, FP8, true, true, kStageK, 8>(a, grid, stream);

@@ -97,7 +97,7 @@ struct GemmPlan {
   int64_t partial_bytes;  // fp32 split-K scratch needed (0 if ksplit == 1)
 };
 
-GemmPlan plan_gemm(const GemmProblem& p);
+GemmPlan plan_gemm(const GemmProblem& p, bool may_split = true);
 bool plan_is_valid(const GemmProblem& p, const GemmPlan& plan);
 // Enqueues the GEMM; `partial` must hold plan.partial_bytes bytes.
 hipError_t launch_gemm(const GemmProblem& p, const GemmPlan& plan, float* partial, hipStream_t stream);

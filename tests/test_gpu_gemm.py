@@ -207,6 +207,24 @@ def test_many_row_blocks_at_few_tokens(o, k, m):
     assert_close_rows(values(y), ref, what=f"{o}x{k} m={m}")
 
 
+@pytest.mark.parametrize("workspace", [True, False])
+@pytest.mark.parametrize("o,k,m", [(10304, 512, 13), (10304, 512, 16), (8192, 7168, 16), (6144, 14336, 13)])
+def test_one_token_block_on_eight_waves(o, k, m, workspace):
+    """FP8 weights at 13-16 tokens, where the planner takes the eight-wave
+    kernel with activations through LDS for one token block: 64-row blocks
+    shortened to fill the CUs (10304 rows: 44-row blocks, the last of 8),
+    tokens past M inside the 16-token block (m = 13), K split into partial
+    sums with a workspace (8192 x 7168, 6144 x 14336) and the four-wave plan
+    without one.  Sampled output columns where the oracle would be slow."""
+    note(f"one token block, eight waves {o}x{k} m={m} workspace={workspace}")
+    w = synth.weight(synth.seed_for(19, o % 97, k % 89), o, k, synth.FP8)
+    x = synth.activations(synth.seed_for(19, o % 97, 50), m, k)
+    y = values(_run_proj(w, x, workspace=workspace))
+    cols = np.arange(o) if o * k <= (1 << 23) else np.sort(np.random.default_rng(3).choice(o, 512, replace=False))
+    ref = gemm.proj_f64(x, np.ascontiguousarray(w.data[cols]), synth.FP8, len(cols), k, w.scale[cols])
+    assert_close_rows(y[:, cols], ref, what=f"{o}x{k} m={m} workspace={workspace}")
+
+
 @pytest.mark.parametrize("o,k,dt,m", [
     (1000, 512, synth.FP8, 300),     # row tail and token tail in the tiled kernel
     (2048, 1024, synth.BF16, 513),

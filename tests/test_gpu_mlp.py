@@ -56,6 +56,21 @@ def test_short_row_blocks_silu(hidden, inter, m):
     assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} m={m}")
 
 
+@pytest.mark.parametrize("m", [13, 16])
+def test_gate_up_one_token_block_on_eight_waves(m):
+    """I = 10240 gives 160 blocks of 64 gate + 64 up rows, so at 13-16 tokens
+    gate_up runs the eight-wave kernel with activations through LDS (the
+    down GEMM, 512 rows, stays on four waves with a K split)."""
+    hidden, inter = 512, 10240
+    note(f"gate_up one token block, eight waves h={hidden} i={inter} m={m}")
+    gu = synth.weight(synth.seed_for(13, 3, 0), 2 * inter, hidden, synth.FP8)
+    d = synth.weight(synth.seed_for(13, 3, 1), hidden, inter, synth.FP8)
+    x = synth.activations(synth.seed_for(13, 3, 50), m, hidden)
+    y = _mlp(gu, d, hidden, inter, x)
+    _, _, ref = gemm.mlp_f64(x, gu.raw(), gu.scale, d.raw(), d.scale, synth.FP8, hidden, inter)
+    assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} m={m}")
+
+
 @pytest.mark.parametrize("hidden,inter,m", [(512, 4096, 64), (448, 4096, 40), (512, 2048, 17)])
 def test_down_split_k_matches_projection(hidden, inter, m):
     """17-64 tokens: the MLP's down GEMM splits K over workgroups (512 x 4096
@@ -154,7 +169,7 @@ def shared_expert_layer():
     return wl, gu, d, x
 
 
-@pytest.mark.parametrize("m", [1, 8, 32, 64])
+@pytest.mark.parametrize("m", [1, 8, 13, 16, 32, 64])
 def test_full_size_shared_expert_mlp(shared_expert_layer, m):
     """Hidden 6144, intermediate 14336, FP8 E4M3FN with row scales; sampled output columns."""
     wl, gu, d, x = shared_expert_layer
