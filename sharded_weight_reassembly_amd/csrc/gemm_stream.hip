@@ -699,6 +699,16 @@ __global__ __launch_bounds__(kThreads, (StagedShape<MT, RTL, FP8, false, false>:
   staged_body<MT, RTL, FP8, false, false>(ga.g[g], x - ga.first[g], 0, blockIdx.z, lds);
 }
 
+// The same with eight K-split waves and X through LDS (FP8 weights).
+template <int MT, int RTL>
+__global__ __launch_bounds__(512, 1) void grouped_staged8_kernel(GroupArgs ga) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[StagedShape<MT, RTL, true, true, true, kStageK, 8>::LDS];
+  const int x = blockIdx.x;
+  int g = 0;
+  while (g + 1 < ga.n && x >= ga.first[g + 1]) ++g;
+  staged_body<MT, RTL, true, true, true, kStageK, 8>(ga.g[g], x - ga.first[g], 0, blockIdx.z, lds);
+}
+
 // Adds the split-K partials in split order and applies scale / SiLU / rounding.
 // One thread per (token, 4 consecutive output columns); where the partial rows
 // and the scales are 16-byte aligned each split is one 16-byte load.
@@ -1140,10 +1150,11 @@ bool grouped_plan(const GemmProblem* ps, int n, int* mt, int* rt) {
   }
   int64_t blocks = 0;
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  // 64-row blocks: a group runs several waves of workgroups, and at two per
-  // CU one workgroup's loop covers the next one's first loads (the deep
-  // 32-row variant holds a CU alone); measured on the 8-projection attention
-  // layer at 16 tokens: 74 against 86 us
+  // 64-row blocks (launch_grouped takes 128 for the eight-wave kernel): a
+  // group runs several waves of workgroups, and at two per CU one
+  // workgroup's loop covers the next one's first loads (the deep 32-row
+  // variant holds a CU alone); measured on the 8-projection attention layer
+  // at 16 tokens with four waves: 74 against 86 us
   *rt = 4;
   for (int i = 0; i < n; ++i) {
     const GemmProblem& p = ps[i];
@@ -1178,7 +1189,14 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
   // last wave is as full as the others.
   const int64_t tok_blocks = (ps[0].M + 16 * mt - 1) / (16 * mt);
   const bool fp8 = ps[0].dtype == SWR_FP8_E4M3FN;
-  const int64_t slots = 256 * int64_t(staged_occupancy(mt, rt, fp8, false, false, kStageK, kWaves));
+  // FP8 at 13-64 tokens: eight K-split waves with X through LDS in 128-row
+  // blocks, one workgroup per CU.  Measured on the 8-projection attention
+  // layer (385 MB): 62.6 against 70.7 us at 16 tokens, 73.1 against 94.2 at
+  // 32 and 95.0 against 139.9 at 64 (64-row blocks: 65.7, 82.4, 117.2 us).
+  const bool eight = fp8 && (mt >= 2 || ps[0].M >= 13);
+  if (eight) rt = 8;
+  const int64_t slots =
+      eight ? 256 : 256 * int64_t(staged_occupancy(mt, rt, fp8, false, false, kStageK, kWaves));
   auto blocks_for = [&](int64_t rb) {
     int64_t b = 0;
     for (int i = 0; i < n; ++i) b += (ps[i].rows + rb - 1) / rb;
@@ -1199,6 +1217,15 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
   }
   ga.first[n] = first;
   const dim3 grid = dim3(unsigned(first), 1, unsigned(tok_blocks));
+  if (eight) {
+    if (mt == 1)
+      hipLaunchKernelGGL((grouped_staged8_kernel<1, 8>), grid, dim3(512), 0, stream, ga);
+    else if (mt == 2)
+      hipLaunchKernelGGL((grouped_staged8_kernel<2, 8>), grid, dim3(512), 0, stream, ga);
+    else
+      hipLaunchKernelGGL((grouped_staged8_kernel<4, 8>), grid, dim3(512), 0, stream, ga);
+    return hipGetLastError();
+  }
   if (mt == 1 && rt == 4)
     return fp8 ? launch_grouped_mt<1, 4, true>(ga, grid, stream) : launch_grouped_mt<1, 4, false>(ga, grid, stream);
   if (mt == 1)

@@ -314,7 +314,7 @@ GROUPS = [
 
 
 @pytest.mark.parametrize("gi", range(len(GROUPS)))
-@pytest.mark.parametrize("m", [1, 4, 16, 17, 33, 64, 65])
+@pytest.mark.parametrize("m", [1, 4, 13, 16, 17, 33, 64, 65])
 def test_grouped_projection_parity(gi, m):
     shapes, dt = GROUPS[gi]
     note(f"grouped projections group={gi} m={m}")
