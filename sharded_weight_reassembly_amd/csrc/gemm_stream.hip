@@ -975,15 +975,18 @@ GemmPlan plan_gemm(const GemmProblem& p, bool may_split) {
       plan.kind = 6;
       plan.rt = (!silu_mode || inter % 64 == 0) ? 8 : 4;
     }
-    // One FP8 token block of 13-16 tokens: the activations of a stage are
-    // then about as many bytes as the weights of a 32-row block, and the
-    // eight-wave kernel reads them once per stage in whole cache lines for
-    // 128 (gate_up) or 64 rows.  Shared-expert MLP: 50.2 against 57.0 us at
-    // 16 tokens, 51.4 against 56.6 at 13, no gain at 12 or fewer.  Only where
-    // those larger blocks, K split as below, still give 160 workgroups.
-    if (plan.mt == 1 && fp8 && p.M >= 13 && (!silu_mode || inter % 64 == 0)) {
+    // One FP8 token block: the eight-wave kernel reads each stage's
+    // activations once, in whole cache lines, for 128 (gate_up) or 64 rows.
+    // From 9 tokens, where those are about as many bytes as the weights of a
+    // 32-row block, it wins wherever its blocks, K split as below, give 160
+    // workgroups (shared-expert MLP: 50.2 against 57.0 us at 16 tokens, 48.8
+    // against 52.6 at 12).  Below 9 tokens only without a K split: the split
+    // and its finalize then cost more than they save (7168 x 8192: 14.7
+    // against 13.7 us), while gate_up and the largest projections still gain
+    // (24576 x 7168 at 8 tokens: 30.2 against 33.4 us).
+    if (plan.mt == 1 && fp8 && (!silu_mode || inter % 64 == 0)) {
       const int64_t blocks = row_blocks_of(p, 64);
-      if (blocks * staged_split(blocks, p.K / kStageK, p.M, may_split) >= 160) {
+      if (blocks * (p.M >= 9 ? staged_split(blocks, p.K / kStageK, p.M, may_split) : 1) >= 160) {
         plan.kind = 6;
         plan.rt = silu_mode ? 8 : 4;
       }

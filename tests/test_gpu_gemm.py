@@ -208,14 +208,15 @@ def test_many_row_blocks_at_few_tokens(o, k, m):
 
 
 @pytest.mark.parametrize("workspace", [True, False])
-@pytest.mark.parametrize("o,k,m", [(10304, 512, 13), (10304, 512, 16), (8192, 7168, 16), (6144, 14336, 13)])
+@pytest.mark.parametrize("o,k,m", [(10304, 512, 1), (10304, 512, 8), (10304, 512, 13), (10304, 512, 16),
+                                   (8192, 7168, 16), (6144, 14336, 9), (6144, 14336, 13)])
 def test_one_token_block_on_eight_waves(o, k, m, workspace):
-    """FP8 weights at 13-16 tokens, where the planner takes the eight-wave
-    kernel with activations through LDS for one token block: 64-row blocks
-    shortened to fill the CUs (10304 rows: 44-row blocks, the last of 8),
-    tokens past M inside the 16-token block (m = 13), K split into partial
-    sums with a workspace (8192 x 7168, 6144 x 14336) and the four-wave plan
-    without one.  Sampled output columns where the oracle would be slow."""
+    """FP8 weights at one token block, where the planner takes the eight-wave
+    kernel with activations through LDS: 64-row blocks shortened to fill the
+    CUs (10304 rows: 44-row blocks, the last of 8), tokens past M inside the
+    16-token block, K split into partial sums with a workspace from 9 tokens
+    (8192 x 7168, 6144 x 14336) and the four-wave plan without one or below
+    9 tokens.  Sampled output columns where the oracle would be slow."""
     note(f"one token block, eight waves {o}x{k} m={m} workspace={workspace}")
     w = synth.weight(synth.seed_for(19, o % 97, k % 89), o, k, synth.FP8)
     x = synth.activations(synth.seed_for(19, o % 97, 50), m, k)

@@ -56,9 +56,9 @@ def test_short_row_blocks_silu(hidden, inter, m):
     assert_close_rows(values(y), ref, what=f"mlp {hidden}/{inter} m={m}")
 
 
-@pytest.mark.parametrize("m", [13, 16])
+@pytest.mark.parametrize("m", [1, 9, 13, 16])
 def test_gate_up_one_token_block_on_eight_waves(m):
-    """I = 10240 gives 160 blocks of 64 gate + 64 up rows, so at 13-16 tokens
+    """I = 10240 gives 160 blocks of 64 gate + 64 up rows, so at 1-16 tokens
     gate_up runs the eight-wave kernel with activations through LDS (the
     down GEMM, 512 rows, stays on four waves with a K split)."""
     hidden, inter = 512, 10240
