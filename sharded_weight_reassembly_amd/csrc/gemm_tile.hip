@@ -685,8 +685,42 @@ hipError_t launch_tile_group(const StreamArgs* as, int n, int bn, bool fp8, hipS
   }
   if (tg.first[n] == 0) return hipSuccess;
   if (tg.first[n] >= (INT64_C(1) << 31)) return hipErrorInvalidValue;
-  if (bn == 256) return fp8 ? launch_group<256, 8, true>(tg, stream) : launch_group<256, 8, false>(tg, stream);
-  return fp8 ? launch_group<128, 4, true>(tg, stream) : launch_group<128, 4, false>(tg, stream);
+  if (bn != 256) return fp8 ? launch_group<128, 4, true>(tg, stream) : launch_group<128, 4, false>(tg, stream);
+  // As launch_tile_gemm: where the last wave of 256-row tiles would be at
+  // most half full, whole columns of those tiles (the last rows of the last
+  // problems) move to 128-row tiles in a second launch.  The problems of a
+  // group share M, so a column is tiles_m tiles.
+  const int64_t tiles_m = (as[0].M + kTileM - 1) / kTileM;
+  const int64_t rem = tg.first[n] % 256;
+  bool same_m = true;
+  for (int i = 0; i < n; ++i) same_m = same_m && as[i].M == as[0].M && as[i].mode != OUT_SILU_BF16;
+  if (!same_m || tg.first[n] <= 256 || rem == 0 || rem > 128 || rem % tiles_m != 0)
+    return fp8 ? launch_group<256, 8, true>(tg, stream) : launch_group<256, 8, false>(tg, stream);
+  int64_t cols = rem / tiles_m;  // 256-row columns to move
+  TileGroup tail{};
+  const int64_t y_elem = as[0].mode == OUT_F32 ? 4 : 2;
+  int nt = 0;
+  for (int i = n - 1; i >= 0 && cols > 0; --i) {
+    const int64_t tiles_n = (as[i].rows + 255) / 256;
+    const int64_t take = cols < tiles_n ? cols : tiles_n;
+    cols -= take;
+    const int64_t rows1 = (tiles_n - take) * 256;
+    StreamArgs t = as[i];
+    t.W = as[i].W + rows1 * as[i].K * (fp8 ? 1 : 2);
+    t.rows = as[i].rows - rows1;
+    t.scale = as[i].scale ? as[i].scale + rows1 : nullptr;
+    t.Y = static_cast<uint8_t*>(as[i].Y) + rows1 * y_elem;
+    tail.g[nt++] = t;
+    tg.g[i].rows = rows1;
+  }
+  tg.first[0] = 0;
+  for (int i = 0; i < n; ++i) tg.first[i + 1] = tg.first[i] + (tg.g[i].rows > 0 ? tile_count(tg.g[i], 256) : 0);
+  tail.n = nt;
+  tail.first[0] = 0;
+  for (int i = 0; i < nt; ++i) tail.first[i + 1] = tail.first[i] + tile_count(tail.g[i], 128);
+  hipError_t e = fp8 ? launch_group<256, 8, true>(tg, stream) : launch_group<256, 8, false>(tg, stream);
+  if (e != hipSuccess) return e;
+  return fp8 ? launch_group<128, 4, true>(tail, stream) : launch_group<128, 4, false>(tail, stream);
 }
 
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
@@ -725,9 +759,34 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
     // 256-row tiles: 8 waves (two per SIMD, 128 x 64 each), so one wave's
     // waits on LDS and barriers are covered by the other's MFMAs
     hipError_t e;
-    if (bn == 256)
-      e = fp8 ? launch_fp8<256, 8>(p, stream) : launch_bf16d<256, 8, 2>(p, stream);
-    else if (fp8 && tile_count(p, 256, 128) >= 512) {
+    if (bn == 256) {
+      // Whole waves of 256-row tiles over the 256 CUs.  Where the last wave
+      // would be at most half full, its rows go to 128-row tiles in a second
+      // launch instead (2048 x 8192 x 28672 BF16: 896 tiles, 3.5 waves; as
+      // 768 + 256 half tiles 1137-1149 against 1095 TFLOP/s).
+      int64_t rows1 = p.rows;
+      if (p.mode != OUT_SILU_BF16) {
+        const int64_t tiles_m = (p.M + kTileM - 1) / kTileM;
+        const int64_t tiles_n = (p.rows + 255) / 256;
+        const int64_t rem = (tiles_m * tiles_n) % 256;
+        if (tiles_m * tiles_n > 256 && rem != 0 && rem <= 128) {
+          int64_t n1 = tiles_n;
+          while (n1 > 0 && (tiles_m * n1) % 256 != 0) --n1;
+          if (n1 > 0) rows1 = n1 * 256;
+        }
+      }
+      StreamArgs p1 = p;
+      p1.rows = rows1;
+      e = fp8 ? launch_fp8<256, 8>(p1, stream) : launch_bf16d<256, 8, 2>(p1, stream);
+      if (e == hipSuccess && rows1 < p.rows) {
+        StreamArgs p2 = p;
+        p2.W = p.W + rows1 * p.K * (fp8 ? 1 : 2);
+        p2.rows = p.rows - rows1;
+        p2.scale = p.scale ? p.scale + rows1 : nullptr;
+        p2.Y = static_cast<uint8_t*>(p.Y) + rows1 * y_elem;
+        e = fp8 ? launch_fp8<128, 4>(p2, stream) : launch_bf16d<128, 4, 3>(p2, stream);
+      }
+    } else if (fp8 && tile_count(p, 256, 128) >= 512) {
       // 128 tokens x 256 weight rows, eight waves of 64 x 64: per FLOP 20%
       // fewer bytes loaded into LDS than 256 x 128 (the BF16 X, twice the
       // bytes of the FP8 W, is the shorter side), and two waves per SIMD

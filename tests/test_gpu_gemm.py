@@ -252,6 +252,25 @@ def test_tiled_prefill_parity(o, k, dt, m):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+def test_tiled_last_wave_in_half_tiles(dt):
+    """2048 tokens x 16484 rows: 8 x 65 = 520 tiles of 256 x 256, a last wave
+    of 8 on 256 CUs, so the first 16384 rows run as 512 full tiles and the
+    last 100 as 128-row tiles in a second launch.  Every column of the tail
+    and a sample of the rest are checked."""
+    o, k, m = 16484, 128, 2048
+    note(f"tiled last wave in half tiles o={o} k={k} {dt} m={m}")
+    w = synth.weight(synth.seed_for(14, 2, 0), o, k, dt)
+    x = synth.activations(synth.seed_for(14, 2, 50), m, k)
+    y = values(_run_proj(w, x))
+    rng = np.random.default_rng(5)
+    cols = np.sort(np.concatenate([rng.choice(16384, 412, replace=False), np.arange(16384, o)]))
+    raw = w.raw().reshape(o, -1)
+    ref = gemm.proj_f64(x, np.ascontiguousarray(raw[cols]), dt, len(cols), k,
+                        None if w.scale is None else w.scale[cols])
+    assert_close_rows(y[:, cols], ref, what=f"tiled {o}x{k} {dt} m={m} sampled columns")
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
 def test_tiled_prefill_x_beyond_4gib(dt):
     """X of 131372 tokens x 16384 (4.01 GiB of bf16) runs in three launches,
     each spanning less than 2 GiB (the tiled kernels address X with 32-bit
