@@ -226,6 +226,31 @@ def test_one_token_block_on_eight_waves(o, k, m, workspace):
     assert_close_rows(y[:, cols], ref, what=f"{o}x{k} m={m} workspace={workspace}")
 
 
+@pytest.mark.parametrize("y_fp32", [False, True])
+@pytest.mark.parametrize("m", [8, 16])
+def test_one_token_block_on_eight_waves_strided(m, y_fp32):
+    """The eight-wave plan at one token block with row strides on both sides
+    (ldx = K + 64, ldy = out + 64) and fp32 output: only the first out
+    columns of each Y row are written."""
+    o, k = 10304, 512
+    note(f"one token block, eight waves, strided {o}x{k} m={m} y_fp32={y_fp32}")
+    w = synth.weight(synth.seed_for(19, 1, 0), o, k, synth.FP8)
+    x = synth.activations(synth.seed_for(19, 1, 50), m, k)
+    ldy = o + 64
+    wd, sd = u8(w.raw()), f32(w.scale)
+    xb = np.zeros((m, k + 64), np.uint16)
+    xb[:, :k] = x
+    y = torch.full((m, ldy), float("nan"), dtype=torch.float32 if y_fp32 else torch.bfloat16, device=DEV)
+    nb = swr.proj_workspace_bytes(m, o, k, synth.FP8)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV)
+    swr.proj_forward(wd, synth.FP8, sd, o, k, bf16(xb), y, m=m, ldx=k + 64, ldy=ldy, y_fp32=y_fp32, workspace=ws)
+    torch.cuda.synchronize()
+    yv = values(y)
+    assert np.isnan(yv[:, o:]).all(), "columns past out_f were written"
+    ref = gemm.proj_f64(x, w.raw(), synth.FP8, o, k, w.scale)
+    assert_close_rows(yv[:, :o], ref, what=f"strided {o}x{k} m={m} y_fp32={y_fp32}")
+
+
 @pytest.mark.parametrize("o,k,dt,m", [
     (1000, 512, synth.FP8, 300),     # row tail and token tail in the tiled kernel
     (2048, 1024, synth.BF16, 513),
@@ -346,6 +371,35 @@ def test_grouped_projection_parity(gi, m):
     for w, y in zip(ws, ys):
         ref = gemm.proj_f64(xs[w.in_features], w.raw(), w.dtype, w.out_features, w.in_features, w.scale)
         assert_close_rows(values(y), ref, what=f"grouped {w.out_features}x{w.in_features} {w.dtype} m={m}")
+
+
+@pytest.mark.parametrize("y_fp32", [False, True])
+@pytest.mark.parametrize("m", [16, 33])
+def test_grouped_projection_strided(m, y_fp32):
+    """FP8 group 0 with every X and Y a strided view (ldx = K + 64, ldy =
+    out + 32): the eight-wave group reads only the first K columns of each
+    token row and writes only the first out columns of each Y row."""
+    shapes, dt = GROUPS[0]
+    note(f"grouped projections strided m={m} y_fp32={y_fp32}")
+    ws = [synth.weight(synth.seed_for(16, 7, j), o, k, dt) for j, (o, k) in enumerate(shapes)]
+    xs = {k: synth.activations(synth.seed_for(16, 7, 50 + k % 97), m, k) for _, k in shapes}
+    xd = {}
+    for k, x in xs.items():
+        xb = np.zeros((m, k + 64), np.uint16)
+        xb[:, :k] = x
+        xd[k] = bf16(xb)
+    ys = [torch.full((m, w.out_features + 32), float("nan"), device=DEV,
+                     dtype=torch.float32 if y_fp32 else torch.bfloat16) for w in ws]
+    projs = [dict(w=u8(w.raw()), dtype=w.dtype, row_scale=f32(w.scale), out_f=w.out_features,
+                  in_f=w.in_features, x=xd[w.in_features], y=y) for w, y in zip(ws, ys)]
+    assert swr.proj_grouped_workspace_bytes(projs, m) == 0
+    swr.proj_forward_grouped(projs, m)
+    torch.cuda.synchronize()
+    for w, y in zip(ws, ys):
+        yv = values(y)
+        assert np.isnan(yv[:, w.out_features:]).all(), "columns past out_f were written"
+        ref = gemm.proj_f64(xs[w.in_features], w.raw(), w.dtype, w.out_features, w.in_features, w.scale)
+        assert_close_rows(yv[:, :w.out_features], ref, what=f"grouped strided {w.out_features}x{w.in_features} m={m}")
 
 
 @pytest.mark.parametrize("gi,y_fp32", [(0, False), (1, False), (0, True)])
