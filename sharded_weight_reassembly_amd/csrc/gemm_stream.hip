@@ -981,8 +981,8 @@ GemmPlan plan_gemm(const GemmProblem& p, bool may_split) {
     // 32-row block, it wins wherever its blocks, K split as below, give 160
     // workgroups (shared-expert MLP: 50.2 against 57.0 us at 16 tokens, 48.8
     // against 52.6 at 12).  Below 9 tokens only without a K split: the split
-    // and its finalize then cost more than they save (7168 x 8192: 14.7
-    // against 13.7 us), while gate_up and the largest projections still gain
+    // and its finalize then cost more than they save (7168 x 8192: 15.6
+    // against 13.4-14.2 us), while gate_up and the largest projections gain
     // (24576 x 7168 at 8 tokens: 30.2 against 33.4 us).
     if (plan.mt == 1 && fp8 && (!silu_mode || inter % 64 == 0)) {
       const int64_t blocks = row_blocks_of(p, 64);
