@@ -373,6 +373,29 @@ def test_grouped_projection_parity(gi, m):
         assert_close_rows(values(y), ref, what=f"grouped {w.out_features}x{w.in_features} {w.dtype} m={m}")
 
 
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+def test_grouped_last_wave_in_half_tiles(dt):
+    """2048 tokens over projections of 8192, 6000 and 2300 rows (K = 128):
+    8 x 65 = 520 tiles of 256 x 256, a last wave of 8, so one tile column
+    of the last projection (its rows past 2048) runs as 128-row tiles in a
+    second grouped launch.  Every column of that tail and a sample of the
+    rest of each projection are checked."""
+    m, k = 2048, 128
+    shapes = [(8192, k), (6000, k), (2300, k)]
+    note(f"grouped last wave in half tiles {dt} m={m}")
+    ws = [synth.weight(synth.seed_for(16, 9, j), o, kk, dt) for j, (o, kk) in enumerate(shapes)]
+    xs = {k: synth.activations(synth.seed_for(16, 9, 50), m, k)}
+    nb, ys = _grouped(ws, xs, m)
+    rng = np.random.default_rng(7)
+    for w, y in zip(ws, ys):
+        o = w.out_features
+        cols = np.sort(np.unique(np.concatenate([rng.choice(o, 256, replace=False), np.arange(max(0, o - 300), o)])))
+        raw = w.raw().reshape(o, -1)
+        ref = gemm.proj_f64(xs[k], np.ascontiguousarray(raw[cols]), dt, len(cols), k,
+                            None if w.scale is None else w.scale[cols])
+        assert_close_rows(values(y)[:, cols], ref, what=f"grouped {o}x{k} {dt} m={m} sampled columns")
+
+
 @pytest.mark.parametrize("y_fp32", [False, True])
 @pytest.mark.parametrize("m", [16, 33])
 def test_grouped_projection_strided(m, y_fp32):
