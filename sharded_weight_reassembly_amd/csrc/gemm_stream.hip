@@ -1192,11 +1192,15 @@ hipError_t launch_grouped(const GemmProblem* ps, int n, int mt, int rt, hipStrea
   // last wave is as full as the others.
   const int64_t tok_blocks = (ps[0].M + 16 * mt - 1) / (16 * mt);
   const bool fp8 = ps[0].dtype == SWR_FP8_E4M3FN;
-  // FP8 at 13-64 tokens: eight K-split waves with X through LDS in 128-row
-  // blocks, one workgroup per CU.  Measured on the 8-projection attention
-  // layer (385 MB): 62.6 against 70.7 us at 16 tokens, 73.1 against 94.2 at
-  // 32 and 95.0 against 139.9 at 64 (64-row blocks: 65.7, 82.4, 117.2 us).
-  const bool eight = fp8 && (mt >= 2 || ps[0].M >= 13);
+  // FP8: eight K-split waves with X through LDS in 128-row blocks, one
+  // workgroup per CU -- at 13-64 tokens, and below where the group has 160
+  // such blocks.  Measured on the 8-projection attention layer (385 MB, 444
+  // blocks): 62.6 against 70.7 us at 16 tokens, 73.1 against 94.2 at 32 and
+  // 95.0 against 139.9 at 64 (64-row blocks: 65.7, 82.4, 117.2 us); 61.0-61.5
+  // against 62.3-62.5 at 1 token, 62.1-62.2 against 66.3-66.7 at 12.
+  int64_t blocks128 = 0;
+  for (int i = 0; i < n; ++i) blocks128 += (ps[i].rows + 127) / 128;
+  const bool eight = fp8 && (mt >= 2 || ps[0].M >= 13 || blocks128 >= 160);
   if (eight) rt = 8;
   const int64_t slots =
       eight ? 256 : 256 * int64_t(staged_occupancy(mt, rt, fp8, false, false, kStageK, kWaves));

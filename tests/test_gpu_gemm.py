@@ -373,6 +373,21 @@ def test_grouped_projection_parity(gi, m):
         assert_close_rows(values(y), ref, what=f"grouped {w.out_features}x{w.in_features} {w.dtype} m={m}")
 
 
+@pytest.mark.parametrize("m", [1, 8])
+def test_grouped_eight_waves_below_13_tokens(m):
+    """An FP8 group with 167 blocks of 128 rows takes the eight-wave group
+    kernel below 13 tokens too (ragged rows, K of 512, 256 and 768)."""
+    shapes = [(12800, 512), (8192, 256), (300, 768)]
+    note(f"grouped eight waves below 13 tokens m={m}")
+    ws = [synth.weight(synth.seed_for(16, 11, j), o, k, synth.FP8) for j, (o, k) in enumerate(shapes)]
+    xs = {k: synth.activations(synth.seed_for(16, 11, 50 + k % 97), m, k) for _, k in shapes}
+    nb, ys = _grouped(ws, xs, m)
+    assert nb == 0  # one launch, no K split
+    for w, y in zip(ws, ys):
+        ref = gemm.proj_f64(xs[w.in_features], w.raw(), w.dtype, w.out_features, w.in_features, w.scale)
+        assert_close_rows(values(y), ref, what=f"grouped {w.out_features}x{w.in_features} m={m}")
+
+
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
 def test_grouped_last_wave_in_half_tiles(dt):
     """2048 tokens over projections of 8192, 6000 and 2300 rows (K = 128):
@@ -467,12 +482,13 @@ def test_grouped_fp32_output_and_zero_tokens():
     assert (y == 3.0).all()
 
 
-def test_full_size_projection_layer_grouped():
-    """The 8 FP8 projections of one replicated attention layer at M=16 in ONE
-    grouped call through views of one reassembled slot; the oracle recomputes
-    a sample of output columns of every projection."""
+@pytest.mark.parametrize("m", [4, 16])
+def test_full_size_projection_layer_grouped(m):
+    """The 8 FP8 projections of one replicated attention layer at M=4 and 16
+    in ONE grouped call through views of one reassembled slot; the oracle
+    recomputes a sample of output columns of every projection."""
     wl = synth.ATTN_PROJECTIONS
-    note("full-size projection layer M=16, grouped")
+    note(f"full-size projection layer M={m}, grouped")
     ws = wl.layer_weights(1)
     shp = [(o, i, d) for _, o, i, d in wl.weights]
     views, lay = swr.plan_layer(shp, wl.n_chunks)
@@ -482,7 +498,6 @@ def test_full_size_projection_layer_grouped():
     del src
     slot = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=DEV)
     swr.reassemble_into_slot(chunks, lay["chunk_bytes"], slot)
-    m = 16
     xs, projs, ys = {}, [], []
     for j, (w, v) in enumerate(zip(ws, views)):
         k, o = w.in_features, w.out_features
