@@ -23,6 +23,13 @@
 //     activations (tile_gemm_f8f8d_kernel): double steps of 128 bytes per row
 //     for both operands (64 K of BF16, 128 K of FP8: whole cache lines per
 //     load), two or three double stages;
+//   * the BF16-activation bodies write their slice pipeline out instruction
+//     by instruction: each MFMA is followed by its share of the next slice's
+//     fragment reads, so a wave keeps its matrix core fed while its LDS reads
+//     are in flight (with one workgroup of eight waves per CU, loads into LDS
+//     and fragment reads overlap only this way);
+//   * the outputs of a wave are staged through the (then idle) LDS ring and
+//     leave in 16-byte stores of whole 128-byte row segments;
 //   * tiles are numbered so that each XCD (workgroups are dealt round-robin
 //     to the 8 XCDs) works through a compact group of 4 token blocks x all
 //     weight blocks, which keeps the X and W tiles of concurrently running
@@ -30,6 +37,8 @@
 //   * in SiLU mode a workgroup owns gate rows J0..J0+BN/2 and the matching up
 //     rows, laid out so that gate j and up j land in the same lane of
 //     different MFMA tiles; the epilogue writes h = bf16(silu(g) * u).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace swr {
@@ -125,6 +134,91 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
   }
 }
 
+// The wave's block of the output, staged through LDS so that it leaves in
+// 16-byte stores of whole 128-byte row segments (rather than one 2-byte store
+// per lane per output): a lane first writes its scaled, rounded outputs into
+// the wave's region (row-major, 16-byte pieces of a row XOR-swizzled by the
+// row), then reads back 16-byte pieces of rows and stores them.  BF16 outputs
+// (plain or SiLU * up); the caller checks that every output row starts
+// 16-byte aligned.  The region holds TM * 32 rows of TN * 32 columns.
+template <int BN, int WN, int TM, int TN>
+__device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t tile_n,
+                                         int wm, int wn, int r32, int kg, int lane, uint8_t* region,
+                                         const float* lds_scale, const float* lds_tscale) {
+  const bool silu_mode = a.mode == OUT_SILU_BF16;
+  constexpr int ROWS = TM * 32;
+  // output columns of the block: TN * 32, or TN * 16 in SiLU mode; 16-byte pieces per row
+  const int cols = silu_mode ? TN * 16 : TN * 32;
+  const int cpr = cols / 8;
+  const int64_t limit = silu_mode ? a.inter : a.rows;
+  const int64_t col0 = silu_mode ? tile_n * (BN / 2) + wn * (WN / 2) : tile_n * BN + wn * WN;
+  const int tn_out = silu_mode ? TN / 2 : TN;
+  auto pos = [&](int row, int col) { return row * cols * 2 + (((col >> 3) ^ (row & (cpr - 1))) << 4) + (col & 7) * 2; };
+#pragma unroll
+  for (int y = 0; y < TN; ++y) {
+    if (y >= tn_out) break;
+    const int c = wn * WN + y * 32 + r32;  // local B row
+    const float sc = lds_scale[c];
+    const float su = silu_mode ? lds_scale[c + WN / 2] : 1.f;
+#pragma unroll
+    for (int x = 0; x < TM; ++x) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
+        const float ts = lds_tscale ? lds_tscale[wm * ROWS + row] : 1.f;
+        float out = acc[x][y][v] * ts * sc;
+        if (silu_mode) out = silu(out) * (acc[x][y + TN / 2][v] * ts * su);
+        *reinterpret_cast<uint16_t*>(region + pos(row, y * 32 + r32)) = bf16_bits(out);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  uint16_t* Y = static_cast<uint16_t*>(a.Y);
+  const int pieces = ROWS * cpr;
+  for (int q = lane; q < pieces; q += 64) {
+    const int row = q / cpr, cp = q % cpr;
+    const int64_t m = m0 + wm * ROWS + row;
+    const int64_t col = col0 + cp * 8;
+    if (m >= a.M || col >= limit) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * cols * 2 + ((cp ^ (row & (cpr - 1))) << 4));
+    if (col + 8 <= limit) {
+      *reinterpret_cast<u32x4*>(Y + m * a.ldy + col) = v;
+    } else {
+      const uint16_t* h = reinterpret_cast<const uint16_t*>(&v);
+      for (int e = 0; e < 8 && col + e < limit; ++e) Y[m * a.ldy + col + e] = h[e];
+    }
+  }
+}
+
+// The E-byte slot of LDS stage memory that holds wave w's output block in the
+// epilogue: the slots of a0, a1, [a2], b0, b1, [b2] in turn.
+template <int E, int SA, int SB, int NS, int WAVES>
+__device__ inline uint8_t* epi_region(int w, uint8_t* a0, uint8_t* a1, uint8_t* a2, uint8_t* b0, uint8_t* b1,
+                                      uint8_t* b2) {
+  constexpr int na = SA / E, nb = SB / E;
+  static_assert(NS * (na + nb) >= WAVES, "the stages must hold every wave's output block");
+  if (w < na) return a0 + w * E;
+  w -= na;
+  if (w < na) return a1 + w * E;
+  w -= na;
+  if (NS > 2) {
+    if (w < na) return a2 + w * E;
+    w -= na;
+  }
+  if (w < nb) return b0 + w * E;
+  w -= nb;
+  if (w < nb) return b1 + w * E;
+  w -= nb;
+  return b2 + w * E;
+}
+
+// Whether the LDS-staged epilogue applies: BF16 outputs whose rows all start
+// 16-byte aligned.
+__device__ inline bool epi_lds_ok(const StreamArgs& a) {
+  return a.mode != OUT_F32 && (a.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
+}
+
 // ---------------------------------------------------------------------------
 // FP8 weights: both operands reach LDS by buffer-to-LDS loads (no staging
 // registers) through a three-stage ring, two k-steps ahead of the MFMAs.
@@ -137,14 +231,20 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
 //     K = 32*s + 16*g + 8*h .. +7 in the MFMA pair h = 0, 1, for both
 //     operands: one 16-byte fragment read of 16 FP8 codes feeds both MFMAs
 //     of the pair (the sum over K does not depend on the order);
-//   * per step t, software-pipelined by 32-K slice: read slice 1 of step t
-//     while the MFMAs of slice 0 run; wait until this wave's reads of stage t
-//     and its loads of step t + 1 are done (loads complete in issue order);
-//     barrier; issue the loads of step t + 3 into stage t; read slice 0 of
-//     step t + 1 while the MFMAs of slice 1 run.  The MFMAs after the barrier
-//     use fragments already in registers, so no wave waits on LDS there
-//     (measured on MI355X: 1-6% faster per GEMM than reading a step's
-//     fragments after its barrier).
+//   * per step t, software-pipelined by 32-K slice: slice 1 of step t is read
+//     while the MFMAs of slice 0 run; once this wave's reads of stage t and
+//     its loads of step t + 1 are done (loads complete in issue order), the
+//     barrier; the loads of step t + 3 go into stage t; slice 0 of step t + 1
+//     is read while the MFMAs of slice 1 run.  The MFMAs after the barrier
+//     use fragments already in registers, so no wave waits on LDS there;
+//   * the pipeline is written out instruction by instruction: each MFMA is
+//     followed by its share of the next slice's fragment reads (the W codes
+//     into a second register set, each X fragment right after its last
+//     MFMA), and scheduling barriers keep that order.  Left to itself the
+//     compiler issues each slice's reads just before the MFMAs that use them
+//     and waits on every few (measured on MI355X: the explicit order is 1-5%
+//     faster per GEMM);
+//   * the outputs leave through LDS (tile_epilogue_lds).
 constexpr int kStages = 3;
 
 __device__ inline int wswz(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
@@ -153,21 +253,16 @@ template <int BN, int WAVES, int BM = kTileM>
 __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
-  constexpr int TM = BM / 64;  // two rows of waves along the tokens
+  constexpr int TM = BM / 64;
   constexpr int TN = WN / 32;
-  constexpr int A_BYTES = BM * kTileK * 2;  // 32 KB for 256 tokens
-  constexpr int B_BYTES = BN * kTileK;          // FP8 codes
-  constexpr int NA = A_BYTES / 1024 / WAVES;    // 1 KB loads of X per wave per stage
-  constexpr int NB = B_BYTES / 1024 / WAVES;    // 1 KB loads of W per wave per stage
+  constexpr int A_BYTES = BM * kTileK * 2;
+  constexpr int B_BYTES = BN * kTileK;
+  constexpr int NA = A_BYTES / 1024 / WAVES;
+  constexpr int NB = B_BYTES / 1024 / WAVES;
   static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
                 "stage must split into whole 1 KB loads per wave");
-  // one array per stage, so the compiler can tell the stages' loads apart
   __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[A_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[B_BYTES];
-  // The row scales of the workgroup's weight rows, for the epilogue.  Being
-  // the most aligned, this array sits at the start of LDS: a stage array
-  // there would have its reads wait for every load in flight, because the
-  // compiler cannot tell an access at the base of LDS from the others.
   __shared__ __attribute__((aligned(4096))) float row_scale[BN];
 
   const int tid = threadIdx.x;
@@ -183,8 +278,6 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
 
   const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * 2);
   const u32x4s wres = raw_rsrc(a.W, a.rows * a.K);
-  // Source offsets of this lane's pieces (step 0); rows past the end are
-  // read from the last row and never stored.
   int aoff[NA], boff[NB];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
@@ -200,7 +293,7 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
     const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
     boff[i] = int(r * a.K + q * 16);
   }
-  auto issue = [&](uint8_t* A, uint8_t* B, int kt) {
+  auto issue = [&](uint8_t* A, uint8_t* B, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kt * kTileK * 2);
 #pragma unroll
@@ -214,40 +307,42 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
 #pragma unroll
     for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
 
-  // The fragments of one 32-K slice s of a stage: the raw FP8 codes of the
-  // wave's TN weight tiles and its TM activation tiles for both MFMA halves.
-  struct Slice {
-    u32x4 w[TN];
-    bf16x8 a[2][TM];
+  // slice s (0, 1) of a stage: W codes of tile y, X fragment of half h, tile x
+  bf16x8 fa[2][TM];
+  u32x4 fw[2][TN];
+  auto w_piece = [&](const uint8_t* B, int s, int y) __attribute__((always_inline)) {
+    return *reinterpret_cast<const u32x4*>(B + wswz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
   };
-  auto read_slice = [&](const uint8_t* A, const uint8_t* B, int s, Slice& f) {
-#pragma unroll
-    for (int y = 0; y < TN; ++y)
-      f.w[y] = *reinterpret_cast<const u32x4*>(B + wswz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int x = 0; x < TM; ++x)
-        f.a[h][x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * (BM / 2) + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
+  auto a_piece = [&](const uint8_t* A, int s, int h, int x) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(A + swz(wm * (BM / 2) + x * 32 + r32, 4 * s + 2 * kg + h) * 16);
   };
-  auto mfma_slice = [&](const Slice& f) {
+  // The MFMAs of the current slice (W codes in set c), each followed by one
+  // read of slice s_next of stage (A, B): first the W codes into set 1 - c,
+  // then each X fragment right after its last MFMA.
+  auto mma_read = [&](auto cc, const uint8_t* A, const uint8_t* B, int s_next) __attribute__((always_inline)) {
+    constexpr int c = decltype(cc)::value;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       bf16x8 fb[TN];
 #pragma unroll
-      for (int y = 0; y < TN; ++y) fb[y] = fp8x8_to_bf16(f.w[y][2 * h], f.w[y][2 * h + 1]);
+      for (int y = 0; y < TN; ++y) fb[y] = fp8x8_to_bf16(fw[c][y][2 * h], fw[c][y][2 * h + 1]);
 #pragma unroll
-      for (int x = 0; x < TM; ++x)
+      for (int x = 0; x < TM; ++x) {
 #pragma unroll
-        for (int y = 0; y < TN; ++y)
-          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[h][x], fb[y], acc[x][y], 0, 0, 0);
+        for (int y = 0; y < TN; ++y) {
+          acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[h][x], fb[y], acc[x][y], 0, 0, 0);
+          const int i = (h * TM + x) * TN + y;
+          if (h == 0 && i < TN) fw[1 - c][i] = w_piece(B, s_next, i);
+          __builtin_amdgcn_sched_barrier(0x0006);
+        }
+        fa[h][x] = a_piece(A, s_next, h, x);
+        __builtin_amdgcn_sched_barrier(0x0006);
+      }
     }
   };
 
-  constexpr int kLoads = NA + NB;  // loads per wave per step
+  constexpr int kLoads = NA + NB;
   const int nk = int(a.K / kTileK);
-  // Prologue: steps 0 and 1 in flight, step 0 landed in every wave, step 2
-  // issued, and slice 0 of step 0 read into registers.
   issue(a0, b0, 0);
   if (nk > 1) issue(a1, b1, 1);
   if (nk > 1)
@@ -257,35 +352,36 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   if (nk > 2) issue(a2, b2, 2);
-  Slice f0, f1;
-  read_slice(a0, b0, 0, f0);
+#pragma unroll
+  for (int y = 0; y < TN; ++y) fw[0][y] = w_piece(b0, 0, y);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int x = 0; x < TM; ++x) fa[h][x] = a_piece(a0, 0, h, x);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Iteration t (stage t % 3 in A, B; the next stage in An, Bn): slice 1's
-  // fragments are read while slice 0's MFMAs run; then, once this wave's
-  // reads of stage t and its loads of step t + 1 are done, one barrier: every
-  // wave is past stage t (the loads of step t + 3 may overwrite it) and step
-  // t + 1 has landed everywhere, so slice 0 of step t + 1 is read while slice
-  // 1's MFMAs run.  No wave waits on LDS right after the barrier.  Steps past
-  // the end are read (into registers never used) but not loaded.
-  auto iter = [&](uint8_t* A, uint8_t* B, const uint8_t* An, const uint8_t* Bn, int kt) {
-    read_slice(A, B, 1, f1);
-    mfma_slice(f0);
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  // Step t: slice 0's MFMAs read slice 1; then, once this wave's reads of
+  // stage t and its loads of step t + 1 are done, the barrier; the loads of
+  // step t + 3 go into stage t; slice 1's MFMAs read slice 0 of step t + 1
+  // (after the last step: stale fragments, never used).
+  auto iter = [&](uint8_t* A, uint8_t* B, const uint8_t* An, const uint8_t* Bn, int kt) __attribute__((always_inline)) {
+    mma_read(C0{}, A, B, 1);
     __builtin_amdgcn_sched_barrier(0);
-    // this wave's loads of step t + 1 (those of t + 2 may stay in flight) and its reads of stage t
-    if (kt + 2 < nk)
-      wait_vm_lds<kLoads>();
-    else
-      wait_vm_lds<0>();
-    __builtin_amdgcn_s_barrier();
+    if (kt + 1 < nk) {
+      if (kt + 2 < nk)
+        wait_vm_lds<kLoads>();
+      else
+        wait_vm_lds<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 3 < nk) issue(A, B, kt + 3);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 3 < nk) issue(A, B, kt + 3);
-    __builtin_amdgcn_sched_barrier(0);
-    read_slice(An, Bn, 0, f0);
-    mfma_slice(f1);
+    mma_read(C1{}, An, Bn, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // whole ring cycles without branches around the MFMAs, then the tail
   int kt = 0;
   for (; kt + kStages <= nk; kt += kStages) {
     iter(a0, b0, a1, b1, kt);
@@ -295,7 +391,14 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
   if (kt < nk) iter(a0, b0, a1, b1, kt);
   if (kt + 1 < nk) iter(a1, b1, a2, b2, kt + 1);
   wait_vm<0>();
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
+  if (epi_lds_ok(a)) {
+    __syncthreads();  // every wave is done with the stages
+    constexpr int E = TM * TN * 32 * 32 * 2;
+    uint8_t* region = epi_region<E, A_BYTES, B_BYTES, 3, WAVES>(wave, a0, a1, a2, b0, b1, b2);
+    tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, nullptr);
+  } else {
+    tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -431,32 +534,45 @@ __device__ inline void ring_tile_body(const StreamArgs& a, int64_t tile, int64_t
   if (kt < nk) step(a0, b0, a3, b3, kt);
   if (kt + 1 < nk) step(a1, b1, a0, b0, kt + 1);
   if (kt + 2 < nk) step(a2, b2, a1, b1, kt + 2);
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, tok_scale);
+  wait_vm<0>();
+  if (epi_lds_ok(a)) {
+    __syncthreads();  // every wave is done with the stages
+    // one 16 KB X stage per wave block (BN = 256: 16 KB W stages for waves 4 .. 7)
+    constexpr int E = TM * TN * 32 * 32 * 2;
+    static_assert(E == A_BYTES && (WAVES <= 4 || E == B_BYTES), "one stage per wave block");
+    const int q = wave & 3;
+    uint8_t* region = wave < 4 ? (q == 0 ? a0 : q == 1 ? a1 : q == 2 ? a2 : a3)
+                               : (q == 0 ? b0 : q == 1 ? b1 : q == 2 ? b2 : b3);
+    tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, tok_scale);
+  } else {
+    tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, tok_scale);
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Both operands in double steps of 128 bytes per row (128 K of FP8 codes for
-// FP8 weights with FP8 activations, 64 K of BF16 for BF16 weights and
-// activations), so each buffer-to-LDS load fills 8 whole 128-byte lines
-// (1 KB) instead of 16 half lines: half the requests per byte of the 64-byte
-// rows of the ring kernel below.  (Measured on MI355X: the 64-K kernel is bound by
-// these loads -- with them removed it runs twice as fast, while removing its
-// MFMAs or its fragment reads changes nothing -- and the double steps take
-// the FP8-activation MLP from 1.39 to 1.08 ms at 4096 tokens and from 5.50
-// to 4.08 ms at 16384; for BF16 the sharded-matmul GEMMs gain 8-11%.)  NST
-// double stages in LDS (2 for 256-row tiles, 3 for 128-row ones), loads
-// NST - 1 double steps ahead; the layout is the 128-byte row swizzle swz() of
-// the FP8-weight kernel's X.  Within a double step of FP8, MFMA slice s
-// (0, 1) takes K = 64s .. 64s + 63: lane group g reads pieces 4s + 2g and
-// 4s + 2g + 1 of its row in both operands; of BF16, slice s (0 .. 3) takes
-// K = 16s .. 16s + 15 and lane group g reads piece 2s + g.
-template <int BN, int WAVES, int NST, bool F8 = true, int BM = kTileM>
-__device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
+// FP8 weights with FP8 activations here, 64 K of BF16 for BF16 weights and
+// activations in bf16_dstep_body below), so each buffer-to-LDS load fills 8
+// whole 128-byte lines (1 KB) instead of 16 half lines: half the requests per
+// byte of the 64-byte rows of the ring kernel above.  (Measured on MI355X:
+// the 64-K kernel is bound by these loads -- with them removed it runs twice
+// as fast, while removing its MFMAs or its fragment reads changes nothing --
+// and the double steps take the FP8-activation MLP from 1.39 to 1.08 ms at
+// 4096 tokens and from 5.50 to 4.08 ms at 16384; for BF16 the sharded-matmul
+// GEMMs gain 8-11%.)  NST double stages in LDS (2 for 256-row tiles, 3 for
+// 128-row ones), loads NST - 1 double steps ahead; the layout is the 128-byte
+// row swizzle swz() of the FP8-weight kernel's X.  Within a double step, MFMA
+// slice s (0, 1) takes K = 64s .. 64s + 63: lane group g reads pieces 4s + 2g
+// and 4s + 2g + 1 of its row in both operands.  (The slice pipeline of the
+// BF16 body, written out the same way here, needs 64 more registers than the
+// eight waves have and spills: measured 9-12% slower.)
+template <int BN, int WAVES, int NST, int BM = kTileM>
+__device__ inline void f8f8_dstep_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
   constexpr int TM = BM / 64;  // two rows of waves along the tokens
   constexpr int TN = WN / 32;
-  constexpr int DK = 128;                     // bytes of a row per double step (128 / EB elements)
+  constexpr int DK = 128;                     // bytes (FP8 codes) of a row per double step
   constexpr int A_BYTES = BM * DK;             // 32 KB for 256 tokens
   constexpr int B_BYTES = BN * DK;
   constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per double step
@@ -467,8 +583,7 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
   __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[NST > 2 ? A_BYTES : 1024];
   __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[NST > 2 ? B_BYTES : 1024];
   __shared__ __attribute__((aligned(4096))) float row_scale[BN];
-  __shared__ float tok_scale[F8 ? BM : 1];
-  constexpr int EB = F8 ? 1 : 2;  // bytes per element of both operands
+  __shared__ float tok_scale[BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -480,11 +595,10 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
     const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
     row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
   }
-  if constexpr (F8)
-    for (int c = tid; c < BM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
+  for (int c = tid; c < BM; c += 64 * WAVES) tok_scale[c] = m0 + c < a.M ? a.xscale[m0 + c] : 0.f;
 
-  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * EB);
-  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * EB);
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K);
   // a load fills rows 8i .. 8i + 7 of the stage: lane l writes slot l % 8 of
   // row l / 8, which holds piece (l % 8) ^ ((row >> 1) & 7) of that row
   int aoff[NA], boff[NB];
@@ -493,14 +607,14 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
     const int row = (wave * NA + i) * 8 + lane / 8;
     const int q = (lane % 8) ^ ((row >> 1) & 7);
     const int64_t m = min(m0 + row, a.M - 1);
-    aoff[i] = int(m * a.ldx * EB + q * 16);
+    aoff[i] = int(m * a.ldx + q * 16);
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int row = (wave * NB + i) * 8 + lane / 8;
     const int q = (lane % 8) ^ ((row >> 1) & 7);
     const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
-    boff[i] = int(r * a.K * EB + q * 16);
+    boff[i] = int(r * a.K + q * 16);
   }
   auto issue = [&](uint8_t* A, uint8_t* B, int kd) {
 #pragma unroll
@@ -522,25 +636,6 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
     return i32x8{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
   };
   auto compute = [&](const uint8_t* A, const uint8_t* B) {
-    if constexpr (!F8) {
-      // BF16: four 16-K slices; lane group g reads piece 2s + g of its row
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 fa[TM], fb[TN];
-#pragma unroll
-        for (int x = 0; x < TM; ++x)
-          fa[x] = *reinterpret_cast<const bf16x8*>(A + swz(wm * (BM / 2) + x * 32 + r32, 2 * s + kg) * 16);
-#pragma unroll
-        for (int y = 0; y < TN; ++y)
-          fb[y] = *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
-#pragma unroll
-        for (int x = 0; x < TM; ++x)
-#pragma unroll
-          for (int y = 0; y < TN; ++y)
-            acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
-      }
-      return;
-    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       i32x8 fa[TM], fb[TN];
@@ -557,7 +652,7 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
   };
 
   constexpr int kLoads = NA + NB;  // loads per wave per double step
-  const int nd = int(a.K * EB / DK);
+  const int nd = int(a.K / DK);
   // prologue: double steps 0 .. NST - 2 in flight
   issue(a0, b0, 0);
   if (NST > 2 && nd > 1) issue(a1, b1, 1);
@@ -593,17 +688,205 @@ __device__ inline void dstep_tile_body(const StreamArgs& a, int64_t tile, int64_
     if (kd < nd) step(a0, b0, a2, b2, kd);
     if (kd + 1 < nd) step(a1, b1, a0, b0, kd + 1);
   }
-  tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, F8 ? tok_scale : nullptr);
+  wait_vm<0>();
+  if (epi_lds_ok(a)) {
+    __syncthreads();  // every wave is done with the stages
+    constexpr int E = TM * TN * 32 * 32 * 2;
+    uint8_t* region = epi_region<E, A_BYTES, B_BYTES, NST, WAVES>(wave, a0, a1, a2, b0, b1, b2);
+    tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, tok_scale);
+  } else {
+    tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale, tok_scale);
+  }
+}
+
+// BF16 weights and BF16 activations in double steps of 64 K (128-byte rows,
+// as above), slice-pipelined: the double step's four 16-K MFMA slices (lane
+// group g reads piece 2s + g of its row in slice s) are written out so that
+// each MFMA is followed by its share of the next slice's fragment reads -- the
+// W fragments into a second register set, each X fragment right after its
+// last MFMA of the slice -- and scheduling barriers keep that order (MFMAs and
+// LDS reads; address arithmetic moves freely).  The step's barrier sits before
+// the last slice's MFMAs, whose fragments are already in registers; right
+// after it the wave issues the loads of step d + NST into the stage it has
+// just finished and reads slice 0 of step d + 1 while those MFMAs run.  Left
+// to itself the compiler reads each slice's fragments just before its MFMAs
+// and waits on them every two MFMAs (measured on MI355X: this order is 3-8%
+// faster on the prefill and sharded-matmul GEMMs, and the LDS-staged
+// epilogue another 4-9%).
+template <int BN, int WAVES, int NST>
+__device__ inline void bf16_dstep_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
+  constexpr int BM = kTileM;
+  constexpr int WGN = WAVES / 2;
+  constexpr int WN = BN / WGN;
+  constexpr int TM = BM / 64;  // two rows of waves along the tokens
+  constexpr int TN = WN / 32;
+  constexpr int DK = 128;       // bytes of a row per double step (64 K)
+  constexpr int A_BYTES = BM * DK;
+  constexpr int B_BYTES = BN * DK;
+  constexpr int NA = A_BYTES / 1024 / WAVES;  // 1 KB loads of X per wave per double step
+  constexpr int NB = B_BYTES / 1024 / WAVES;
+  static_assert(TN >= 1 && NA >= 1 && NB >= 1 && NA * 1024 * WAVES == A_BYTES && NB * 1024 * WAVES == B_BYTES,
+                "stage must split into whole 1 KB loads per wave");
+  static_assert(NST == 2 || NST == 3, "two or three double stages");
+  __shared__ __attribute__((aligned(1024))) uint8_t a0[A_BYTES], a1[A_BYTES], a2[NST > 2 ? A_BYTES : 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t b0[B_BYTES], b1[B_BYTES], b2[NST > 2 ? B_BYTES : 1024];
+  __shared__ __attribute__((aligned(4096))) float row_scale[BN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave / WGN, wn = wave % WGN;
+  const TileCoord tc = tile_coord<BN, BM>(a, tile, ntiles);
+  const int64_t m0 = tc.m0;
+  for (int c = tid; c < BN; c += 64 * WAVES) {
+    const int64_t r = w_row<BN, WN>(a, tc.tile_n, c);
+    row_scale[c] = (a.scale && r < a.rows) ? a.scale[r] : 1.f;
+  }
+
+  const u32x4s xres = raw_rsrc(a.X, a.M * a.ldx * 2);
+  const u32x4s wres = raw_rsrc(a.W, a.rows * a.K * 2);
+  // a load fills rows 8i .. 8i + 7 of the stage: lane l writes slot l % 8 of
+  // row l / 8, which holds piece (l % 8) ^ ((row >> 1) & 7) of that row
+  int aoff[NA], boff[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int row = (wave * NA + i) * 8 + lane / 8;
+    const int q = (lane % 8) ^ ((row >> 1) & 7);
+    const int64_t m = min(m0 + row, a.M - 1);
+    aoff[i] = int(m * a.ldx * 2 + q * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int row = (wave * NB + i) * 8 + lane / 8;
+    const int q = (lane % 8) ^ ((row >> 1) & 7);
+    const int64_t r = min(w_row<BN, WN>(a, tc.tile_n, row), a.rows - 1);
+    boff[i] = int(r * a.K * 2 + q * 16);
+  }
+  // (the lambdas are forced inline: out of line, the stage pointers would
+  // lose their address space and the accumulators would live in memory)
+  auto issue = [&](uint8_t* A, uint8_t* B, int kd) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) lds_load16<false>(xres, A + (wave * NA + i) * 1024, aoff[i], kd * DK);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) lds_load16<true>(wres, B + (wave * NB + i) * 1024, boff[i], kd * DK);
+  };
+
+  const int r32 = lane & 31, kg = lane >> 5;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int x = 0; x < TM; ++x)
+#pragma unroll
+    for (int y = 0; y < TN; ++y) acc[x][y] = f32x16{};
+
+  // X fragments in one set, W fragments in two (current, next slice)
+  bf16x8 fa[TM], fb[2][TN];
+  auto a_frag = [&](const uint8_t* A, int s, int x) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(A + swz(wm * (BM / 2) + x * 32 + r32, 2 * s + kg) * 16);
+  };
+  auto b_frag = [&](const uint8_t* B, int s, int y) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8*>(B + swz(wn * WN + y * 32 + r32, 2 * s + kg) * 16);
+  };
+  // The MFMAs of the current slice (W fragments in set c, a compile-time
+  // constant so that the sets stay in registers), reading slice s_next of
+  // stage (A, B): W fragment y after MFMA y, X fragment x after its last MFMA.
+  auto mma_read = [&](auto cc, const uint8_t* A, const uint8_t* B, int s_next) __attribute__((always_inline)) {
+    constexpr int c = decltype(cc)::value;
+#pragma unroll
+    for (int x = 0; x < TM; ++x) {
+#pragma unroll
+      for (int y = 0; y < TN; ++y) {
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[c][y], acc[x][y], 0, 0, 0);
+        const int i = x * TN + y;
+        if (i < TN) fb[1 - c][i] = b_frag(B, s_next, i);
+        __builtin_amdgcn_sched_barrier(0x0006);
+      }
+      fa[x] = a_frag(A, s_next, x);
+      __builtin_amdgcn_sched_barrier(0x0006);
+    }
+  };
+
+  constexpr int kLoads = NA + NB;  // loads per wave per double step
+  const int nd = int(a.K * 2 / DK);
+  // prologue: double steps 0 .. NST - 1 in flight, step 0 landed everywhere,
+  // slice 0 of step 0 in registers
+  issue(a0, b0, 0);
+  if (nd > 1) issue(a1, b1, 1);
+  if (NST > 2 && nd > 2) issue(a2, b2, 2);
+  if (nd >= NST)
+    wait_vm<(NST - 1) * kLoads>();
+  else if (nd == 2)
+    wait_vm<kLoads>();
+  else
+    wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int x = 0; x < TM; ++x) fa[x] = a_frag(a0, 0, x);
+#pragma unroll
+  for (int y = 0; y < TN; ++y) fb[0][y] = b_frag(b0, 0, y);
+  __builtin_amdgcn_sched_barrier(0);
+
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  // Double step d in stage (A, B); (An, Bn) holds step d + 1.  Slices 0..2
+  // each read the next; then, once this wave's loads of step d + 1 have
+  // landed (with three stages those of d + 2 may stay in flight) and its
+  // reads of stage d are done, the barrier: every wave is past stage d (the
+  // loads of step d + NST may overwrite it) and step d + 1 has landed
+  // everywhere.  Slice 3 reads slice 0 of step d + 1 (after the last step:
+  // stale fragments, never used -- no branch around the MFMAs, which would
+  // merge two copies of the accumulators).
+  auto step = [&](uint8_t* A, uint8_t* B, const uint8_t* An, const uint8_t* Bn, int kd) __attribute__((always_inline)) {
+    mma_read(C0{}, A, B, 1);
+    mma_read(C1{}, A, B, 2);
+    mma_read(C0{}, A, B, 3);
+    if (kd + 1 < nd) {
+      if (NST > 2 && kd + 2 < nd)
+        wait_vm_lds<kLoads>();
+      else
+        wait_vm_lds<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kd + NST < nd) issue(A, B, kd + NST);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma_read(C1{}, An, Bn, 0);
+  };
+  int kd = 0;
+  if constexpr (NST == 2) {
+    for (; kd + 2 <= nd; kd += 2) {
+      step(a0, b0, a1, b1, kd);
+      step(a1, b1, a0, b0, kd + 1);
+    }
+    if (kd < nd) step(a0, b0, a1, b1, kd);
+  } else {
+    for (; kd + 3 <= nd; kd += 3) {
+      step(a0, b0, a1, b1, kd);
+      step(a1, b1, a2, b2, kd + 1);
+      step(a2, b2, a0, b0, kd + 2);
+    }
+    if (kd < nd) step(a0, b0, a1, b1, kd);
+    if (kd + 1 < nd) step(a1, b1, a2, b2, kd + 1);
+  }
+  wait_vm<0>();
+  if (epi_lds_ok(a)) {
+    __syncthreads();  // every wave is done with the stages
+    constexpr int E = TM * TN * 32 * 32 * 2;
+    uint8_t* region = epi_region<E, A_BYTES, B_BYTES, NST, WAVES>(wave, a0, a1, a2, b0, b1, b2);
+    tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, nullptr);
+  } else {
+    tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
+  }
 }
 
 template <int BN, int WAVES, int NST, int BM = kTileM>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8d_kernel(StreamArgs a) {
-  dstep_tile_body<BN, WAVES, NST, true, BM>(a, blockIdx.x, gridDim.x);
+  f8f8_dstep_body<BN, WAVES, NST, BM>(a, blockIdx.x, gridDim.x);
 }
 
 template <int BN, int WAVES, int NST>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16d_kernel(StreamArgs a) {
-  dstep_tile_body<BN, WAVES, NST, false>(a, blockIdx.x, gridDim.x);
+  bf16_dstep_body<BN, WAVES, NST>(a, blockIdx.x, gridDim.x);
 }
 
 template <int BN, int WAVES, int BM = kTileM>
@@ -630,7 +913,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_group_kernel(TileGroup tg)
   if constexpr (FP8)
     fp8_tile_body<BN, WAVES>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
   else
-    dstep_tile_body<BN, WAVES, BN == 256 ? 2 : 3, false>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
+    bf16_dstep_body<BN, WAVES, BN == 256 ? 2 : 3>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
 }
 
 int64_t tile_count(const StreamArgs& a, int bn, int bm = kTileM) {

@@ -277,6 +277,27 @@ def test_tiled_prefill_parity(o, k, dt, m):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+@pytest.mark.parametrize("o,pad", [(1000, 64), (1004, 64), (1000, 4)])
+def test_tiled_strided_output(o, pad, dt):
+    """Tiled kernels writing into Y rows of ldy = out + pad: with ldy a multiple
+    of 8 the outputs leave through LDS in 16-byte stores (out = 1004 ends in a
+    partial 8-column piece), otherwise one element per store.  Nothing past
+    column out of a row is written."""
+    k, m = 192, 300
+    note(f"tiled strided output o={o} pad={pad} {dt} m={m}")
+    w = synth.weight(synth.seed_for(14, 3, o % 89), o, k, dt)
+    x = synth.activations(synth.seed_for(14, 3, 50), m, k)
+    y = torch.full((m, o + pad), float("nan"), dtype=torch.bfloat16, device=DEV)
+    swr.proj_forward(u8(w.raw()), dt, f32(w.scale) if w.scale is not None else None, o, k, bf16(x), y, m=m,
+                     ldx=k, ldy=o + pad)
+    torch.cuda.synchronize()
+    yv = values(y)
+    assert np.isnan(yv[:, o:]).all(), "columns past out_f were written"
+    ref = gemm.proj_f64(x, w.raw(), dt, o, k, w.scale)
+    assert_close_rows(yv[:, :o], ref, what=f"tiled strided {o}x{k} {dt} m={m} ldy={o + pad}")
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
 def test_tiled_last_wave_in_half_tiles(dt):
     """2048 tokens x 16484 rows: 8 x 65 = 520 tiles of 256 x 256, a last wave
     of 8 on 256 CUs, so the first 16384 rows run as 512 full tiles and the
