@@ -1006,6 +1006,31 @@ hipError_t launch_tile_group(const StreamArgs* as, int n, int bn, bool fp8, hipS
   return fp8 ? launch_group<128, 4, true>(tail, stream) : launch_group<128, 4, false>(tail, stream);
 }
 
+// Where 128-token x 256-row tiles were chosen because 256 x 256 tiles fill
+// less than two waves of workgroups, and the last wave of 256 x 256 tiles is
+// at most half full: the weight rows whose 256 x 256 tiles make whole waves
+// (the first columns of tiles).  The other columns then run as 128-token
+// tiles, at most one more wave.  0 where this does not apply.
+static int64_t whole_wave_rows(const StreamArgs& p) {
+  if (p.mode == OUT_SILU_BF16) return 0;
+  const int64_t tiles_m = (p.M + kTileM - 1) / kTileM;
+  const int64_t tiles_n = (p.rows + 255) / 256;
+  const int64_t rem = (tiles_m * tiles_n) % 256;
+  if (tiles_m * tiles_n <= 256 || rem == 0 || rem > 128 || rem % tiles_m != 0) return 0;
+  return (tiles_n - rem / tiles_m) * 256;
+}
+
+// p restricted to weight rows r0 ..: the weights, scales and output columns
+// from row r0 on
+static StreamArgs rows_from(const StreamArgs& p, int64_t r0, int64_t w_elem, int64_t y_elem) {
+  StreamArgs q = p;
+  q.W = p.W + r0 * p.K * w_elem;
+  q.rows = p.rows - r0;
+  q.scale = p.scale ? p.scale + r0 : nullptr;
+  q.Y = static_cast<uint8_t*>(p.Y) + r0 * y_elem;
+  return q;
+}
+
 hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t stream) {
   // The kernels address X through 32-bit buffer offsets: tokens go in parts
   // whose X spans less than 2 GiB (whole 256-token tiles).
@@ -1026,11 +1051,21 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
         // 128-K double steps: whole 128-byte lines per load
         if (bn == 256)
           hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 2>), tile_grid<256>(p), dim3(512), 0, stream, p);
-        else if (tile_count(p, 256, 128) >= 512)
-          // 128 tokens x 256 weight rows, eight waves (as for FP8 weights)
-          hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 3, 128>), (tile_grid<256, 128>(p)), dim3(512), 0, stream,
-                             p);
-        else
+        else if (tile_count(p, 256, 128) >= 512) {
+          // 128 tokens x 256 weight rows, eight waves (as for FP8 weights),
+          // after whole waves of 256 x 256 tiles where they fit
+          const int64_t rows1 = whole_wave_rows(p);
+          StreamArgs p2 = p;
+          if (rows1 > 0) {
+            StreamArgs p1 = p;
+            p1.rows = rows1;
+            hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 2>), tile_grid<256>(p1), dim3(512), 0, stream, p1);
+            p2 = rows_from(p, rows1, 1, y_elem);
+          }
+          if (hipPeekAtLastError() == hipSuccess)
+            hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<256, 8, 3, 128>), (tile_grid<256, 128>(p2)), dim3(512), 0,
+                               stream, p2);
+        } else
           hipLaunchKernelGGL((tile_gemm_f8f8d_kernel<128, 4, 3>), tile_grid<128>(p), dim3(256), 0, stream, p);
         e = hipGetLastError();
       } else {
@@ -1062,20 +1097,28 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
       p1.rows = rows1;
       e = fp8 ? launch_fp8<256, 8>(p1, stream) : launch_bf16d<256, 8, 2>(p1, stream);
       if (e == hipSuccess && rows1 < p.rows) {
-        StreamArgs p2 = p;
-        p2.W = p.W + rows1 * p.K * (fp8 ? 1 : 2);
-        p2.rows = p.rows - rows1;
-        p2.scale = p.scale ? p.scale + rows1 : nullptr;
-        p2.Y = static_cast<uint8_t*>(p.Y) + rows1 * y_elem;
+        const StreamArgs p2 = rows_from(p, rows1, fp8 ? 1 : 2, y_elem);
         e = fp8 ? launch_fp8<128, 4>(p2, stream) : launch_bf16d<128, 4, 3>(p2, stream);
       }
     } else if (fp8 && tile_count(p, 256, 128) >= 512) {
       // 128 tokens x 256 weight rows, eight waves of 64 x 64: per FLOP 20%
       // fewer bytes loaded into LDS than 256 x 128 (the BF16 X, twice the
       // bytes of the FP8 W, is the shorter side), and two waves per SIMD
-      // (measured on the 4096-token down GEMM: 1065 against 1000 TFLOP/s)
-      hipLaunchKernelGGL((tile_gemm_fp8_kernel<256, 8, 128>), (tile_grid<256, 128>(p)), dim3(512), 0, stream, p);
-      e = hipGetLastError();
+      // (measured on the 4096-token down GEMM: 1065 against 1000 TFLOP/s).
+      // Whole waves of 256 x 256 tiles first where they fit.
+      const int64_t rows1 = whole_wave_rows(p);
+      StreamArgs p2 = p;
+      e = hipSuccess;
+      if (rows1 > 0) {
+        StreamArgs p1 = p;
+        p1.rows = rows1;
+        e = launch_fp8<256, 8>(p1, stream);
+        p2 = rows_from(p, rows1, 1, y_elem);
+      }
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL((tile_gemm_fp8_kernel<256, 8, 128>), (tile_grid<256, 128>(p2)), dim3(512), 0, stream, p2);
+        e = hipGetLastError();
+      }
     } else
       e = fp8 ? launch_fp8<128, 4>(p, stream) : launch_bf16d<128, 4, 3>(p, stream);
     if (e != hipSuccess) return e;
