@@ -48,6 +48,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTileM = 256;
+
+// SiLU for the tile epilogues: z * (1 / (1 + e^-z)) with the hardware
+// reciprocal (1 ulp) rather than an IEEE division, a few fp32 ulps from the
+// exact value and far inside the BF16 rounding of the output (measured on
+// MI355X: the division was about 2% of the FP8-activation prefill MLP).
+// Saturates correctly: e^-z = inf gives -0, e^-z = 0 gives z.
+__device__ inline float silu_tile(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 constexpr int kGroupM = 4;  // token blocks per XCD group
 
 __device__ inline int swz(int row, int piece) { return row * 8 + (piece ^ ((row >> 1) & 7)); }
@@ -122,7 +129,7 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
         float out = acc[x][y][v] * ts * sc;
         if (silu_mode) {
           const float u = acc[x][y + TN / 2][v] * ts * su;
-          out = silu(out) * u;
+          out = silu_tile(out) * u;
           static_cast<uint16_t*>(a.Y)[m * a.ldy + ocol] = bf16_bits(out);
         } else if (a.mode == OUT_F32) {
           static_cast<float*>(a.Y)[m * a.ldy + ocol] = out;
@@ -167,7 +174,7 @@ __device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc
         const int row = x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
         const float ts = lds_tscale ? lds_tscale[wm * ROWS + row] : 1.f;
         float out = acc[x][y][v] * ts * sc;
-        if (silu_mode) out = silu(out) * (acc[x][y + TN / 2][v] * ts * su);
+        if (silu_mode) out = silu_tile(out) * (acc[x][y + TN / 2][v] * ts * su);
         *reinterpret_cast<uint16_t*>(region + pos(row, y * 32 + r32)) = bf16_bits(out);
       }
     }
