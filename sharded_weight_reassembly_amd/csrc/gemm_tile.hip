@@ -7,8 +7,9 @@
 // into LDS more than by the matrix cores):
 //   * a workgroup computes a BM-token x BN-row tile of Y (BM = 256, or 128
 //     for FP8 weights where 256 x 256 tiles would not fill two waves of
-//     workgroups) with 2 x WAVES/2 waves; each wave a BM/2 x (2*BN/WAVES)
-//     sub-tile with
+//     workgroups -- then only for the weight rows past whole waves of
+//     256 x 256 tiles) with 2 x WAVES/2 waves; each wave a BM/2 x
+//     (2*BN/WAVES) sub-tile with
 //     v_mfma_f32_32x32x16_bf16 (tokens are the MFMA rows, weight rows the
 //     MFMA columns, so a lane's outputs run along a row of Y);
 //   * both operands go from memory straight into an LDS ring with
@@ -48,6 +49,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTileM = 256;
+constexpr int kGroupM = 4;  // token blocks per XCD group
 
 // SiLU for the tile epilogues: z * (1 / (1 + e^-z)) with the hardware
 // reciprocal (1 ulp) rather than an IEEE division, a few fp32 ulps from the
@@ -55,7 +57,6 @@ constexpr int kTileM = 256;
 // MI355X: the division was about 2% of the FP8-activation prefill MLP).
 // Saturates correctly: e^-z = inf gives -0, e^-z = 0 gives z.
 __device__ inline float silu_tile(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
-constexpr int kGroupM = 4;  // token blocks per XCD group
 
 __device__ inline int swz(int row, int piece) { return row * 8 + (piece ^ ((row >> 1) & 7)); }
 
