@@ -202,6 +202,84 @@ __device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc
   }
 }
 
+// As tile_epilogue_lds, for fp32 outputs (F32 = true; the split-K
+// partials of a K-sharded product): twice the bytes, so in two passes of
+// TM / 2 row tiles each through the same region.  (Written for either
+// element size, but used for fp32 only: the BF16 kernels keep the leaner
+// function above.)
+template <int BN, int WN, int TM, int TN, bool F32>
+__device__ inline void tile_epilogue_lds_t(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0,
+                                           int64_t tile_n, int wm, int wn, int r32, int kg, int lane, uint8_t* region,
+                                           const float* lds_scale, const float* lds_tscale) {
+  const bool silu_mode = !F32 && a.mode == OUT_SILU_BF16;
+  constexpr bool f32_out = F32;
+  constexpr int ROWS = TM * 32;
+  static_assert(TM % 2 == 0, "fp32 outputs go in two halves of the row tiles");
+  // output columns of the block: TN * 32, or TN * 16 in SiLU mode
+  const int cols = silu_mode ? TN * 16 : TN * 32;
+  constexpr int eb = F32 ? 4 : 2;      // bytes per output
+  constexpr int epp = 16 / eb;          // outputs per 16-byte piece
+  const int cpr = cols / epp;           // pieces per row (a power of two)
+  const int64_t limit = silu_mode ? a.inter : a.rows;
+  const int64_t col0 = silu_mode ? tile_n * (BN / 2) + wn * (WN / 2) : tile_n * BN + wn * WN;
+  const int tn_out = silu_mode ? TN / 2 : TN;
+  constexpr int passes = F32 ? 2 : 1;
+  constexpr int xs = TM / passes;       // row tiles per pass
+  auto pos = [&](int row, int col) {
+    return row * cols * eb + (((col / epp) ^ (row & (cpr - 1))) << 4) + (col % epp) * eb;
+  };
+#pragma unroll
+  for (int pass = 0; pass < passes; ++pass) {
+    if (pass > 0) {
+      // this wave's reads of the first half are done before it is overwritten
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int y = 0; y < TN; ++y) {
+      if (y >= tn_out) break;
+      const int c = wn * WN + y * 32 + r32;  // local B row
+      const float sc = lds_scale[c];
+      const float su = silu_mode ? lds_scale[c + WN / 2] : 1.f;
+#pragma unroll
+      for (int x = 0; x < TM; ++x) {
+        if (x / (TM / 2) != pass && f32_out) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);  // row in the wave's block
+          const int prow = row - pass * xs * 32;                     // row in this pass
+          const float ts = lds_tscale ? lds_tscale[wm * ROWS + row] : 1.f;
+          float out = acc[x][y][v] * ts * sc;
+          if (silu_mode) out = silu_tile(out) * (acc[x][y + TN / 2][v] * ts * su);
+          if (f32_out)
+            *reinterpret_cast<float*>(region + pos(prow, y * 32 + r32)) = out;
+          else
+            *reinterpret_cast<uint16_t*>(region + pos(prow, y * 32 + r32)) = bf16_bits(out);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_wave_barrier();
+    uint8_t* Y = static_cast<uint8_t*>(a.Y);
+    const int pieces = xs * 32 * cpr;
+    for (int q = lane; q < pieces; q += 64) {
+      const int prow = q / cpr, cp = q % cpr;
+      const int64_t m = m0 + wm * ROWS + pass * xs * 32 + prow;
+      const int64_t col = col0 + cp * epp;
+      if (m >= a.M || col >= limit) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(region + prow * cols * eb + ((cp ^ (prow & (cpr - 1))) << 4));
+      uint8_t* dst = Y + (m * a.ldy + col) * eb;
+      if (col + epp <= limit) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const uint8_t* h = reinterpret_cast<const uint8_t*>(&v);
+        for (int e = 0; e < epp && col + e < limit; ++e)
+          for (int b = 0; b < eb; ++b) dst[e * eb + b] = h[e * eb + b];
+      }
+    }
+  }
+}
+
 // The E-byte slot of LDS stage memory that holds wave w's output block in the
 // epilogue: the slots of a0, a1, [a2], b0, b1, [b2] in turn.
 template <int E, int SA, int SB, int NS, int WAVES>
@@ -228,6 +306,11 @@ __device__ inline uint8_t* epi_region(int w, uint8_t* a0, uint8_t* a1, uint8_t* 
 // 16-byte aligned.
 __device__ inline bool epi_lds_ok(const StreamArgs& a) {
   return a.mode != OUT_F32 && (a.ldy % 8) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
+}
+
+// The same for fp32 outputs (the kernels' F32OUT instantiations).
+__device__ inline bool epi_lds_ok_f32(const StreamArgs& a) {
+  return a.mode == OUT_F32 && (a.ldy % 4) == 0 && (reinterpret_cast<uintptr_t>(a.Y) % 16) == 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -260,7 +343,7 @@ constexpr int kStages = 3;
 
 __device__ inline int wswz(int row, int q) { return row * 4 + (q ^ ((row >> 2) & 3)); }
 
-template <int BN, int WAVES, int BM = kTileM>
+template <int BN, int WAVES, int BM = kTileM, bool F32OUT = false>
 __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int WGN = WAVES / 2;
   constexpr int WN = BN / WGN;
@@ -402,11 +485,15 @@ __device__ inline void fp8_tile_body(const StreamArgs& a, int64_t tile, int64_t 
   if (kt < nk) iter(a0, b0, a1, b1, kt);
   if (kt + 1 < nk) iter(a1, b1, a2, b2, kt + 1);
   wait_vm<0>();
-  if (epi_lds_ok(a)) {
+  if (F32OUT ? epi_lds_ok_f32(a) : epi_lds_ok(a)) {
     __syncthreads();  // every wave is done with the stages
     constexpr int E = TM * TN * 32 * 32 * 2;
     uint8_t* region = epi_region<E, A_BYTES, B_BYTES, 3, WAVES>(wave, a0, a1, a2, b0, b1, b2);
-    tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, nullptr);
+    if constexpr (F32OUT)
+      tile_epilogue_lds_t<BN, WN, TM, TN, true>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale,
+                                                nullptr);
+    else
+      tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, nullptr);
   } else {
     tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
   }
@@ -724,7 +811,7 @@ __device__ inline void f8f8_dstep_body(const StreamArgs& a, int64_t tile, int64_
 // and waits on them every two MFMAs (measured on MI355X: this order is 3-8%
 // faster on the prefill and sharded-matmul GEMMs, and the LDS-staged
 // epilogue another 4-9%).
-template <int BN, int WAVES, int NST>
+template <int BN, int WAVES, int NST, bool F32OUT = false>
 __device__ inline void bf16_dstep_body(const StreamArgs& a, int64_t tile, int64_t ntiles) {
   constexpr int BM = kTileM;
   constexpr int WGN = WAVES / 2;
@@ -880,11 +967,15 @@ __device__ inline void bf16_dstep_body(const StreamArgs& a, int64_t tile, int64_
     if (kd + 1 < nd) step(a1, b1, a2, b2, kd + 1);
   }
   wait_vm<0>();
-  if (epi_lds_ok(a)) {
+  if (F32OUT ? epi_lds_ok_f32(a) : epi_lds_ok(a)) {
     __syncthreads();  // every wave is done with the stages
     constexpr int E = TM * TN * 32 * 32 * 2;
     uint8_t* region = epi_region<E, A_BYTES, B_BYTES, NST, WAVES>(wave, a0, a1, a2, b0, b1, b2);
-    tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, nullptr);
+    if constexpr (F32OUT)
+      tile_epilogue_lds_t<BN, WN, TM, TN, true>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale,
+                                                nullptr);
+    else
+      tile_epilogue_lds<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, lane, region, row_scale, nullptr);
   } else {
     tile_epilogue<BN, WN, TM, TN>(a, acc, m0, tc.tile_n, wm, wn, r32, kg, row_scale);
   }
@@ -895,14 +986,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8d_kernel(StreamAr
   f8f8_dstep_body<BN, WAVES, NST, BM>(a, blockIdx.x, gridDim.x);
 }
 
-template <int BN, int WAVES, int NST>
+// (F32OUT: the instantiation for fp32 outputs, whose epilogue stages them
+// through LDS in two halves; kept apart, the BF16-output kernels do not
+// carry its registers -- measured 3% faster)
+template <int BN, int WAVES, int NST, bool F32OUT = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_bf16d_kernel(StreamArgs a) {
-  bf16_dstep_body<BN, WAVES, NST>(a, blockIdx.x, gridDim.x);
+  bf16_dstep_body<BN, WAVES, NST, F32OUT>(a, blockIdx.x, gridDim.x);
 }
 
-template <int BN, int WAVES, int BM = kTileM>
+template <int BN, int WAVES, int BM = kTileM, bool F32OUT = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_fp8_kernel(StreamArgs a) {
-  fp8_tile_body<BN, WAVES, BM>(a, blockIdx.x, gridDim.x);
+  fp8_tile_body<BN, WAVES, BM, F32OUT>(a, blockIdx.x, gridDim.x);
 }
 
 // FP8 weights and FP8 activations in 64-K steps, for K a multiple of 64 but
@@ -915,16 +1009,16 @@ __global__ __launch_bounds__(64 * WAVES, 1) void tile_gemm_f8f8_kernel(StreamArg
 // Several GEMMs of one weight dtype in one launch (a layer's projections, the
 // shards of a sharded product): workgroup x computes tile x - first[g] of
 // problem g, the g with first[g] <= x < first[g + 1].
-template <int BN, int WAVES, bool FP8>
+template <int BN, int WAVES, bool FP8, bool F32OUT = false>
 __global__ __launch_bounds__(64 * WAVES, 1) void tile_group_kernel(TileGroup tg) {
   const int64_t x = blockIdx.x;
   int g = 0;
   while (g + 1 < tg.n && x >= tg.first[g + 1]) ++g;
   g = __builtin_amdgcn_readfirstlane(g);  // one problem per workgroup
   if constexpr (FP8)
-    fp8_tile_body<BN, WAVES>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
+    fp8_tile_body<BN, WAVES, kTileM, F32OUT>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
   else
-    bf16_dstep_body<BN, WAVES, BN == 256 ? 2 : 3>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
+    bf16_dstep_body<BN, WAVES, BN == 256 ? 2 : 3, F32OUT>(tg.g[g], x - tg.first[g], tg.first[g + 1] - tg.first[g]);
 }
 
 int64_t tile_count(const StreamArgs& a, int bn, int bm = kTileM) {
@@ -949,20 +1043,33 @@ hipError_t launch_f8f8_ring(const StreamArgs& a, hipStream_t stream) {
 
 template <int BN, int WAVES, int NST>
 hipError_t launch_bf16d(const StreamArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tile_gemm_bf16d_kernel<BN, WAVES, NST>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  if (a.mode == OUT_F32)
+    hipLaunchKernelGGL((tile_gemm_bf16d_kernel<BN, WAVES, NST, true>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tile_gemm_bf16d_kernel<BN, WAVES, NST>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int BN, int WAVES>
 hipError_t launch_fp8(const StreamArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((tile_gemm_fp8_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  if (a.mode == OUT_F32)
+    hipLaunchKernelGGL((tile_gemm_fp8_kernel<BN, WAVES, kTileM, true>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
+  else
+    hipLaunchKernelGGL((tile_gemm_fp8_kernel<BN, WAVES>), tile_grid<BN>(a), dim3(64 * WAVES), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int BN, int WAVES, bool FP8>
 hipError_t launch_group(const TileGroup& tg, hipStream_t stream) {
-  hipLaunchKernelGGL((tile_group_kernel<BN, WAVES, FP8>), dim3(unsigned(tg.first[tg.n])), dim3(64 * WAVES), 0,
-                     stream, tg);
+  // the fp32-output instantiation when every problem of the group writes fp32
+  bool f32 = tg.n > 0;
+  for (int i = 0; i < tg.n; ++i) f32 = f32 && tg.g[i].mode == OUT_F32;
+  if (f32)
+    hipLaunchKernelGGL((tile_group_kernel<BN, WAVES, FP8, true>), dim3(unsigned(tg.first[tg.n])), dim3(64 * WAVES), 0,
+                       stream, tg);
+  else
+    hipLaunchKernelGGL((tile_group_kernel<BN, WAVES, FP8>), dim3(unsigned(tg.first[tg.n])), dim3(64 * WAVES), 0,
+                       stream, tg);
   return hipGetLastError();
 }
 
@@ -1127,7 +1234,11 @@ hipError_t launch_tile_gemm(const StreamArgs& a, int bn, bool fp8, hipStream_t s
         p2 = rows_from(p, rows1, 1, y_elem);
       }
       if (e == hipSuccess) {
-        hipLaunchKernelGGL((tile_gemm_fp8_kernel<256, 8, 128>), (tile_grid<256, 128>(p2)), dim3(512), 0, stream, p2);
+        if (p2.mode == OUT_F32)
+          hipLaunchKernelGGL((tile_gemm_fp8_kernel<256, 8, 128, true>), (tile_grid<256, 128>(p2)), dim3(512), 0, stream,
+                             p2);
+        else
+          hipLaunchKernelGGL((tile_gemm_fp8_kernel<256, 8, 128>), (tile_grid<256, 128>(p2)), dim3(512), 0, stream, p2);
         e = hipGetLastError();
       }
     } else

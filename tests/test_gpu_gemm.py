@@ -277,19 +277,21 @@ def test_tiled_prefill_parity(o, k, dt, m):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
-@pytest.mark.parametrize("o,pad", [(1000, 64), (1004, 64), (1000, 4)])
-def test_tiled_strided_output(o, pad, dt):
-    """Tiled kernels writing into Y rows of ldy = out + pad: with ldy a multiple
-    of 8 the outputs leave through LDS in 16-byte stores (out = 1004 ends in a
-    partial 8-column piece), otherwise one element per store.  Nothing past
+@pytest.mark.parametrize("o,pad,y_fp32", [(1000, 64, False), (1004, 64, False), (1000, 4, False),
+                                          (1000, 64, True), (1002, 62, True), (1000, 2, True)])
+def test_tiled_strided_output(o, pad, y_fp32, dt):
+    """Tiled kernels writing into Y rows of ldy = out + pad: with every row
+    16-byte aligned (ldy a multiple of 8 for BF16, of 4 for fp32) the outputs
+    leave through LDS in 16-byte stores (out = 1004 in BF16 and 1002 in fp32
+    end in a partial piece), otherwise one element per store.  Nothing past
     column out of a row is written."""
     k, m = 192, 300
-    note(f"tiled strided output o={o} pad={pad} {dt} m={m}")
+    note(f"tiled strided output o={o} pad={pad} y_fp32={y_fp32} {dt} m={m}")
     w = synth.weight(synth.seed_for(14, 3, o % 89), o, k, dt)
     x = synth.activations(synth.seed_for(14, 3, 50), m, k)
-    y = torch.full((m, o + pad), float("nan"), dtype=torch.bfloat16, device=DEV)
+    y = torch.full((m, o + pad), float("nan"), dtype=torch.float32 if y_fp32 else torch.bfloat16, device=DEV)
     swr.proj_forward(u8(w.raw()), dt, f32(w.scale) if w.scale is not None else None, o, k, bf16(x), y, m=m,
-                     ldx=k, ldy=o + pad)
+                     ldx=k, ldy=o + pad, y_fp32=y_fp32)
     torch.cuda.synchronize()
     yv = values(y)
     assert np.isnan(yv[:, o:]).all(), "columns past out_f were written"
