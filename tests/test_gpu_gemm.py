@@ -300,6 +300,21 @@ def test_tiled_strided_output(o, pad, y_fp32, dt):
 
 
 @pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
+def test_tiled_fp32_output_large(dt):
+    """fp32 outputs at 4096 tokens x 6144 rows: for FP8 weights the first 4096
+    rows run as a whole wave of 256 x 256 tiles and the last 2048 as
+    128-token tiles, both through the fp32 LDS epilogue; for BF16 weights
+    256 x 128 tiles.  Every output is checked."""
+    o, k, m = 6144, 512, 4096
+    note(f"tiled fp32 output o={o} k={k} {dt} m={m}")
+    w = synth.weight(synth.seed_for(14, 4, 0), o, k, dt)
+    x = synth.activations(synth.seed_for(14, 4, 50), m, k)
+    y = values(_run_proj(w, x, y_fp32=True))
+    ref = gemm.proj_f64(x, w.raw(), dt, o, k, w.scale)
+    assert_close_rows(y, ref, what=f"tiled fp32 {o}x{k} {dt} m={m}")
+
+
+@pytest.mark.parametrize("dt", [synth.BF16, synth.FP8])
 def test_tiled_last_wave_in_half_tiles(dt):
     """2048 tokens x 16484 rows: 8 x 65 = 520 tiles of 256 x 256, a last wave
     of 8 on 256 CUs, so the first 16384 rows run as 512 full tiles and the
