@@ -152,18 +152,18 @@ __device__ inline void tile_epilogue(const StreamArgs& a, const f32x16 (&acc)[TM
 // row), then reads back 16-byte pieces of rows and stores them.  BF16 outputs
 // (plain or SiLU * up); the caller checks that every output row starts
 // 16-byte aligned.  The region holds TM * 32 rows of TN * 32 columns.
-template <int BN, int WN, int TM, int TN>
-__device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t tile_n,
-                                         int wm, int wn, int r32, int kg, int lane, uint8_t* region,
-                                         const float* lds_scale, const float* lds_tscale) {
-  const bool silu_mode = a.mode == OUT_SILU_BF16;
+template <int BN, int WN, int TM, int TN, bool SILU>
+__device__ inline void tile_epilogue_lds_m(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0,
+                                           int64_t tile_n, int wm, int wn, int r32, int kg, int lane, uint8_t* region,
+                                           const float* lds_scale, const float* lds_tscale) {
+  constexpr bool silu_mode = SILU;
   constexpr int ROWS = TM * 32;
   // output columns of the block: TN * 32, or TN * 16 in SiLU mode; 16-byte pieces per row
-  const int cols = silu_mode ? TN * 16 : TN * 32;
-  const int cpr = cols / 8;
+  constexpr int cols = silu_mode ? TN * 16 : TN * 32;
+  constexpr int cpr = cols / 8;
   const int64_t limit = silu_mode ? a.inter : a.rows;
   const int64_t col0 = silu_mode ? tile_n * (BN / 2) + wn * (WN / 2) : tile_n * BN + wn * WN;
-  const int tn_out = silu_mode ? TN / 2 : TN;
+  constexpr int tn_out = silu_mode ? TN / 2 : TN;
   auto pos = [&](int row, int col) { return row * cols * 2 + (((col >> 3) ^ (row & (cpr - 1))) << 4) + (col & 7) * 2; };
 #pragma unroll
   for (int y = 0; y < TN; ++y) {
@@ -178,7 +178,7 @@ __device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc
         const int row = x * 32 + 8 * (v / 4) + 4 * kg + (v % 4);
         const float ts = lds_tscale ? lds_tscale[wm * ROWS + row] : 1.f;
         float out = acc[x][y][v] * ts * sc;
-        if (silu_mode) out = silu_tile(out) * (acc[x][y + TN / 2][v] * ts * su);
+        if constexpr (silu_mode) out = silu_tile(out) * (acc[x][y + TN / 2][v] * ts * su);
         *reinterpret_cast<uint16_t*>(region + pos(row, y * 32 + r32)) = bf16_bits(out);
       }
     }
@@ -186,8 +186,11 @@ __device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
   __builtin_amdgcn_wave_barrier();
   uint16_t* Y = static_cast<uint16_t*>(a.Y);
-  const int pieces = ROWS * cpr;
-  for (int q = lane; q < pieces; q += 64) {
+  constexpr int pieces = ROWS * cpr;
+  static_assert(pieces % 64 == 0, "whole passes of the wave over the block's pieces");
+#pragma unroll
+  for (int q0 = 0; q0 < pieces; q0 += 64) {
+    const int q = q0 + lane;
     const int row = q / cpr, cp = q % cpr;
     const int64_t m = m0 + wm * ROWS + row;
     const int64_t col = col0 + cp * 8;
@@ -200,6 +203,21 @@ __device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc
       for (int e = 0; e < 8 && col + e < limit; ++e) Y[m * a.ldy + col + e] = h[e];
     }
   }
+}
+
+// The LDS epilogue with the output mode (SiLU * up, or plain BF16) fixed at
+// compile time, so that neither mode computes the other's outputs and the
+// swizzled LDS offsets fold into immediates.
+template <int BN, int WN, int TM, int TN>
+__device__ inline void tile_epilogue_lds(const StreamArgs& a, const f32x16 (&acc)[TM][TN], int64_t m0, int64_t tile_n,
+                                         int wm, int wn, int r32, int kg, int lane, uint8_t* region,
+                                         const float* lds_scale, const float* lds_tscale) {
+  if (a.mode == OUT_SILU_BF16)
+    tile_epilogue_lds_m<BN, WN, TM, TN, true>(a, acc, m0, tile_n, wm, wn, r32, kg, lane, region, lds_scale,
+                                              lds_tscale);
+  else
+    tile_epilogue_lds_m<BN, WN, TM, TN, false>(a, acc, m0, tile_n, wm, wn, r32, kg, lane, region, lds_scale,
+                                               lds_tscale);
 }
 
 // As tile_epilogue_lds, for fp32 outputs (F32 = true; the split-K
