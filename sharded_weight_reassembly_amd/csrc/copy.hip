@@ -16,16 +16,27 @@ constexpr int kThreads = 256;
 // weight_sharding, flat layout step 3: after the gather every rank holds the
 // whole T, i.e. slot[i*C, (i+1)*C) = chunk_i.  Grid: (blocks per chunk, N).
 // Each workgroup copies one 32 KiB span of one chunk in a single round of
-// 16-byte nontemporal loads (8 per thread, all in flight) and stores; many
+// 16-byte loads (8 per thread, all in flight) and stores; many
 // short-lived workgroups keep more bytes in flight per CU than long loops
 // (measured on MI355X: 6.45 TB/s of read+write against 5.5 TB/s for
 // 64-128 KiB spans).
+//
+// The slot is written for the GEMMs that read it next.  Workgroups are
+// dispatched in grid order, so chunk y of the grid is chunk N-1-y of T: the
+// front of the slot, where a layer's first weights sit, is written last.
+// The stores carry no streaming hint, so those most recent lines are still
+// in the 256 MB last-level cache when the first GEMM starts, and their
+// write-back to HBM overlaps that GEMM.  Measured on the shared-expert
+// decode stack (8 layers of 264 MB): 1.8-2.8% less wall time per forward at
+// every token count than streaming stores in chunk order; streaming stores
+// in reverse order gained nothing, cached stores in chunk order lost 1.5%
+// at 64 tokens.  The chunks are read once per gather: their loads stream.
 constexpr int kCopyUnroll = 8;
 constexpr int64_t kCopySpanVecs = 256 * kCopyUnroll;  // 32 KiB per workgroup
 
 __global__ __launch_bounds__(kThreads) void reassemble_kernel(ChunkPtrs chunks, u32x4* __restrict__ slot,
                                                               int64_t chunk_vecs, int64_t span_vecs) {
-  const int c = blockIdx.y;
+  const int c = int(gridDim.y) - 1 - int(blockIdx.y);
   const u32x4* __restrict__ src = static_cast<const u32x4*>(chunks.p[c]);
   u32x4* __restrict__ dst = slot + int64_t(c) * chunk_vecs;
   const int64_t step = int64_t(kThreads) * kCopyUnroll;
@@ -39,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void reassemble_kernel(ChunkPtrs chunks, 
 #pragma unroll
       for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
 #pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], dst + i + u * kThreads);
+      for (int u = 0; u < kCopyUnroll; ++u) dst[i + u * kThreads] = v[u];
     }
     for (; i < end; i += kThreads) dst[i] = src[i];
   }
